@@ -1,0 +1,7 @@
+"""Low-bit weight-only matmul for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``liblowbit.so`` (hand-written HIP kernels behind a C
+ABI declared in ``include/lowbit.h``); this package is a thin ctypes binding
+with the same entry-point names.  PyTorch is used only for device memory and
+streams.  ``synth`` draws the seeded synthetic workloads.
+"""

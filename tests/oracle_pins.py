@@ -1,0 +1,499 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``check_*`` takes one build of the oracle (``oracle.Oracle``) and raises
+AssertionError on a mismatch.  They use only:
+  * values written out by hand in ``tests/golden`` (cited there);
+  * library routines (numpy float16, torch bfloat16 / float8 decodes,
+    numpy float64 matmul) on the cases that reduce to them;
+  * exact rational arithmetic (``fractions.Fraction``) on tiny inputs;
+  * invariants of the definitions (one-hot input, all codes at the zero
+    point, power-of-two scaling, K split at a group boundary, routing
+    bookkeeping).
+``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+runs them on copies of the oracle with a planted mistake and expects a failure.
+"""
+import json
+import os
+from fractions import Fraction as F
+
+import numpy as np
+import torch
+
+from bit_weight_only_pack_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _hex(s):
+    return int(s, 16)
+
+
+def _np_f16_bits(v):
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def _same_or_both_nan(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nan = np.isnan(a) & np.isnan(b)
+    same = a.view(np.uint64) == b.view(np.uint64)
+    return bool(np.all(nan | same))
+
+
+def _frac_f16(bits):
+    """Exact value of fp16 bit patterns via numpy's decode."""
+    return [F(float(v)) for v in np.asarray(bits, np.uint16).view(np.float16).astype(np.float64).ravel()]
+
+
+def _torch_bf16_to_f64(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def _torch_e4m3_to_f64(b):
+    t = torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _torch_ue8m0_to_f64(b):
+    t = torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e8m0fnu)
+    return t.to(torch.float64).numpy()
+
+
+def _pack_codes(codes):
+    """codes u8 [N][K] -> bytes [N][K/2], low nibble = even k (the page's order)."""
+    codes = np.asarray(codes, np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+# ------------------------------------------------------------------ formats
+def check_f16_decode(o):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert _same_or_both_nan(o.f16_to_double(bits), ref), "fp16 decode differs from numpy"
+
+
+def check_f16_encode(o):
+    finite = np.arange(0, 0x7c00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (finite[:-1] + finite[1:]) / 2.0                   # exact ties
+    near = np.concatenate([mids * (1 + 2.0 ** -40), mids * (1 - 2.0 ** -40)])
+    r = np.random.default_rng(11)
+    rand = np.exp2(r.uniform(-30, 17, 20000)) * r.choice([-1.0, 1.0], 20000)
+    edge = np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e6, 2.0 ** -25, 3 * 2.0 ** -26,
+                     2.0 ** -24, 2.0 ** -14 - 2.0 ** -25, 0.0, -0.0, np.inf, -np.inf])
+    v = np.concatenate([finite, -finite, mids, -mids, near, rand, edge])
+    got = o.double_to_f16(v)
+    ref = _np_f16_bits(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "fp16 RNE differs from numpy at %r" % (v[bad[:5]],)
+
+
+def check_bf16_decode(o):
+    bits = np.arange(65536, dtype=np.uint16)
+    assert _same_or_both_nan(o.bf16_to_double(bits), _torch_bf16_to_f64(bits)), "bf16 decode differs from torch"
+
+
+def check_bf16_encode(o):
+    allb = np.arange(65536, dtype=np.uint16)
+    vals = _torch_bf16_to_f64(allb)
+    fin = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    mids = (fin[:-1] + fin[1:]) / 2.0                         # 9 significant bits: exact in fp32
+    r = np.random.default_rng(12)
+    rand = (np.exp2(r.uniform(-130, 127, 20000)) * r.choice([-1.0, 1.0], 20000)).astype(np.float32)
+    v = np.concatenate([fin, -fin, mids, -mids, rand.astype(np.float64)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = o.double_to_bf16(v.astype(np.float64))
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "bf16 RNE differs from torch at %r" % (v[bad[:5]],)
+
+
+def check_e4m3_decode(o):
+    b = np.arange(256, dtype=np.uint8)
+    assert _same_or_both_nan(o.e4m3_to_double(b), _torch_e4m3_to_f64(b)), "E4M3 decode differs from torch"
+
+
+def check_ue8m0_decode(o):
+    b = np.arange(256, dtype=np.uint8)
+    assert _same_or_both_nan(o.ue8m0_to_double(b), _torch_ue8m0_to_f64(b)), "UE8M0 decode differs from torch"
+
+
+# ------------------------------------------------------------------ INT4: hand-worked values
+def check_hand_bytes(o):
+    g = _golden("w4_hand_examples.json")
+    for scale_hex, frac in g["fp16_scales"].items():
+        assert F(float(o.f16_to_double(np.array([_hex(scale_hex)], np.uint16))[0])) == F(frac), scale_hex
+    for ex in g["bytes"]:
+        q = np.array([[_hex(ex["byte"])]], np.uint8)
+        assert list(o.w4_unpack(q)[0]) == ex["codes"], ex["name"]
+        s = np.array([[_hex(ex["scale"])]], np.uint16)
+        z = None if ex["zero"] == 8 else np.array([[ex["zero"]]], np.int8)
+        w = o.w4_dequant(q, s, z, 2)[0]
+        assert [F(float(v)) for v in w] == [F(t) for t in ex["w"]], ex["name"]
+        assert [F(float(v)) for v in w] == [F(t) for t in ex["w_decimal"]], ex["name"]
+
+
+def check_sixteen_codes(o):
+    g = _golden("w4_hand_examples.json")["sixteen_codes"]
+    codes = np.arange(16, dtype=np.uint8)[None, :]
+    q = _pack_codes(codes)
+    s = np.array([[_hex(g["scale"])]], np.uint16)
+    w8 = o.w4_dequant(q, s, None, 16)[0]
+    assert [F(float(v)) for v in w8] == [F(t) for t in g["z8_decimal"]], "16-code identity, z=8"
+    w5 = o.w4_dequant(q, s, np.array([[5]], np.int8), 16)[0]
+    sv = F(1311, 131072)
+    assert [F(float(v)) for v in w5] == [(c - 5) * sv for c in range(16)], "16-code identity, z=5"
+
+
+def check_dequant_exact_all_scales(o):
+    """(q - z) * s is exact in fp32 for every finite fp16 scale, every code and
+    zero points over the int8 range: compare with the float64 product, which
+    is exact here (<= 19 significant bits)."""
+    sc = np.arange(0, 0x7c00, dtype=np.uint16)
+    sc = np.concatenate([sc, sc | 0x8000])
+    n = sc.size
+    r = np.random.default_rng(13)
+    K = 16
+    codes = np.tile(np.arange(16, dtype=np.uint8), (n, 1))
+    zeros = r.integers(-128, 128, size=(n, 1)).astype(np.int8)
+    w = o.w4_dequant(_pack_codes(codes), sc[:, None], zeros, K)
+    ref = (codes.astype(np.float64) - zeros.astype(np.float64)) * sc.view(np.float16).astype(np.float64)[:, None]
+    assert np.array_equal(w.astype(np.float64), ref), "dequant not exact"
+    wsym = o.w4_dequant(_pack_codes(codes), sc[:, None], None, K)
+    refsym = (codes.astype(np.float64) - 8.0) * sc.view(np.float16).astype(np.float64)[:, None]
+    assert np.array_equal(wsym.astype(np.float64), refsym), "symmetric dequant not exact"
+
+
+def check_fp16_tie(o):
+    t = _golden("w4_hand_examples.json")["fp16_rounding_tie"]
+    q = _pack_codes(np.array([[t["code"], 0]], np.uint8))
+    s = np.array([[_hex(t["scale"])]], np.uint16)
+    w = o.w4_dequant(q, s, None, 2)[0, 0]
+    assert F(float(w)) == F(t["w_exact"])
+    h = o.double_to_f16(np.array([float(w)]))
+    assert F(float(o.f16_to_double(h)[0])) == F(t["w_f16_rne"]), "tie must round to even"
+
+
+def check_gemv_2x4(o):
+    g = _golden("w4_hand_examples.json")["gemv_2x4"]
+    q = np.array([[_hex(b) for b in row] for row in g["qweight"]], np.uint8)
+    s = np.array([[_hex(b) for b in row] for row in g["scales"]], np.uint16)
+    x = np.array([float(F(v)) for v in g["x"]], np.float16)[None, :]
+    for key in ("symmetric", "asymmetric"):
+        case = g[key]
+        z = None if key == "symmetric" else np.array(case["zeros"], np.int8)
+        W = o.w4_dequant(q, s, z, 2)
+        assert [[F(float(v)) for v in row] for row in W] == [[F(v) for v in row] for row in case["W"]], key
+        y64, yb = o.w4_matmul(x, "f16", q, s, z, 2, "f16")
+        assert [F(float(v)) for v in y64[0]] == [F(v) for v in case["y"]], key
+        assert np.array_equal(yb[0], _np_f16_bits([float(F(v)) for v in case["y"]])), key
+
+
+# ------------------------------------------------------------------ INT4: brute force and invariants
+def _exact_matmul(x_frac, codes, zeros, s_frac, G):
+    """Exact rational y[m][n] = sum_k x[m][k] * (q - z) * s over Python Fractions."""
+    M, K = len(x_frac), len(x_frac[0])
+    N = codes.shape[0]
+    out = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = F(0)
+            mag = F(0)
+            for k in range(K):
+                z = 8 if zeros is None else int(zeros[n, k // G])
+                t = x_frac[m][k] * (int(codes[n, k]) - z) * s_frac[n][k // G]
+                acc += t
+                mag += abs(t)
+            row.append((acc, mag))
+        out.append(row)
+    return out
+
+
+def _check_bruteforce_case(o, M, N, K, G, x_dtype, out_dtype, asym, seed):
+    r = np.random.default_rng(seed)
+    codes = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    q = _pack_codes(codes)
+    s_bits = r.uniform(0.002, 0.05, size=(N, K // G)).astype(np.float16).view(np.uint16)
+    s_bits[0, 0] = 0x0203                                      # an fp16 subnormal scale
+    zeros = r.integers(-128, 128, size=(N, K // G)).astype(np.int8) if asym else None
+    xv = r.standard_normal((M, K)) * 3
+    if x_dtype == "f16":
+        xb = xv.astype(np.float16).view(np.uint16)
+        xf = [[F(float(v)) for v in row] for row in xb.view(np.float16).astype(np.float64)]
+    else:
+        xb = torch.from_numpy(xv.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        xf = [[F(float(v)) for v in row] for row in _torch_bf16_to_f64(xb)]
+    sf = [_frac_f16(row) for row in s_bits]
+    exact = _exact_matmul(xf, codes, zeros, sf, G)
+    y64, yb = o.w4_matmul(xb, x_dtype, q, s_bits, zeros, G, out_dtype)
+    for m in range(M):
+        for n in range(N):
+            e, mag = exact[m][n]
+            bound = (K + 1) * F(1, 2 ** 53) * mag
+            assert abs(F(float(y64[m, n])) - e) <= bound, ("sum", M, N, K, G, m, n)
+            if out_dtype == "f16":
+                ref_bits = _np_f16_bits([float(e)])[0]
+            else:
+                ref_bits = o.double_to_bf16(np.array([float(e)]))[0]
+            assert yb[m, n] == ref_bits, ("rounding", M, N, K, G, m, n)
+
+
+def check_bruteforce_tiny(o):
+    _check_bruteforce_case(o, 1, 5, 8, 2, "f16", "f16", False, 1)
+    _check_bruteforce_case(o, 3, 7, 64, 32, "f16", "f16", True, 2)
+    _check_bruteforce_case(o, 2, 9, 96, 32, "bf16", "bf16", False, 3)
+    _check_bruteforce_case(o, 2, 4, 128, 64, "bf16", "bf16", True, 4)
+    _check_bruteforce_case(o, 1, 3, 256, 128, "f16", "f16", True, 5)
+
+
+def check_bruteforce_tiny_gemv_workload(o):
+    """All 65,536 terms of the tiny GEMV workload (M=1, K=256, N=256, G=32,
+    symmetric) against exact rationals."""
+    w = synth.w4_weights(256, 256, 32, scale_range=(0.005, 0.02), workload_id=0)
+    x = synth.activations_f16(1, 256, workload_id=0)
+    codes = np.empty((256, 256), np.uint8)
+    codes[:, 0::2] = w["qweight"] & 0xF
+    codes[:, 1::2] = w["qweight"] >> 4
+    xf = [[F(float(v)) for v in x[0].astype(np.float64)]]
+    sf = [_frac_f16(row) for row in w["scales"].view(np.uint16)]
+    exact = _exact_matmul(xf, codes, None, sf, 32)
+    y64, yb = o.w4_matmul(x, "f16", w["qweight"], w["scales"], None, 32, "f16")
+    for n in range(256):
+        e, mag = exact[0][n]
+        assert abs(F(float(y64[0, n])) - e) <= 257 * F(1, 2 ** 53) * mag, n
+        assert yb[0, n] == _np_f16_bits([float(e)])[0], n
+
+
+def _random_w4(r, N, K, G, asym):
+    codes = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = r.uniform(0.002, 0.02, size=(N, K // G)).astype(np.float16)
+    z = r.integers(0, 16, size=(N, K // G)).astype(np.int8) if asym else None
+    return codes, _pack_codes(codes), s, z
+
+
+def check_numpy_matmul(o):
+    """Oracle product == numpy float64 matmul of the (pinned) dequantized W."""
+    r = np.random.default_rng(21)
+    for (M, N, K, G, asym, xd) in ((3, 48, 256, 32, True, "f16"), (5, 40, 384, 128, False, "bf16"),
+                                   (1, 96, 512, 64, True, "f16")):
+        codes, q, s, z = _random_w4(r, N, K, G, asym)
+        xv = r.standard_normal((M, K))
+        if xd == "f16":
+            xb = xv.astype(np.float16)
+            x64 = xb.astype(np.float64)
+        else:
+            xb = torch.from_numpy(xv.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            x64 = _torch_bf16_to_f64(xb)
+        W = o.w4_dequant(q, s, z, G).astype(np.float64)
+        ref = x64 @ W.T
+        y64, _ = o.w4_matmul(xb, xd, q, s, z, G, "f16")
+        err = np.max(np.abs(y64 - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-12, ("numpy matmul", M, N, K, G, err)
+
+
+def check_one_hot(o):
+    r = np.random.default_rng(22)
+    N, K, G = 32, 128, 32
+    codes, q, s, z = _random_w4(r, N, K, G, True)
+    W = o.w4_dequant(q, s, z, G)
+    for k in (0, 1, 37, 127):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 1.0
+        y64, yb = o.w4_matmul(x, "f16", q, s, z, G, "f16")
+        assert np.array_equal(y64[0], W[:, k].astype(np.float64)), k
+        assert np.array_equal(yb[0], W[:, k].astype(np.float16).view(np.uint16)), k
+
+
+def check_codes_at_zero_point(o):
+    r = np.random.default_rng(23)
+    N, K, G = 16, 128, 32
+    z = r.integers(0, 16, size=(N, K // G)).astype(np.int8)
+    codes = np.repeat(z.astype(np.uint8), G, axis=1)
+    s = r.uniform(0.002, 0.02, size=(N, K // G)).astype(np.float16)
+    x = r.standard_normal((2, K)).astype(np.float16)
+    y64, _ = o.w4_matmul(x, "f16", _pack_codes(codes), s, z, G, "f16")
+    assert np.all(y64 == 0.0), "codes at the zero point must give 0 (asym)"
+    codes8 = np.full((N, K), 8, np.uint8)
+    y64, _ = o.w4_matmul(x, "f16", _pack_codes(codes8), s, None, G, "f16")
+    assert np.all(y64 == 0.0), "code 8 must give 0 (sym)"
+
+
+def check_pow2_scaling(o):
+    r = np.random.default_rng(24)
+    N, K, G = 24, 256, 64
+    codes, q, s, z = _random_w4(r, N, K, G, True)
+    x = np.clip(r.standard_normal((2, K)), -4, 4)
+    x = np.where(np.abs(x) < 0.05, 0.5, x).astype(np.float16)
+    y0, _ = o.w4_matmul(x, "f16", q, s, z, G, "f16")
+    for j in (-3, 5):
+        xs = (x.astype(np.float64) * 2.0 ** j).astype(np.float16)
+        assert np.array_equal(xs.astype(np.float64), x.astype(np.float64) * 2.0 ** j)
+        yj, _ = o.w4_matmul(xs, "f16", q, s, z, G, "f16")
+        assert np.array_equal(yj, y0 * 2.0 ** j), j
+
+
+def check_k_split(o):
+    r = np.random.default_rng(25)
+    N, K, G = 20, 512, 128
+    codes, q, s, z = _random_w4(r, N, K, G, True)
+    x = r.standard_normal((2, K)).astype(np.float16)
+    y, _ = o.w4_matmul(x, "f16", q, s, z, G, "f16")
+    h = 256
+    y1, _ = o.w4_matmul(x[:, :h], "f16", q[:, :h // 2], s[:, :h // G], z[:, :h // G], G, "f16")
+    y2, _ = o.w4_matmul(x[:, h:], "f16", q[:, h // 2:], s[:, h // G:], z[:, h // G:], G, "f16")
+    assert np.max(np.abs(y - (y1 + y2))) <= 1e-12 * np.max(np.abs(y)), "K split at a group boundary"
+
+
+def check_rows_subset(o):
+    r = np.random.default_rng(26)
+    N, K, G = 16, 256, 128
+    codes, q, s, z = _random_w4(r, N, K, G, False)
+    xv = r.standard_normal((9, K)).astype(np.float32)
+    xb = torch.from_numpy(xv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    y64, yb = o.w4_matmul(xb, "bf16", q, s, z, G, "bf16")
+    rows = np.array([8, 0, 3])
+    r64, rb = o.w4_matmul_rows(xb, "bf16", q, s, z, G, "bf16", rows)
+    assert np.array_equal(r64, y64[rows]) and np.array_equal(rb, yb[rows])
+
+
+# ------------------------------------------------------------------ LUT3 / MXFP8 / MoE
+def check_lut3_hand(o):
+    g = _golden("lut3_hand_example.json")
+    b = np.array([_hex(k) for k in g["e4m3"]], np.uint8)
+    got = o.e4m3_to_double(b)
+    assert [F(float(v)) for v in got] == [F(v) for v in g["e4m3"].values()], "E4M3 hand values"
+    E, N, K = 1, 8, 64
+    cb = np.zeros((E, N // 8, K // 64, 8), np.uint8)
+    cb[0, 0, 0, :] = [_hex(c) for c in g["codebook"]]
+    ex = np.full((E, N // 8, K // 64), g["tile_exponent"], np.uint8)
+    idx = np.full((E, N, K), 4, np.uint8)
+    idx[0, 0, :8] = np.arange(8)
+    w = o.lut3_dequant(idx, cb, ex)
+    want = [F(g["decoded_weights"][str(i)]) for i in range(8)]
+    assert [F(float(v)) for v in w[0, 0, :8]] == want, "decoded codebook entries"
+    # the dot product of the worked example
+    idx2 = np.full((E, N, K), 4, np.uint8)
+    idx2[0, 0, 0], idx2[0, 0, 1] = 2, 6
+    aq = np.zeros((1, K), np.uint8)
+    aq[0, 0], aq[0, 1] = [_hex(v) for v in g["activation"]["bytes"]]
+    as_ = np.array([[g["activation"]["block_scale"], 127]], np.uint8)
+    y64, ob = o.moe_gemm(idx2, cb, ex, aq, as_, 1, np.array([[0]], np.int32))
+    assert F(float(y64[0, 0])) == F(g["dot"]["y_exact"]), "worked dot product"
+    want_bits = torch.tensor([float(F(g["dot"]["y_bf16_rne"]))], dtype=torch.float32) \
+        .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0]
+    assert ob[0, 0] == want_bits, "worked dot product, bf16"
+
+
+def _lut_fracs(idx, cb, ex):
+    """Exact rational decoded weights via torch E4M3 decode and 2^(e-127)."""
+    E, N, K = idx.shape
+    cbv = _torch_e4m3_to_f64(cb.ravel()).reshape(cb.shape)
+    out = np.empty((E, N, K), dtype=object)
+    for e in range(E):
+        for n in range(N):
+            for k in range(K):
+                out[e, n, k] = F(float(cbv[e, n // 8, k // 64, idx[e, n, k]])) * F(2) ** (int(ex[e, n // 8, k // 64]) - 127)
+    return out
+
+
+def check_lut3_bruteforce(o):
+    d = synth.lut3_weights(3, 16, 128, workload_id=90)
+    want = _lut_fracs(d["idx"], d["cb"], d["ex"])
+    got = o.lut3_dequant(d["idx"], d["cb"], d["ex"])
+    assert all(F(float(g)) == w for g, w in zip(got.ravel(), want.ravel())), "LUT3 decode"
+
+
+def _moe_exact(o, d, aq, as_, a_row_div, topk, emap):
+    E, N, K = d["idx"].shape
+    W = _lut_fracs(d["idx"], d["cb"], d["ex"])
+    av = _torch_e4m3_to_f64(aq.ravel()).reshape(aq.shape)
+    T, top_k = topk.shape
+    y64, ob = o.moe_gemm(d["idx"], d["cb"], d["ex"], aq, as_, a_row_div, topk, emap)
+    for sid in range(T * top_k):
+        g = int(topk.ravel()[sid])
+        e = g if emap is None else int(emap[g])
+        row = sid // a_row_div
+        a = [F(float(av[row, k])) * F(2) ** (int(as_[row, k // 32]) - 127) for k in range(K)]
+        for n in range(N):
+            if e < 0:
+                assert y64[sid, n] == 0.0 and ob[sid, n] == 0, ("EP zero", sid, n)
+                continue
+            terms = [a[k] * W[e, n, k] for k in range(K)]
+            ex_ = sum(terms, F(0))
+            mag = sum((abs(t) for t in terms), F(0))
+            assert abs(F(float(y64[sid, n])) - ex_) <= (K + 1) * F(1, 2 ** 53) * mag, ("moe sum", sid, n)
+            assert ob[sid, n] == o.double_to_bf16(np.array([float(ex_)]))[0], ("moe bf16", sid, n)
+
+
+def check_moe_bruteforce(o):
+    E, T, top_k, N, K = 4, 3, 2, 8, 64
+    d = synth.lut3_weights(E, N, K, workload_id=91)
+    topk = synth.moe_routing(T, E, top_k, workload_id=91)
+    emap = np.array([0, 1, -1, 2], np.int32)                  # expert 2 not local
+    d_local = dict(idx=d["idx"][[0, 1, 3]], cb=d["cb"][[0, 1, 3]], ex=d["ex"][[0, 1, 3]])
+    aq, as_ = synth.mxfp8_activations(T, K, workload_id=91)    # gate/up style: row = token
+    _moe_exact(o, d_local, aq, as_, top_k, topk, emap)
+    aq2, as2 = synth.mxfp8_activations(T * top_k, K, workload_id=92)  # down style: row = slot
+    _moe_exact(o, d, aq2, as2, 1, topk, None)
+
+
+def check_moe_numpy(o):
+    E, T, top_k, N, K = 8, 16, 2, 32, 256
+    d = synth.lut3_weights(E, N, K, workload_id=93)
+    topk = synth.moe_routing(T, E, top_k, workload_id=93)
+    aq, as_ = synth.mxfp8_activations(T, K, workload_id=93)
+    W = o.lut3_dequant(d["idx"], d["cb"], d["ex"])
+    a = _torch_e4m3_to_f64(aq.ravel()).reshape(T, K) * np.exp2(np.repeat(as_.astype(np.float64) - 127, 32, axis=1))
+    y64, _ = o.moe_gemm(d["idx"], d["cb"], d["ex"], aq, as_, top_k, topk)
+    for sid in range(T * top_k):
+        ref = W[topk.ravel()[sid]] @ a[sid // top_k]
+        err = np.max(np.abs(y64[sid] - ref)) / max(np.max(np.abs(ref)), 1e-300)
+        assert err <= 1e-12, ("moe numpy", sid, err)
+
+
+def check_moe_align(o):
+    r = np.random.default_rng(31)
+    for (T, E, top_k, bm, use_map) in ((64, 16, 4, 16, False), (37, 12, 3, 32, True), (5, 64, 8, 16, True)):
+        topk = np.stack([r.choice(E, size=top_k, replace=False) for _ in range(T)]).astype(np.int32)
+        emap = None
+        if use_map:
+            emap = np.full(E, -1, np.int32)
+            loc = np.sort(r.choice(E, size=E // 3, replace=False))
+            emap[loc] = np.arange(loc.size, dtype=np.int32)
+        ids, blk, P = o.moe_align(topk, E, bm, emap)
+        nv = T * top_k
+        flat = topk.ravel()
+        assert P % bm == 0 and ids.size == P and blk.size == P // bm
+        counts = np.bincount(flat, minlength=E)
+        assert P == int(np.sum((counts + bm - 1) // bm * bm)), "padded length"
+        assert sorted(ids[ids < nv].tolist()) == list(range(nv)), "every slot exactly once"
+        assert np.all((ids <= nv) & (ids >= 0)), "ids are slots or the sentinel"
+        pos = 0
+        for e in range(E):
+            c = int(counts[e])
+            if c == 0:
+                continue
+            seg = ids[pos:pos + (c + bm - 1) // bm * bm]
+            assert np.all(seg[:c] < nv) and np.all(flat[seg[:c]] == e), ("expert segment", e)
+            assert np.all(np.diff(seg[:c]) > 0), ("ascending within expert", e)
+            assert np.all(seg[c:] == nv), ("sentinel padding", e)
+            want = e if emap is None else int(emap[e])
+            assert np.all(blk[pos // bm:(pos + seg.size) // bm] == want), ("block expert", e)
+            pos += seg.size
+        assert pos == P
+
+
+ALL_CHECKS = [
+    check_f16_decode, check_f16_encode, check_bf16_decode, check_bf16_encode,
+    check_e4m3_decode, check_ue8m0_decode,
+    check_hand_bytes, check_sixteen_codes, check_dequant_exact_all_scales, check_fp16_tie, check_gemv_2x4,
+    check_bruteforce_tiny, check_bruteforce_tiny_gemv_workload, check_numpy_matmul, check_one_hot,
+    check_codes_at_zero_point, check_pow2_scaling, check_k_split, check_rows_subset,
+    check_lut3_hand, check_lut3_bruteforce, check_moe_bruteforce, check_moe_numpy, check_moe_align,
+]
