@@ -1,0 +1,138 @@
+"""ctypes binding of liblowbit.so: one Python function per C entry point, same
+name, same argument order.  Marshalling only -- every step of the computation
+runs in the library's HIP kernels.
+
+Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw integer
+address, or None (NULL).  ``stream=None`` means torch's current stream on the
+current device.  Functions return the library's int status code unchanged;
+``check(status)`` raises LowbitError for a non-zero one.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblowbit.so")
+
+LOWBIT_OK = 0
+LOWBIT_E_INVALID_ARG = 1
+LOWBIT_E_UNSUPPORTED = 2
+LOWBIT_E_WORKSPACE = 3
+LOWBIT_E_HIP = 4
+
+LOWBIT_W4_SYM = 0
+LOWBIT_W4_ASYM = 1
+LOWBIT_LUT3_E4M3 = 2
+
+LOWBIT_F16 = 0
+LOWBIT_BF16 = 1
+
+LOWBIT_OP_GEMV = 0
+LOWBIT_OP_GEMM = 1
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/lowbit.h
+SIGNATURES = {
+    "lowbit_strerror": (ctypes.c_char_p, [_i]),
+    "lowbit_last_hip_error": (_i, []),
+    "lowbit_version": (_i, []),
+    "lowbit_packed_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "lowbit_pack_weights": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lowbit_unpack_weights": (_i, [_i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp]),
+    "lowbit_dequant": (_i, [_i, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status):
+        msg = lib().lowbit_strerror(status).decode()
+        if status == LOWBIT_E_HIP:
+            msg += " (hipError %d)" % lib().lowbit_last_hip_error()
+        super().__init__("lowbit status %d: %s" % (status, msg))
+        self.status = status
+
+
+def lib():
+    """Load liblowbit.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("liblowbit.so is not built (%s); run python -m bit_weight_only_pack_amd.build"
+                               % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status):
+    if status != LOWBIT_OK:
+        raise LowbitError(status)
+    return status
+
+
+def _ptr(p):
+    if p is None:
+        return None
+    if isinstance(p, int):
+        return p
+    return p.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        if torch.cuda.is_available() and torch.cuda.is_initialized():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def lowbit_strerror(status):
+    return lib().lowbit_strerror(status).decode()
+
+
+def lowbit_last_hip_error():
+    return lib().lowbit_last_hip_error()
+
+
+def lowbit_version():
+    return lib().lowbit_version()
+
+
+def lowbit_packed_bytes(fmt, E, N, K, group_size):
+    return lib().lowbit_packed_bytes(fmt, E, N, K, group_size)
+
+
+def lowbit_pack_weights(fmt, E, N, K, group_size, codes, scales, zeros, packed, packed_bytes, stream=None):
+    return lib().lowbit_pack_weights(fmt, E, N, K, group_size, _ptr(codes), _ptr(scales), _ptr(zeros),
+                                     _ptr(packed), packed_bytes, _stream(stream))
+
+
+def lowbit_unpack_weights(fmt, E, N, K, group_size, packed, packed_bytes, codes, scales, zeros, stream=None):
+    return lib().lowbit_unpack_weights(fmt, E, N, K, group_size, _ptr(packed), packed_bytes, _ptr(codes),
+                                       _ptr(scales), _ptr(zeros), _stream(stream))
+
+
+def lowbit_dequant(fmt, N, K, group_size, packed, packed_bytes, w_out, stream=None):
+    return lib().lowbit_dequant(fmt, N, K, group_size, _ptr(packed), packed_bytes, _ptr(w_out), _stream(stream))
+
+
+def lowbit_workspace_bytes(op, fmt, M, N, K, group_size):
+    return lib().lowbit_workspace_bytes(op, fmt, M, N, K, group_size)
+
+
+def lowbit_gemv(fmt, M, N, K, group_size, packed, x, y, workspace=None, ws_bytes=0, stream=None):
+    return lib().lowbit_gemv(fmt, M, N, K, group_size, _ptr(packed), _ptr(x), _ptr(y), _ptr(workspace),
+                             ws_bytes, _stream(stream))

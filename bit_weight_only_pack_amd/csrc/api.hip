@@ -1,0 +1,153 @@
+// api.hip -- the C ABI of liblowbit.so: host-side argument validation and
+// dispatch to the launchers.  Nothing here allocates device memory; every
+// error is detected before the first enqueue.
+#include "lowbit_internal.hpp"
+
+using namespace lowbit;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return LOWBIT_OK;
+    g_last_hip_error = (int)e;
+    return LOWBIT_E_HIP;
+}
+
+bool is_w4(int fmt) { return fmt == LOWBIT_W4_SYM || fmt == LOWBIT_W4_ASYM; }
+
+bool w4_group_ok(int G) { return G == 32 || G == 64 || G == 128; }
+
+// Shape rules shared by every W4 entry point.
+int check_w4_shape(int fmt, int N, int K, int G)
+{
+    if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
+    if (N < 0 || K < 0) return LOWBIT_E_INVALID_ARG;
+    if (G <= 0 || K % G != 0) return LOWBIT_E_INVALID_ARG;
+    if (!w4_group_ok(G)) return LOWBIT_E_UNSUPPORTED;
+    // indices inside the kernels are 32-bit for rows and K offsets
+    if ((int64_t)N > (1 << 30) || (int64_t)K > (1 << 30)) return LOWBIT_E_UNSUPPORTED;
+    return LOWBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lowbit_strerror(int status)
+{
+    switch (status) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_E_INVALID_ARG: return "invalid argument";
+    case LOWBIT_E_UNSUPPORTED: return "unsupported format, group size or shape";
+    case LOWBIT_E_WORKSPACE: return "workspace or packed buffer too small";
+    case LOWBIT_E_HIP: return "HIP runtime error (see lowbit_last_hip_error)";
+    default: return "unknown status";
+    }
+}
+
+int lowbit_last_hip_error(void) { return g_last_hip_error; }
+
+int lowbit_version(void) { return 1; }
+
+size_t lowbit_packed_bytes(int fmt, int E, int N, int K, int group_size)
+{
+    if (E < 0) return 0;
+    if (is_w4(fmt)) {
+        if (check_w4_shape(fmt, N, K, group_size) != LOWBIT_OK) return 0;
+        return (size_t)E * (size_t)w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM).bytes;
+    }
+    return 0;
+}
+
+int lowbit_pack_weights(int fmt, int E, int N, int K, int group_size, const void *codes,
+                        const void *scales, const void *zeros, void *packed, size_t packed_bytes,
+                        void *stream)
+{
+    if (E < 0) return LOWBIT_E_INVALID_ARG;
+    if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
+    int st = check_w4_shape(fmt, N, K, group_size);
+    if (st != LOWBIT_OK) return st;
+    const bool asym = fmt == LOWBIT_W4_ASYM;
+    if (asym != (zeros != nullptr)) return LOWBIT_E_INVALID_ARG;
+    const W4Layout L = w4_layout(N, K, group_size, asym);
+    if (packed_bytes < (size_t)E * (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
+    if (E == 0) return LOWBIT_OK;
+    if (packed == nullptr) return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)N * K > 0 && (codes == nullptr || scales == nullptr)) return LOWBIT_E_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ncode = (int64_t)N * (K / 2), nmeta = (int64_t)N * (K / group_size);
+    for (int e = 0; e < E; ++e) {
+        hipError_t err = launch_w4_pack(
+            L, static_cast<const uint8_t *>(codes) + e * ncode, static_cast<const uint16_t *>(scales) + e * nmeta,
+            asym ? static_cast<const int8_t *>(zeros) + e * nmeta : nullptr,
+            static_cast<uint8_t *>(packed) + (int64_t)e * L.bytes, s);
+        if (err != hipSuccess) return hip_status(err);
+    }
+    return LOWBIT_OK;
+}
+
+int lowbit_unpack_weights(int fmt, int E, int N, int K, int group_size, const void *packed,
+                          size_t packed_bytes, void *codes, void *scales, void *zeros, void *stream)
+{
+    if (E < 0) return LOWBIT_E_INVALID_ARG;
+    if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
+    int st = check_w4_shape(fmt, N, K, group_size);
+    if (st != LOWBIT_OK) return st;
+    const bool asym = fmt == LOWBIT_W4_ASYM;
+    if (asym != (zeros != nullptr)) return LOWBIT_E_INVALID_ARG;
+    const W4Layout L = w4_layout(N, K, group_size, asym);
+    if (packed_bytes < (size_t)E * (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
+    if (E == 0 || (int64_t)N * K == 0) return LOWBIT_OK;
+    if (packed == nullptr || codes == nullptr || scales == nullptr) return LOWBIT_E_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ncode = (int64_t)N * (K / 2), nmeta = (int64_t)N * (K / group_size);
+    for (int e = 0; e < E; ++e) {
+        hipError_t err = launch_w4_unpack(
+            L, static_cast<const uint8_t *>(packed) + (int64_t)e * L.bytes,
+            static_cast<uint8_t *>(codes) + e * ncode, static_cast<uint16_t *>(scales) + e * nmeta,
+            asym ? static_cast<int8_t *>(zeros) + e * nmeta : nullptr, s);
+        if (err != hipSuccess) return hip_status(err);
+    }
+    return LOWBIT_OK;
+}
+
+int lowbit_dequant(int fmt, int N, int K, int group_size, const void *packed, size_t packed_bytes,
+                   float *w_out, void *stream)
+{
+    int st = check_w4_shape(fmt, N, K, group_size);
+    if (st != LOWBIT_OK) return st;
+    const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
+    if (packed_bytes < (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
+    if ((int64_t)N * K == 0) return LOWBIT_OK;
+    if (packed == nullptr || w_out == nullptr) return LOWBIT_E_INVALID_ARG;
+    return hip_status(launch_w4_dequant(L, static_cast<const uint8_t *>(packed), w_out, (hipStream_t)stream));
+}
+
+size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_size)
+{
+    if (op == LOWBIT_OP_GEMV && is_w4(fmt) && check_w4_shape(fmt, N, K, group_size) == LOWBIT_OK && M >= 0)
+        return gemv_w4_workspace(M, N, K, group_size);
+    return 0;
+}
+
+int lowbit_gemv(int fmt, int M, int N, int K, int group_size, const void *packed, const void *x,
+                void *y, void *workspace, size_t ws_bytes, void *stream)
+{
+    int st = check_w4_shape(fmt, N, K, group_size);
+    if (st != LOWBIT_OK) return st;
+    if (M < 0) return LOWBIT_E_INVALID_ARG;
+    if (M > 16) return LOWBIT_E_UNSUPPORTED;
+    if (M == 0 || N == 0) return LOWBIT_OK;
+    if (packed == nullptr || y == nullptr || (K > 0 && x == nullptr)) return LOWBIT_E_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+    if (ws_bytes < gemv_w4_workspace(M, N, K, group_size)) return LOWBIT_E_WORKSPACE;
+    const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
+    return hip_status(launch_gemv_w4(L, M, static_cast<const uint8_t *>(packed),
+                                     static_cast<const _Float16 *>(x), static_cast<_Float16 *>(y), workspace,
+                                     ws_bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

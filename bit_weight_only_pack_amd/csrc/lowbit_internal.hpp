@@ -1,0 +1,84 @@
+// lowbit_internal.hpp -- types, packed layouts and launcher declarations
+// shared by the HIP sources of liblowbit.so (never by the CPU oracle).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lowbit.h"
+
+namespace lowbit {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
+
+// ---------------------------------------------------------------------------
+// Packed INT4 layout (one matrix of N outputs x K inputs).
+//
+// The weight is cut into tiles of 16 output rows x 128 K (1 KiB of codes).
+// Tile (s, t) covers rows 16s..16s+15 and K 128t..128t+127; tiles are stored
+// strip-major (all K tiles of strip s, then strip s+1) so that a wavefront
+// walking one strip along K reads contiguous memory.  Inside a tile the
+// 64 lanes of a wavefront each own 16 bytes, in the operand order of
+// v_mfma_f32_16x16x32_f16 with the weight as the B matrix:
+//   lane l, dword i (i = 0..3)  <->  row 16s + (l % 16),
+//                                     K = 128t + 32i + 8(l / 16) + j, j = 0..7
+// so one coalesced 16-byte load per lane feeds four MFMAs.  Inside a dword the
+// eight 4-bit codes sit in nibble slots ordered k+0, k+2, k+4, k+6, k+1, k+3,
+// k+5, k+7: masking with 0x000F000F (or 0x00F000F0, and the same after a
+// shift by 8) puts the codes of k+2p and k+2p+1 into the two fp16 halves of a
+// register, which is the unpack the kernels use.
+//
+// Scales follow in tile order: for tile (s, t), 16 rows x (128/G) fp16, row
+// major, so a lane reads its row's (128/G) scales in one load.  Zero points
+// (asymmetric only) use the same order as int8.  Rows past N and K past the
+// end are padding: codes 0, scales 0, zeros 0.  Every section starts at a
+// 256-byte boundary.
+// ---------------------------------------------------------------------------
+struct W4Layout {
+    int64_t N, K;
+    int G;
+    bool asym;
+    int64_t strips;      // ceil(N / 16)
+    int64_t ktiles;      // ceil(K / 128)
+    int64_t codes_off, scales_off, zeros_off, bytes;
+};
+
+inline W4Layout w4_layout(int64_t N, int64_t K, int G, bool asym)
+{
+    W4Layout L;
+    L.N = N; L.K = K; L.G = G; L.asym = asym;
+    L.strips = (N + 15) / 16;
+    L.ktiles = (K + 127) / 128;
+    const int64_t tiles = L.strips * L.ktiles;
+    const int64_t gpt = 128 / G;
+    L.codes_off = 0;
+    L.scales_off = align256(tiles * 1024);
+    L.zeros_off = align256(L.scales_off + tiles * 16 * gpt * 2);
+    L.bytes = align256(L.zeros_off + (asym ? tiles * 16 * gpt : 0));
+    return L;
+}
+
+// slot of the code of K offset j (0..7) inside a packed dword
+__host__ __device__ constexpr int w4_slot(int j) { return (j & 1) * 4 + (j >> 1); }
+
+// ---------------------------------------------------------------------------
+// Launchers (enqueue only; argument validation happens in api.hip).
+// ---------------------------------------------------------------------------
+hipError_t launch_w4_pack(const W4Layout &L, const uint8_t *codes, const uint16_t *scales,
+                          const int8_t *zeros, uint8_t *packed, hipStream_t s);
+hipError_t launch_w4_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *codes,
+                            uint16_t *scales, int8_t *zeros, hipStream_t s);
+hipError_t launch_w4_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s);
+
+size_t gemv_w4_workspace(int M, int64_t N, int64_t K, int G);
+hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
+                          _Float16 *y, void *ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace lowbit

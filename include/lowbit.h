@@ -1,0 +1,157 @@
+/*
+ * lowbit.h -- C ABI of liblowbit.so: low-bit weight-only matmul with fused
+ * group-wise dequantization on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (web pages cited by title and section):
+ *   - "Low Bit Metal Kernels" (GPU MODE lecture 49 notes), MSL listing
+ *     `int4_matmul`: weights are INT4 codes packed two per byte, the low
+ *     nibble being the even K row and the high nibble the odd one; each is
+ *     dequantized just before use as (code - zero) * scale[group] and
+ *     multiplied with fp16 activations (buffer arguments W_packed, scales, X,
+ *     Y, M, N, K).
+ *   - "Low Bit ARM kernels" (GPU MODE lecture 38 notes): decode at batch 1 is
+ *     a GEMV and dominates latency, prefill is a GEMM; quantization is
+ *     group-wise along K with groups of 32, 64 or 128, symmetric (scale only)
+ *     or asymmetric (fp16 scale plus int8 zero point per group); weights are
+ *     re-packed offline into the kernel's layout; kernels are plain native
+ *     functions.
+ *   - "vLLM PR #62759 analysis" (LUT-B MoE with MXFP8 activations): 3-bit
+ *     LUT-codebook expert weights, MXFP8 activations, grouped expert GEMM over
+ *     rows bucketed per expert, zero rows for experts that are not local.
+ *
+ * Conventions, for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains device memory.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Arguments are validated on the host before anything is
+ *     enqueued; a call that returns an error has enqueued nothing.  Faults in
+ *     enqueued kernels surface at the caller's next synchronisation.
+ *   - Matrices are row-major and densely packed unless stated otherwise.
+ *   - Return value: LOWBIT_OK or one of the LOWBIT_E_* codes.  No call throws
+ *     or aborts.  Calls are thread-safe; the library keeps no mutable global
+ *     state besides the per-thread last HIP error.
+ *   - Shapes: M, N, K >= 0.  M == 0 or N == 0 is a valid empty call that
+ *     enqueues nothing.  K == 0 gives an all-zero output.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define LOWBIT_OK             0
+#define LOWBIT_E_INVALID_ARG  1  /* null pointer, negative size, K % group_size != 0, ... */
+#define LOWBIT_E_UNSUPPORTED  2  /* valid request this library has no kernel for */
+#define LOWBIT_E_WORKSPACE    3  /* workspace or packed buffer smaller than required */
+#define LOWBIT_E_HIP          4  /* a HIP call failed; see lowbit_last_hip_error() */
+
+/* ---- weight formats ---------------------------------------------------- */
+#define LOWBIT_W4_SYM     0  /* INT4 codes, fp16 scale per group, zero point 8   */
+#define LOWBIT_W4_ASYM    1  /* INT4 codes, fp16 scale + int8 zero point / group */
+#define LOWBIT_LUT3_E4M3  2  /* 3-bit index into an 8-entry E4M3 codebook per
+                                8 outputs x 64 K tile, one UE8M0 exponent per tile */
+
+/* ---- activation / output element types --------------------------------- */
+#define LOWBIT_F16   0
+#define LOWBIT_BF16  1
+
+/* ---- operations (for lowbit_workspace_bytes) ---------------------------- */
+#define LOWBIT_OP_GEMV  0
+#define LOWBIT_OP_GEMM  1
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *lowbit_strerror(int status);
+
+/* HIP error code (hipError_t value) of the last call on this thread that
+ * returned LOWBIT_E_HIP; 0 if none. */
+int lowbit_last_hip_error(void);
+
+/* ABI version of this library (incremented on any incompatible change). */
+int lowbit_version(void);
+
+/*
+ * Size in bytes of the packed weight blob for E matrices of N outputs x K
+ * inputs.  For W4 formats the blob of matrix e starts at
+ * e * lowbit_packed_bytes(fmt, 1, N, K, group_size).  Returns 0 for an
+ * invalid combination (W4: group_size not in {32, 64, 128}, K % group_size,
+ * negative sizes).  Pure host arithmetic; never touches the GPU.
+ */
+size_t lowbit_packed_bytes(int fmt, int E, int N, int K, int group_size);
+
+/*
+ * Offline re-pack of canonical quantized weights into the device layout the
+ * kernels read ("Low Bit ARM kernels": weights are pre-packed once into a
+ * cache-friendly layout; the vLLM PR #62759 analysis, "weights pre-arranged
+ * at load time": the costly layout transform is a one-off at load).  The
+ * packing is a lossless permutation: lowbit_unpack_weights returns the input
+ * bytes exactly.
+ *
+ * W4 formats (group_size in {32, 64, 128}, K % group_size == 0):
+ *   codes  : u8  [E][N][K/2]   byte j of row n holds k = 2j (low nibble) and
+ *                               k = 2j+1 (high nibble); codes 0..15
+ *   scales : f16 [E][N][K/group_size]
+ *   zeros  : i8  [E][N][K/group_size] for LOWBIT_W4_ASYM; must be NULL for
+ *            LOWBIT_W4_SYM (zero point 8)
+ * LOWBIT_LUT3_E4M3 (group_size ignored, N % 8 == 0, K % 64 == 0):
+ *   codes  : u8  [E][N][K]           one index 0..7 per weight
+ *   scales : u8  [E][N/8][K/64][8]   E4M3 codebook of each 8 x 64 tile
+ *   zeros  : u8  [E][N/8][K/64]      UE8M0 exponent of each tile
+ * packed : output, packed_bytes >= lowbit_packed_bytes(fmt, E, N, K, group_size)
+ *          (else LOWBIT_E_WORKSPACE).  Padding inside the blob is written too,
+ *          so the blob is fully defined.
+ * Inputs must not overlap the output.
+ */
+int lowbit_pack_weights(int fmt, int E, int N, int K, int group_size,
+                        const void *codes, const void *scales, const void *zeros,
+                        void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * Inverse of lowbit_pack_weights (test and export hook): writes the canonical
+ * arrays described above.  zeros must be NULL for LOWBIT_W4_SYM.
+ */
+int lowbit_unpack_weights(int fmt, int E, int N, int K, int group_size,
+                          const void *packed, size_t packed_bytes,
+                          void *codes, void *scales, void *zeros, void *stream);
+
+/*
+ * Dequantize one packed W4 matrix to fp32 (test hook):
+ *   w[n][k] = (q[n][k] - z) * s[n][k / group_size],  w_out f32 [N][K].
+ * The product is exact in fp32 (|q - z| <= 143 has 8 significant bits, an
+ * fp16 scale 11), so the result is bit-identical to any exact evaluation.
+ */
+int lowbit_dequant(int fmt, int N, int K, int group_size,
+                   const void *packed, size_t packed_bytes, float *w_out, void *stream);
+
+/*
+ * Workspace bytes an operation needs for this shape (0 if none).  Pass a
+ * workspace of at least this size to that operation.
+ */
+size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_size);
+
+/*
+ * Decode GEMV / small-batch product with W4 weights ("Low Bit Metal
+ * Kernels", int4_matmul; "Low Bit ARM kernels", decode = GEMV):
+ *   y[m][n] = sum_k x[m][k] * (q[n][k] - z) * s[n][k / group_size]
+ * accumulated in fp32, rounded to nearest even into fp16.
+ *   fmt     : LOWBIT_W4_SYM or LOWBIT_W4_ASYM
+ *   M       : 0..16 rows (tokens); larger M -> LOWBIT_E_UNSUPPORTED (use lowbit_gemm)
+ *   packed  : blob from lowbit_pack_weights(fmt, 1, N, K, group_size, ...)
+ *   x       : f16 [M][K], 16-byte aligned
+ *   y       : f16 [M][N] (output; must not overlap x or packed)
+ *   workspace / ws_bytes : per lowbit_workspace_bytes(LOWBIT_OP_GEMV, ...)
+ *            (may be NULL when that is 0)
+ */
+int lowbit_gemv(int fmt, int M, int N, int K, int group_size,
+                const void *packed, const void *x, void *y,
+                void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

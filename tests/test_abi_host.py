@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (CPU only, no GPU needed):
+the library loads, exports every entry point include/lowbit.h declares, the
+Python binding covers the same set, and invalid arguments come back as status
+codes before anything is enqueued (no HIP call is made on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_weight_only_pack_amd as lb
+from bit_weight_only_pack_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            with open(os.path.join(ROOT, "include", fn)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(lowbit_\w+)\s*\(", text))
+    return names
+
+
+def test_header_declares_the_north_star_entry_points():
+    d = _declared()
+    for name in ("lowbit_pack_weights", "lowbit_gemv"):
+        assert name in d
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in sorted(_declared()) if not hasattr(handle, n)]
+    assert not missing, missing
+
+
+def test_binding_matches_header():
+    assert set(_lib.SIGNATURES) == _declared()
+    for name in _declared():
+        assert callable(getattr(lb, name))
+
+
+def test_strerror_and_version():
+    assert lb.lowbit_version() >= 1
+    for code in range(5):
+        assert isinstance(lb.lowbit_strerror(code), str) and lb.lowbit_strerror(code)
+    assert lb.lowbit_strerror(99) == "unknown status"
+
+
+def test_packed_bytes_closed_form():
+    # 16-row x 128-K tiles of 1 KiB + 16 x (128/G) fp16 scales (+ int8 zeros), sections 256-aligned
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, 1, 256, 256, 32) == 32 * 1024 + 32 * 16 * 4 * 2
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_ASYM, 1, 256, 256, 32) == 32 * 1024 + 32 * 16 * 4 * 3
+    n, k = 4096, 14336
+    tiles = (n // 16) * (k // 128)
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, 1, n, k, 128) == tiles * 1024 + tiles * 32
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, 3, n, k, 128) == 3 * (tiles * 1024 + tiles * 32)
+    # ragged shapes round up to whole tiles
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, 1, 17, 96, 32) == 2 * 1024 + 256
+    # invalid -> 0
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, 1, 16, 100, 32) == 0
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, 1, 16, 96, 48) == 0
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_W4_SYM, -1, 16, 128, 32) == 0
+
+
+SYM, ASYM = lb.LOWBIT_W4_SYM, lb.LOWBIT_W4_ASYM
+E_ARG, E_UNS, E_WS = lb.LOWBIT_E_INVALID_ARG, lb.LOWBIT_E_UNSUPPORTED, lb.LOWBIT_E_WORKSPACE
+FAKE = 1 << 20  # a non-null address that must never be dereferenced on these paths
+
+
+@pytest.mark.parametrize("args,want", [
+    ((SYM, 1, 256, 250, 32), E_ARG),          # K % G
+    ((SYM, 1, 256, 256, 48), E_ARG),          # K % G (48 does not divide 256)
+    ((SYM, 1, 256, 192, 96), E_UNS),          # group size not in {32, 64, 128}
+    ((SYM, 17, 256, 256, 32), E_UNS),         # M above the GEMV limit
+    ((SYM, -1, 256, 256, 32), E_ARG),
+    ((SYM, 1, -5, 256, 32), E_ARG),
+    ((7, 1, 256, 256, 32), E_UNS),            # unknown format
+    ((lb.LOWBIT_LUT3_E4M3, 1, 256, 256, 32), E_UNS),
+])
+def test_gemv_rejects_bad_shapes(args, want):
+    assert lb.lowbit_gemv(*args, FAKE, FAKE, FAKE, None, 0) == want
+
+
+def test_gemv_null_and_alignment():
+    assert lb.lowbit_gemv(SYM, 1, 256, 256, 32, None, FAKE, FAKE, None, 0) == E_ARG
+    assert lb.lowbit_gemv(SYM, 1, 256, 256, 32, FAKE, None, FAKE, None, 0) == E_ARG
+    assert lb.lowbit_gemv(SYM, 1, 256, 256, 32, FAKE, FAKE, None, None, 0) == E_ARG
+    assert lb.lowbit_gemv(SYM, 1, 256, 256, 32, FAKE, FAKE + 2, FAKE, None, 0) == E_ARG   # x not 16-B aligned
+
+
+def test_empty_calls_are_ok_without_touching_memory():
+    assert lb.lowbit_gemv(SYM, 0, 256, 256, 32, None, None, None, None, 0) == lb.LOWBIT_OK
+    assert lb.lowbit_gemv(SYM, 4, 0, 256, 32, None, None, None, None, 0) == lb.LOWBIT_OK
+
+
+def test_pack_argument_checks():
+    nb = lb.lowbit_packed_bytes(SYM, 1, 64, 256, 32)
+    assert lb.lowbit_pack_weights(SYM, 1, 64, 256, 32, FAKE, FAKE, None, FAKE, nb - 1) == E_WS
+    assert lb.lowbit_pack_weights(SYM, 1, 64, 256, 32, FAKE, FAKE, FAKE, FAKE, nb) == E_ARG     # zeros with SYM
+    nba = lb.lowbit_packed_bytes(ASYM, 1, 64, 256, 32)
+    assert lb.lowbit_pack_weights(ASYM, 1, 64, 256, 32, FAKE, FAKE, None, FAKE, nba) == E_ARG   # ASYM needs zeros
+    assert lb.lowbit_pack_weights(SYM, 1, 64, 256, 32, None, FAKE, None, FAKE, nb) == E_ARG
+    assert lb.lowbit_pack_weights(SYM, 1, 64, 256, 32, FAKE, FAKE, None, None, nb) == E_ARG
+    assert lb.lowbit_pack_weights(SYM, -2, 64, 256, 32, FAKE, FAKE, None, FAKE, nb) == E_ARG
+    assert lb.lowbit_unpack_weights(SYM, 1, 64, 256, 32, FAKE, nb - 1, FAKE, FAKE, None) == E_WS
+    assert lb.lowbit_dequant(SYM, 64, 256, 32, FAKE, nb - 1, FAKE) == E_WS
+    assert lb.lowbit_dequant(SYM, 64, 256, 32, None, nb, FAKE) == E_ARG
+
+
+def test_workspace_query():
+    assert lb.lowbit_workspace_bytes(lb.LOWBIT_OP_GEMV, SYM, 1, 4096, 4096, 128) >= 0
+    assert lb.lowbit_workspace_bytes(lb.LOWBIT_OP_GEMV, SYM, 1, 4096, 4000, 128) == 0
+
+
+def test_last_hip_error_starts_clear():
+    assert lb.lowbit_last_hip_error() == 0
