@@ -29,8 +29,7 @@ namespace lowbit {
 
 namespace {
 
-constexpr int kMaxWaves = 8;
-constexpr int kUnroll = 4;
+constexpr size_t kMaxLds = 64 * 1024;
 
 template <typename T>
 __device__ __forceinline__ T bitcast(uint32_t v) { return __builtin_bit_cast(T, v); }
@@ -48,44 +47,54 @@ __device__ __forceinline__ h8 unpack8(uint32_t w, uint32_t magic, h2 blo, h2 bhi
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// per-tile group metadata of one lane's row: GPT scales (and zero points)
-template <int G, bool ASYM> struct MetaRaw;
-template <> struct MetaRaw<128, false> { uint16_t s; };
-template <> struct MetaRaw<64, false> { uint32_t s; };
-template <> struct MetaRaw<32, false> { uint2 s; };
-template <> struct MetaRaw<128, true> { uint16_t s; uint8_t z; };
-template <> struct MetaRaw<64, true> { uint32_t s; uint16_t z; };
-template <> struct MetaRaw<32, true> { uint2 s; uint32_t z; };
+// per-tile group metadata of one lane's row: 128/G fp16 scales in s (two per
+// dword) and, for asymmetric weights, 128/G int8 zero points in z
+template <int G, bool ASYM> struct MetaRaw {
+    uint32_t s[(128 / G + 1) / 2];
+    uint32_t z;
+};
 
+// Loads the group metadata of tile-row `idx` (= tile * 16 + row) from the
+// strip's scale / zero-point descriptors; idx < 0 reads zeros.
 template <int G, bool ASYM>
-__device__ __forceinline__ MetaRaw<G, ASYM> load_meta(const uint8_t *scales, const uint8_t *zeros, int64_t idx)
+__device__ __forceinline__ MetaRaw<G, ASYM> load_meta(__amdgpu_buffer_rsrc_t srs, __amdgpu_buffer_rsrc_t zrs, int idx)
 {
-    // idx = (tile * 16 + row) ; GPT entries per row
     constexpr int GPT = 128 / G;
     MetaRaw<G, ASYM> m;
-    if constexpr (G == 128) m.s = reinterpret_cast<const uint16_t *>(scales)[idx];
-    if constexpr (G == 64) m.s = reinterpret_cast<const uint32_t *>(scales)[idx];
-    if constexpr (G == 32) m.s = reinterpret_cast<const uint2 *>(scales)[idx];
-    if constexpr (ASYM) {
-        if constexpr (G == 128) m.z = zeros[idx];
-        if constexpr (G == 64) m.z = reinterpret_cast<const uint16_t *>(zeros)[idx];
-        if constexpr (G == 32) m.z = reinterpret_cast<const uint32_t *>(zeros)[idx];
+    const uint32_t so = idx < 0 ? kBufferOob : (uint32_t)idx * GPT * 2;
+    if constexpr (G == 128) m.s[0] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, 0, 0);
+    if constexpr (G == 64) m.s[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
+    if constexpr (G == 32) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(srs, so, 0, 0);
+        m.s[0] = v[0];
+        m.s[1] = v[1];
     }
-    (void)GPT;
+    m.z = 0;
+    if constexpr (ASYM) {
+        const uint32_t zo = idx < 0 ? kBufferOob : (uint32_t)idx * GPT;
+        if constexpr (G == 128) m.z = __builtin_amdgcn_raw_buffer_load_b8(zrs, zo, 0, 0);
+        if constexpr (G == 64) m.z = __builtin_amdgcn_raw_buffer_load_b16(zrs, zo, 0, 0);
+        if constexpr (G == 32) m.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zo, 0, 0);
+    }
     return m;
+}
+
+// Makes the metadata opaque at its point of use, so its decode is not hoisted.
+template <int G, bool ASYM>
+__device__ __forceinline__ void pin_meta(MetaRaw<G, ASYM> &m)
+{
+#pragma unroll
+    for (int i = 0; i < (128 / G + 1) / 2; ++i) asm volatile("" : "+v"(m.s[i]));
+    if constexpr (ASYM) asm volatile("" : "+v"(m.z));
 }
 
 template <int G, bool ASYM>
 __device__ __forceinline__ void decode_meta(const MetaRaw<G, ASYM> &m, float *sc, h2 *blo, h2 *bhi)
 {
     constexpr int GPT = 128 / G;
-    uint32_t sw[2];
-    if constexpr (G == 128) { sw[0] = m.s; }
-    if constexpr (G == 64) { sw[0] = m.s; }
-    if constexpr (G == 32) { sw[0] = m.s.x; sw[1] = m.s.y; }
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
-        const uint16_t hb = (uint16_t)(sw[g / 2] >> (16 * (g & 1)));
+        const uint16_t hb = (uint16_t)(m.s[g / 2] >> (16 * (g & 1)));
         sc[g] = (float)__builtin_bit_cast(_Float16, hb);
         int z = 8;
         if constexpr (ASYM) z = (int)(int8_t)(uint8_t)(m.z >> (8 * g));
@@ -122,78 +131,114 @@ __device__ __forceinline__ void tile_product(const u4 &q, const MetaRaw<G, ASYM>
     }
 }
 
-template <int G, bool ASYM, int MR>
-__global__ __launch_bounds__(kMaxWaves * 64)
-void gemv_w4_kernel(const u4 *__restrict__ codes, const uint8_t *__restrict__ scales,
-                    const uint8_t *__restrict__ zeros, const _Float16 *__restrict__ x,
-                    _Float16 *__restrict__ y, int M, int N, int K, int ktiles)
+// Dynamic LDS of one workgroup: a chunk of `ct` K tiles of every activation
+// row, each row padded by 16 bytes (so the 16 A rows of an MFMA operand fall
+// in different banks), followed by the cross-wave reduction buffer.
+__host__ __device__ inline int x_row_halfs(int ct) { return ct * 128 + 8; }
+__host__ __device__ inline int64_t gemv_lds_bytes(int M, int ct, int W, int MR)
 {
-    __shared__ float red[kMaxWaves][MR][64];
+    return (int64_t)M * x_row_halfs(ct) * 2 + (int64_t)W * MR * 64 * 4;
+}
 
+// One workgroup = one 16-row strip (all of K).  Its K tiles are taken in
+// rounds of W*P: in a round, wave w owns tiles round + w + u*W (u < P) and
+// issues all of their weight loads before any arithmetic (branch-free buffer
+// loads; slots past the last tile read zeros and are skipped).  The
+// activations of the round are staged in LDS `ct` tiles at a time (all at
+// once whenever they fit, which covers every decode shape).
+template <int G, bool ASYM, int MR, int P>
+// min waves per SIMD (VGPR budget 512 / waves): 8 (64) for 4 tiles in flight,
+// 6 (85) for 8; asymmetric G=32 carries three metadata words per tile
+__global__ __launch_bounds__(1024, (P <= 4 ? (ASYM && G == 32 ? 7 : 8) : (ASYM ? 5 : 6)))
+void gemv_w4_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                    const uint8_t *__restrict__ zeros, const _Float16 *__restrict__ x,
+                    _Float16 *__restrict__ y, int M, int N, int K, int ktiles, int ct)
+{
+    constexpr int GPT = 128 / G;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
     const int strip = blockIdx.x;
     const int r = lane & 15;                         // B column (weight row) and A row (token)
     const int kq = lane >> 4;                        // 8-K slice inside each 32-K MFMA block
-    // A row r only feeds C row r, so lanes past M read a valid row (M - 1) and
-    // their results are never stored: the activation loads need no mask.
-    const _Float16 *xr = x + (int64_t)(r < M ? r : M - 1) * K + kq * 8;
-    const u4 *cw = codes + (int64_t)strip * ktiles * 64 + lane;
-    const int64_t meta0 = (int64_t)strip * ktiles * 16 + r;
-    const int full = K / 128;                        // tiles with all 128 K inside the matrix
+    const int xrow = x_row_halfs(ct);
+    _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
+    float *red = reinterpret_cast<float *>(smem + (int64_t)M * xrow * 2);
+
+    // descriptors over this strip's codes / scales / zero points and over x
+    const int64_t tiles0 = (int64_t)strip * ktiles;
+    const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)ktiles * 1024);
+    const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)ktiles * 16 * GPT * 2);
+    const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)ktiles * 16 * GPT : 0u);
+    const auto xrs = buffer_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+    // A row r reads token min(r, M-1): rows past M only feed C rows that are never stored
+    const _Float16 *xa = xs + (r < M ? r : M - 1) * xrow + kq * 8;
 
     uint32_t magic = 0x64006400u;                    // fp16 1024.0 in both halves
     asm volatile("" : "+v"(magic));                  // keep it in a register: mask+or becomes one op
 
     f4 acc = {0.f, 0.f, 0.f, 0.f};
-
-    for (int t0 = wave; t0 < full; t0 += W * kUnroll) {
-        u4 q[kUnroll];
-        MetaRaw<G, ASYM> mr[kUnroll];
-        h8 a[kUnroll][4];
-        // issue every load of the unrolled tiles before any arithmetic
+    for (int b0 = 0; b0 < ktiles; b0 += W * P) {
+        // 1. weight and group-metadata loads of this wave's tiles in the round
+        u4 q[P];
+        MetaRaw<G, ASYM> mr[P];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int t = t0 + u * W;
-            if (t < full) {
-                q[u] = __builtin_nontemporal_load(cw + (int64_t)t * 64);
-                mr[u] = load_meta<G, ASYM>(scales, zeros, meta0 + (int64_t)t * 16);
-                const _Float16 *xt = xr + t * 128;
+        for (int u = 0; u < P; ++u) {
+            const int t = b0 + wave + u * W;
+            const bool ok = t < ktiles;
+            q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0, 0);
+            mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+        }
+        const int rend = min(b0 + W * P, ktiles);
+        for (int c0 = b0; c0 < rend; c0 += ct) {
+            const int cend = min(c0 + ct, rend);
+            // 2. stage x[0..M)[128*c0, 128*cend) into LDS, 8 halfs per thread and
+            //    step; K % 32 == 0, so a chunk is inside the row or wholly padding
+            if (c0 > 0) __syncthreads();                 // previous chunk fully read
+            const int cpr = (cend - c0) * 16;            // 8-half chunks per row
+            for (int j = threadIdx.x; j < M * cpr; j += blockDim.x) {
+                const int m = j / cpr;
+                const int kl = (j - m * cpr) * 8;
+                const int k = c0 * 128 + kl;
+                const uint32_t off = k < K ? (uint32_t)(((int64_t)m * K + k) * 2) : kBufferOob;
+                const u4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+                *reinterpret_cast<u4 *>(xs + m * xrow + kl) = v;
+            }
+            __syncthreads();
+            // 3. products of the tiles of this chunk
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[u][i] = *reinterpret_cast<const h8 *>(xt + i * 32);
+            for (int u = 0; u < P; ++u) {
+                const int t = b0 + wave + u * W;
+                if (t >= c0 && t < cend) {
+                    // keep each tile's operands live only for that tile: the
+                    // empty asm stops the compiler from unpacking every tile
+                    // ahead of the activation staging
+                    __builtin_amdgcn_sched_barrier(0);
+                    u4 qv = q[u];
+                    asm volatile("" : "+v"(qv));
+                    MetaRaw<G, ASYM> mv = mr[u];
+                    pin_meta<G, ASYM>(mv);
+                    h8 a[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a[i] = *reinterpret_cast<const h8 *>(xa + (t - c0) * 128 + i * 32);
+                    tile_product<G, ASYM, MR>(qv, mv, a, magic, acc);
+                }
             }
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int t = t0 + u * W;
-            if (t < full) tile_product<G, ASYM, MR>(q[u], mr[u], a[u], magic, acc);
-        }
-    }
-    // ragged last tile (K % 128 != 0): its 32-K blocks past K read zeros
-    if (full < ktiles && wave == full % W) {
-        const int t = full;
-        const u4 q = cw[(int64_t)t * 64];
-        const MetaRaw<G, ASYM> mr = load_meta<G, ASYM>(scales, zeros, meta0 + (int64_t)t * 16);
-        h8 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = t * 128 + i * 32;
-            a[i] = h8{};
-            if (k < K) a[i] = *reinterpret_cast<const h8 *>(xr + k);
-        }
-        tile_product<G, ASYM, MR>(q, mr, a, magic, acc);
     }
 
+    // 4. fixed-order cross-wave sum, fp16 RNE store
     if (W > 1) {
 #pragma unroll
-        for (int j = 0; j < MR; ++j) red[wave][j][lane] = acc[j];
+        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                float s = red[0][j][lane];
-                for (int w = 1; w < W; ++w) s += red[w][j][lane];
+                float s = red[j * 64 + lane];
+                for (int w = 1; w < W; ++w) s += red[(w * MR + j) * 64 + lane];
                 acc[j] = s;
             }
         }
@@ -209,17 +254,26 @@ void gemv_w4_kernel(const u4 *__restrict__ codes, const uint8_t *__restrict__ sc
     }
 }
 
-template <int G, bool ASYM>
-hipError_t launch_gm(int MR, dim3 grid, dim3 block, hipStream_t s, const u4 *codes, const uint8_t *scales,
-                     const uint8_t *zeros, const _Float16 *x, _Float16 *y, int M, int N, int K, int ktiles)
+template <int G, bool ASYM, int MR>
+hipError_t launch_p(int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const uint8_t *codes,
+                    const uint8_t *scales, const uint8_t *zeros, const _Float16 *x, _Float16 *y, int M, int N,
+                    int K, int ktiles, int ct)
 {
-    if (MR == 1)
-        gemv_w4_kernel<G, ASYM, 1><<<grid, block, 0, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles);
-    else if (MR == 2)
-        gemv_w4_kernel<G, ASYM, 2><<<grid, block, 0, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles);
+    if (P <= 4)
+        gemv_w4_kernel<G, ASYM, MR, 4><<<grid, block, lds, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles, ct);
     else
-        gemv_w4_kernel<G, ASYM, 4><<<grid, block, 0, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles);
+        gemv_w4_kernel<G, ASYM, MR, 8><<<grid, block, lds, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles, ct);
     return hipGetLastError();
+}
+
+template <int G, bool ASYM>
+hipError_t launch_gm(int MR, int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const uint8_t *codes,
+                     const uint8_t *scales, const uint8_t *zeros, const _Float16 *x, _Float16 *y, int M, int N,
+                     int K, int ktiles, int ct)
+{
+    if (MR == 1) return launch_p<G, ASYM, 1>(P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, ct);
+    if (MR == 2) return launch_p<G, ASYM, 2>(P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, ct);
+    return launch_p<G, ASYM, 4>(P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, ct);
 }
 
 }  // namespace
@@ -230,27 +284,35 @@ hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const
                           _Float16 *y, void *, size_t, hipStream_t s)
 {
     if (M == 0 || L.N == 0) return hipSuccess;
-    // waves per workgroup: about four 1 KiB tiles per wave along the strip's K
+    // waves per workgroup: enough that each wave holds at most 4 tiles (8 for
+    // long K), capped at 16 waves
     const int64_t kt = L.ktiles;
-    int W = (int)((kt + kUnroll - 1) / kUnroll);
+    int W = (int)((kt + 3) / 4);
     if (W < 1) W = 1;
-    if (W > kMaxWaves) W = kMaxWaves;
-    const dim3 grid((unsigned)L.strips), block((unsigned)(W * 64));
+    if (W > 16) W = 16;
+    const int P = (int)((kt + W - 1) / W) <= 4 ? 4 : 8;
     const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    const u4 *codes = reinterpret_cast<const u4 *>(packed + L.codes_off);
+    // activation chunk: every K tile of a round when it fits the LDS budget
+    const int64_t round_tiles = (int64_t)W * P;
+    int64_t ct = kt < round_tiles ? kt : round_tiles;
+    while (ct > 1 && gemv_lds_bytes(M, (int)ct, W, MR) > (int64_t)kMaxLds) ct = (ct + 1) / 2;
+    if (ct < 1) ct = 1;
+    const size_t lds = (size_t)gemv_lds_bytes(M, (int)ct, W, MR);
+    const dim3 grid((unsigned)L.strips), block((unsigned)(W * 64));
+    const uint8_t *codes = packed + L.codes_off;
     const uint8_t *scales = packed + L.scales_off;
     const uint8_t *zeros = L.asym ? packed + L.zeros_off : nullptr;
     const int N = (int)L.N, K = (int)L.K, ktiles = (int)L.ktiles;
     switch (L.G) {
     case 32:
-        return L.asym ? launch_gm<32, true>(MR, grid, block, s, codes, scales, zeros, x, y, M, N, K, ktiles)
-                      : launch_gm<32, false>(MR, grid, block, s, codes, scales, zeros, x, y, M, N, K, ktiles);
+        return L.asym ? launch_gm<32, true>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct)
+                      : launch_gm<32, false>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct);
     case 64:
-        return L.asym ? launch_gm<64, true>(MR, grid, block, s, codes, scales, zeros, x, y, M, N, K, ktiles)
-                      : launch_gm<64, false>(MR, grid, block, s, codes, scales, zeros, x, y, M, N, K, ktiles);
+        return L.asym ? launch_gm<64, true>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct)
+                      : launch_gm<64, false>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct);
     default:
-        return L.asym ? launch_gm<128, true>(MR, grid, block, s, codes, scales, zeros, x, y, M, N, K, ktiles)
-                      : launch_gm<128, false>(MR, grid, block, s, codes, scales, zeros, x, y, M, N, K, ktiles);
+        return L.asym ? launch_gm<128, true>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct)
+                      : launch_gm<128, false>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct);
     }
 }
 

@@ -15,6 +15,15 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+// Raw buffer access: an SGPR descriptor plus a 32-bit byte offset per lane.
+// Reads at an offset past `bytes` return zeros without touching memory,
+// which lets kernels issue loads unconditionally.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kBufferOob = 0x80000000u;   // an offset past any descriptor used here
+
 constexpr int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
 
