@@ -46,6 +46,7 @@ SIGNATURES = {
     "lowbit_dequant": (_i, [_i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lowbit_gemm": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]),
 }
 
 
@@ -136,3 +137,8 @@ def lowbit_workspace_bytes(op, fmt, M, N, K, group_size):
 def lowbit_gemv(fmt, M, N, K, group_size, packed, x, y, workspace=None, ws_bytes=0, stream=None):
     return lib().lowbit_gemv(fmt, M, N, K, group_size, _ptr(packed), _ptr(x), _ptr(y), _ptr(workspace),
                              ws_bytes, _stream(stream))
+
+
+def lowbit_gemm(fmt, M, N, K, group_size, packed, a, a_dtype, c, c_dtype, workspace=None, ws_bytes=0, stream=None):
+    return lib().lowbit_gemm(fmt, M, N, K, group_size, _ptr(packed), _ptr(a), a_dtype, _ptr(c), c_dtype,
+                             _ptr(workspace), ws_bytes, _stream(stream))

@@ -128,8 +128,9 @@ int lowbit_dequant(int fmt, int N, int K, int group_size, const void *packed, si
 
 size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_size)
 {
-    if (op == LOWBIT_OP_GEMV && is_w4(fmt) && check_w4_shape(fmt, N, K, group_size) == LOWBIT_OK && M >= 0)
-        return gemv_w4_workspace(M, N, K, group_size);
+    if (!is_w4(fmt) || check_w4_shape(fmt, N, K, group_size) != LOWBIT_OK || M < 0) return 0;
+    if (op == LOWBIT_OP_GEMV) return gemv_w4_workspace(M, N, K, group_size);
+    if (op == LOWBIT_OP_GEMM) return gemm_w4_workspace(M, N, K, group_size);
     return 0;
 }
 
@@ -148,6 +149,24 @@ int lowbit_gemv(int fmt, int M, int N, int K, int group_size, const void *packed
     return hip_status(launch_gemv_w4(L, M, static_cast<const uint8_t *>(packed),
                                      static_cast<const _Float16 *>(x), static_cast<_Float16 *>(y), workspace,
                                      ws_bytes, (hipStream_t)stream));
+}
+
+int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed, const void *a, int a_dtype,
+                void *c, int c_dtype, void *workspace, size_t ws_bytes, void *stream)
+{
+    int st = check_w4_shape(fmt, N, K, group_size);
+    if (st != LOWBIT_OK) return st;
+    if (M < 0) return LOWBIT_E_INVALID_ARG;
+    if ((a_dtype != LOWBIT_F16 && a_dtype != LOWBIT_BF16) || (c_dtype != LOWBIT_F16 && c_dtype != LOWBIT_BF16))
+        return LOWBIT_E_UNSUPPORTED;
+    if (M == 0 || N == 0) return LOWBIT_OK;
+    if (packed == nullptr || c == nullptr || (K > 0 && a == nullptr)) return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)M * K > (int64_t)INT32_MAX || (int64_t)M * N > (int64_t)INT32_MAX) return LOWBIT_E_UNSUPPORTED;
+    const size_t need = gemm_w4_workspace(M, N, K, group_size);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LOWBIT_E_WORKSPACE;
+    const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
+    return hip_status(launch_gemm_w4(L, M, static_cast<const uint8_t *>(packed), a, a_dtype == LOWBIT_BF16, c,
+                                     c_dtype == LOWBIT_BF16, workspace, ws_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

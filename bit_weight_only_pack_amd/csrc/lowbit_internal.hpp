@@ -90,4 +90,8 @@ size_t gemv_w4_workspace(int M, int64_t N, int64_t K, int G);
 hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
                           _Float16 *y, void *ws, size_t ws_bytes, hipStream_t s);
 
+size_t gemm_w4_workspace(int M, int64_t N, int64_t K, int G);
+hipError_t launch_gemm_w4(const W4Layout &L, int M, const uint8_t *packed, const void *a, int a_bf16, void *c,
+                          int c_bf16, void *ws, size_t ws_bytes, hipStream_t s);
+
 }  // namespace lowbit

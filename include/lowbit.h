@@ -150,6 +150,28 @@ int lowbit_gemv(int fmt, int M, int N, int K, int group_size,
                 const void *packed, const void *x, void *y,
                 void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Prefill GEMM with W4 weights ("Low Bit ARM kernels": prefill is the same
+ * product over many tokens; "Low Bit Metal Kernels": activation and weight
+ * tiles staged on chip and multiplied):
+ *   c[m][n] = sum_k a[m][k] * (q[n][k] - z) * s[n][k / group_size]
+ * on the matrix cores with fp32 accumulation; weights are never rounded
+ * (scales are applied in fp32 per group); the sum is rounded to nearest even
+ * into c_dtype.
+ *   fmt             : LOWBIT_W4_SYM or LOWBIT_W4_ASYM
+ *   M               : any number of rows >= 0
+ *   packed          : blob from lowbit_pack_weights(fmt, 1, N, K, group_size, ...)
+ *   a / a_dtype     : [M][K] activations, LOWBIT_BF16 or LOWBIT_F16
+ *   c / c_dtype     : [M][N] output, LOWBIT_BF16 or LOWBIT_F16 (must not overlap a)
+ *   workspace       : >= lowbit_workspace_bytes(LOWBIT_OP_GEMM, fmt, M, N, K,
+ *                     group_size) bytes (fp32 split-K partials for shapes whose
+ *                     output tiles alone cannot fill the GPU; may be NULL when 0)
+ * Scales must be finite; a zero scale contributes nothing (exactly).
+ */
+int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed,
+                const void *a, int a_dtype, void *c, int c_dtype,
+                void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
