@@ -47,6 +47,8 @@ SIGNATURES = {
     "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lowbit_gemm": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]),
+    "lowbit_moe_align": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "lowbit_moe_gemm": (_i, [_i, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
 }
 
 
@@ -142,3 +144,16 @@ def lowbit_gemv(fmt, M, N, K, group_size, packed, x, y, workspace=None, ws_bytes
 def lowbit_gemm(fmt, M, N, K, group_size, packed, a, a_dtype, c, c_dtype, workspace=None, ws_bytes=0, stream=None):
     return lib().lowbit_gemm(fmt, M, N, K, group_size, _ptr(packed), _ptr(a), a_dtype, _ptr(c), c_dtype,
                              _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def lowbit_moe_align(topk_ids, T, top_k, E, block_m, expert_map, sorted_ids, expert_offsets, block_expert,
+                     num_post_padded, stream=None):
+    return lib().lowbit_moe_align(_ptr(topk_ids), T, top_k, E, block_m, _ptr(expert_map), _ptr(sorted_ids),
+                                  _ptr(expert_offsets), _ptr(block_expert), _ptr(num_post_padded), _stream(stream))
+
+
+def lowbit_moe_gemm(fmt, E_local, N, K, packed, E, a_e4m3, a_ue8m0, a_rows, a_row_div, sorted_ids,
+                    expert_offsets, block_expert, num_valid, block_m, out, stream=None):
+    return lib().lowbit_moe_gemm(fmt, E_local, N, K, _ptr(packed), E, _ptr(a_e4m3), _ptr(a_ue8m0), a_rows,
+                                 a_row_div, _ptr(sorted_ids), _ptr(expert_offsets), _ptr(block_expert), num_valid,
+                                 block_m, _ptr(out), _stream(stream))

@@ -32,6 +32,17 @@ int check_w4_shape(int fmt, int N, int K, int G)
     return LOWBIT_OK;
 }
 
+bool is_lut3(int fmt) { return fmt == LOWBIT_LUT3_E4M3; }
+
+int check_lut3_shape(int E, int N, int K)
+{
+    if (E < 0 || N < 0 || K < 0) return LOWBIT_E_INVALID_ARG;
+    if (N % 8 != 0 || K % 64 != 0) return LOWBIT_E_INVALID_ARG;
+    // 32-bit byte offsets inside the kernels
+    if (lut3_layout(E, N, K).bytes >= ((int64_t)1 << 31)) return LOWBIT_E_UNSUPPORTED;
+    return LOWBIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +70,10 @@ size_t lowbit_packed_bytes(int fmt, int E, int N, int K, int group_size)
         if (check_w4_shape(fmt, N, K, group_size) != LOWBIT_OK) return 0;
         return (size_t)E * (size_t)w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM).bytes;
     }
+    if (is_lut3(fmt)) {
+        if (check_lut3_shape(E, N, K) != LOWBIT_OK) return 0;
+        return (size_t)lut3_layout(E, N, K).bytes;
+    }
     return 0;
 }
 
@@ -67,6 +82,17 @@ int lowbit_pack_weights(int fmt, int E, int N, int K, int group_size, const void
                         void *stream)
 {
     if (E < 0) return LOWBIT_E_INVALID_ARG;
+    if (is_lut3(fmt)) {
+        int st = check_lut3_shape(E, N, K);
+        if (st != LOWBIT_OK) return st;
+        const Lut3Layout L = lut3_layout(E, N, K);
+        if (packed_bytes < (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
+        if ((int64_t)E * N * K == 0) return LOWBIT_OK;
+        if (packed == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr) return LOWBIT_E_INVALID_ARG;
+        return hip_status(launch_lut3_pack(L, static_cast<const uint8_t *>(codes), static_cast<const uint8_t *>(scales),
+                                           static_cast<const uint8_t *>(zeros), static_cast<uint8_t *>(packed),
+                                           (hipStream_t)stream));
+    }
     if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
     int st = check_w4_shape(fmt, N, K, group_size);
     if (st != LOWBIT_OK) return st;
@@ -93,6 +119,17 @@ int lowbit_unpack_weights(int fmt, int E, int N, int K, int group_size, const vo
                           size_t packed_bytes, void *codes, void *scales, void *zeros, void *stream)
 {
     if (E < 0) return LOWBIT_E_INVALID_ARG;
+    if (is_lut3(fmt)) {
+        int st = check_lut3_shape(E, N, K);
+        if (st != LOWBIT_OK) return st;
+        const Lut3Layout L = lut3_layout(E, N, K);
+        if (packed_bytes < (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
+        if ((int64_t)E * N * K == 0) return LOWBIT_OK;
+        if (packed == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr) return LOWBIT_E_INVALID_ARG;
+        return hip_status(launch_lut3_unpack(L, static_cast<const uint8_t *>(packed), static_cast<uint8_t *>(codes),
+                                             static_cast<uint8_t *>(scales), static_cast<uint8_t *>(zeros),
+                                             (hipStream_t)stream));
+    }
     if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
     int st = check_w4_shape(fmt, N, K, group_size);
     if (st != LOWBIT_OK) return st;
@@ -167,6 +204,45 @@ int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed
     const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
     return hip_status(launch_gemm_w4(L, M, static_cast<const uint8_t *>(packed), a, a_dtype == LOWBIT_BF16, c,
                                      c_dtype == LOWBIT_BF16, workspace, ws_bytes, (hipStream_t)stream));
+}
+
+int lowbit_moe_align(const int32_t *topk_ids, int T, int top_k, int E, int block_m, const int32_t *expert_map,
+                     int32_t *sorted_ids, int32_t *expert_offsets, int32_t *block_expert,
+                     int32_t *num_post_padded, void *stream)
+{
+    if (T < 0 || top_k < 0 || E <= 0 || block_m <= 0) return LOWBIT_E_INVALID_ARG;
+    if (E > 1024 || block_m > 4096) return LOWBIT_E_UNSUPPORTED;
+    const int64_t num_valid = (int64_t)T * top_k;
+    const int64_t capacity = num_valid + (int64_t)E * (block_m - 1);
+    if (capacity >= ((int64_t)1 << 31)) return LOWBIT_E_UNSUPPORTED;
+    if (sorted_ids == nullptr || expert_offsets == nullptr || block_expert == nullptr || num_post_padded == nullptr)
+        return LOWBIT_E_INVALID_ARG;
+    if (num_valid > 0 && topk_ids == nullptr) return LOWBIT_E_INVALID_ARG;
+    return hip_status(launch_moe_align(topk_ids, (int)num_valid, E, block_m, expert_map, sorted_ids, expert_offsets,
+                                       block_expert, num_post_padded, (int)capacity, (hipStream_t)stream));
+}
+
+int lowbit_moe_gemm(int fmt, int E_local, int N, int K, const void *packed, int E, const uint8_t *a_e4m3,
+                    const uint8_t *a_ue8m0, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                    const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
+                    void *out, void *stream)
+{
+    if (!is_lut3(fmt)) return LOWBIT_E_UNSUPPORTED;
+    int st = check_lut3_shape(E_local, N, K);
+    if (st != LOWBIT_OK) return st;
+    if (E <= 0 || a_rows < 0 || a_row_div <= 0 || num_valid < 0 || block_m <= 0) return LOWBIT_E_INVALID_ARG;
+    if (block_m % 16 != 0) return LOWBIT_E_UNSUPPORTED;
+    if (num_valid > 0 && (int64_t)(num_valid - 1) / a_row_div >= a_rows) return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)a_rows * K >= ((int64_t)1 << 31) || (int64_t)num_valid * N >= ((int64_t)1 << 31))
+        return LOWBIT_E_UNSUPPORTED;
+    if (num_valid == 0 || N == 0) return LOWBIT_OK;
+    if (packed == nullptr || out == nullptr || sorted_ids == nullptr || expert_offsets == nullptr ||
+        block_expert == nullptr || (K > 0 && (a_e4m3 == nullptr || a_ue8m0 == nullptr)))
+        return LOWBIT_E_INVALID_ARG;
+    const Lut3Layout L = lut3_layout(E_local, N, K);
+    return hip_status(launch_moe_gemm(L, static_cast<const uint8_t *>(packed), E, a_e4m3, a_ue8m0, a_rows,
+                                      a_row_div, sorted_ids, expert_offsets, block_expert, num_valid, block_m,
+                                      static_cast<uint16_t *>(out), (hipStream_t)stream));
 }
 
 }  // extern "C"

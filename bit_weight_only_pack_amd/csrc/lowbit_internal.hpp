@@ -90,6 +90,37 @@ size_t gemv_w4_workspace(int M, int64_t N, int64_t K, int G);
 hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
                           _Float16 *y, void *ws, size_t ws_bytes, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Packed 3-bit LUT-codebook layout (E experts of N outputs x K inputs).
+//
+// Units of 16 output columns x 128 K (2048 weights), ordered expert, strip,
+// K step.  Three sections, each 256-byte aligned:
+//   idx : 768 bytes per unit, 12 per lane in the operand order of
+//         v_mfma_scale_f32_16x16x128_f8f6f4 (lane l: column l % 16, K chunk
+//         32 * (l / 16) .. +32); bit layout in moe_lut3.hip (lut_put)
+//   cb  : 32 bytes per unit, the four 8-entry E4M3 codebooks of the unit's
+//         tiles, ordered (column half, K half)
+//   ex  : 4 bytes per unit, the four UE8M0 tile exponents in the same order
+// Padding columns / K: index 0, codebook zeros, exponent 127.
+// ---------------------------------------------------------------------------
+struct Lut3Layout {
+    int64_t E, N, K;
+    int64_t strips, ksteps;
+    int64_t idx_off, cb_off, ex_off, bytes;
+};
+Lut3Layout lut3_layout(int64_t E, int64_t N, int64_t K);
+hipError_t launch_lut3_pack(const Lut3Layout &L, const uint8_t *idx, const uint8_t *cb, const uint8_t *ex,
+                            uint8_t *packed, hipStream_t s);
+hipError_t launch_lut3_unpack(const Lut3Layout &L, const uint8_t *packed, uint8_t *idx, uint8_t *cb, uint8_t *ex,
+                              hipStream_t s);
+hipError_t launch_moe_align(const int32_t *topk_ids, int num_valid, int E, int block_m, const int32_t *expert_map,
+                            int32_t *sorted_ids, int32_t *expert_offsets, int32_t *block_expert,
+                            int32_t *num_post_padded, int capacity, hipStream_t s);
+hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
+                           const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                           const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
+                           uint16_t *out, hipStream_t s);
+
 size_t gemm_w4_workspace(int M, int64_t N, int64_t K, int G);
 hipError_t launch_gemm_w4(const W4Layout &L, int M, const uint8_t *packed, const void *a, int a_bf16, void *c,
                           int c_bf16, void *ws, size_t ws_bytes, hipStream_t s);

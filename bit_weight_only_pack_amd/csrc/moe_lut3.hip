@@ -1,0 +1,474 @@
+// moe_lut3.hip -- 3-bit LUT-codebook MoE: weight re-pack, routing alignment
+// and the grouped expert GEMM with MXFP8 activations.
+//
+// Format ("vLLM PR #62759 analysis", section "Format"): every weight is a
+// 3-bit index into an 8-entry E4M3 codebook; a codebook and one UE8M0
+// exponent are shared by a tile of 8 output channels x 64 K.  Activations are
+// MXFP8: E4M3 values with one UE8M0 scale per 32 K.  Rows reach the experts
+// through sorted slot ids (section "A gather": a slot is valid when its id is
+// below the number of routed slots); experts that are not local produce zero
+// rows (section "Expert parallelism").
+//
+// MI355X design (the page's tensor-core LUT decode does not exist on CDNA4):
+//   * Load-time re-pack into 16-column x 128-K units in the lane order of
+//     v_mfma_scale_f32_16x16x128_f8f6f4, measured on gfx950: lane l holds
+//     column (row) l % 16; with g = l / 16 its bytes 0..15 are K 16g..16g+15
+//     and bytes 16..31 are K 64+16g..64+16g+15; the block scale of 32-K block
+//     b of row/column r is taken from lane r + 16b.  A lane's 32 indices take
+//     12 bytes arranged so
+//     that each run of four indices becomes byte selectors with one to four
+//     bit operations; one v_perm_b32 per four weights then turns selectors into
+//     E4M3 bytes from the codebook held in two registers.  The 3-bit format is
+//     kept: 768 index bytes + 32 codebook bytes + 4 exponent bytes per 2048
+//     weights = 3.140625 bits per weight.
+//   * The block-scaled fp8 MFMA applies the activation UE8M0 scale per 32 K
+//     (scale A) and the tile exponent (scale B, the same exponent for both
+//     32-K halves of a 64-K tile), accumulating in fp32.
+//   * One workgroup per (expert, 128-column tile) loops over all 16-row
+//     blocks of its expert, so each expert's weights stream from HBM once.
+#include "lowbit_internal.hpp"
+
+namespace lowbit {
+
+namespace {
+
+constexpr int kThreads = 256;
+inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+// Bit position of index j (0..31) of a lane inside its 3 packed dwords.
+// Indices 0..23 sit in bits 0-2 / 3-5 of the bytes of dwords 0..2; indices
+// 24..31 use bits 6-7 of dwords 0/1 for their low two bits and bit 6/7 of
+// dword 2 for the high bit.
+__host__ __device__ inline void lut_put(uint32_t w[3], int j, uint32_t v)
+{
+    if (j < 24) {
+        const int d = j / 8, half = (j / 4) & 1, b = j & 3;
+        w[d] |= (v & 7u) << (8 * b + 3 * half);
+    } else {
+        const int hi = j >= 28, b = j & 3;
+        w[hi] |= (v & 3u) << (8 * b + 6);
+        w[2] |= ((v >> 2) & 1u) << (8 * b + 6 + hi);
+    }
+}
+
+__host__ __device__ inline uint32_t lut_get(const uint32_t w[3], int j)
+{
+    if (j < 24) {
+        const int d = j / 8, half = (j / 4) & 1, b = j & 3;
+        return (w[d] >> (8 * b + 3 * half)) & 7u;
+    }
+    const int hi = j >= 28, b = j & 3;
+    return ((w[hi] >> (8 * b + 6)) & 3u) | (((w[2] >> (8 * b + 6 + hi)) & 1u) << 2);
+}
+
+// ---------------------------------------------------------------- re-pack
+// K offset (within a 128-K step) of byte j of lane group lg
+__host__ __device__ inline int lane_k(int lg, int j) { return 64 * (j >> 4) + 16 * lg + (j & 15); }
+
+__global__ void lut3_pack_idx(const uint8_t *__restrict__ idx, uint32_t *__restrict__ out, int64_t N, int64_t K,
+                              int64_t strips, int64_t ksteps, int64_t total_lanes)
+{
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // one thread per lane-slot
+    if (g >= total_lanes) return;
+    const int lane = (int)(g & 63);
+    const int64_t unit = g >> 6;                                       // (e, s, t)
+    const int64_t t = unit % ksteps, s = (unit / ksteps) % strips, e = unit / (ksteps * strips);
+    const int64_t n = s * 16 + (lane & 15);
+    uint32_t w[3] = {0u, 0u, 0u};
+    if (n < N)
+        for (int j = 0; j < 32; ++j) {
+            const int64_t k = t * 128 + lane_k(lane >> 4, j);
+            if (k < K) lut_put(w, j, idx[(e * N + n) * K + k]);
+        }
+    out[g * 3 + 0] = w[0];
+    out[g * 3 + 1] = w[1];
+    out[g * 3 + 2] = w[2];
+}
+
+__global__ void lut3_unpack_idx(const uint32_t *__restrict__ in, uint8_t *__restrict__ idx, int64_t N, int64_t K,
+                                int64_t strips, int64_t ksteps, int64_t total_lanes)
+{
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (g >= total_lanes) return;
+    const int lane = (int)(g & 63);
+    const int64_t unit = g >> 6;
+    const int64_t t = unit % ksteps, s = (unit / ksteps) % strips, e = unit / (ksteps * strips);
+    const int64_t n = s * 16 + (lane & 15);
+    if (n >= N) return;
+    const uint32_t w[3] = {in[g * 3 + 0], in[g * 3 + 1], in[g * 3 + 2]};
+    for (int j = 0; j < 32; ++j) {
+        const int64_t k = t * 128 + lane_k(lane >> 4, j);
+        if (k < K) idx[(e * N + n) * K + k] = (uint8_t)lut_get(w, j);
+    }
+}
+
+// unit c = (column half h, K half kh) -> codebook / exponent of tile (n/8, k/64)
+__global__ void lut3_pack_meta(const uint8_t *__restrict__ cb, const uint8_t *__restrict__ ex,
+                               uint8_t *__restrict__ cb_out, uint8_t *__restrict__ ex_out, int64_t N, int64_t K,
+                               int64_t strips, int64_t ksteps, int64_t total)
+{
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // one thread per (unit, c)
+    if (g >= total) return;
+    const int c = (int)(g & 3);
+    const int64_t unit = g >> 2;
+    const int64_t t = unit % ksteps, s = (unit / ksteps) % strips, e = unit / (ksteps * strips);
+    const int64_t nt = s * 2 + (c >> 1), kt = t * 2 + (c & 1);       // tile indices (8 cols x 64 K)
+    const int64_t ntiles = N / 8, ktiles = K / 64;
+    const bool ok = nt < ntiles && kt < ktiles;
+    const int64_t src = (e * ntiles + nt) * ktiles + kt;
+    for (int i = 0; i < 8; ++i) cb_out[g * 8 + i] = ok ? cb[src * 8 + i] : (uint8_t)0;
+    ex_out[g] = ok ? ex[src] : (uint8_t)127;
+}
+
+__global__ void lut3_unpack_meta(const uint8_t *__restrict__ cb_in, const uint8_t *__restrict__ ex_in,
+                                 uint8_t *__restrict__ cb, uint8_t *__restrict__ ex, int64_t N, int64_t K,
+                                 int64_t strips, int64_t ksteps, int64_t total)
+{
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (g >= total) return;
+    const int c = (int)(g & 3);
+    const int64_t unit = g >> 2;
+    const int64_t t = unit % ksteps, s = (unit / ksteps) % strips, e = unit / (ksteps * strips);
+    const int64_t nt = s * 2 + (c >> 1), kt = t * 2 + (c & 1);
+    const int64_t ntiles = N / 8, ktiles = K / 64;
+    if (nt >= ntiles || kt >= ktiles) return;
+    const int64_t dst = (e * ntiles + nt) * ktiles + kt;
+    for (int i = 0; i < 8; ++i) cb[dst * 8 + i] = cb_in[g * 8 + i];
+    ex[dst] = ex_in[g];
+}
+
+// ---------------------------------------------------------------- align
+// Bucket the routed slots by expert (ascending expert, ascending slot id),
+// pad each expert to a multiple of block_m with the sentinel num_valid, and
+// record the expert of every block.  One workgroup of 1024 threads; slots are
+// taken 1024 at a time and placed with a stable counting sort: a slot's rank
+// among equal experts is built from ballots inside a wave and prefix sums
+// over the waves of the chunk.
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kMaxExperts = 1024;
+
+__global__ __launch_bounds__(kAlignThreads)
+void moe_align_kernel(const int32_t *__restrict__ topk_ids, int num_valid, int E, int block_m,
+                      const int32_t *__restrict__ expert_map, int32_t *__restrict__ sorted_ids,
+                      int32_t *__restrict__ expert_offsets, int32_t *__restrict__ block_expert,
+                      int32_t *__restrict__ num_post_padded, int capacity)
+{
+    __shared__ int counts[kMaxExperts];
+    __shared__ int offs[kMaxExperts + 1];
+    __shared__ int placed[kMaxExperts];
+    __shared__ int wave_cnt[kAlignWaves][kMaxExperts / 8];   // per-chunk, per-wave counts of a slice of experts
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    for (int e = tid; e < E; e += kAlignThreads) { counts[e] = 0; placed[e] = 0; }
+    __syncthreads();
+    for (int i = tid; i < num_valid; i += kAlignThreads) {
+        const int e = topk_ids[i];
+        if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {                                   // E <= 1024: a serial scan is short
+        int acc = 0;
+        for (int e = 0; e < E; ++e) {
+            offs[e] = acc;
+            acc += (counts[e] + block_m - 1) / block_m * block_m;
+        }
+        offs[E] = acc;
+        num_post_padded[0] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kAlignThreads) expert_offsets[e] = offs[e];
+    for (int i = tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;   // sentinel everywhere first
+    for (int b = tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
+    __syncthreads();
+    for (int e = tid; e < E; e += kAlignThreads) {
+        const int local = expert_map ? expert_map[e] : e;
+        for (int b = offs[e] / block_m; b < offs[e + 1] / block_m; ++b) block_expert[b] = local;
+    }
+
+    // stable placement, chunk by chunk
+    for (int base = 0; base < num_valid; base += kAlignThreads) {
+        const int sid = base + tid;
+        const int e = sid < num_valid ? topk_ids[sid] : -1;
+        const bool valid = e >= 0 && e < E;
+        // rank among earlier lanes of this wave with the same expert
+        int rank_in_wave = 0, wave_total = 0;
+        uint64_t todo = __builtin_amdgcn_ballot_w64(valid);
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const int le = __shfl(e, leader);
+            const uint64_t same = __builtin_amdgcn_ballot_w64(valid && e == le);
+            if (valid && e == le) {
+                rank_in_wave = __builtin_popcountll(same & ((1ull << lane) - 1));
+                wave_total = __builtin_popcountll(same);
+            }
+            todo &= ~same;
+        }
+        // prefix over the waves of this chunk, a slice of experts at a time
+        int before = 0;
+        for (int e0 = 0; e0 < E; e0 += kMaxExperts / 8) {
+            for (int i = tid; i < kAlignWaves * (kMaxExperts / 8); i += kAlignThreads)
+                wave_cnt[i / (kMaxExperts / 8)][i % (kMaxExperts / 8)] = 0;
+            __syncthreads();
+            if (valid && e >= e0 && e < e0 + kMaxExperts / 8 && rank_in_wave == 0)
+                wave_cnt[wave][e - e0] = wave_total;
+            __syncthreads();
+            if (valid && e >= e0 && e < e0 + kMaxExperts / 8)
+                for (int w = 0; w < wave; ++w) before += wave_cnt[w][e - e0];
+            __syncthreads();
+        }
+        if (valid) sorted_ids[offs[e] + placed[e] + before + rank_in_wave] = sid;
+        __syncthreads();                              // every position of the chunk taken
+        if (valid) atomicAdd(&placed[e], 1);          // advance the per-expert cursors
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- grouped GEMM
+typedef int i8v __attribute__((ext_vector_type(8)));
+
+constexpr int kMoeWaves = 4;          // 4 waves x 2 strips = 128 columns per workgroup
+constexpr int kStripsPerWave = 2;
+constexpr int kMaxMBlocks = 4;        // 16-row blocks held at once (64 rows); more rows -> more passes
+
+struct MoeArgs {
+    const uint8_t *idx, *cb, *ex;      // packed sections
+    const uint8_t *aq, *as;            // activations [rows][K] E4M3, scales [rows][K/32] UE8M0
+    const int32_t *sorted_ids, *expert_offsets, *block_expert;
+    uint16_t *out;                     // bf16 [num_valid][N]
+    int E, N, K, strips, ksteps, a_row_div, num_valid, block_m, n_tiles, a_rows;
+};
+
+// 32 decoded E4M3 bytes of one lane from its 12 index bytes; bytes 0..15 use
+// the codebook of the first 64-K half (c0 = lo dword, c1 = hi dword), bytes
+// 16..31 that of the second half (c2, c3)
+__device__ __forceinline__ i8v lut3_decode(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t c0, uint32_t c1,
+                                           uint32_t c2, uint32_t c3)
+{
+    const uint32_t m7 = 0x07070707u;
+    const uint32_t s0 = w0 & m7;
+    const uint32_t s1 = (w0 >> 3) & m7;
+    const uint32_t s2 = w1 & m7;
+    const uint32_t s3 = (w1 >> 3) & m7;
+    const uint32_t s4 = w2 & m7;
+    const uint32_t s5 = (w2 >> 3) & m7;
+    const uint32_t s6 = ((w0 >> 6) & 0x03030303u) | ((w2 >> 4) & 0x04040404u);
+    const uint32_t s7 = ((w1 >> 6) & 0x03030303u) | ((w2 >> 5) & 0x04040404u);
+    // selector byte v in 0..3 picks byte v of the lo dword, 4..7 byte v-4 of the hi dword
+    i8v r;
+    r[0] = (int)__builtin_amdgcn_perm(c1, c0, s0);
+    r[1] = (int)__builtin_amdgcn_perm(c1, c0, s1);
+    r[2] = (int)__builtin_amdgcn_perm(c1, c0, s2);
+    r[3] = (int)__builtin_amdgcn_perm(c1, c0, s3);
+    r[4] = (int)__builtin_amdgcn_perm(c3, c2, s4);
+    r[5] = (int)__builtin_amdgcn_perm(c3, c2, s5);
+    r[6] = (int)__builtin_amdgcn_perm(c3, c2, s6);
+    r[7] = (int)__builtin_amdgcn_perm(c3, c2, s7);
+    return r;
+}
+
+__global__ __launch_bounds__(kMoeWaves * 64)
+void moe_lut3_gemm_kernel(MoeArgs p)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int e = blockIdx.x / p.n_tiles;                      // global expert
+    const int nt = blockIdx.x % p.n_tiles;
+    const int row0 = p.expert_offsets[e], row1 = p.expert_offsets[e + 1];
+    if (row0 >= row1) return;                                  // no slot routed here
+    const int local = p.block_expert[row0 / p.block_m];
+    const int strip_base = nt * (kMoeWaves * kStripsPerWave) + wave * kStripsPerWave;
+
+    if (local < 0) {
+        // expert not on this device: its routed slots get zero rows
+        for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kMoeWaves * 4) {
+            const int sid = p.sorted_ids[rr];
+            if (sid >= p.num_valid) continue;
+            for (int c = (threadIdx.x & 15); c < kMoeWaves * kStripsPerWave * 16; c += 16) {
+                const int n = nt * kMoeWaves * kStripsPerWave * 16 + c;
+                if (n < p.N) p.out[(int64_t)sid * p.N + n] = 0;
+            }
+        }
+        return;
+    }
+
+    const int64_t units_per_strip = p.ksteps;
+    const int64_t expert_units = (int64_t)p.strips * p.ksteps;
+    const auto irs = buffer_rsrc(p.idx, (uint32_t)((int64_t)(p.E) * expert_units * 768));
+    const auto crs = buffer_rsrc(p.cb, (uint32_t)((int64_t)(p.E) * expert_units * 32));
+    const auto ers = buffer_rsrc(p.ex, (uint32_t)((int64_t)(p.E) * expert_units * 4));
+    const auto ars = buffer_rsrc(p.aq, (uint32_t)((int64_t)p.a_rows * p.K));
+    const auto srs = buffer_rsrc(p.as, (uint32_t)((int64_t)p.a_rows * (p.K / 32)));
+    const int colhalf = r16 >> 3;                              // which 8-column tile of the strip
+    const int exsel = (colhalf << 1) | (kg >> 1);              // exponent of this lane's 32-K block
+    const int k_chunks = p.K / 32;
+
+    for (int pass = row0; pass < row1; pass += kMaxMBlocks * 16) {
+        const int nmb = min(kMaxMBlocks, (row1 - pass) / 16);
+        // slot ids and activation rows of this lane's A row in each block
+        int arow[kMaxMBlocks];
+        bool aok[kMaxMBlocks];
+#pragma unroll
+        for (int mb = 0; mb < kMaxMBlocks; ++mb) {
+            const int sid = mb < nmb ? p.sorted_ids[pass + mb * 16 + r16] : p.num_valid;
+            aok[mb] = sid < p.num_valid;
+            arow[mb] = aok[mb] ? sid / p.a_row_div : 0;
+        }
+        f4 acc[kMaxMBlocks][kStripsPerWave];
+#pragma unroll
+        for (int mb = 0; mb < kMaxMBlocks; ++mb)
+#pragma unroll
+            for (int j = 0; j < kStripsPerWave; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+        for (int t = 0; t < p.ksteps; ++t) {
+            // weights of this wave's strips for K step t
+            uint32_t w[kStripsPerWave][3];
+            u4 cbk[kStripsPerWave];
+            int bscale[kStripsPerWave];
+#pragma unroll
+            for (int j = 0; j < kStripsPerWave; ++j) {
+                const int s = strip_base + j;
+                const bool ok = s < p.strips;
+                const int64_t unit = ((int64_t)local * p.strips + s) * units_per_strip + t;
+                const auto iv = __builtin_amdgcn_raw_buffer_load_b96(irs, ok ? (uint32_t)(unit * 768 + lane * 12) : kBufferOob, 0, 0);
+                w[j][0] = iv[0];
+                w[j][1] = iv[1];
+                w[j][2] = iv[2];
+                // both K halves' codebooks of this lane's 8-column tile (16 bytes)
+                cbk[j] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)(unit * 32 + colhalf * 16) : kBufferOob, 0, 0);
+                bscale[j] = ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(ers, (uint32_t)(unit * 4 + exsel), 0, 0) : 127;
+            }
+            // activations of the lane's row: K 16kg..+16 and 64+16kg..+16 of this
+            // step; the scale of 32-K block kg (this lane provides block kg's scale)
+            i8v a[kMaxMBlocks];
+            int ascale[kMaxMBlocks];
+            const int kc = t * 4 + kg;                                 // 32-K block of the scale
+            const int k_lo = t * 128 + 16 * kg, k_hi = k_lo + 64;
+#pragma unroll
+            for (int mb = 0; mb < kMaxMBlocks; ++mb) {
+                const bool ok = mb < nmb && aok[mb];
+                const uint32_t row = (uint32_t)arow[mb] * (uint32_t)p.K;
+                const u4 lo = __builtin_amdgcn_raw_buffer_load_b128(ars, ok && k_lo < p.K ? row + k_lo : kBufferOob, 0, 0);
+                const u4 hi = __builtin_amdgcn_raw_buffer_load_b128(ars, ok && k_hi < p.K ? row + k_hi : kBufferOob, 0, 0);
+                a[mb] = i8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                ascale[mb] = ok && kc < k_chunks
+                                 ? (int)__builtin_amdgcn_raw_buffer_load_b8(srs, (uint32_t)arow[mb] * (uint32_t)k_chunks + kc, 0, 0)
+                                 : 127;
+            }
+#pragma unroll
+            for (int j = 0; j < kStripsPerWave; ++j) {
+                const i8v b = lut3_decode(w[j][0], w[j][1], w[j][2], cbk[j].x, cbk[j].y, cbk[j].z, cbk[j].w);
+#pragma unroll
+                for (int mb = 0; mb < kMaxMBlocks; ++mb)
+                    if (mb < nmb)
+                        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a[mb], b, acc[mb][j], 0, 0, 0, ascale[mb], 0, bscale[j]);
+            }
+        }
+        // store: lane holds column (lane % 16), rows 4*(lane/16) + i of each block
+#pragma unroll
+        for (int mb = 0; mb < kMaxMBlocks; ++mb) {
+            if (mb >= nmb) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sid = p.sorted_ids[pass + mb * 16 + kg * 4 + i];
+                if (sid >= p.num_valid) continue;
+#pragma unroll
+                for (int j = 0; j < kStripsPerWave; ++j) {
+                    const int n = (strip_base + j) * 16 + r16;
+                    if (n < p.N) {
+                        const __bf16 v = (__bf16)acc[mb][j][i];
+                        p.out[(int64_t)sid * p.N + n] = __builtin_bit_cast(uint16_t, v);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+Lut3Layout lut3_layout(int64_t E, int64_t N, int64_t K)
+{
+    Lut3Layout L;
+    L.E = E; L.N = N; L.K = K;
+    L.strips = (N + 15) / 16;
+    L.ksteps = (K + 127) / 128;
+    const int64_t units = E * L.strips * L.ksteps;
+    L.idx_off = 0;
+    L.cb_off = align256(units * 768);
+    L.ex_off = align256(L.cb_off + units * 32);
+    L.bytes = align256(L.ex_off + units * 4);
+    return L;
+}
+
+hipError_t launch_lut3_pack(const Lut3Layout &L, const uint8_t *idx, const uint8_t *cb, const uint8_t *ex,
+                            uint8_t *packed, hipStream_t s)
+{
+    const int64_t units = L.E * L.strips * L.ksteps;
+    if (units == 0) return hipSuccess;
+    const int64_t lanes = units * 64;
+    lut3_pack_idx<<<blocks_for(lanes), kThreads, 0, s>>>(idx, reinterpret_cast<uint32_t *>(packed + L.idx_off), L.N,
+                                                          L.K, L.strips, L.ksteps, lanes);
+    lut3_pack_meta<<<blocks_for(units * 4), kThreads, 0, s>>>(cb, ex, packed + L.cb_off, packed + L.ex_off, L.N, L.K,
+                                                              L.strips, L.ksteps, units * 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_lut3_unpack(const Lut3Layout &L, const uint8_t *packed, uint8_t *idx, uint8_t *cb, uint8_t *ex,
+                              hipStream_t s)
+{
+    const int64_t units = L.E * L.strips * L.ksteps;
+    if (units == 0) return hipSuccess;
+    const int64_t lanes = units * 64;
+    lut3_unpack_idx<<<blocks_for(lanes), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(packed + L.idx_off), idx,
+                                                            L.N, L.K, L.strips, L.ksteps, lanes);
+    lut3_unpack_meta<<<blocks_for(units * 4), kThreads, 0, s>>>(packed + L.cb_off, packed + L.ex_off, cb, ex, L.N,
+                                                                L.K, L.strips, L.ksteps, units * 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_align(const int32_t *topk_ids, int num_valid, int E, int block_m, const int32_t *expert_map,
+                            int32_t *sorted_ids, int32_t *expert_offsets, int32_t *block_expert,
+                            int32_t *num_post_padded, int capacity, hipStream_t s)
+{
+    moe_align_kernel<<<1, kAlignThreads, 0, s>>>(topk_ids, num_valid, E, block_m, expert_map, sorted_ids,
+                                                  expert_offsets, block_expert, num_post_padded, capacity);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
+                           const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                           const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
+                           uint16_t *out, hipStream_t s)
+{
+    MoeArgs p;
+    p.idx = packed + L.idx_off;
+    p.cb = packed + L.cb_off;
+    p.ex = packed + L.ex_off;
+    p.aq = aq;
+    p.as = as;
+    p.sorted_ids = sorted_ids;
+    p.expert_offsets = expert_offsets;
+    p.block_expert = block_expert;
+    p.out = out;
+    p.E = (int)L.E;
+    p.N = (int)L.N;
+    p.K = (int)L.K;
+    p.strips = (int)L.strips;
+    p.ksteps = (int)L.ksteps;
+    p.a_row_div = a_row_div;
+    p.num_valid = num_valid;
+    p.block_m = block_m;
+    p.n_tiles = (int)((L.strips + kMoeWaves * kStripsPerWave - 1) / (kMoeWaves * kStripsPerWave));
+    p.a_rows = a_rows;
+    const unsigned blocks = (unsigned)((int64_t)E_global * p.n_tiles);
+    if (blocks == 0) return hipSuccess;
+    moe_lut3_gemm_kernel<<<blocks, kMoeWaves * 64, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace lowbit

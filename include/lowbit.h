@@ -172,6 +172,58 @@ int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed
                 const void *a, int a_dtype, void *c, int c_dtype,
                 void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Bucket routed token slots by expert ("vLLM PR #62759 analysis", section
+ * "A gather": the grouped GEMM walks rows through sorted_token_ids built by
+ * moe_align_block_size; a slot id below the number of routed slots is a real
+ * row).  Slot sid = t * top_k + j is token t's j-th routed expert
+ * topk_ids[t][j].  Output order: experts ascending by global id, slot ids
+ * ascending within an expert; each expert's run is padded to a multiple of
+ * block_m with the sentinel T * top_k; experts with no slot have no block.
+ *   topk_ids       : i32 [T][top_k], values in [0, E) (other values are ignored)
+ *   expert_map     : i32 [E] global -> local expert id or -1 (not on this
+ *                    device); NULL = identity
+ *   sorted_ids     : i32 [T*top_k + E*(block_m-1)] (output; entries past the
+ *                    padded length hold the sentinel)
+ *   expert_offsets : i32 [E+1] (output) start of each expert's padded run;
+ *                    expert_offsets[E] = padded length
+ *   block_expert   : i32 [(T*top_k + E*(block_m-1)) / block_m] (output) local
+ *                    expert of each block (-1 if not local, and past the end)
+ *   num_post_padded: i32 [1] (output) padded length
+ * E <= 1024.  Deterministic: identical inputs give identical outputs.
+ */
+int lowbit_moe_align(const int32_t *topk_ids, int T, int top_k, int E, int block_m,
+                     const int32_t *expert_map, int32_t *sorted_ids, int32_t *expert_offsets,
+                     int32_t *block_expert, int32_t *num_post_padded, void *stream);
+
+/*
+ * Grouped expert GEMM with 3-bit LUT-codebook weights and MXFP8 activations
+ * ("vLLM PR #62759 analysis": sections "Format", "A gather", "Expert
+ * parallelism"; numerics of section "Emulation path"):
+ *   out[sid][n] = RNE_bf16( sum_k a[row][k] * w_e[n][k] ),  row = sid / a_row_div
+ *   a[row][k]   = E4M3(a_e4m3[row][k]) * 2^(a_ue8m0[row][k/32] - 127)
+ *   w_e[n][k]   = E4M3(codebook of tile (n/8, k/64))[index] * 2^(tile exponent - 127)
+ * for every slot sid < num_valid listed in sorted_ids, where e is the local
+ * expert block_expert[] gives for the slot's block.  Slots of experts that are
+ * not local (block_expert = -1) get zero rows.  Rows of out that no slot
+ * names are not written.  Accumulation is fp32.
+ *   fmt            : LOWBIT_LUT3_E4M3
+ *   E_local, N, K  : packed blob from lowbit_pack_weights(LOWBIT_LUT3_E4M3,
+ *                    E_local, N, K, ...); N % 8 == 0, K % 64 == 0
+ *   E              : number of global experts (expert_offsets has E + 1 entries)
+ *   a_e4m3/a_ue8m0 : u8 [a_rows][K] and u8 [a_rows][K/32]
+ *   a_row_div      : top_k when every routed copy of a token reads the token's
+ *                    row (gate/up), 1 when each slot has its own row (down)
+ *   sorted_ids, expert_offsets, block_expert : from lowbit_moe_align with the
+ *                    same block_m (a multiple of 16)
+ *   out            : bf16 [num_valid][N]
+ */
+int lowbit_moe_gemm(int fmt, int E_local, int N, int K, const void *packed, int E,
+                    const uint8_t *a_e4m3, const uint8_t *a_ue8m0, int a_rows, int a_row_div,
+                    const int32_t *sorted_ids, const int32_t *expert_offsets,
+                    const int32_t *block_expert, int num_valid, int block_m, void *out,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

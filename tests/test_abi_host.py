@@ -118,3 +118,30 @@ def test_workspace_query():
 
 def test_last_hip_error_starts_clear():
     assert lb.lowbit_last_hip_error() == 0
+
+
+def test_lut3_packed_bytes_closed_form():
+    """3-bit indices + one 8-entry E4M3 codebook and one UE8M0 exponent per
+    8 x 64 tile = 3 + 72/512 = 3.140625 bits per weight; the packed blob holds
+    exactly that (plus 256-byte section alignment)."""
+    E, N, K = 128, 1536, 2048
+    nb = lb.lowbit_packed_bytes(lb.LOWBIT_LUT3_E4M3, E, N, K, 0)
+    weights = E * N * K
+    assert abs(nb * 8 / weights - 3.140625) < 1e-6
+    # a 128 x 128 tile: 128*128*3/8 = 6144 index bytes, 512 codebook bytes, 32 exponent bytes
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_LUT3_E4M3, 1, 128, 128, 0) == 6144 + 256 + 256  # sections 256-aligned
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_LUT3_E4M3, 1, 12, 128, 0) == 0      # N % 8
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_LUT3_E4M3, 1, 16, 96, 0) == 0       # K % 64
+
+
+def test_moe_argument_checks():
+    L = lb.LOWBIT_LUT3_E4M3
+    assert lb.lowbit_moe_align(FAKE, 4, 2, 0, 16, None, FAKE, FAKE, FAKE, FAKE) == E_ARG
+    assert lb.lowbit_moe_align(FAKE, 4, 2, 2048, 16, None, FAKE, FAKE, FAKE, FAKE) == E_UNS
+    assert lb.lowbit_moe_align(FAKE, 4, 2, 8, 16, None, None, FAKE, FAKE, FAKE) == E_ARG
+    assert lb.lowbit_moe_gemm(SYM, 8, 64, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 8, 16, FAKE) == E_UNS
+    assert lb.lowbit_moe_gemm(L, 8, 60, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 8, 16, FAKE) == E_ARG
+    assert lb.lowbit_moe_gemm(L, 8, 64, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 8, 24, FAKE) == E_UNS
+    # slot 8 with a_row_div 2 reads row 4 of a 4-row activation matrix
+    assert lb.lowbit_moe_gemm(L, 8, 64, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 9, 16, FAKE) == E_ARG
+    assert lb.lowbit_moe_gemm(L, 8, 64, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 0, 16, FAKE) == lb.LOWBIT_OK
