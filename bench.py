@@ -1,19 +1,28 @@
-"""Benchmark: Llama-3-8B-shaped W4 decode step on one MI355X.
+"""Benchmark of the low-bit weight-only matmul on one MI355X.
 
-One step = the 224 decode GEMVs of a 32-layer Llama-3-8B-shaped decoder in
-layer order (q, k, v, o, gate, up, down per layer; K x N = 4096x4096,
-4096x1024, 4096x1024, 4096x4096, 4096x14336, 4096x14336, 14336x4096), M = 1,
-symmetric INT4 with group size 128, fp16 scales U[0.002, 0.01], fp16
-activations N(0,1) (one distinct input vector per GEMV), fp16 outputs.  Every
-weight is distinct, 3.49 GB of packed codes and 0.11 GB of scales, so the step
-streams 3,603,955,712 algorithmic bytes from HBM and no cache can hold it.
-The step is captured once as a HIP graph and replayed.
+Default workload (the headline): a Llama-3-8B-shaped W4 decode step.  One
+step = the 224 decode GEMVs of a 32-layer decoder in layer order (q, k, v, o,
+gate, up, down; K x N = 4096x4096, 4096x1024, 4096x1024, 4096x4096,
+4096x14336, 4096x14336, 14336x4096), M = 1, symmetric INT4 with group size
+128, fp16 scales U[0.002, 0.01], fp16 activations N(0,1) (one distinct input
+vector per GEMV), fp16 outputs.  Every weight is distinct (3.49 GB of packed
+codes, 0.11 GB of scales): the step streams 3,603,955,712 algorithmic bytes
+and no cache can hold it.  The projections that read the same layer input run
+as one batched launch (q/k/v, gate/up), so a layer is 4 launches in
+dependency order; --unfused runs 7.  The step is captured once as a HIP graph
+and replayed.  Printed: one JSON line with the step's effective HBM GB/s (the
+metric), tokens/s (= steps/s at M = 1), the dominant kernel's roofline entry
+and the CPU oracle's rate on a bounded sample of the same step.
 
-Printed: one JSON line with the effective HBM GB/s of the step (the metric),
-tokens/s (= steps/s at M = 1), the dominant kernel's roofline entry and the
-CPU oracle's rate on a bounded sample.
+Other workloads (--workload), one JSON line each:
+  decode-asym : the same 224 GEMVs with asymmetric INT4, group size 32, int8
+                zero points U{0..15}, M in {1, 2, 4, 8}, 1% outlier channels x20
+  prefill     : W4 GEMM, M in {512, 2048, 8192}, (K, N) in {(4096, 14336),
+                (14336, 4096)}, bf16 in/out, symmetric G=128
+  moe         : 3-bit LUT-codebook MoE, 128 experts, top-8 over 256 tokens,
+                gate/up K=2048 N=1536 and down K=768 N=2048, MXFP8 activations
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-layers L]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
 import json
@@ -29,157 +38,166 @@ import numpy as np  # noqa: E402
 
 METRIC = "W4 decode GEMV effective HBM GB/s (% of peak) and tokens/s at 8B shapes"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 LAYERS = 32
-G = 128
-WORKLOAD_ID = 1
 
 
-def algorithmic_bytes(K, N, M=1, G=128):
-    """Bytes a W4 GEMV must move at least once: codes (0.5 B/weight), fp16
-    scales (2/G B/weight), the fp16 input and output vectors."""
-    return N * K // 2 + N * (K // G) * 2 + M * K * 2 + M * N * 2
+def w4_bytes(K, N, M, G, asym):
+    """Bytes a W4 product must move at least once: codes (0.5 B/weight), fp16
+    scales (2/G B/weight), int8 zero points (1/G B/weight, asymmetric), the
+    fp16 input and output rows."""
+    return N * K // 2 + N * (K // G) * 2 + (N * (K // G) if asym else 0) + M * K * 2 + M * N * 2
 
 
-def build_step(lb, synth, torch):
-    """Pack every weight of the 32-layer step on the GPU; return the launch list."""
-    fmt = lb.LOWBIT_W4_SYM
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+GROUPS_FUSED = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+GROUPS_UNFUSED = (("q",), ("k",), ("v",), ("o",), ("gate",), ("up",), ("down",))
+
+
+def build_step(lb, synth, torch, M, G, asym, workload_id, fused, outlier_frac=0.0):
+    """Pack every weight of the 32-layer step on the GPU; return the launch list.
+    Each launch = one lowbit_gemv_batched call over a group of projections."""
+    fmt = lb.LOWBIT_W4_ASYM if asym else lb.LOWBIT_W4_SYM
+    projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
     launches = []
+    keep = []
     for layer in range(LAYERS):
-        for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS):
-            w = synth.w4_weights(N, K, G, scale_range=(0.002, 0.01), workload_id=WORKLOAD_ID, layer=layer, part=pid)
-            nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
-            packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
-            codes = torch.from_numpy(w["qweight"]).cuda()
-            scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
-            lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, None, packed, nb))
-            x = torch.from_numpy(synth.activations_f16(1, K, workload_id=WORKLOAD_ID, layer=layer, part=pid)).cuda()
-            y = torch.empty((1, N), dtype=torch.float16, device="cuda")
-            wsb = lb.lowbit_workspace_bytes(lb.LOWBIT_OP_GEMV, fmt, 1, N, K, G)
-            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-            launches.append(dict(name=name, K=K, N=N, packed=packed, x=x, y=y, ws=ws, wsb=wsb,
-                                 bytes=algorithmic_bytes(K, N)))
-            del codes, scales
+        for group in (GROUPS_FUSED if fused else GROUPS_UNFUSED):
+            items = []
+            nbytes = 0
+            for name in group:
+                pid, K, N = projs[name]
+                w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
+                                     layer=layer, part=pid)
+                nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
+                packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+                codes = torch.from_numpy(w["qweight"]).cuda()
+                scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
+                zeros = torch.from_numpy(w["zeros"]).cuda() if asym else None
+                lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, zeros, packed, nb))
+                x = torch.from_numpy(synth.activations_f16(M, K, outlier_frac=outlier_frac, workload_id=workload_id,
+                                                           layer=layer, part=pid)).cuda()
+                y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                items.append((packed, x, y, N, K))
+                nbytes += w4_bytes(K, N, M, G, asym)
+                del codes, scales, zeros
+            keep.append(items)
+            launches.append(dict(names=group, probs=lb.make_gemv_problems(items), count=len(items), bytes=nbytes))
     torch.cuda.synchronize()
-    return fmt, launches
+    return fmt, launches, keep
 
 
-def run_step(lb, fmt, launches, stream):
+def run_step(lb, fmt, M, G, launches, stream):
     for L in launches:
-        st = lb.lowbit_gemv(fmt, 1, L["N"], L["K"], G, L["packed"], L["x"], L["y"], L["ws"], L["wsb"], stream)
+        st = lb.lowbit_gemv_batched(fmt, M, G, L["count"], L["probs"], stream)
         if st != 0:
             raise lb.LowbitError(st)
 
 
-def cpu_baseline(synth, layers):
+def capture(torch, fn, stream):
+    with torch.cuda.stream(stream):
+        fn()                                                    # eager warm-up
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def time_graph(torch, graph, stream, steps, warmup):
+    """Exactly `steps` replays after `warmup`, synchronized on both sides.
+    Returns (wall ms per replay, GPU-event ms per replay)."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def time_launches(torch, lb, fmt, M, G, launches, stream, reps):
+    """Each launch bracketed by its own HIP event pair on the launch stream,
+    queued behind a bounded spin kernel so no host gap falls inside a pair.
+    Returns the median duration (us) of every launch over `reps` passes."""
+    per = []
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            pairs = []
+            torch.cuda._sleep(50_000_000)                       # bounded spin while the launches are queued
+            for L in launches:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                st = lb.lowbit_gemv_batched(fmt, M, G, L["count"], L["probs"], stream.cuda_stream)
+                b.record(stream)
+                if st != 0:
+                    raise lb.LowbitError(st)
+                pairs.append((a, b))
+            torch.cuda.synchronize()
+            per.append([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    return np.median(np.array(per), axis=0)
+
+
+def read_traffic(name):
+    """HBM bytes per launch measured with rocprofv3 counters, if recorded."""
+    path = os.path.join(ROOT, "profiles", name)
+    if os.path.exists(path):
+        for line in open(path):
+            if line.startswith("traffic_bytes_per_launch:"):
+                return float(line.split(":")[1])
+    return None
+
+
+def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0):
     """The CPU oracle on the first `layers` layers of the same step (single thread)."""
     import oracle
     t_total = 0.0
     nbytes = 0
     for layer in range(layers):
         for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS):
-            w = synth.w4_weights(N, K, G, scale_range=(0.002, 0.01), workload_id=WORKLOAD_ID, layer=layer, part=pid)
-            x = synth.activations_f16(1, K, workload_id=WORKLOAD_ID, layer=layer, part=pid)
+            w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
+                                 layer=layer, part=pid)
+            x = synth.activations_f16(M, K, outlier_frac=outlier_frac, workload_id=workload_id, layer=layer,
+                                      part=pid)
             t0 = time.perf_counter()
-            oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], None, G, "f16")
+            oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
             t_total += time.perf_counter() - t0
-            nbytes += algorithmic_bytes(K, N)
+            nbytes += w4_bytes(K, N, M, G, asym)
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample="layers 0..%d of the 32-layer step (%d GEMVs, %.1f MB), one thread, %.1f s"
                        % (layers - 1, 7 * layers, nbytes / 1e6, t_total),
-                tokens_per_s=round(layers / LAYERS / t_total, 6))
+                tokens_per_s=round(M * layers / LAYERS / t_total, 6))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-layers", type=int, default=2, help="layers of the step the CPU oracle runs (0 = skip)")
-    ap.add_argument("--kernel-reps", type=int, default=5, help="event-timed passes over the step's launches")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the decode step on a single MI355X "
-              "(--gpus %d requested); multi-GPU sharding is described, not run." % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import bit_weight_only_pack_amd as lb
-    from bit_weight_only_pack_amd import synth
-
-    torch.cuda.set_device(0)
-    fmt, launches = build_step(lb, synth, torch)
+def bench_decode(args, torch, lb, synth):
+    M, G, asym, wid = 1, 128, False, 1
+    fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=not args.unfused)
     step_bytes = sum(L["bytes"] for L in launches)
-
-    # ---- capture the step once as a HIP graph
     stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        run_step(lb, fmt, launches, stream.cuda_stream)        # eager warm-up
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            run_step(lb, fmt, launches, stream.cuda_stream)
-    torch.cuda.synchronize()
-
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            graph.replay()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` replays, synchronized on both sides
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-
-    # ---- dominant kernel: every launch of the step is the W4 GEMV kernel.
-    # Each launch is bracketed by its own HIP event pair on the launch stream,
-    # queued behind a busy stream so no host gap falls inside a pair.
-    per = []
-    with torch.cuda.stream(stream):
-        for _ in range(args.kernel_reps):
-            pairs = []
-            torch.cuda._sleep(50_000_000)                       # bounded spin: keeps the GPU busy while we enqueue
-            for L in launches:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                st = lb.lowbit_gemv(fmt, 1, L["N"], L["K"], G, L["packed"], L["x"], L["y"], L["ws"], L["wsb"],
-                                    stream.cuda_stream)
-                b.record(stream)
-                if st != 0:
-                    raise lb.LowbitError(st)
-                pairs.append((a, b, L))
-            torch.cuda.synchronize()
-            per.append([(a.elapsed_time(b) * 1e3, L) for a, b, L in pairs])
-    kern_us = np.array([[t for t, _ in rep] for rep in per])          # [reps][224]
-    avg_launch_us = float(np.median(kern_us, axis=0).mean())
+    graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
+    ms_per_step, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
+    med = time_launches(torch, lb, fmt, M, G, launches, stream, args.kernel_reps)
+    avg_launch_us = float(med.mean())
     bytes_per_launch = step_bytes / len(launches)
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
-    by_proj = {}
-    med = np.median(kern_us, axis=0)
-    for (t, L), m in zip(per[0], med):
-        by_proj.setdefault(L["name"], []).append((m, L["bytes"]))
-    proj_stats = {k: dict(us=round(float(np.mean([a for a, _ in v])), 3),
-                          GBps=round(float(np.mean([b / (a * 1e-6) / 1e9 for a, b in v])), 1))
-                  for k, v in by_proj.items()}
-
-    profile_txt = os.path.join(ROOT, "profiles", "w4_gemv_decode_step_traffic.txt")
-    traffic = None
-    if os.path.exists(profile_txt):
-        for line in open(profile_txt):
-            if line.startswith("traffic_bytes_per_launch:"):
-                traffic = float(line.split(":")[1])
-
+    groups = {}
+    for L, t in zip(launches, med):
+        groups.setdefault("+".join(L["names"]), []).append((t, L["bytes"]))
+    per_group = {k: dict(us=round(float(np.mean([a for a, _ in v])), 3),
+                         GBps=round(float(np.mean([b / (a * 1e-6) / 1e9 for a, b in v])), 1))
+                 for k, v in groups.items()}
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -194,21 +212,160 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic (seeded; random INT4 codes, U[0.002,0.01] fp16 scales, N(0,1) fp16 inputs)",
-        "config": {"workload": "llama3-8b-w4-decode-step", "layers": LAYERS, "gemvs_per_step": len(launches),
-                   "M": 1, "group_size": G, "format": "int4 symmetric, fp16 scales", "bytes_per_step": step_bytes},
+        "config": {"workload": "llama3-8b-w4-decode-step", "layers": LAYERS, "gemvs_per_step": 7 * LAYERS,
+                   "launches_per_step": len(launches), "M": M, "group_size": G,
+                   "format": "int4 symmetric, fp16 scales", "bytes_per_step": step_bytes},
         "tokens_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "gpu_ms_per_step": round(gpu_ms, 4),
         "kernel_sum_ms_per_step": round(float(med.sum()) / 1e3, 4),
-        "per_projection": proj_stats,
+        "per_launch_group": per_group,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": read_traffic("w4_gemv_decode_step_traffic.txt"),
                      "kernel": "gemv_w4_kernel<G=128,sym,M=1>", "bytes_per_launch": round(bytes_per_launch),
                      "avg_launch_us": round(avg_launch_us, 3)},
     }
     if args.cpu_layers > 0:
-        out["cpu_baseline"] = cpu_baseline(synth, args.cpu_layers)
-    print(json.dumps(out), flush=True)
+        out["cpu_baseline"] = cpu_baseline_decode(synth, args.cpu_layers, M, G, asym, wid)
+    del keep
+    return out
+
+
+def bench_decode_asym(args, torch, lb, synth):
+    G, asym, wid = 32, True, 2
+    res = {}
+    for M in (1, 2, 4, 8):
+        fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=True, outlier_frac=0.01)
+        step_bytes = sum(L["bytes"] for L in launches)
+        stream = torch.cuda.Stream()
+        graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
+        ms, _ = time_graph(torch, graph, stream, args.steps, args.warmup)
+        med = time_launches(torch, lb, fmt, M, G, launches, stream, 2)
+        res["M=%d" % M] = dict(ms_per_step=round(ms, 4), GBps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                               tokens_per_s=round(M * 1e3 / ms, 1), bytes_per_step=step_bytes,
+                               kernel_sum_ms=round(float(med.sum()) / 1e3, 4))
+        del graph, keep, launches
+        torch.cuda.empty_cache()
+    best = max(v["GBps"] for v in res.values())
+    return {"metric": "W4 asymmetric G=32 small-batch decode step effective HBM GB/s", "value": best,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "dtype": "f16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": "llama3-8b-w4-asym-g32-decode-step", "M": [1, 2, 4, 8], "group_size": G},
+            "per_M": res}
+
+
+def bench_prefill(args, torch, lb, synth):
+    fmt, G = lb.LOWBIT_W4_SYM, 128
+    res = {}
+    total_flop, total_ms = 0.0, 0.0
+    for K, N in ((4096, 14336), (14336, 4096)):
+        w = synth.w4_weights(N, K, G, workload_id=3, layer=0, part=N)
+        nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
+        packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, torch.from_numpy(w["qweight"]).cuda(),
+                                        torch.from_numpy(w["scales"].view(np.uint16)).cuda(), None, packed, nb))
+        for M in (512, 2048, 8192):
+            a = torch.from_numpy(synth.activations_bf16(M, K, workload_id=3, layer=M, part=K).view(np.int16)).cuda()
+            c = torch.empty((M, N), dtype=torch.int16, device="cuda")
+            wsb = lb.lowbit_workspace_bytes(lb.LOWBIT_OP_GEMM, fmt, M, N, K, G)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+            stream = torch.cuda.Stream()
+
+            def fn():
+                st = lb.lowbit_gemm(fmt, M, N, K, G, packed, a, lb.LOWBIT_BF16, c, lb.LOWBIT_BF16, ws, wsb,
+                                    stream.cuda_stream)
+                if st != 0:
+                    raise lb.LowbitError(st)
+            graph = capture(torch, fn, stream)
+            ms, _ = time_graph(torch, graph, stream, max(3, args.steps // 5), 2)
+            flop = 2.0 * M * N * K
+            tf = flop / (ms * 1e-3) / 1e12
+            res["M=%d K=%d N=%d" % (M, K, N)] = dict(us=round(ms * 1e3, 1), TFLOPs=round(tf, 1),
+                                                     pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2))
+            total_flop += flop
+            total_ms += ms
+            del graph
+    agg = total_flop / (total_ms * 1e-3) / 1e12
+    return {"metric": "W4 prefill GEMM TFLOP/s (bf16 MFMA, fp32 accumulate)", "value": round(agg, 1),
+            "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "vs_baseline": None, "config": {"workload": "w4-prefill-gemm", "group_size": G},
+            "roofline": {"bound": "mfma", "achieved": round(agg, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "per_shape": res}
+
+
+def bench_moe(args, torch, lb, synth):
+    T, E, top_k, bm = 256, 128, 8, 16
+    L3 = lb.LOWBIT_LUT3_E4M3
+    topk = torch.from_numpy(synth.moe_routing(T, E, top_k, workload_id=4)).cuda()
+    cap = T * top_k + E * (bm - 1)
+    ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    blk = torch.empty(cap // bm, dtype=torch.int32, device="cuda")
+    npp = torch.empty(1, dtype=torch.int32, device="cuda")
+    res = {}
+    stream = torch.cuda.Stream()
+    for proj, (K, N, div, part) in (("gate_up", (2048, 1536, top_k, 0)), ("down", (768, 2048, 1, 1))):
+        d = synth.lut3_weights(E, N, K, workload_id=4, part=part)
+        nb = lb.lowbit_packed_bytes(L3, E, N, K, 0)
+        packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        lb.check(lb.lowbit_pack_weights(L3, E, N, K, 0, torch.from_numpy(d["idx"]).cuda(),
+                                        torch.from_numpy(d["cb"]).cuda(), torch.from_numpy(d["ex"]).cuda(), packed,
+                                        nb))
+        del d
+        rows = T if div == top_k else T * top_k
+        aq, as_ = synth.mxfp8_activations(rows, K, workload_id=4, part=part)
+        aq, as_ = torch.from_numpy(aq).cuda(), torch.from_numpy(as_).cuda()
+        out = torch.empty((T * top_k, N), dtype=torch.int16, device="cuda")
+
+        def fn():
+            lb.check(lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, stream.cuda_stream))
+            lb.check(lb.lowbit_moe_gemm(L3, E, N, K, packed, E, aq, as_, rows, div, ids, offs, blk, T * top_k, bm,
+                                        out, stream.cuda_stream))
+        graph = capture(torch, fn, stream)
+        ms, _ = time_graph(torch, graph, stream, args.steps, args.warmup)
+        byts = nb + aq.numel() + as_.numel() + out.numel() * 2
+        gbps = byts / (ms * 1e-3) / 1e9
+        res[proj] = dict(us=round(ms * 1e3, 2), bytes=int(byts), GBps=round(gbps, 1),
+                         pct_hbm_peak=round(100 * gbps / HBM_PEAK_GBPS, 2))
+        del graph, packed
+    total_b = sum(v["bytes"] for v in res.values())
+    total_us = sum(v["us"] for v in res.values())
+    gbps = total_b / (total_us * 1e-6) / 1e9
+    return {"metric": "3-bit LUT MoE grouped GEMM (align + GEMM) effective HBM GB/s", "value": round(gbps, 1),
+            "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "fp8 (MXFP8 x LUT3 E4M3)",
+            "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": "lut3-moe-256tok-128e-top8", "block_m": bm},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4)},
+            "per_projection": res}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "decode-asym", "prefill", "moe"])
+    ap.add_argument("--unfused", action="store_true", help="decode: one launch per GEMV (7 per layer)")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="decode: layers the CPU oracle runs (0 = skip)")
+    ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the decode step, prefill GEMM and MoE run on a single MI355X "
+              "(--gpus %d requested); multi-GPU sharding is described, not run." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_only_pack_amd as lb
+    from bit_weight_only_pack_amd import synth
+
+    torch.cuda.set_device(0)
+    fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "prefill": bench_prefill,
+          "moe": bench_moe}[args.workload]
+    print(json.dumps(fn(args, torch, lb, synth)), flush=True)
 
 
 if __name__ == "__main__":

@@ -32,6 +32,13 @@ LOWBIT_OP_GEMM = 1
 _lib = None
 
 _vp = ctypes.c_void_p
+
+
+class lowbit_gemv_problem(ctypes.Structure):
+    """Mirror of the C struct of the same name in include/lowbit.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
 
@@ -46,6 +53,7 @@ SIGNATURES = {
     "lowbit_dequant": (_i, [_i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lowbit_gemv_batched": (_i, [_i, _i, _i, _i, _vp, _vp]),
     "lowbit_gemm": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "lowbit_moe_align": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lowbit_moe_gemm": (_i, [_i, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
@@ -157,3 +165,17 @@ def lowbit_moe_gemm(fmt, E_local, N, K, packed, E, a_e4m3, a_ue8m0, a_rows, a_ro
     return lib().lowbit_moe_gemm(fmt, E_local, N, K, _ptr(packed), E, _ptr(a_e4m3), _ptr(a_ue8m0), a_rows,
                                  a_row_div, _ptr(sorted_ids), _ptr(expert_offsets), _ptr(block_expert), num_valid,
                                  block_m, _ptr(out), _stream(stream))
+
+
+def make_gemv_problems(problems):
+    """[(packed, x, y, N, K), ...] -> a ctypes array of lowbit_gemv_problem."""
+    arr = (lowbit_gemv_problem * max(len(problems), 1))()
+    for i, (packed, x, y, N, K) in enumerate(problems):
+        arr[i] = lowbit_gemv_problem(_ptr(packed), _ptr(x), _ptr(y), N, K)
+    return arr
+
+
+def lowbit_gemv_batched(fmt, M, group_size, count, problems, stream=None):
+    """problems: a ctypes array from make_gemv_problems (host memory)."""
+    return lib().lowbit_gemv_batched(fmt, M, group_size, count, ctypes.cast(problems, ctypes.c_void_p),
+                                     _stream(stream))

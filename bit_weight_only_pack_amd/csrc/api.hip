@@ -188,6 +188,33 @@ int lowbit_gemv(int fmt, int M, int N, int K, int group_size, const void *packed
                                      ws_bytes, (hipStream_t)stream));
 }
 
+int lowbit_gemv_batched(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems, void *stream)
+{
+    if (count < 0 || M < 0) return LOWBIT_E_INVALID_ARG;
+    if (count > kMaxGemvBatch || M > 16) return LOWBIT_E_UNSUPPORTED;
+    if (count == 0 || M == 0) return LOWBIT_OK;
+    if (problems == nullptr) return LOWBIT_E_INVALID_ARG;
+    W4Layout L[kMaxGemvBatch];
+    const uint8_t *packed[kMaxGemvBatch];
+    const _Float16 *x[kMaxGemvBatch];
+    _Float16 *y[kMaxGemvBatch];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        const lowbit_gemv_problem &p = problems[i];
+        int st = check_w4_shape(fmt, p.N, p.K, group_size);
+        if (st != LOWBIT_OK) return st;
+        if (p.N == 0) continue;                        // nothing to compute for this one
+        if (p.packed == nullptr || p.y == nullptr || (p.K > 0 && p.x == nullptr)) return LOWBIT_E_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(p.x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+        L[n] = w4_layout(p.N, p.K, group_size, fmt == LOWBIT_W4_ASYM);
+        packed[n] = static_cast<const uint8_t *>(p.packed);
+        x[n] = static_cast<const _Float16 *>(p.x);
+        y[n] = static_cast<_Float16 *>(p.y);
+        ++n;
+    }
+    return hip_status(launch_gemv_w4_batch(L, n, M, packed, x, y, (hipStream_t)stream));
+}
+
 int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed, const void *a, int a_dtype,
                 void *c, int c_dtype, void *workspace, size_t ws_bytes, void *stream)
 {

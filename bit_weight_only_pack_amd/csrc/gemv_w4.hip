@@ -140,26 +140,34 @@ __host__ __device__ inline int64_t gemv_lds_bytes(int M, int ct, int W, int MR)
     return (int64_t)M * x_row_halfs(ct) * 2 + (int64_t)W * MR * 64 * 4;
 }
 
-// One workgroup = one 16-row strip (all of K).  Its K tiles are taken in
-// rounds of W*P: in a round, wave w owns tiles round + w + u*W (u < P) and
-// issues all of their weight loads before any arithmetic (branch-free buffer
-// loads; slots past the last tile read zeros and are skipped).  The
-// activations of the round are staged in LDS `ct` tiles at a time (all at
-// once whenever they fit, which covers every decode shape).
+// One workgroup = one 16-row strip (all of K) of one problem of the batch
+// (problems are laid end to end over blockIdx.x).  The strip's K tiles are
+// taken in rounds of W*P: in a round, wave w owns tiles round + w + u*W
+// (u < P) and issues all of their weight loads before any arithmetic
+// (branch-free buffer loads; slots past the last tile read zeros and are
+// skipped).  The activations of the round are staged in LDS `ct` tiles at a
+// time (all at once whenever they fit, which covers every decode shape).
 template <int G, bool ASYM, int MR, int P>
 // min waves per SIMD (VGPR budget 512 / waves): 8 (64) for 4 tiles in flight,
 // 6 (85) for 8; asymmetric G=32 carries three metadata words per tile
 __global__ __launch_bounds__(1024, (P <= 4 ? (ASYM && G == 32 ? 7 : 8) : (ASYM ? 5 : 6)))
-void gemv_w4_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                    const uint8_t *__restrict__ zeros, const _Float16 *__restrict__ x,
-                    _Float16 *__restrict__ y, int M, int N, int K, int ktiles, int ct)
+void gemv_w4_kernel(const GemvBatch b)
 {
     constexpr int GPT = 128 / G;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // the problem of this workgroup (wave-uniform scan of at most 8 entries)
+    int pi = 0;
+    while (pi + 1 < b.count && (int)blockIdx.x >= b.p[pi + 1].strip_begin) ++pi;
+    const GemvProblem &pr = b.p[pi];
+    const uint8_t *codes = pr.codes, *scales = pr.scales, *zeros = pr.zeros;
+    const _Float16 *x = pr.x;
+    _Float16 *y = pr.y;
+    const int M = b.M, N = pr.N, K = pr.K, ktiles = pr.ktiles, ct = b.ct;
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const int strip = blockIdx.x;
+    const int strip = (int)blockIdx.x - pr.strip_begin;
     const int r = lane & 15;                         // B column (weight row) and A row (token)
     const int kq = lane >> 4;                        // 8-K slice inside each 32-K MFMA block
     const int xrow = x_row_halfs(ct);
@@ -255,38 +263,52 @@ void gemv_w4_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict
 }
 
 template <int G, bool ASYM, int MR>
-hipError_t launch_p(int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const uint8_t *codes,
-                    const uint8_t *scales, const uint8_t *zeros, const _Float16 *x, _Float16 *y, int M, int N,
-                    int K, int ktiles, int ct)
+hipError_t launch_p(int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const GemvBatch &b)
 {
     if (P <= 4)
-        gemv_w4_kernel<G, ASYM, MR, 4><<<grid, block, lds, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles, ct);
+        gemv_w4_kernel<G, ASYM, MR, 4><<<grid, block, lds, s>>>(b);
     else
-        gemv_w4_kernel<G, ASYM, MR, 8><<<grid, block, lds, s>>>(codes, scales, zeros, x, y, M, N, K, ktiles, ct);
+        gemv_w4_kernel<G, ASYM, MR, 8><<<grid, block, lds, s>>>(b);
     return hipGetLastError();
 }
 
 template <int G, bool ASYM>
-hipError_t launch_gm(int MR, int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const uint8_t *codes,
-                     const uint8_t *scales, const uint8_t *zeros, const _Float16 *x, _Float16 *y, int M, int N,
-                     int K, int ktiles, int ct)
+hipError_t launch_gm(int MR, int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const GemvBatch &b)
 {
-    if (MR == 1) return launch_p<G, ASYM, 1>(P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, ct);
-    if (MR == 2) return launch_p<G, ASYM, 2>(P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, ct);
-    return launch_p<G, ASYM, 4>(P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, ct);
+    if (MR == 1) return launch_p<G, ASYM, 1>(P, grid, block, lds, s, b);
+    if (MR == 2) return launch_p<G, ASYM, 2>(P, grid, block, lds, s, b);
+    return launch_p<G, ASYM, 4>(P, grid, block, lds, s, b);
 }
 
 }  // namespace
 
 size_t gemv_w4_workspace(int, int64_t, int64_t, int) { return 0; }
 
-hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
-                          _Float16 *y, void *, size_t, hipStream_t s)
+hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
+                                const _Float16 *const *x, _Float16 *const *y, hipStream_t s)
 {
-    if (M == 0 || L.N == 0) return hipSuccess;
+    if (M == 0 || count == 0) return hipSuccess;
+    GemvBatch b;
+    int64_t strips = 0, kt = 0;
+    for (int i = 0; i < count; ++i) {
+        GemvProblem &p = b.p[i];
+        p.codes = packed[i] + L[i].codes_off;
+        p.scales = packed[i] + L[i].scales_off;
+        p.zeros = L[i].asym ? packed[i] + L[i].zeros_off : nullptr;
+        p.x = x[i];
+        p.y = y[i];
+        p.N = (int)L[i].N;
+        p.K = (int)L[i].K;
+        p.ktiles = (int)L[i].ktiles;
+        p.strip_begin = (int)strips;
+        strips += L[i].strips;
+        if (L[i].ktiles > kt) kt = L[i].ktiles;
+    }
+    b.count = count;
+    b.M = M;
+    if (strips == 0) return hipSuccess;
     // waves per workgroup: enough that each wave holds at most 4 tiles (8 for
     // long K), capped at 16 waves
-    const int64_t kt = L.ktiles;
     int W = (int)((kt + 3) / 4);
     if (W < 1) W = 1;
     if (W > 16) W = 16;
@@ -297,23 +319,20 @@ hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const
     int64_t ct = kt < round_tiles ? kt : round_tiles;
     while (ct > 1 && gemv_lds_bytes(M, (int)ct, W, MR) > (int64_t)kMaxLds) ct = (ct + 1) / 2;
     if (ct < 1) ct = 1;
+    b.ct = (int)ct;
     const size_t lds = (size_t)gemv_lds_bytes(M, (int)ct, W, MR);
-    const dim3 grid((unsigned)L.strips), block((unsigned)(W * 64));
-    const uint8_t *codes = packed + L.codes_off;
-    const uint8_t *scales = packed + L.scales_off;
-    const uint8_t *zeros = L.asym ? packed + L.zeros_off : nullptr;
-    const int N = (int)L.N, K = (int)L.K, ktiles = (int)L.ktiles;
-    switch (L.G) {
-    case 32:
-        return L.asym ? launch_gm<32, true>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct)
-                      : launch_gm<32, false>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct);
-    case 64:
-        return L.asym ? launch_gm<64, true>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct)
-                      : launch_gm<64, false>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct);
-    default:
-        return L.asym ? launch_gm<128, true>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct)
-                      : launch_gm<128, false>(MR, P, grid, block, lds, s, codes, scales, zeros, x, y, M, N, K, ktiles, (int)ct);
+    const dim3 grid((unsigned)strips), block((unsigned)(W * 64));
+    switch (L[0].G) {
+    case 32: return L[0].asym ? launch_gm<32, true>(MR, P, grid, block, lds, s, b) : launch_gm<32, false>(MR, P, grid, block, lds, s, b);
+    case 64: return L[0].asym ? launch_gm<64, true>(MR, P, grid, block, lds, s, b) : launch_gm<64, false>(MR, P, grid, block, lds, s, b);
+    default: return L[0].asym ? launch_gm<128, true>(MR, P, grid, block, lds, s, b) : launch_gm<128, false>(MR, P, grid, block, lds, s, b);
     }
+}
+
+hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
+                          _Float16 *y, void *, size_t, hipStream_t s)
+{
+    return launch_gemv_w4_batch(&L, 1, M, &packed, &x, &y, s);
 }
 
 }  // namespace lowbit

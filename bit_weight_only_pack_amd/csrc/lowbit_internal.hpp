@@ -86,6 +86,22 @@ hipError_t launch_w4_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *c
                             uint16_t *scales, int8_t *zeros, hipStream_t s);
 hipError_t launch_w4_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s);
 
+// A batch of independent GEMVs with the same format, M and group size, run by
+// one launch (problems laid end to end over the grid, one strip per workgroup).
+constexpr int kMaxGemvBatch = 8;
+struct GemvProblem {
+    const uint8_t *codes, *scales, *zeros;
+    const _Float16 *x;
+    _Float16 *y;
+    int N, K, ktiles, strip_begin;
+};
+struct GemvBatch {
+    GemvProblem p[kMaxGemvBatch];
+    int count, M, ct;
+};
+hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
+                                const _Float16 *const *x, _Float16 *const *y, hipStream_t s);
+
 size_t gemv_w4_workspace(int M, int64_t N, int64_t K, int G);
 hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
                           _Float16 *y, void *ws, size_t ws_bytes, hipStream_t s);

@@ -150,6 +150,27 @@ int lowbit_gemv(int fmt, int M, int N, int K, int group_size,
                 const void *packed, const void *x, void *y,
                 void *workspace, size_t ws_bytes, void *stream);
 
+/* One GEMV of a batch: y = x @ W^T with W packed for (fmt, 1, N, K, group_size). */
+typedef struct lowbit_gemv_problem {
+    const void *packed;  /* device blob from lowbit_pack_weights               */
+    const void *x;       /* device f16 [M][K], 16-byte aligned                 */
+    void *y;             /* device f16 [M][N]; must not overlap any input      */
+    int N, K;
+} lowbit_gemv_problem;
+
+/*
+ * Up to 8 independent GEMVs (same fmt, M and group_size, any N and K) in one
+ * launch, each with exactly the result of lowbit_gemv.  This is the fused
+ * launch for projections that read the same layer input, e.g. q/k/v and
+ * gate/up of a decoder layer ("BaseRT" wiki chapter, "BaseRT's approach":
+ * interleaved QKV weights and fewer, batched submissions cut the per-kernel
+ * overhead that dominates batch-1 decode).  `problems` is a HOST array of
+ * `count` entries, read during the call.  count > 8 -> LOWBIT_E_UNSUPPORTED.
+ * No workspace.
+ */
+int lowbit_gemv_batched(int fmt, int M, int group_size, int count,
+                        const lowbit_gemv_problem *problems, void *stream);
+
 /*
  * Prefill GEMM with W4 weights ("Low Bit ARM kernels": prefill is the same
  * product over many tokens; "Low Bit Metal Kernels": activation and weight

@@ -145,3 +145,15 @@ def test_moe_argument_checks():
     # slot 8 with a_row_div 2 reads row 4 of a 4-row activation matrix
     assert lb.lowbit_moe_gemm(L, 8, 64, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 9, 16, FAKE) == E_ARG
     assert lb.lowbit_moe_gemm(L, 8, 64, 128, FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, 0, 16, FAKE) == lb.LOWBIT_OK
+
+
+def test_gemv_batched_argument_checks():
+    probs = lb.make_gemv_problems([(FAKE, FAKE, FAKE, 64, 256)] * 9)
+    assert lb.lowbit_gemv_batched(SYM, 1, 32, 9, probs) == E_UNS          # more than 8 problems
+    assert lb.lowbit_gemv_batched(SYM, 1, 32, 0, probs) == lb.LOWBIT_OK
+    assert lb.lowbit_gemv_batched(SYM, 1, 32, -1, probs) == E_ARG
+    bad = lb.make_gemv_problems([(FAKE, FAKE, FAKE, 64, 256), (FAKE, FAKE, FAKE, 64, 250)])
+    assert lb.lowbit_gemv_batched(SYM, 1, 32, 2, bad) == E_ARG              # K % G in the second problem
+    nul = lb.make_gemv_problems([(FAKE, FAKE, None, 64, 256)])
+    assert lb.lowbit_gemv_batched(SYM, 1, 32, 1, nul) == E_ARG
+    assert lb.lowbit_gemv_batched(SYM, 17, 32, 1, probs) == E_UNS

@@ -168,3 +168,41 @@ def test_gemv_llama3_8b_shapes_asym_g32(proj, M):
     rows = np.sort(np.random.default_rng(pid).choice(N, size=128, replace=False))
     sub = dict(qweight=w["qweight"][rows], scales=w["scales"][rows], zeros=w["zeros"][rows])
     assert_close(y[:, rows], _ref(sub, x, 32), "%s M=%d" % (proj, M))
+
+
+# ---------------------------------------------------------------- batched GEMV
+def test_gemv_batched_matches_single_bitexact():
+    """q/k/v-shaped problems (same K) in one launch give exactly the single-GEMV results."""
+    shapes = [(4096, 4096), (4096, 1024), (4096, 1024)]
+    ws, xs, packs = [], [], []
+    for i, (K, N) in enumerate(shapes):
+        w = synth.w4_weights(N, K, 128, workload_id=WL, layer=77, part=i)
+        ws.append(w)
+        xs.append(synth.activations_f16(1, K, workload_id=WL, layer=77, part=i))
+        packs.append(pack_w4(w, 128)[1])
+    singles = [gemv(w, x, 128, p) for w, x, p in zip(ws, xs, packs)]
+    xd = [dev(x) for x in xs]
+    yd = [torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda") for _, N in shapes]
+    probs = lb.make_gemv_problems([(packs[i], xd[i], yd[i], shapes[i][1], shapes[i][0]) for i in range(3)])
+    lb.check(lb.lowbit_gemv_batched(lb.LOWBIT_W4_SYM, 1, 128, 3, probs))
+    torch.cuda.synchronize()
+    for y, s in zip(yd, singles):
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), s.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_gemv_batched_mixed_shapes(M):
+    """Different K and ragged N in one launch (asymmetric G=32), each against the oracle."""
+    shapes = [(4096, 4096), (14336, 512), (1056, 300), (256, 16)]
+    items = []
+    for i, (K, N) in enumerate(shapes):
+        w = synth.w4_weights(N, K, 32, asym=True, workload_id=WL, layer=78, part=i)
+        x = synth.activations_f16(M, K, outlier_frac=0.01, workload_id=WL, layer=78 + M, part=i)
+        fmt, packed, _ = pack_w4(w, 32)
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        items.append((w, x, packed, dev(x), y, N, K))
+    probs = lb.make_gemv_problems([(p, xd, y, N, K) for (_, _, p, xd, y, N, K) in items])
+    lb.check(lb.lowbit_gemv_batched(lb.LOWBIT_W4_ASYM, M, 32, len(items), probs))
+    torch.cuda.synchronize()
+    for (w, x, _, _, y, N, K) in items:
+        assert_close(f16_to_f64(y.cpu().numpy()), _ref(w, x, 32), "batched K=%d N=%d" % (K, N))
