@@ -189,7 +189,9 @@ def bench_decode(args, torch, lb, synth):
     graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
     ms_per_step, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
     med = time_launches(torch, lb, fmt, M, G, launches, stream, args.kernel_reps)
-    avg_launch_us = float(med.mean())
+    # every node of the step graph is one GEMV launch, back to back on `stream`:
+    # the event-timed replay region divided by the launches is their mean duration
+    avg_launch_us = gpu_ms * 1e3 / len(launches)
     bytes_per_launch = step_bytes / len(launches)
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
     groups = {}
@@ -224,7 +226,8 @@ def bench_decode(args, torch, lb, synth):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": read_traffic("w4_gemv_decode_step_traffic.txt"),
                      "kernel": "gemv_w4_kernel<G=128,sym,M=1>", "bytes_per_launch": round(bytes_per_launch),
-                     "avg_launch_us": round(avg_launch_us, 3)},
+                     "avg_launch_us": round(avg_launch_us, 3),
+                     "avg_launch_us_isolated": round(float(med.mean()), 3)},
     }
     if args.cpu_layers > 0:
         out["cpu_baseline"] = cpu_baseline_decode(synth, args.cpu_layers, M, G, asym, wid)
@@ -351,6 +354,8 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="decode: one launch per GEMV (7 per layer)")
     ap.add_argument("--cpu-layers", type=int, default=2, help="decode: layers the CPU oracle runs (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic for counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -363,6 +368,12 @@ def main():
     from bit_weight_only_pack_amd import synth
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "prefill": bench_prefill,
           "moe": bench_moe}[args.workload]
     print(json.dumps(fn(args, torch, lb, synth)), flush=True)
