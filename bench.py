@@ -9,8 +9,9 @@ vector per GEMV), fp16 outputs.  Every weight is distinct (3.49 GB of packed
 codes, 0.11 GB of scales): the step streams 3,603,955,712 algorithmic bytes
 and no cache can hold it.  The projections that read the same layer input run
 as one batched launch (q/k/v, gate/up), so a layer is 4 launches in
-dependency order; --unfused runs 7.  The step is captured once as a HIP graph
-and replayed.  Printed: one JSON line with the step's effective HBM GB/s (the
+dependency order (--mode unfused runs 7; --mode chain runs the whole step as
+one persistent launch whose stages wait for each other on the GPU).  The step
+is captured once as a HIP graph and replayed.  Printed: one JSON line with the step's effective HBM GB/s (the
 metric), tokens/s (= steps/s at M = 1), the dominant kernel's roofline entry
 and the CPU oracle's rate on a bounded sample of the same step.
 
@@ -94,6 +95,29 @@ def run_step(lb, fmt, M, G, launches, stream):
         st = lb.lowbit_gemv_batched(fmt, M, G, L["count"], L["probs"], stream)
         if st != 0:
             raise lb.LowbitError(st)
+
+
+def build_chain(lb, torch, fmt, M, G, keep):
+    """The whole step as one lowbit_gemv_chain: stage = launch group in layer
+    order (q+k+v | o | gate+up | down per layer), so every group waits for the
+    previous one exactly as the launches of the batched step do."""
+    items, stages = [], []
+    for gi, group in enumerate(keep):
+        for it in group:
+            items.append(it)
+            stages.append(gi)
+    probs = lb.make_gemv_problems(items)
+    nb = lb.lowbit_gemv_chain_bytes(len(items), stages[-1] + 1)
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    chain = lb.lowbit_gemv_chain()
+    lb.check(lb.lowbit_gemv_chain_init(chain, fmt, M, G, len(items), probs, stages, 0, buf, nb))
+    return chain, (buf, probs)
+
+
+def run_chain(lb, chain, stream):
+    st = lb.lowbit_gemv_chain_run(chain, stream)
+    if st != 0:
+        raise lb.LowbitError(st)
 
 
 def capture(torch, fn, stream):
@@ -183,23 +207,39 @@ def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0
 
 def bench_decode(args, torch, lb, synth):
     M, G, asym, wid = 1, 128, False, 1
-    fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=not args.unfused)
+    mode = args.mode
+    fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=(mode != "unfused"))
     step_bytes = sum(L["bytes"] for L in launches)
     stream = torch.cuda.Stream()
-    graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
+    if mode == "chain":
+        chain, chain_keep = build_chain(lb, torch, fmt, M, G, keep)
+        graph = capture(torch, lambda: run_chain(lb, chain, stream.cuda_stream), stream)
+    else:
+        graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
     ms_per_step, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
-    med = time_launches(torch, lb, fmt, M, G, launches, stream, args.kernel_reps)
-    # every node of the step graph is one GEMV launch, back to back on `stream`:
-    # the event-timed replay region divided by the launches is their mean duration
-    avg_launch_us = gpu_ms * 1e3 / len(launches)
-    bytes_per_launch = step_bytes / len(launches)
+    st_err = 0
+    if mode == "chain":
+        # one launch per step: its duration is the event-timed replay region per step
+        n_launch, kernel = 1, "gemv_chain_kernel<G=128,sym,M=1> (whole step, one launch)"
+        st, st_err = lb.lowbit_gemv_chain_error(chain, stream.cuda_stream)
+        lb.check(st)
+        if st_err:
+            raise RuntimeError("chain dependency wait timed out (error word %d)" % st_err)
+        per_group = None
+    else:
+        med = time_launches(torch, lb, fmt, M, G, launches, stream, args.kernel_reps)
+        n_launch, kernel = len(launches), "gemv_w4_kernel<G=128,sym,M=1>"
+        groups = {}
+        for L, t in zip(launches, med):
+            groups.setdefault("+".join(L["names"]), []).append((t, L["bytes"]))
+        per_group = {k: dict(us=round(float(np.mean([a for a, _ in v])), 3),
+                             GBps=round(float(np.mean([b / (a * 1e-6) / 1e9 for a, b in v])), 1))
+                     for k, v in groups.items()}
+    # the graph's nodes run back to back on `stream`: the event-timed replay
+    # region divided by the launches of a step is their mean duration
+    avg_launch_us = gpu_ms * 1e3 / n_launch
+    bytes_per_launch = step_bytes / n_launch
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
-    groups = {}
-    for L, t in zip(launches, med):
-        groups.setdefault("+".join(L["names"]), []).append((t, L["bytes"]))
-    per_group = {k: dict(us=round(float(np.mean([a for a, _ in v])), 3),
-                         GBps=round(float(np.mean([b / (a * 1e-6) / 1e9 for a, b in v])), 1))
-                 for k, v in groups.items()}
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -215,20 +255,20 @@ def bench_decode(args, torch, lb, synth):
         "dtype": "f16",
         "data": "synthetic (seeded; random INT4 codes, U[0.002,0.01] fp16 scales, N(0,1) fp16 inputs)",
         "config": {"workload": "llama3-8b-w4-decode-step", "layers": LAYERS, "gemvs_per_step": 7 * LAYERS,
-                   "launches_per_step": len(launches), "M": M, "group_size": G,
+                   "launches_per_step": n_launch, "M": M, "group_size": G, "mode": mode,
                    "format": "int4 symmetric, fp16 scales", "bytes_per_step": step_bytes},
         "tokens_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "gpu_ms_per_step": round(gpu_ms, 4),
-        "kernel_sum_ms_per_step": round(float(med.sum()) / 1e3, 4),
-        "per_launch_group": per_group,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic("w4_gemv_decode_step_traffic.txt"),
-                     "kernel": "gemv_w4_kernel<G=128,sym,M=1>", "bytes_per_launch": round(bytes_per_launch),
-                     "avg_launch_us": round(avg_launch_us, 3),
-                     "avg_launch_us_isolated": round(float(med.mean()), 3)},
+                     "traffic": read_traffic("w4_gemv_decode_step_traffic.txt" if mode != "chain"
+                                             else "w4_gemv_chain_decode_step_traffic.txt"),
+                     "kernel": kernel, "bytes_per_launch": round(bytes_per_launch),
+                     "avg_launch_us": round(avg_launch_us, 3)},
     }
+    if per_group is not None:
+        out["per_launch_group"] = per_group
     if args.cpu_layers > 0:
         out["cpu_baseline"] = cpu_baseline_decode(synth, args.cpu_layers, M, G, asym, wid)
     del keep
@@ -351,7 +391,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=["decode", "decode-asym", "prefill", "moe"])
-    ap.add_argument("--unfused", action="store_true", help="decode: one launch per GEMV (7 per layer)")
+    ap.add_argument("--mode", default="batched", choices=["chain", "batched", "unfused"],
+                    help="decode: chain = the whole step as one persistent launch with stage dependencies; "
+                         "batched = one launch per group of GEMVs sharing an input (4 per layer); "
+                         "unfused = one launch per GEMV (7 per layer)")
     ap.add_argument("--cpu-layers", type=int, default=2, help="decode: layers the CPU oracle runs (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
     ap.add_argument("--calibrate-copy", action="store_true",

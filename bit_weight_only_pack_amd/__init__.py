@@ -3,8 +3,7 @@
 The compute lives in ``liblowbit.so`` (hand-written HIP kernels behind the C
 ABI declared in ``include/lowbit.h``); ``_lib`` is a thin ctypes binding with
 the same entry-point names.  PyTorch is used only for device memory and
-streams.  ``synth`` draws the seeded synthetic workloads.  ``ops`` holds small
-tensor-level helpers built on the binding.
+streams.  ``synth`` draws the seeded synthetic workloads.
 """
 from ._lib import *  # noqa: F401,F403
 from ._lib import LowbitError, check, lib  # noqa: F401

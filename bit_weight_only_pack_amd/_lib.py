@@ -39,6 +39,13 @@ class lowbit_gemv_problem(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int), ("K", ctypes.c_int)]
 
+class lowbit_gemv_chain(ctypes.Structure):
+    """Mirror of the C struct of the same name in include/lowbit.h."""
+    _fields_ = [("fmt", ctypes.c_int), ("M", ctypes.c_int), ("group_size", ctypes.c_int), ("count", ctypes.c_int),
+                ("stages", ctypes.c_int), ("grid", ctypes.c_int), ("xrow", ctypes.c_int),
+                ("spin_limit", ctypes.c_uint), ("buf", ctypes.c_void_p), ("buf_bytes", ctypes.c_size_t)]
+
+
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
 
@@ -54,6 +61,10 @@ SIGNATURES = {
     "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lowbit_gemv_batched": (_i, [_i, _i, _i, _i, _vp, _vp]),
+    "lowbit_gemv_chain_bytes": (_sz, [_i, _i]),
+    "lowbit_gemv_chain_init": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, ctypes.c_uint, _vp, _sz, _vp]),
+    "lowbit_gemv_chain_run": (_i, [_vp, _vp]),
+    "lowbit_gemv_chain_error": (_i, [_vp, _vp, _vp]),
     "lowbit_gemm": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "lowbit_moe_align": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lowbit_moe_gemm": (_i, [_i, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
@@ -179,3 +190,28 @@ def lowbit_gemv_batched(fmt, M, group_size, count, problems, stream=None):
     """problems: a ctypes array from make_gemv_problems (host memory)."""
     return lib().lowbit_gemv_batched(fmt, M, group_size, count, ctypes.cast(problems, ctypes.c_void_p),
                                      _stream(stream))
+
+
+def lowbit_gemv_chain_bytes(count, stages):
+    return lib().lowbit_gemv_chain_bytes(count, stages)
+
+
+def lowbit_gemv_chain_init(chain, fmt, M, group_size, count, problems, stage_of, spin_limit, buf, buf_bytes,
+                           stream=None):
+    """chain: a lowbit_gemv_chain (filled in); problems: from make_gemv_problems;
+    stage_of: a sequence of ints (copied into a host int array)."""
+    st = (ctypes.c_int * max(len(stage_of), 1))(*stage_of)
+    return lib().lowbit_gemv_chain_init(ctypes.byref(chain), fmt, M, group_size, count,
+                                        ctypes.cast(problems, ctypes.c_void_p), ctypes.cast(st, ctypes.c_void_p),
+                                        spin_limit, _ptr(buf), buf_bytes, _stream(stream))
+
+
+def lowbit_gemv_chain_run(chain, stream=None):
+    return lib().lowbit_gemv_chain_run(ctypes.byref(chain), _stream(stream))
+
+
+def lowbit_gemv_chain_error(chain, stream=None):
+    """Returns (status, error_word)."""
+    v = ctypes.c_uint(0)
+    st = lib().lowbit_gemv_chain_error(ctypes.byref(chain), ctypes.byref(v), _stream(stream))
+    return st, v.value

@@ -3,6 +3,8 @@
 // error is detected before the first enqueue.
 #include "lowbit_internal.hpp"
 
+#include <vector>
+
 using namespace lowbit;
 
 namespace {
@@ -213,6 +215,123 @@ int lowbit_gemv_batched(int fmt, int M, int group_size, int count, const lowbit_
         ++n;
     }
     return hip_status(launch_gemv_w4_batch(L, n, M, packed, x, y, (hipStream_t)stream));
+}
+
+size_t lowbit_gemv_chain_bytes(int count, int stages)
+{
+    if (count <= 0 || stages <= 0 || stages > count) return 0;
+    return (size_t)chain_layout(count, stages).bytes;
+}
+
+int lowbit_gemv_chain_init(lowbit_gemv_chain *chain, int fmt, int M, int group_size, int count,
+                           const lowbit_gemv_problem *problems, const int *stage_of, unsigned spin_limit,
+                           void *buf, size_t buf_bytes, void *stream)
+{
+    if (chain == nullptr || problems == nullptr || stage_of == nullptr || buf == nullptr) return LOWBIT_E_INVALID_ARG;
+    if (count <= 0 || M <= 0) return LOWBIT_E_INVALID_ARG;
+    if (!is_w4(fmt) || !w4_group_ok(group_size) || M > 4) return LOWBIT_E_UNSUPPORTED;
+    if (stage_of[0] != 0) return LOWBIT_E_INVALID_ARG;
+    for (int i = 1; i < count; ++i) {
+        const int d = stage_of[i] - stage_of[i - 1];
+        if (d != 0 && d != 1) return LOWBIT_E_INVALID_ARG;
+    }
+    const int stages = stage_of[count - 1] + 1;
+    const ChainLayout CL = chain_layout(count, stages);
+    if (buf_bytes < (size_t)CL.bytes) return LOWBIT_E_WORKSPACE;
+
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e);
+    const int grid = cus;
+
+    const bool asym = fmt == LOWBIT_W4_ASYM;
+    std::vector<uint8_t> img((size_t)CL.bytes, 0);
+    ChainProb *P = reinterpret_cast<ChainProb *>(img.data() + CL.probs_off);
+    int *arrivals = reinterpret_cast<int *>(img.data() + CL.arrivals_off);
+    std::vector<int64_t> stage_items(stages, 0);
+    int64_t items = 0, max_ktiles = 0;
+    for (int i = 0; i < count; ++i) {
+        const lowbit_gemv_problem &q = problems[i];
+        int st = check_w4_shape(fmt, q.N, q.K, group_size);
+        if (st != LOWBIT_OK) return st;
+        if (q.N == 0 || q.K == 0) return LOWBIT_E_UNSUPPORTED;
+        if (q.packed == nullptr || q.x == nullptr || q.y == nullptr) return LOWBIT_E_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(q.x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+        const W4Layout L = w4_layout(q.N, q.K, group_size, asym);
+        if ((int64_t)M * q.K * 2 >= ((int64_t)1 << 31) || (int64_t)M * q.N * 2 >= ((int64_t)1 << 31))
+            return LOWBIT_E_UNSUPPORTED;
+        const uint8_t *pk = static_cast<const uint8_t *>(q.packed);
+        ChainProb &c = P[i];
+        c.codes = pk + L.codes_off;
+        c.scales = pk + L.scales_off;
+        c.zeros = asym ? pk + L.zeros_off : nullptr;
+        c.x = static_cast<const _Float16 *>(q.x);
+        c.y = static_cast<_Float16 *>(q.y);
+        c.N = q.N;
+        c.K = q.K;
+        c.ktiles = (int)L.ktiles;
+        c.rounds = (int)((L.ktiles + kChainRoundTiles - 1) / kChainRoundTiles);
+        c.item_begin = (int)items;
+        items += L.strips;
+        if (items >= ((int64_t)1 << 30)) return LOWBIT_E_UNSUPPORTED;
+        c.item_end = (int)items;
+        c.stage = stage_of[i];
+        c.pad = 0;
+        stage_items[stage_of[i]] += L.strips;
+        if (L.ktiles > max_ktiles) max_ktiles = L.ktiles;
+    }
+    for (int s = 0; s < stages; ++s)
+        arrivals[s] = (int)(stage_items[s] < grid ? stage_items[s] : grid);
+    // x window: whole rows of M x round_up(K, 512) halfs plus a 16-byte pad
+    const int64_t xrow = round_up(max_ktiles * 128, 512) + 8;
+    if ((int64_t)M * (xrow - 8) > 65536) return LOWBIT_E_UNSUPPORTED;
+    const size_t lds = gemv_chain_lds_bytes(M, (int)xrow);
+    if (gemv_chain_occupancy(group_size, asym, M, lds) < 1) return LOWBIT_E_UNSUPPORTED;
+
+    e = hipMemcpyAsync(buf, img.data(), img.size(), hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+
+    chain->fmt = fmt;
+    chain->M = M;
+    chain->group_size = group_size;
+    chain->count = count;
+    chain->stages = stages;
+    chain->grid = grid;
+    chain->xrow = (int)xrow;
+    chain->spin_limit = spin_limit ? spin_limit : (1u << 20);
+    chain->buf = buf;
+    chain->buf_bytes = (size_t)CL.bytes;
+    return LOWBIT_OK;
+}
+
+int lowbit_gemv_chain_run(const lowbit_gemv_chain *chain, void *stream)
+{
+    if (chain == nullptr || chain->buf == nullptr || chain->count <= 0 || chain->grid <= 0) return LOWBIT_E_INVALID_ARG;
+    const ChainLayout CL = chain_layout(chain->count, chain->stages);
+    uint8_t *b = static_cast<uint8_t *>(chain->buf);
+    ChainArgs a;
+    a.probs = reinterpret_cast<const ChainProb *>(b + CL.probs_off);
+    a.arrivals = reinterpret_cast<const int *>(b + CL.arrivals_off);
+    a.ctr = reinterpret_cast<uint32_t *>(b);
+    a.nprob = chain->count;
+    a.M = chain->M;
+    a.xrow = chain->xrow;
+    a.spin_limit = chain->spin_limit;
+    return hip_status(launch_gemv_chain(chain->group_size, chain->fmt == LOWBIT_W4_ASYM, a, chain->grid,
+                                        (hipStream_t)stream));
+}
+
+int lowbit_gemv_chain_error(const lowbit_gemv_chain *chain, unsigned *error, void *stream)
+{
+    if (chain == nullptr || chain->buf == nullptr || error == nullptr) return LOWBIT_E_INVALID_ARG;
+    uint32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, chain->buf, 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    *error = v;
+    return LOWBIT_OK;
 }
 
 int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed, const void *a, int a_dtype,

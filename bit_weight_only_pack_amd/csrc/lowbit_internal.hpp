@@ -102,6 +102,43 @@ struct GemvBatch {
 hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
                                 const _Float16 *const *x, _Float16 *const *y, hipStream_t s);
 
+// A chain of dependent GEMV stages run by one persistent launch
+// (gemv_chain.hip).  Device buffer: counters, then the ChainProb table, then
+// the per-stage arrival counts.
+constexpr int kChainSlots = 32;          // completion counters per stage
+constexpr int kChainSlotStride = 32;     // words between them (one per 128-byte line)
+constexpr int kChainCtrHeader = 64;      // words before the first stage's counters
+struct ChainProb {
+    const uint8_t *codes, *scales, *zeros;
+    const _Float16 *x;
+    _Float16 *y;
+    int N, K, ktiles, rounds;            // rounds = ceil(ktiles / 32)
+    int item_begin, item_end, stage, pad;
+};
+struct ChainArgs {
+    const ChainProb *probs;
+    const int *arrivals;                 // workgroups that signal each stage
+    uint32_t *ctr;
+    int nprob, M, xrow;                  // xrow: LDS row stride of x in halfs
+    uint32_t spin_limit;
+};
+struct ChainLayout {
+    int64_t ctr_words, probs_off, arrivals_off, bytes;
+};
+inline ChainLayout chain_layout(int count, int stages)
+{
+    ChainLayout L;
+    L.ctr_words = kChainCtrHeader + (int64_t)stages * kChainSlots * kChainSlotStride;
+    L.probs_off = align256(L.ctr_words * 4);
+    L.arrivals_off = align256(L.probs_off + (int64_t)count * (int64_t)sizeof(ChainProb));
+    L.bytes = align256(L.arrivals_off + (int64_t)stages * 4);
+    return L;
+}
+constexpr int kChainRoundTiles = 32;
+size_t gemv_chain_lds_bytes(int M, int xrow);
+int gemv_chain_occupancy(int G, bool asym, int M, size_t lds);
+hipError_t launch_gemv_chain(int G, bool asym, const ChainArgs &a, int grid, hipStream_t s);
+
 size_t gemv_w4_workspace(int M, int64_t N, int64_t K, int G);
 hipError_t launch_gemv_w4(const W4Layout &L, int M, const uint8_t *packed, const _Float16 *x,
                           _Float16 *y, void *ws, size_t ws_bytes, hipStream_t s);

@@ -172,6 +172,69 @@ int lowbit_gemv_batched(int fmt, int M, int group_size, int count,
                         const lowbit_gemv_problem *problems, void *stream);
 
 /*
+ * A chain of dependent GEMV stages executed by ONE persistent launch: a whole
+ * decode step (every projection of every layer) as a single submission
+ * ("BaseRT" wiki chapter, limitations and approach: at batch 1 the per-command
+ * submission overhead dominates, so the many small operations of a step are
+ * encoded into one submission; "Low Bit ARM kernels": each projection is a
+ * bandwidth-bound GEMV).
+ *
+ * Problem i (same fmt, M and group_size for all) belongs to stage stage_of[i];
+ * stage_of[0] == 0 and stage_of[i] - stage_of[i-1] is 0 or 1.  Every problem
+ * of stage s+1 reads its x only after every problem of stage s has written its
+ * y, so the y of one stage may be the x of the next.  Within one stage no y
+ * may overlap any input of that stage.  Each y is the product lowbit_gemv
+ * defines (fp32 accumulation in a fixed order, fp16 RNE); the summation order
+ * is fixed, so a run is bit-reproducible.
+ *
+ * Usage: lowbit_gemv_chain_bytes -> allocate a device buffer of that size ->
+ * lowbit_gemv_chain_init (once; copies the plan into the buffer, host-
+ * synchronous) -> lowbit_gemv_chain_run (each step; asynchronous, capturable
+ * in a graph: the buffer needs no clearing between runs).  Runs of one chain
+ * must not overlap in time (keep them on one stream).  The device buffer, the
+ * weights and the x/y buffers named at init must stay valid while the chain is
+ * used; x contents may change between runs.
+ *
+ * Limits: 1 <= M <= 4; every problem has N >= 1 and K >= 1 (else
+ * LOWBIT_E_UNSUPPORTED), M * K * 2 bytes of x must fit the LDS window
+ * (M * round_up(K, 512) <= 65536 halfs, else LOWBIT_E_UNSUPPORTED).
+ */
+typedef struct lowbit_gemv_chain {
+    int fmt, M, group_size;
+    int count;                 /* problems */
+    int stages;
+    int grid;                  /* persistent workgroups: one per compute unit */
+    int xrow;                  /* internal: LDS row stride of x */
+    unsigned spin_limit;       /* polls before a dependency wait gives up */
+    void *buf;                 /* the device buffer passed to init */
+    size_t buf_bytes;
+} lowbit_gemv_chain;
+
+/* Device bytes of the chain buffer for `count` problems in `stages` stages
+ * (0 for invalid counts). */
+size_t lowbit_gemv_chain_bytes(int count, int stages);
+
+/*
+ * Validate the problems (HOST arrays `problems` and `stage_of`, read during
+ * the call), build the plan and copy it with zeroed counters into `buf`
+ * (device, >= lowbit_gemv_chain_bytes(count, stages)) on `stream`; returns
+ * after the copy completed.  spin_limit: polls of a dependency wait before it
+ * gives up (0 = default, about seconds); a wait that gives up sets bit 0 of
+ * the chain's error word (lowbit_gemv_chain_error) and the run's results are
+ * undefined, but the launch still completes.  Fills *chain.
+ */
+int lowbit_gemv_chain_init(lowbit_gemv_chain *chain, int fmt, int M, int group_size, int count,
+                           const lowbit_gemv_problem *problems, const int *stage_of,
+                           unsigned spin_limit, void *buf, size_t buf_bytes, void *stream);
+
+/* Enqueue one run of the chain on `stream`. */
+int lowbit_gemv_chain_run(const lowbit_gemv_chain *chain, void *stream);
+
+/* Read the chain's error word (0 = every wait so far was met) into *error;
+ * synchronizes `stream`. */
+int lowbit_gemv_chain_error(const lowbit_gemv_chain *chain, unsigned *error, void *stream);
+
+/*
  * Prefill GEMM with W4 weights ("Low Bit ARM kernels": prefill is the same
  * product over many tokens; "Low Bit Metal Kernels": activation and weight
  * tiles staged on chip and multiplied):
