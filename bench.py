@@ -4,8 +4,9 @@ Default workload (the headline): a Llama-3-8B-shaped W4 decode step.  One
 step = the 224 decode GEMVs of a 32-layer decoder in layer order (q, k, v, o,
 gate, up, down; K x N = 4096x4096, 4096x1024, 4096x1024, 4096x4096,
 4096x14336, 4096x14336, 14336x4096), M = 1, symmetric INT4 with group size
-128, fp16 scales U[0.002, 0.01], fp16 activations N(0,1) (one distinct input
-vector per GEMV), fp16 outputs.  Every weight is distinct (3.49 GB of packed
+128, fp16 scales U[0.002, 0.01], fp16 activations N(0,1) (as in a decoder
+layer, q/k/v read one input vector and gate/up another; o and down have their
+own), fp16 outputs.  Every weight is distinct (3.49 GB of packed
 codes, 0.11 GB of scales): the step streams 3,603,955,712 algorithmic bytes
 and no cache can hold it.  The projections that read the same layer input run
 as one batched launch (q/k/v, gate/up), so a layer is 4 launches in
@@ -54,20 +55,24 @@ def w4_bytes(K, N, M, G, asym):
 # decode step
 # ---------------------------------------------------------------------------
 GROUPS_FUSED = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
-GROUPS_UNFUSED = (("q",), ("k",), ("v",), ("o",), ("gate",), ("up",), ("down",))
 
 
 def build_step(lb, synth, torch, M, G, asym, workload_id, fused, outlier_frac=0.0):
     """Pack every weight of the 32-layer step on the GPU; return the launch list.
-    Each launch = one lowbit_gemv_batched call over a group of projections."""
+    Each launch = one lowbit_gemv_batched call over a group of projections.
+    As in a decoder layer, the projections of one group read the same input
+    row(s): q/k/v share one activation vector, gate/up share one (drawn with
+    the seed of the group's first projection); o and down have their own."""
     fmt = lb.LOWBIT_W4_ASYM if asym else lb.LOWBIT_W4_SYM
     projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
     launches = []
     keep = []
     for layer in range(LAYERS):
-        for group in (GROUPS_FUSED if fused else GROUPS_UNFUSED):
+        for group in GROUPS_FUSED:
+            pid0, K0, _ = projs[group[0]]
+            x = torch.from_numpy(synth.activations_f16(M, K0, outlier_frac=outlier_frac, workload_id=workload_id,
+                                                       layer=layer, part=pid0)).cuda()
             items = []
-            nbytes = 0
             for name in group:
                 pid, K, N = projs[name]
                 w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
@@ -78,14 +83,17 @@ def build_step(lb, synth, torch, M, G, asym, workload_id, fused, outlier_frac=0.
                 scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
                 zeros = torch.from_numpy(w["zeros"]).cuda() if asym else None
                 lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, zeros, packed, nb))
-                x = torch.from_numpy(synth.activations_f16(M, K, outlier_frac=outlier_frac, workload_id=workload_id,
-                                                           layer=layer, part=pid)).cuda()
                 y = torch.empty((M, N), dtype=torch.float16, device="cuda")
                 items.append((packed, x, y, N, K))
-                nbytes += w4_bytes(K, N, M, G, asym)
                 del codes, scales, zeros
             keep.append(items)
-            launches.append(dict(names=group, probs=lb.make_gemv_problems(items), count=len(items), bytes=nbytes))
+            if fused:
+                launches.append(dict(names=group, probs=lb.make_gemv_problems(items), count=len(items),
+                                     bytes=sum(w4_bytes(K, N, M, G, asym) for (_, _, _, N, K) in items)))
+            else:
+                for (name, it) in zip(group, items):
+                    launches.append(dict(names=(name,), probs=lb.make_gemv_problems([it]), count=1,
+                                         bytes=w4_bytes(it[4], it[3], M, G, asym)))
     torch.cuda.synchronize()
     return fmt, launches, keep
 
@@ -187,18 +195,22 @@ def read_traffic(name):
 def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0):
     """The CPU oracle on the first `layers` layers of the same step (single thread)."""
     import oracle
+    projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
     t_total = 0.0
     nbytes = 0
     for layer in range(layers):
-        for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS):
-            w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
-                                 layer=layer, part=pid)
-            x = synth.activations_f16(M, K, outlier_frac=outlier_frac, workload_id=workload_id, layer=layer,
-                                      part=pid)
-            t0 = time.perf_counter()
-            oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
-            t_total += time.perf_counter() - t0
-            nbytes += w4_bytes(K, N, M, G, asym)
+        for group in GROUPS_FUSED:
+            pid0, K0, _ = projs[group[0]]
+            x = synth.activations_f16(M, K0, outlier_frac=outlier_frac, workload_id=workload_id, layer=layer,
+                                      part=pid0)
+            for name in group:
+                pid, K, N = projs[name]
+                w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
+                                     layer=layer, part=pid)
+                t0 = time.perf_counter()
+                oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
+                t_total += time.perf_counter() - t0
+                nbytes += w4_bytes(K, N, M, G, asym)
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample="layers 0..%d of the 32-layer step (%d GEMVs, %.1f MB), one thread, %.1f s"
                        % (layers - 1, 7 * layers, nbytes / 1e6, t_total),

@@ -26,10 +26,10 @@
 //   * Work items are (problem, 16-row strip) pairs numbered across the chain
 //     in stage order; workgroup w takes items w, w + grid, w + 2 grid, ...
 //     An item is processed in rounds of 32 K tiles (4 per compute wave).
-//   * Weight loads run two rounds ahead of the MFMAs, across item and stage
-//     boundaries (three register slots, unrolled so that no slot is ever
-//     copied while its loads are in flight): while the control wave waits for
-//     stage s, the weights of the next rounds are already streaming.
+//   * Weight loads run several rounds ahead of the MFMAs, across item and
+//     stage boundaries (a ring of register slots, unrolled so that no slot is
+//     ever copied while its loads are in flight): while the control wave
+//     waits for stage s, the weights of the next rounds are already streaming.
 //   * Stage completion: a workgroup signals once per stage in which it had
 //     items (after its last one), by a relaxed atomic add on one of 32
 //     counters of that stage (one per 128-byte line, picked by workgroup
@@ -125,6 +125,10 @@ __device__ __forceinline__ void load_round(Slot<G, ASYM> &s, const Cursor &p, CP
     }
 }
 
+// Branch-free: a tile past the strip's end has zero codes and zero scales
+// (its loads read out of range), so its product adds exactly zero; its
+// activation address is clamped to the last real tile so it only reads
+// finite values.
 template <int G, bool ASYM, int MR>
 __device__ __forceinline__ void compute_round(const Slot<G, ASYM> &s, const Cursor &c, CProb *P,
                                               const _Float16 *xa, int wave, uint32_t magic, f4 &acc)
@@ -133,17 +137,16 @@ __device__ __forceinline__ void compute_round(const Slot<G, ASYM> &s, const Curs
 #pragma unroll
     for (int u = 0; u < kTilesPerWave; ++u) {
         const int t = c.rr * kRoundTiles + wave + u * kComputeWaves;
-        if (t < kt) {
-            __builtin_amdgcn_sched_barrier(0);
-            u4 qv = s.q[u];
-            asm volatile("" : "+v"(qv));
-            MetaRaw<G, ASYM> mv = s.m[u];
-            pin_meta<G, ASYM>(mv);
-            h8 av[4];
+        const int tx = t < kt ? t : kt - 1;
+        __builtin_amdgcn_sched_barrier(0);
+        u4 qv = s.q[u];
+        asm volatile("" : "+v"(qv));
+        MetaRaw<G, ASYM> mv = s.m[u];
+        pin_meta<G, ASYM>(mv);
+        h8 av[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const h8 *>(xa + t * 128 + i * 32);
-            tile_product<G, ASYM, MR>(qv, mv, av, magic, acc);
-        }
+        for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const h8 *>(xa + tx * 128 + i * 32);
+        tile_product<G, ASYM, MR>(qv, mv, av, magic, acc);
     }
 }
 
@@ -187,36 +190,50 @@ __device__ __forceinline__ void stage_x(CProb &pr, int M, int xrow, _Float16 *xs
 // Compute waves: stream weights two rounds ahead and run the MFMAs.  This
 // loop holds no other vector memory traffic, so the compiler's wait before
 // each tile counts only the weight loads issued after it.
+// Register slots of weight loads in flight: D - 1 rounds ahead of the MFMAs.
+template <int G, bool ASYM> struct ChainDepth { static constexpr int D = (ASYM && G == 32) ? 4 : 5; };
+
+// Compute waves: stream weights D - 1 rounds ahead and run the MFMAs.  This
+// loop holds no other vector memory traffic and no data-dependent branch
+// around a load or a use, so the compiler's wait before each tile counts
+// exactly the weight loads issued after it.
 template <int G, bool ASYM, int MR>
 __device__ __forceinline__ void compute_loop(const ChainArgs &a, CProb *P, const _Float16 *xs, float *red, int wave,
                                              int lane)
 {
+    constexpr int D = ChainDepth<G, ASYM>::D;
     const int nprob = a.nprob, nwg = gridDim.x;
     const int r = lane & 15, kq = lane >> 4;
     const _Float16 *xa = xs + (r < a.M ? r : a.M - 1) * a.xrow + kq * 8;
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));
 
-    Slot<G, ASYM> s0, s1, s2;
+    Slot<G, ASYM> s[D];
     Cursor c = {0, (int)blockIdx.x, 0};
     seek(c, P, nprob);
     Cursor p = c;
-    load_round<G, ASYM>(s0, p, P, nprob, wave, lane);
-    advance(p, P, nprob, nwg);
-    load_round<G, ASYM>(s1, p, P, nprob, wave, lane);
-    advance(p, P, nprob, nwg);
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k) {
+        load_round<G, ASYM>(s[k], p, P, nprob, wave, lane);
+        advance(p, P, nprob, nwg);
+    }
 
     int x_pi = -1, rb = 0;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto step = [&](Slot<G, ASYM> &cur, Slot<G, ASYM> &pf) -> bool {
-        if (c.pi >= nprob) return false;
+    // One round.  Past the last item the step still runs (its loads read
+    // nothing, its products are discarded); only the barrier bookkeeping is
+    // guarded, and that branch holds no vector memory operation, so every
+    // step has the same load/wait structure.
+    auto step = [&](Slot<G, ASYM> &cur, Slot<G, ASYM> &pf) {
+        const bool alive = c.pi < nprob;
+        const Cursor cc = {alive ? c.pi : nprob - 1, c.item, c.rr};
         load_round<G, ASYM>(pf, p, P, nprob, wave, lane);
-        if (c.rr == 0 && c.pi != x_pi) {
+        if (alive && c.rr == 0 && c.pi != x_pi) {
             x_pi = c.pi;
             __syncthreads();                                   // (A) control wave: dependency met, x staged
         }
-        compute_round<G, ASYM, MR>(cur, c, P, xa, wave, magic, acc);
-        if (c.rr == P[c.pi].rounds - 1) {
+        compute_round<G, ASYM, MR>(cur, cc, P, xa, wave, magic, acc);
+        if (alive && c.rr == P[cc.pi].rounds - 1) {
             float *rbuf = red + rb * (kComputeWaves * MR * 64);
 #pragma unroll
             for (int j = 0; j < MR; ++j) rbuf[(wave * MR + j) * 64 + lane] = acc[j];
@@ -226,12 +243,10 @@ __device__ __forceinline__ void compute_loop(const ChainArgs &a, CProb *P, const
         }
         advance(c, P, nprob, nwg);
         advance(p, P, nprob, nwg);
-        return true;
     };
-    for (;;) {
-        if (!step(s0, s2)) break;
-        if (!step(s1, s0)) break;
-        if (!step(s2, s1)) break;
+    while (c.pi < nprob) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) step(s[k], s[(k + D - 1) % D]);
     }
 }
 
