@@ -407,7 +407,7 @@ def main():
                     help="decode: chain = the whole step as one persistent launch with stage dependencies; "
                          "batched = one launch per group of GEMVs sharing an input (4 per layer); "
                          "unfused = one launch per GEMV (7 per layer)")
-    ap.add_argument("--cpu-layers", type=int, default=2, help="decode: layers the CPU oracle runs (0 = skip)")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="decode: layers the CPU oracle runs (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (a kernel of known traffic for counter runs)")
