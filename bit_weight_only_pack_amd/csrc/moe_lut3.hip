@@ -140,13 +140,18 @@ __global__ void lut3_unpack_meta(const uint8_t *__restrict__ cb_in, const uint8_
 // ---------------------------------------------------------------- align
 // Bucket the routed slots by expert (ascending expert, ascending slot id),
 // pad each expert to a multiple of block_m with the sentinel num_valid, and
-// record the expert of every block.  One workgroup of 1024 threads; slots are
-// taken 1024 at a time and placed with a stable counting sort: a slot's rank
-// among equal experts is built from ballots inside a wave and prefix sums
-// over the waves of the chunk.
+// record the expert of every block.  One workgroup of 1024 threads:
+//   1. per-expert counts (LDS histogram) and the exclusive scan of the padded
+//      counts (wave prefix sums, then a prefix over the wave totals);
+//   2. placement, a chunk of slots at a time: every slot sets its bit in its
+//      expert's bitmask of the chunk; a slot's rank among its expert's slots
+//      is the number of set bits below its own plus that expert's count from
+//      earlier chunks -- a stable order with no sequential pass;
+//   3. sentinels in the padding and past the end, block_expert.
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
+constexpr int kAlignMaskWords = 8192;             // LDS words for the chunk bitmasks (32 KB)
 
 __global__ __launch_bounds__(kAlignThreads)
 void moe_align_kernel(const int32_t *__restrict__ topk_ids, int num_valid, int E, int block_m,
@@ -156,73 +161,86 @@ void moe_align_kernel(const int32_t *__restrict__ topk_ids, int num_valid, int E
 {
     __shared__ int counts[kMaxExperts];
     __shared__ int offs[kMaxExperts + 1];
-    __shared__ int placed[kMaxExperts];
-    __shared__ int wave_cnt[kAlignWaves][kMaxExperts / 8];   // per-chunk, per-wave counts of a slice of experts
+    __shared__ int running[kMaxExperts];
+    __shared__ int wave_sum[kAlignWaves];
+    __shared__ uint32_t mask[kAlignMaskWords];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 
-    for (int e = tid; e < E; e += kAlignThreads) { counts[e] = 0; placed[e] = 0; }
+    // 1. counts and padded offsets (thread e owns expert e, E <= 1024)
+    counts[tid] = 0;
+    running[tid] = 0;
     __syncthreads();
     for (int i = tid; i < num_valid; i += kAlignThreads) {
         const int e = topk_ids[i];
         if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
     }
     __syncthreads();
-    if (tid == 0) {                                   // E <= 1024: a serial scan is short
-        int acc = 0;
-        for (int e = 0; e < E; ++e) {
-            offs[e] = acc;
-            acc += (counts[e] + block_m - 1) / block_m * block_m;
-        }
-        offs[E] = acc;
-        num_post_padded[0] = acc;
+    const int padded = tid < E ? (counts[tid] + block_m - 1) / block_m * block_m : 0;
+    int incl = padded;                                // inclusive prefix inside the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
     }
+    if (lane == 63) wave_sum[wave] = incl;
     __syncthreads();
-    for (int e = tid; e <= E; e += kAlignThreads) expert_offsets[e] = offs[e];
-    for (int i = tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;   // sentinel everywhere first
-    for (int b = tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_sum[w];
+    const int excl = before + incl - padded;
+    if (tid < E) offs[tid] = excl;
+    if (tid == E - 1) offs[E] = excl + padded;
     __syncthreads();
-    for (int e = tid; e < E; e += kAlignThreads) {
-        const int local = expert_map ? expert_map[e] : e;
-        for (int b = offs[e] / block_m; b < offs[e + 1] / block_m; ++b) block_expert[b] = local;
+    const int total = offs[E];
+    if (tid < E) expert_offsets[tid] = offs[tid];
+    if (tid == 0) {
+        expert_offsets[E] = total;                    // (E may equal the thread count)
+        num_post_padded[0] = total;
     }
 
-    // stable placement, chunk by chunk
-    for (int base = 0; base < num_valid; base += kAlignThreads) {
-        const int sid = base + tid;
-        const int e = sid < num_valid ? topk_ids[sid] : -1;
-        const bool valid = e >= 0 && e < E;
-        // rank among earlier lanes of this wave with the same expert
-        int rank_in_wave = 0, wave_total = 0;
-        uint64_t todo = __builtin_amdgcn_ballot_w64(valid);
-        while (todo) {
-            const int leader = __builtin_ctzll(todo);
-            const int le = __shfl(e, leader);
-            const uint64_t same = __builtin_amdgcn_ballot_w64(valid && e == le);
-            if (valid && e == le) {
-                rank_in_wave = __builtin_popcountll(same & ((1ull << lane) - 1));
-                wave_total = __builtin_popcountll(same);
+    // 2. stable placement, chunk by chunk: a chunk's bitmask holds
+    //    chunk / 32 words per expert, rows one word longer than that so the
+    //    rows of different experts start in different LDS banks
+    const int words = max(1, min(32, kAlignMaskWords / E - 1));   // words per expert per chunk
+    const int stride = words + 1;
+    const int chunk = words * 32;
+    for (int base = 0; base < num_valid; base += chunk) {
+        for (int i = tid; i < E * stride; i += kAlignThreads) mask[i] = 0;
+        __syncthreads();
+        int e = -1, local = 0;
+        if (tid < chunk && base + tid < num_valid) {
+            e = topk_ids[base + tid];
+            if (e >= 0 && e < E) {
+                local = tid;
+                atomicOr(&mask[e * stride + (local >> 5)], 1u << (local & 31));
+            } else {
+                e = -1;
             }
-            todo &= ~same;
         }
-        // prefix over the waves of this chunk, a slice of experts at a time
-        int before = 0;
-        for (int e0 = 0; e0 < E; e0 += kMaxExperts / 8) {
-            for (int i = tid; i < kAlignWaves * (kMaxExperts / 8); i += kAlignThreads)
-                wave_cnt[i / (kMaxExperts / 8)][i % (kMaxExperts / 8)] = 0;
-            __syncthreads();
-            if (valid && e >= e0 && e < e0 + kMaxExperts / 8 && rank_in_wave == 0)
-                wave_cnt[wave][e - e0] = wave_total;
-            __syncthreads();
-            if (valid && e >= e0 && e < e0 + kMaxExperts / 8)
-                for (int w = 0; w < wave; ++w) before += wave_cnt[w][e - e0];
-            __syncthreads();
+        __syncthreads();
+        if (e >= 0) {
+            const uint32_t *m = mask + e * stride;
+            int rank = __builtin_popcount(m[local >> 5] & ((1u << (local & 31)) - 1u));
+            for (int w = 0; w < (local >> 5); ++w) rank += __builtin_popcount(m[w]);
+            sorted_ids[offs[e] + running[e] + rank] = base + local;
         }
-        if (valid) sorted_ids[offs[e] + placed[e] + before + rank_in_wave] = sid;
-        __syncthreads();                              // every position of the chunk taken
-        if (valid) atomicAdd(&placed[e], 1);          // advance the per-expert cursors
+        __syncthreads();
+        if (tid < E) {
+            int c = 0;
+            for (int w = 0; w < words; ++w) c += __builtin_popcount(mask[tid * stride + w]);
+            running[tid] += c;
+        }
         __syncthreads();
     }
+
+    // 3. sentinels in each expert's padding and past the end; expert of every block
+    if (tid < E) {
+        for (int p = offs[tid] + counts[tid]; p < offs[tid + 1]; ++p) sorted_ids[p] = num_valid;
+        const int local = expert_map ? expert_map[tid] : tid;
+        for (int b = offs[tid] / block_m; b < offs[tid + 1] / block_m; ++b) block_expert[b] = local;
+    }
+    for (int i = total + tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;
+    for (int b = total / block_m + tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
 }
 
 // ---------------------------------------------------------------- grouped GEMM
@@ -388,6 +406,170 @@ void moe_lut3_gemm_kernel(MoeArgs p)
     }
 }
 
+// ---------------------------------------------------------------- grouped GEMM, activations in LDS
+// The same product as moe_lut3_gemm_kernel for passes whose activation rows
+// fit in LDS.  Each pass first stages its rows (and their block scales) in
+// LDS; after that the only vector-memory traffic of the K loop is the weight
+// stream, which runs D - 1 K steps ahead of the MFMAs in a ring of register
+// slots (unrolled so that no slot is copied while its loads are in flight).
+constexpr int kLdsRowPad = 16;        // bytes added to each staged row (rows fall in different banks)
+
+struct WSlot {
+    uint32_t w[kStripsPerWave][3];
+    u4 cbk[kStripsPerWave];
+    uint32_t bscale[kStripsPerWave];
+};
+
+__host__ __device__ inline int moe_lds_bytes(int MB, int K)
+{
+    return MB * 16 * (K + kLdsRowPad) + MB * 16 * (K / 32);
+}
+
+template <int MB, int D>
+__global__ __launch_bounds__(kMoeWaves * 64)
+void moe_lut3_gemm_lds_kernel(MoeArgs p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int e = blockIdx.x / p.n_tiles;                      // global expert
+    const int nt = blockIdx.x % p.n_tiles;
+    const int row0 = p.expert_offsets[e], row1 = p.expert_offsets[e + 1];
+    if (row0 >= row1) return;                                  // no slot routed here
+    const int local = p.block_expert[row0 / p.block_m];
+    const int strip_base = nt * (kMoeWaves * kStripsPerWave) + wave * kStripsPerWave;
+
+    if (local < 0) {
+        // expert not on this device: its routed slots get zero rows
+        for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kMoeWaves * 4) {
+            const int sid = p.sorted_ids[rr];
+            if (sid >= p.num_valid) continue;
+            for (int c = (threadIdx.x & 15); c < kMoeWaves * kStripsPerWave * 16; c += 16) {
+                const int n = nt * kMoeWaves * kStripsPerWave * 16 + c;
+                if (n < p.N) p.out[(int64_t)sid * p.N + n] = 0;
+            }
+        }
+        return;
+    }
+
+    const int K = p.K, ksteps = p.ksteps, k_chunks = K / 32;
+    const int astride = K + kLdsRowPad;
+    uint8_t *a_lds = smem;                                     // [MB*16][astride]
+    uint8_t *s_lds = smem + MB * 16 * astride;                 // [MB*16][k_chunks]
+
+    // weight descriptors over this wave's strips of the local expert (strips past N read zeros)
+    const int nstrips = max(0, min(kStripsPerWave, p.strips - strip_base));
+    const int64_t unit0 = ((int64_t)local * p.strips + (nstrips > 0 ? strip_base : 0)) * ksteps;
+    const uint32_t nunits = (uint32_t)(nstrips * ksteps);
+    const auto irs = buffer_rsrc(p.idx + unit0 * 768, nunits * 768);
+    const auto crs = buffer_rsrc(p.cb + unit0 * 32, nunits * 32);
+    const auto ers = buffer_rsrc(p.ex + unit0 * 4, nunits * 4);
+    const auto ars = buffer_rsrc(p.aq, (uint32_t)((int64_t)p.a_rows * K));
+    const auto srs = buffer_rsrc(p.as, (uint32_t)((int64_t)p.a_rows * k_chunks));
+    const int colhalf = r16 >> 3;                              // which 8-column tile of the strip
+    const int exsel = (colhalf << 1) | (kg >> 1);              // exponent of this lane's 32-K block
+
+    auto load_w = [&](WSlot &ws, int t) {
+        const bool ok = t < ksteps;
+#pragma unroll
+        for (int j = 0; j < kStripsPerWave; ++j) {
+            const uint32_t unit = (uint32_t)(j * ksteps + t);
+            const auto iv = __builtin_amdgcn_raw_buffer_load_b96(irs, ok ? unit * 768 + lane * 12 : kBufferOob, 0, 0);
+            ws.w[j][0] = iv[0];
+            ws.w[j][1] = iv[1];
+            ws.w[j][2] = iv[2];
+            // both K halves' codebooks of this lane's 8-column tile (16 bytes)
+            ws.cbk[j] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? unit * 32 + colhalf * 16 : kBufferOob, 0, 0);
+            // the unit's four tile exponents; the lane's own byte is picked at use
+            ws.bscale[j] = __builtin_amdgcn_raw_buffer_load_b32(ers, ok ? unit * 4 : kBufferOob, 0, 0);
+        }
+    };
+
+    for (int pass = row0; pass < row1; pass += MB * 16) {
+        const int nmb = min(MB, (row1 - pass) / 16);
+        // 1. stage the pass's activation rows and block scales (invalid rows: zeros)
+        __syncthreads();                                       // previous pass done with the LDS rows
+        const int chunks = K / 16;
+        for (int i = threadIdx.x; i < MB * 16 * chunks; i += kMoeWaves * 64) {
+            const int row = i / chunks, c = i - row * chunks;
+            const int sid = row < nmb * 16 ? p.sorted_ids[pass + row] : p.num_valid;
+            const uint32_t off = sid < p.num_valid ? (uint32_t)(sid / p.a_row_div) * (uint32_t)K + c * 16 : kBufferOob;
+            *reinterpret_cast<u4 *>(a_lds + row * astride + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
+        }
+        for (int i = threadIdx.x; i < MB * 16 * k_chunks; i += kMoeWaves * 64) {
+            const int row = i / k_chunks, c = i - row * k_chunks;
+            const int sid = row < nmb * 16 ? p.sorted_ids[pass + row] : p.num_valid;
+            const uint32_t off = sid < p.num_valid ? (uint32_t)(sid / p.a_row_div) * (uint32_t)k_chunks + c : kBufferOob;
+            s_lds[i] = __builtin_amdgcn_raw_buffer_load_b8(srs, off, 0, 0);
+        }
+        __syncthreads();
+
+        f4 acc[MB][kStripsPerWave];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < kStripsPerWave; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+        // 2. stream the weights D - 1 steps ahead
+        WSlot wsl[D];
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) load_w(wsl[d], d);
+        auto step = [&](int t, WSlot &wcur, WSlot &wpf) {
+            load_w(wpf, t + D - 1);
+            const int k_lo = t * 128 + 16 * kg;
+            const int kc = t * 4 + kg;                         // this lane supplies block kc's scale
+#pragma unroll
+            for (int j = 0; j < kStripsPerWave; ++j) {
+                const i8v b = lut3_decode(wcur.w[j][0], wcur.w[j][1], wcur.w[j][2], wcur.cbk[j].x, wcur.cbk[j].y,
+                                          wcur.cbk[j].z, wcur.cbk[j].w);
+                const int bs = (int)((wcur.bscale[j] >> (8 * exsel)) & 0xffu);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    if (mb < nmb) {
+                        const uint8_t *ar = a_lds + (mb * 16 + r16) * astride;
+                        const u4 lo = *reinterpret_cast<const u4 *>(ar + k_lo);
+                        const u4 hi = *reinterpret_cast<const u4 *>(ar + k_lo + 64);
+                        const i8v a = i8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        const int as = kc < k_chunks ? (int)s_lds[(mb * 16 + r16) * k_chunks + kc] : 127;
+                        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[mb][j], 0, 0, 0, as,
+                                                                                      0, bs);
+                    }
+                }
+            }
+        };
+        // unrolled by D so every slot index is a constant; the tail repeats the order
+        int t = 0;
+        for (; t + D <= ksteps; t += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(t + d, wsl[d], wsl[(d + D - 1) % D]);
+        }
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (t + d < ksteps) step(t + d, wsl[d], wsl[(d + D - 1) % D]);
+
+        // 3. store: lane holds column (lane % 16), rows 4*(lane/16) + i of each block
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (mb >= nmb) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sid = p.sorted_ids[pass + mb * 16 + kg * 4 + i];
+                if (sid >= p.num_valid) continue;
+#pragma unroll
+                for (int j = 0; j < kStripsPerWave; ++j) {
+                    const int n = (strip_base + j) * 16 + r16;
+                    if (n < p.N) {
+                        const __bf16 v = (__bf16)acc[mb][j][i];
+                        p.out[(int64_t)sid * p.N + n] = __builtin_bit_cast(uint16_t, v);
+                    }
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
@@ -467,7 +649,24 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
     p.a_rows = a_rows;
     const unsigned blocks = (unsigned)((int64_t)E_global * p.n_tiles);
     if (blocks == 0) return hipSuccess;
-    moe_lut3_gemm_kernel<<<blocks, kMoeWaves * 64, 0, s>>>(p);
+    // Activation rows in LDS when a pass of 32 rows (or 16) fits in 80 KB;
+    // otherwise the kernel that reads activations straight from memory.
+    constexpr int kMaxLds = 80 * 1024;
+    if (moe_lds_bytes(2, p.K) <= kMaxLds) {
+        const int lds = moe_lds_bytes(2, p.K);
+        auto k = moe_lut3_gemm_lds_kernel<2, 5>;
+        hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        k<<<blocks, kMoeWaves * 64, lds, s>>>(p);
+    } else if (moe_lds_bytes(1, p.K) <= kMaxLds) {
+        const int lds = moe_lds_bytes(1, p.K);
+        auto k = moe_lut3_gemm_lds_kernel<1, 5>;
+        hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        k<<<blocks, kMoeWaves * 64, lds, s>>>(p);
+    } else {
+        moe_lut3_gemm_kernel<<<blocks, kMoeWaves * 64, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 
