@@ -28,6 +28,8 @@
 //     blocks of its expert, so each expert's weights stream from HBM once.
 #include "lowbit_internal.hpp"
 
+#include <algorithm>
+
 namespace lowbit {
 
 namespace {
@@ -408,11 +410,16 @@ void moe_lut3_gemm_kernel(MoeArgs p)
 
 // ---------------------------------------------------------------- grouped GEMM, activations in LDS
 // The same product as moe_lut3_gemm_kernel for passes whose activation rows
-// fit in LDS.  Each pass first stages its rows (and their block scales) in
-// LDS; after that the only vector-memory traffic of the K loop is the weight
-// stream, which runs D - 1 K steps ahead of the MFMAs in a ring of register
-// slots (unrolled so that no slot is copied while its loads are in flight).
-constexpr int kLdsRowPad = 16;        // bytes added to each staged row (rows fall in different banks)
+// fit in LDS.  One workgroup of 8 waves per (expert, group of column tiles):
+// each pass stages its activation rows and block scales in LDS once, then
+// every wave walks its two strips of each tile of the group along K; the
+// weight stream runs D - 1 K steps ahead of the MFMAs in a ring of register
+// slots that continues from one tile into the next (unrolled so that no slot
+// is copied while its loads are in flight), and it is the only vector-memory
+// traffic of the loop.
+constexpr int kGWaves = 8;                          // waves per workgroup
+constexpr int kGTileStrips = kGWaves * kStripsPerWave;   // 16 strips = 256 columns per tile
+constexpr int kLdsRowPad = 16;                      // bytes added to each staged row (rows fall in different banks)
 
 struct WSlot {
     uint32_t w[kStripsPerWave][3];
@@ -422,33 +429,39 @@ struct WSlot {
 
 __host__ __device__ inline int moe_lds_bytes(int MB, int K)
 {
-    return MB * 16 * (K + kLdsRowPad) + MB * 16 * (K / 32);
+    return MB * 16 * (K + kLdsRowPad) + MB * 16 * (K / 32) + MB * 16 * 4;
 }
 
+struct MoeGroupArgs {
+    MoeArgs m;
+    int gtiles, tiles_per_group, n_groups;         // tiles of 256 columns; tiles per workgroup
+};
+
 template <int MB, int D>
-__global__ __launch_bounds__(kMoeWaves * 64)
-void moe_lut3_gemm_lds_kernel(MoeArgs p)
+__global__ __launch_bounds__(kGWaves * 64)
+void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
 {
+    const MoeArgs &p = ga.m;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, kg = lane >> 4;
-    const int e = blockIdx.x / p.n_tiles;                      // global expert
-    const int nt = blockIdx.x % p.n_tiles;
+    const int e = blockIdx.x / ga.n_groups;                   // global expert
+    const int grp = blockIdx.x % ga.n_groups;
+    const int tile0 = grp * ga.tiles_per_group;
+    const int ntl = min(ga.tiles_per_group, ga.gtiles - tile0);
+    if (ntl <= 0) return;
     const int row0 = p.expert_offsets[e], row1 = p.expert_offsets[e + 1];
     if (row0 >= row1) return;                                  // no slot routed here
     const int local = p.block_expert[row0 / p.block_m];
-    const int strip_base = nt * (kMoeWaves * kStripsPerWave) + wave * kStripsPerWave;
+    const int col0 = tile0 * kGTileStrips * 16, col1 = min(p.N, (tile0 + ntl) * kGTileStrips * 16);
 
     if (local < 0) {
         // expert not on this device: its routed slots get zero rows
-        for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kMoeWaves * 4) {
+        for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kGWaves * 4) {
             const int sid = p.sorted_ids[rr];
             if (sid >= p.num_valid) continue;
-            for (int c = (threadIdx.x & 15); c < kMoeWaves * kStripsPerWave * 16; c += 16) {
-                const int n = nt * kMoeWaves * kStripsPerWave * 16 + c;
-                if (n < p.N) p.out[(int64_t)sid * p.N + n] = 0;
-            }
+            for (int n = col0 + (threadIdx.x & 15); n < col1; n += 16) p.out[(int64_t)sid * p.N + n] = 0;
         }
         return;
     }
@@ -457,24 +470,29 @@ void moe_lut3_gemm_lds_kernel(MoeArgs p)
     const int astride = K + kLdsRowPad;
     uint8_t *a_lds = smem;                                     // [MB*16][astride]
     uint8_t *s_lds = smem + MB * 16 * astride;                 // [MB*16][k_chunks]
+    int *sid_lds = reinterpret_cast<int *>(s_lds + MB * 16 * k_chunks);   // [MB*16]
 
-    // weight descriptors over this wave's strips of the local expert (strips past N read zeros)
-    const int nstrips = max(0, min(kStripsPerWave, p.strips - strip_base));
-    const int64_t unit0 = ((int64_t)local * p.strips + (nstrips > 0 ? strip_base : 0)) * ksteps;
-    const uint32_t nunits = (uint32_t)(nstrips * ksteps);
-    const auto irs = buffer_rsrc(p.idx + unit0 * 768, nunits * 768);
-    const auto crs = buffer_rsrc(p.cb + unit0 * 32, nunits * 32);
-    const auto ers = buffer_rsrc(p.ex + unit0 * 4, nunits * 4);
+    // weight descriptors over the local expert's units (strips past N read zeros)
+    const int64_t eunit0 = (int64_t)local * p.strips * ksteps;
+    const uint32_t eunits = (uint32_t)(p.strips * ksteps);
+    const auto irs = buffer_rsrc(p.idx + eunit0 * 768, eunits * 768);
+    const auto crs = buffer_rsrc(p.cb + eunit0 * 32, eunits * 32);
+    const auto ers = buffer_rsrc(p.ex + eunit0 * 4, eunits * 4);
     const auto ars = buffer_rsrc(p.aq, (uint32_t)((int64_t)p.a_rows * K));
     const auto srs = buffer_rsrc(p.as, (uint32_t)((int64_t)p.a_rows * k_chunks));
     const int colhalf = r16 >> 3;                              // which 8-column tile of the strip
     const int exsel = (colhalf << 1) | (kg >> 1);              // exponent of this lane's 32-K block
+    const int total = ntl * ksteps;                            // (tile, K step) pairs of this wave
 
-    auto load_w = [&](WSlot &ws, int t) {
-        const bool ok = t < ksteps;
+    // weights of pair g = ti * ksteps + t for this wave's two strips of tile ti
+    auto load_w = [&](WSlot &ws, int g) __attribute__((always_inline)) {
+        const int ti = g / ksteps, t = g - ti * ksteps;
+        const bool live = g < total;
 #pragma unroll
         for (int j = 0; j < kStripsPerWave; ++j) {
-            const uint32_t unit = (uint32_t)(j * ksteps + t);
+            const int s = (tile0 + ti) * kGTileStrips + wave * kStripsPerWave + j;
+            const bool ok = live && s < p.strips;
+            const uint32_t unit = (uint32_t)(s * ksteps + t);
             const auto iv = __builtin_amdgcn_raw_buffer_load_b96(irs, ok ? unit * 768 + lane * 12 : kBufferOob, 0, 0);
             ws.w[j][0] = iv[0];
             ws.w[j][1] = iv[1];
@@ -488,20 +506,54 @@ void moe_lut3_gemm_lds_kernel(MoeArgs p)
 
     for (int pass = row0; pass < row1; pass += MB * 16) {
         const int nmb = min(MB, (row1 - pass) / 16);
-        // 1. stage the pass's activation rows and block scales (invalid rows: zeros)
+        // 1. stage the pass's slot ids, then its activation rows and block
+        //    scales (invalid rows: zeros); the first weight loads of the pass
+        //    are issued just before the staging loads so their latencies
+        //    overlap, and the staging loads go out 8 per thread before any
+        //    LDS store
         __syncthreads();                                       // previous pass done with the LDS rows
+        for (int i = threadIdx.x; i < MB * 16; i += kGWaves * 64)
+            sid_lds[i] = i < nmb * 16 ? p.sorted_ids[pass + i] : p.num_valid;
+        __syncthreads();                                       // (waits for every outstanding load)
+        WSlot wsl[D];
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) load_w(wsl[d], d);
+        // thread -> (row, lane in row): every thread stages 16-byte chunks of one row
+        constexpr int kRows = MB * 16;
+        constexpr int kTpr = kGWaves * 64 / kRows;            // threads per staged row
+        constexpr int kBatch = 8;
+        const int srow = threadIdx.x / kTpr, sl = threadIdx.x % kTpr;
+        const int ssid = sid_lds[srow];
+        const bool srow_ok = ssid < p.num_valid;
+        const uint32_t arow_off = srow_ok ? (uint32_t)(ssid / p.a_row_div) : 0u;
         const int chunks = K / 16;
-        for (int i = threadIdx.x; i < MB * 16 * chunks; i += kMoeWaves * 64) {
-            const int row = i / chunks, c = i - row * chunks;
-            const int sid = row < nmb * 16 ? p.sorted_ids[pass + row] : p.num_valid;
-            const uint32_t off = sid < p.num_valid ? (uint32_t)(sid / p.a_row_div) * (uint32_t)K + c * 16 : kBufferOob;
-            *reinterpret_cast<u4 *>(a_lds + row * astride + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
+        for (int c0 = 0; c0 < chunks; c0 += kBatch * kTpr) {
+            u4 v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 + sl + u * kTpr;
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    ars, srow_ok && c < chunks ? arow_off * (uint32_t)K + c * 16 : kBufferOob, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 + sl + u * kTpr;
+                if (c < chunks) *reinterpret_cast<u4 *>(a_lds + srow * astride + c * 16) = v[u];
+            }
         }
-        for (int i = threadIdx.x; i < MB * 16 * k_chunks; i += kMoeWaves * 64) {
-            const int row = i / k_chunks, c = i - row * k_chunks;
-            const int sid = row < nmb * 16 ? p.sorted_ids[pass + row] : p.num_valid;
-            const uint32_t off = sid < p.num_valid ? (uint32_t)(sid / p.a_row_div) * (uint32_t)k_chunks + c : kBufferOob;
-            s_lds[i] = __builtin_amdgcn_raw_buffer_load_b8(srs, off, 0, 0);
+        for (int c0 = 0; c0 < k_chunks; c0 += kBatch * kTpr) {
+            uint32_t v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 + sl + u * kTpr;
+                v[u] = __builtin_amdgcn_raw_buffer_load_b8(
+                    srs, srow_ok && c < k_chunks ? arow_off * (uint32_t)k_chunks + c : kBufferOob, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 + sl + u * kTpr;
+                if (c < k_chunks) s_lds[srow * k_chunks + c] = (uint8_t)v[u];
+            }
         }
         __syncthreads();
 
@@ -511,62 +563,67 @@ void moe_lut3_gemm_lds_kernel(MoeArgs p)
 #pragma unroll
             for (int j = 0; j < kStripsPerWave; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-        // 2. stream the weights D - 1 steps ahead
-        WSlot wsl[D];
+        // 2. stream the weights D - 1 pairs ahead (the first D - 1 are in flight)
+        int ti = 0, t = 0;                                     // the pair being computed
+        auto step = [&](int g, WSlot &wcur, WSlot &wpf) __attribute__((always_inline)) {
+            load_w(wpf, g + D - 1);
+            if (g < total) {
+                const int k_lo = t * 128 + 16 * kg;
+                const int kc = t * 4 + kg;                     // this lane supplies block kc's scale
 #pragma unroll
-        for (int d = 0; d < D - 1; ++d) load_w(wsl[d], d);
-        auto step = [&](int t, WSlot &wcur, WSlot &wpf) {
-            load_w(wpf, t + D - 1);
-            const int k_lo = t * 128 + 16 * kg;
-            const int kc = t * 4 + kg;                         // this lane supplies block kc's scale
+                for (int j = 0; j < kStripsPerWave; ++j) {
+                    const i8v b = lut3_decode(wcur.w[j][0], wcur.w[j][1], wcur.w[j][2], wcur.cbk[j].x,
+                                              wcur.cbk[j].y, wcur.cbk[j].z, wcur.cbk[j].w);
+                    const int bs = (int)((wcur.bscale[j] >> (8 * exsel)) & 0xffu);
 #pragma unroll
-            for (int j = 0; j < kStripsPerWave; ++j) {
-                const i8v b = lut3_decode(wcur.w[j][0], wcur.w[j][1], wcur.w[j][2], wcur.cbk[j].x, wcur.cbk[j].y,
-                                          wcur.cbk[j].z, wcur.cbk[j].w);
-                const int bs = (int)((wcur.bscale[j] >> (8 * exsel)) & 0xffu);
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    if (mb < nmb) {
-                        const uint8_t *ar = a_lds + (mb * 16 + r16) * astride;
-                        const u4 lo = *reinterpret_cast<const u4 *>(ar + k_lo);
-                        const u4 hi = *reinterpret_cast<const u4 *>(ar + k_lo + 64);
-                        const i8v a = i8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                        const int as = kc < k_chunks ? (int)s_lds[(mb * 16 + r16) * k_chunks + kc] : 127;
-                        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[mb][j], 0, 0, 0, as,
-                                                                                      0, bs);
+                    for (int mb = 0; mb < MB; ++mb) {
+                        if (mb < nmb) {
+                            const uint8_t *ar = a_lds + (mb * 16 + r16) * astride;
+                            const u4 lo = *reinterpret_cast<const u4 *>(ar + k_lo);
+                            const u4 hi = *reinterpret_cast<const u4 *>(ar + k_lo + 64);
+                            const i8v a = i8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                            const int as = kc < k_chunks ? (int)s_lds[(mb * 16 + r16) * k_chunks + kc] : 127;
+                            acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[mb][j], 0, 0,
+                                                                                          0, as, 0, bs);
+                        }
                     }
                 }
+                if (t == ksteps - 1) {
+                    // 3. tile done: lane holds column (lane % 16), rows 4*(lane/16) + i of each block
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        if (mb >= nmb) continue;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int sid = sid_lds[mb * 16 + kg * 4 + i];
+#pragma unroll
+                            for (int j = 0; j < kStripsPerWave; ++j) {
+                                const int n = ((tile0 + ti) * kGTileStrips + wave * kStripsPerWave + j) * 16 + r16;
+                                if (sid < p.num_valid && n < p.N) {
+                                    const __bf16 v = (__bf16)acc[mb][j][i];
+                                    p.out[(int64_t)sid * p.N + n] = __builtin_bit_cast(uint16_t, v);
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int j = 0; j < kStripsPerWave; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+                // advance (arithmetic, not a branch: keeps both counters in registers)
+                const int last = t == ksteps - 1 ? 1 : 0;
+                ti += last;
+                t = last ? 0 : t + 1;
             }
         };
         // unrolled by D so every slot index is a constant; the tail repeats the order
-        int t = 0;
-        for (; t + D <= ksteps; t += D) {
+        int g = 0;
+        for (; g + D <= total; g += D) {
 #pragma unroll
-            for (int d = 0; d < D; ++d) step(t + d, wsl[d], wsl[(d + D - 1) % D]);
+            for (int d = 0; d < D; ++d) step(g + d, wsl[d], wsl[(d + D - 1) % D]);
         }
 #pragma unroll
-        for (int d = 0; d < D - 1; ++d)
-            if (t + d < ksteps) step(t + d, wsl[d], wsl[(d + D - 1) % D]);
-
-        // 3. store: lane holds column (lane % 16), rows 4*(lane/16) + i of each block
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            if (mb >= nmb) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sid = p.sorted_ids[pass + mb * 16 + kg * 4 + i];
-                if (sid >= p.num_valid) continue;
-#pragma unroll
-                for (int j = 0; j < kStripsPerWave; ++j) {
-                    const int n = (strip_base + j) * 16 + r16;
-                    if (n < p.N) {
-                        const __bf16 v = (__bf16)acc[mb][j][i];
-                        p.out[(int64_t)sid * p.N + n] = __builtin_bit_cast(uint16_t, v);
-                    }
-                }
-            }
-        }
+        for (int d = 0; d < D - 1; ++d) step(g + d, wsl[d], wsl[(d + D - 1) % D]);
     }
 }
 
@@ -652,18 +709,23 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
     // Activation rows in LDS when a pass of 32 rows (or 16) fits in 80 KB;
     // otherwise the kernel that reads activations straight from memory.
     constexpr int kMaxLds = 80 * 1024;
-    if (moe_lds_bytes(2, p.K) <= kMaxLds) {
-        const int lds = moe_lds_bytes(2, p.K);
-        auto k = moe_lut3_gemm_lds_kernel<2, 5>;
+    const int mb = moe_lds_bytes(2, p.K) <= kMaxLds ? 2 : (moe_lds_bytes(1, p.K) <= kMaxLds ? 1 : 0);
+    if (mb > 0) {
+        // workgroups of 8 waves over groups of 256-column tiles: about 256
+        // workgroups in all, so each expert's activations are staged once per
+        // group instead of once per tile
+        MoeGroupArgs ga;
+        ga.m = p;
+        ga.gtiles = (int)((L.strips + kGTileStrips - 1) / kGTileStrips);
+        const int64_t want = (E_global * (int64_t)ga.gtiles + 255) / 256;     // tiles per workgroup for ~256
+        ga.tiles_per_group = (int)std::max<int64_t>(1, std::min<int64_t>(want, ga.gtiles));
+        ga.n_groups = (ga.gtiles + ga.tiles_per_group - 1) / ga.tiles_per_group;
+        const unsigned gblocks = (unsigned)((int64_t)E_global * ga.n_groups);
+        const int lds = moe_lds_bytes(mb, p.K);
+        auto k = mb == 2 ? moe_lut3_gemm_lds_kernel<2, 5> : moe_lut3_gemm_lds_kernel<1, 5>;
         hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        k<<<blocks, kMoeWaves * 64, lds, s>>>(p);
-    } else if (moe_lds_bytes(1, p.K) <= kMaxLds) {
-        const int lds = moe_lds_bytes(1, p.K);
-        auto k = moe_lut3_gemm_lds_kernel<1, 5>;
-        hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        k<<<blocks, kMoeWaves * 64, lds, s>>>(p);
+        k<<<gblocks, kGWaves * 64, lds, s>>>(ga);
     } else {
         moe_lut3_gemm_kernel<<<blocks, kMoeWaves * 64, 0, s>>>(p);
     }
