@@ -36,8 +36,6 @@ namespace {
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
-constexpr int kLdsRowHalfs = 128 + 8;             // A row in LDS: 128 K + 16 bytes of padding
-
 template <typename T>
 __device__ __forceinline__ T bitcast_u32(uint32_t v) { return __builtin_bit_cast(T, v); }
 
@@ -64,49 +62,6 @@ __device__ __forceinline__ u4 unpack_bf16_biased(uint32_t w, uint32_t magic)
     return r;
 }
 
-template <int G, bool ASYM>
-struct GemmMeta {
-    uint32_t s[(128 / G + 1) / 2];
-    uint32_t z;
-};
-
-template <int G, bool ASYM>
-__device__ __forceinline__ GemmMeta<G, ASYM> gemm_load_meta(__amdgpu_buffer_rsrc_t srs, __amdgpu_buffer_rsrc_t zrs,
-                                                            uint32_t idx, bool ok)
-{
-    constexpr int GPT = 128 / G;
-    GemmMeta<G, ASYM> m;
-    const uint32_t so = ok ? idx * GPT * 2 : kBufferOob;
-    if constexpr (G == 128) m.s[0] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, 0, 0);
-    if constexpr (G == 64) m.s[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
-    if constexpr (G == 32) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(srs, so, 0, 0);
-        m.s[0] = v[0];
-        m.s[1] = v[1];
-    }
-    m.z = 0;
-    if constexpr (ASYM) {
-        const uint32_t zo = ok ? idx * GPT : kBufferOob;
-        if constexpr (G == 128) m.z = __builtin_amdgcn_raw_buffer_load_b8(zrs, zo, 0, 0);
-        if constexpr (G == 64) m.z = __builtin_amdgcn_raw_buffer_load_b16(zrs, zo, 0, 0);
-        if constexpr (G == 32) m.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zo, 0, 0);
-    }
-    return m;
-}
-
-template <int G, bool ASYM>
-__device__ __forceinline__ float meta_scale(const GemmMeta<G, ASYM> &m, int g)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(m.s[g / 2] >> (16 * (g & 1))));
-}
-
-template <int G, bool ASYM>
-__device__ __forceinline__ int meta_zero(const GemmMeta<G, ASYM> &m, int g)
-{
-    if constexpr (ASYM) return (int)(int8_t)(uint8_t)(m.z >> (8 * g));
-    return 8;
-}
-
 // Kernel parameters shared by the instantiations.
 struct GemmArgs {
     const uint8_t *codes, *scales, *zeros;   // packed sections
@@ -117,71 +72,124 @@ struct GemmArgs {
     int m_tiles, n_tiles;
 };
 
-// WM x WN waves; each wave owns TM x TN blocks of 16 x 16 outputs.
-template <bool A_BF16, int G, bool ASYM, int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(WM * WN * 64, 2)
-void gemm_w4_kernel(GemmArgs p)
+// ---------------------------------------------------------------- pipelined GEMM
+// Workgroup tile 128 x 256 (8 waves as 2 x 4, each 64 x 64 = 4 x 4 MFMA
+// blocks), K in steps of one packed 128-K tile.  Every operand moves from
+// memory to LDS with LDS-direct loads (no registers), kV2Stages - 1 K steps
+// ahead of the MFMAs, in a ring of kV2Stages LDS stages:
+//   A : 128 rows x 128 K, rows of 256 bytes whose 16-byte chunks are XOR-
+//       swizzled by the row (chunk c of row r stored at c ^ (r % 16)), so the
+//       16 rows of an MFMA operand read 16 different bank groups;
+//   B : the 16 packed 1 KiB tiles of the workgroup's columns, as stored;
+//   scale / zero-point blocks of those tiles.
+// Each wave issues the same fixed set of load instructions per stage, so
+// "stage k has landed" is a vmcnt count; a barrier then publishes it.
+// bf16 activations: the row sums of each quantization group come from one
+// more MFMA per A operand against a B of ones, in the same accumulator layout
+// as the products (no LDS round trip for them).
+constexpr int kV2Waves = 8;
+constexpr int kV2BM = 128, kV2BN = 256;
+constexpr int kV2Stages = 3;
+constexpr int kV2AStage = kV2BM * 256;                 // bytes
+constexpr int kV2BStage = (kV2BN / 16) * 1024;         // 16 strips
+constexpr int kV2MStage = kV2Waves * 256;              // per-wave 256-byte metadata slots
+template <bool ASYM> constexpr int v2_stage_bytes() { return kV2AStage + kV2BStage + kV2MStage * (ASYM ? 2 : 1); }
+template <bool ASYM> constexpr int v2_dma_per_stage() { return 4 + 2 + 1 + (ASYM ? 1 : 0); }
+
+template <int BYTES>
+__device__ __forceinline__ void v2_dma(__amdgpu_buffer_rsrc_t rs, uint8_t *lds, uint32_t off)
 {
-    constexpr int NT = WM * WN * 64;                  // threads
-    constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
+    static_assert(BYTES == 16 || BYTES == 4, "LDS-direct load size");
+    auto *l = (__attribute__((address_space(3))) void *)lds;
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 4, off, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void v2_wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void v2_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <bool A_BF16, int G, bool ASYM>
+__global__ __launch_bounds__(kV2Waves * 64, 1)
+void gemm_w4_v2_kernel(GemmArgs p)
+{
     constexpr int GPT = 128 / G;
     constexpr int SPG = G / 32;                       // 32-K MFMA steps per group
-    static_assert(NT == 2 * BM, "two staging threads per A row");
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * kLdsRowHalfs];
-    __shared__ __attribute__((aligned(16))) float Rs[GPT][BM];   // activation row sums per group
+    constexpr int TM = 4, TN = 4;
+    constexpr int SB = v2_stage_bytes<ASYM>();
+    constexpr int NDMA = v2_dma_per_stage<ASYM>();
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave >> 2, wn = wave & 3;
     const int r16 = lane & 15, kq = lane >> 4;
 
-    // tile coordinates; consecutive workgroups on one XCD (blockIdx % 8) walk
-    // the N tiles of the same A rows so those rows stay in that XCD's L2
+    // tile coordinates (XCD-aware: consecutive workgroups on one XCD share A rows)
     const int nblk = gridDim.x;
     int lin = blockIdx.x;
     if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     const int split = lin % p.splits;
     const int tile = lin / p.splits;
     const int mt = tile / p.n_tiles, nt = tile % p.n_tiles;
-    const int m0 = mt * BM, n0 = nt * BN;
+    const int m0 = mt * kV2BM, n0 = nt * kV2BN;
     const int kt0 = (int)((int64_t)p.ktiles * split / p.splits);
     const int kt1 = (int)((int64_t)p.ktiles * (split + 1) / p.splits);
 
-    // A staging: thread -> row tid/2, 64 K (8 x 16 bytes) of the 128-K tile
-    const int arow = tid >> 1, ahalf = tid & 1;
-    const bool arow_ok = m0 + arow < p.M;
-    const auto ars = buffer_rsrc(p.a, (uint32_t)((int64_t)p.M * p.K * 2));
-    const uint32_t a_base = (uint32_t)(((int64_t)(m0 + arow) * p.K + ahalf * 64) * 2);
-
-    // B: this wave's TN strips
-    const int strip0 = n0 / 16 + wn * TN;
     const int strips_total = (p.N + 15) / 16;
+    const auto ars = buffer_rsrc(p.a, (uint32_t)((int64_t)p.M * p.K * 2));
     const auto crs = buffer_rsrc(p.codes, (uint32_t)((int64_t)strips_total * p.ktiles * 1024));
     const auto srs = buffer_rsrc(p.scales, (uint32_t)((int64_t)strips_total * p.ktiles * 16 * GPT * 2));
-    const auto zrs = buffer_rsrc(ASYM ? p.zeros : p.scales, ASYM ? (uint32_t)((int64_t)strips_total * p.ktiles * 16 * GPT) : 0u);
+    const auto zrs = buffer_rsrc(ASYM ? p.zeros : p.scales,
+                                 ASYM ? (uint32_t)((int64_t)strips_total * p.ktiles * 16 * GPT) : 0u);
 
-    u4 areg[8];
-    u4 bcur[TN], bnext[TN];
-    GemmMeta<G, ASYM> mcur[TN], mnext[TN];
-
-    auto load_a = [&](int kt) {
+    // issue the loads of K tile kt into stage st (a tile past kt1 loads zeros)
+    auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+        uint8_t *sa = smem + st * SB;
+        uint8_t *sb = sa + kV2AStage;
+        uint8_t *sm = sb + kV2BStage;
+        const bool live = kt < kt1;
+        // A: instruction i of wave w fills LDS rows 4(4w + i) .. +3, lane -> (row, stored chunk)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            // K % 32 == 0: an 8-element chunk is inside the row or wholly past K
-            const bool ok = arow_ok && kt * 128 + ahalf * 64 + c * 8 < p.K;
-            const uint32_t off = ok ? a_base + (uint32_t)kt * 256 + c * 16 : kBufferOob;
-            areg[c] = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wave * 4 + i) * 4 + (lane >> 4);
+            const int pos = lane & 15;
+            const int chunk = pos ^ (row & 15);
+            const int k = kt * 128 + chunk * 8;
+            const bool ok = live && m0 + row < p.M && k < p.K;
+            v2_dma<16>(ars, sa + (wave * 4 + i) * 1024,
+                   ok ? (uint32_t)(((int64_t)(m0 + row) * p.K + k) * 2) : kBufferOob);
         }
-    };
-    auto load_b = [&](int kt, u4 *b, GemmMeta<G, ASYM> *m) {
+        // B: wave w loads strips 2w, 2w + 1 of the tile's 16
 #pragma unroll
-        for (int nb = 0; nb < TN; ++nb) {
-            const int s = strip0 + nb;
-            const bool ok = s < strips_total;
-            const uint32_t t = (uint32_t)s * p.ktiles + kt;
-            b[nb] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? t * 1024 + lane * 16 : kBufferOob, 0, 0);
-            m[nb] = gemm_load_meta<G, ASYM>(srs, zrs, t * 16 + r16, ok);
+        for (int j = 0; j < 2; ++j) {
+            const int s = n0 / 16 + wave * 2 + j;
+            const bool ok = live && s < strips_total;
+            v2_dma<16>(crs, sb + (wave * 2 + j) * 1024,
+                   ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 1024 + lane * 16) : kBufferOob);
+        }
+        // scales of those two strips: 2 x 32*GPT bytes, 4 bytes per lane
+        {
+            const int b = lane * 4, j = b / (32 * GPT), off = b - j * 32 * GPT;
+            const int s = n0 / 16 + wave * 2 + j;
+            const bool ok = live && j < 2 && s < strips_total;
+            v2_dma<4>(srs, sm + wave * 256,
+                   ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 32 * GPT + off) : kBufferOob);
+        }
+        if constexpr (ASYM) {
+            const int b = lane * 4, j = b / (16 * GPT), off = b - j * 16 * GPT;
+            const int s = n0 / 16 + wave * 2 + j;
+            const bool ok = live && j < 2 && s < strips_total;
+            v2_dma<4>(zrs, sm + kV2MStage + wave * 256,
+                   ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 16 * GPT + off) : kBufferOob);
         }
     };
 
@@ -190,111 +198,92 @@ void gemm_w4_kernel(GemmArgs p)
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-    float unit[TN];                                   // current scale unit of each owned column
+    float unit[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) unit[j] = 1.0f;
 
     uint32_t magic = A_BF16 ? 0x43004300u : 0x64006400u;   // 128.0 (bf16) / 1024.0 (fp16)
     asm volatile("" : "+v"(magic));
+    const u4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 x 8
 
-    if (kt0 < kt1) {
-        load_a(kt0);
-        load_b(kt0, bcur, mcur);
-    }
+    // prologue: stages 0 .. kV2Stages-2
+#pragma unroll
+    for (int s = 0; s < kV2Stages - 1; ++s) issue(kt0 + s, s);
+
     for (int kt = kt0; kt < kt1; ++kt) {
-        // 1. row sums of this thread's 64 activations, per quantization group
-        //    (bf16 only), then the A tile and the sums go to LDS
-        float rsum[2] = {0.f, 0.f};
-        if constexpr (A_BF16) {
-            const bf2v one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int h = (G == 32) ? (c >> 2) : 0;       // 32-K group within the 64-K half
-#pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    rsum[h] = __builtin_amdgcn_fdot2_f32_bf16(bitcast_u32<bf2v>(areg[c][d]), one, rsum[h], false);
-            }
-        }
-        __syncthreads();                              // previous tile fully consumed
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            *reinterpret_cast<u4 *>(&As[arow * kLdsRowHalfs + ahalf * 64 + c * 8]) = areg[c];
-        if constexpr (A_BF16) {
-            if constexpr (G == 128) {
-                const float other = __shfl_xor(rsum[0], 1);
-                if (ahalf == 0) Rs[0][arow] = rsum[0] + other;
-            } else if constexpr (G == 64) {
-                Rs[ahalf][arow] = rsum[0];
-            } else {
-                Rs[ahalf * 2][arow] = rsum[0];
-                Rs[ahalf * 2 + 1][arow] = rsum[1];
-            }
-        }
-        __syncthreads();
+        const int st = (kt - kt0) % kV2Stages;
+        v2_wait_vm<NDMA * (kV2Stages - 2)>();          // this wave's loads of stage st landed
+        v2_barrier();                                  // every wave's; stage (st + 2) % 3 free
+        issue(kt + kV2Stages - 1, (st + kV2Stages - 1) % kV2Stages);
 
-        // 2. prefetch the next K tile while this one is multiplied
-        if (kt + 1 < kt1) {
-            load_a(kt + 1);
-            load_b(kt + 1, bnext, mnext);
-        }
+        const uint8_t *sa = smem + st * SB;
+        const uint8_t *sb = sa + kV2AStage;
+        const uint8_t *sm = sb + kV2BStage;
+        // this wave's B strips (wn * 4 + nb) and their metadata
+        u4 bq[TN];
+#pragma unroll
+        for (int nb = 0; nb < TN; ++nb) bq[nb] = *reinterpret_cast<const u4 *>(sb + (wn * 4 + nb) * 1024 + lane * 16);
 
-        // 3. per quantization group: rescale + bias correction, then MFMAs
 #pragma unroll
         for (int g = 0; g < GPT; ++g) {
-            float ratio[TN];
-            float bz[TN];                              // -(128 + z) for the bf16 bias correction
+            float ratio[TN], bz[TN];
             bool zcol[TN];
             bool anyzero = false;
 #pragma unroll
             for (int nb = 0; nb < TN; ++nb) {
-                const float s = meta_scale<G, ASYM>(mcur[nb], g);
-                zcol[nb] = (s == 0.0f);
-                anyzero |= zcol[nb];
-                ratio[nb] = zcol[nb] ? 1.0f : unit[nb] * __builtin_amdgcn_rcpf(s);
-                unit[nb] = zcol[nb] ? unit[nb] : s;
-                bz[nb] = zcol[nb] ? 0.0f : -(128.0f + (float)meta_zero<G, ASYM>(mcur[nb], g));
-            }
-            // zero scales are rare: one wave-uniform test
-            const bool wave_zero = __builtin_amdgcn_ballot_w64(anyzero) != 0;
-            // acc <- acc * ratio (+ bias correction of this group, bf16 only)
-#pragma unroll
-            for (int mb = 0; mb < TM; ++mb) {
-                f4 rrow = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (A_BF16) {
-                    const int row = wm * TM * 16 + mb * 16 + kq * 4;
-                    rrow = *reinterpret_cast<const f4 *>(&Rs[g][row]);
+                const int s = wn * 4 + nb;             // strip in the tile; its loader wave = s / 2
+                const uint8_t *ms = sm + (s >> 1) * 256 + (s & 1) * 32 * GPT;
+                const float sc = (float)*reinterpret_cast<const _Float16 *>(ms + (r16 * GPT + g) * 2);
+                int z = 8;
+                if constexpr (ASYM) {
+                    const uint8_t *mz = sm + kV2MStage + (s >> 1) * 256 + (s & 1) * 16 * GPT;
+                    z = (int)*reinterpret_cast<const int8_t *>(mz + r16 * GPT + g);
                 }
-#pragma unroll
-                for (int nb = 0; nb < TN; ++nb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (A_BF16)
-                            acc[mb][nb][i] = __builtin_fmaf(acc[mb][nb][i], ratio[nb], rrow[i] * bz[nb]);
-                        else
-                            acc[mb][nb][i] = acc[mb][nb][i] * ratio[nb];
-                    }
+                zcol[nb] = (sc == 0.0f);
+                anyzero |= zcol[nb];
+                ratio[nb] = zcol[nb] ? 1.0f : unit[nb] * __builtin_amdgcn_rcpf(sc);
+                unit[nb] = zcol[nb] ? unit[nb] : sc;
+                bz[nb] = zcol[nb] ? 0.0f : -(128.0f + (float)z);
+                if constexpr (!A_BF16) bz[nb] = (float)z;   // (fp16 path: z goes into the unpack)
             }
+            const bool wave_zero = __builtin_amdgcn_ballot_w64(anyzero) != 0;
+#pragma unroll
+            for (int mb = 0; mb < TM; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < TN; ++nb) acc[mb][nb] = acc[mb][nb] * ratio[nb];
+
+            f4 rs[TM];
+#pragma unroll
+            for (int mb = 0; mb < TM; ++mb) rs[mb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ss = 0; ss < SPG; ++ss) {
                 const int ks = g * SPG + ss;           // 32-K step inside the tile
                 u4 bops[TN];
 #pragma unroll
                 for (int nb = 0; nb < TN; ++nb) {
-                    const uint32_t w = bcur[nb][ks];
+                    const uint32_t w = bq[nb][ks];
                     if constexpr (A_BF16) {
                         bops[nb] = unpack_bf16_biased(w, magic);
                     } else {
-                        const int z = meta_zero<G, ASYM>(mcur[nb], g);
+                        const int z = (int)bz[nb];
                         const _Float16 lo = (_Float16)(-1024.0f - (float)z);
                         const _Float16 hi = (_Float16)(-64.0f - (float)z);
                         bops[nb] = __builtin_bit_cast(u4, unpack_f16(w, magic, h2{lo, lo}, h2{hi, hi}));
                     }
-                    if (wave_zero && zcol[nb]) bops[nb] = u4{0u, 0u, 0u, 0u};
+                }
+                // a column with a zero scale takes no part in this group (rare:
+                // a wave-uniform branch, kept out of the common path)
+                if (__builtin_expect(wave_zero, 0)) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int nb = 0; nb < TN; ++nb)
+                        if (zcol[nb]) bops[nb] = u4{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
                 for (int mb = 0; mb < TM; ++mb) {
-                    const int row = wm * TM * 16 + mb * 16 + r16;
-                    const u4 av = *reinterpret_cast<const u4 *>(&As[row * kLdsRowHalfs + ks * 32 + kq * 8]);
+                    const int row = wm * 64 + mb * 16 + r16;
+                    const int chunk = (ks * 4 + kq) ^ (row & 15);
+                    const u4 av = *reinterpret_cast<const u4 *>(sa + row * 256 + chunk * 16);
 #pragma unroll
                     for (int nb = 0; nb < TN; ++nb) {
                         if constexpr (A_BF16)
@@ -304,26 +293,37 @@ void gemm_w4_kernel(GemmArgs p)
                             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                                 __builtin_bit_cast(h8, av), __builtin_bit_cast(h8, bops[nb]), acc[mb][nb], 0, 0, 0);
                     }
+                    if constexpr (A_BF16)
+                        rs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
+                                                                         __builtin_bit_cast(bf8v, ones), rs[mb], 0, 0, 0);
                 }
             }
-        }
+            // bf16: remove the bias (128 + z) of this group, in the group's units
+            if constexpr (A_BF16) {
 #pragma unroll
-        for (int nb = 0; nb < TN; ++nb) {
-            bcur[nb] = bnext[nb];
-            mcur[nb] = mnext[nb];
+                for (int mb = 0; mb < TM; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < TN; ++nb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = __builtin_fmaf(rs[mb][i], bz[nb], acc[mb][nb][i]);
+            }
         }
     }
 
-    // 4. epilogue: back to real units; C layout of the 16x16 MFMA: lane holds
-    //    column (lane % 16) and rows 4*(lane / 16) + i of each block
+    // the loads issued for stages past the end write LDS too: let them land
+    // before this workgroup's LDS can be handed to another one
+    v2_wait_vm<0>();
+
+    // epilogue: back to real units; C layout of the 16x16 MFMA: lane holds
+    // column (lane % 16) and rows 4*(lane / 16) + i of each block
 #pragma unroll
     for (int mb = 0; mb < TM; ++mb)
 #pragma unroll
         for (int nb = 0; nb < TN; ++nb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * TM * 16 + mb * 16 + kq * 4 + i;
-                const int n = n0 + wn * TN * 16 + nb * 16 + r16;
+                const int m = m0 + wm * 64 + mb * 16 + kq * 4 + i;
+                const int n = n0 + wn * 64 + nb * 16 + r16;
                 if (m < p.M && n < p.N) {
                     const float v = acc[mb][nb][i] * unit[nb];
                     const int64_t o = (int64_t)m * p.N + n;
@@ -356,15 +356,15 @@ struct GemmPlan {
     int m_tiles, n_tiles;
 };
 
-// 128 x 128 output tiles (4 waves of 64 x 64); split K over workgroups while
+// 128 x 256 output tiles (8 waves of 64 x 64); split K over workgroups while
 // the tiles alone give fewer than 256 work units and each split keeps >= 8
 // K tiles.
 GemmPlan plan_gemm(int M, int N, int K)
 {
     const int ktiles = (K + 127) / 128;
     GemmPlan pl;
-    pl.m_tiles = (M + 127) / 128;
-    pl.n_tiles = (N + 127) / 128;
+    pl.m_tiles = (M + kV2BM - 1) / kV2BM;
+    pl.n_tiles = (N + kV2BN - 1) / kV2BN;
     const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
     pl.splits = 1;
     while (tiles * pl.splits < 256 && ktiles / (pl.splits * 2) >= 8) pl.splits *= 2;
@@ -375,7 +375,11 @@ template <bool A_BF16, int G, bool ASYM>
 hipError_t launch_cfg(const GemmPlan &pl, const GemmArgs &a, hipStream_t s)
 {
     const unsigned blocks = (unsigned)((int64_t)pl.m_tiles * pl.n_tiles * pl.splits);
-    gemm_w4_kernel<A_BF16, G, ASYM, 2, 2, 4, 4><<<blocks, 256, 0, s>>>(a);
+    constexpr int lds = kV2Stages * v2_stage_bytes<ASYM>();
+    auto k = gemm_w4_v2_kernel<A_BF16, G, ASYM>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    k<<<blocks, kV2Waves * 64, lds, s>>>(a);
     return hipGetLastError();
 }
 
