@@ -120,7 +120,7 @@ __device__ __forceinline__ void load_round(Slot<G, ASYM> &s, const Cursor &p, CP
     for (int u = 0; u < kTilesPerWave; ++u) {
         const int t = p.rr * kRoundTiles + wave + u * kComputeWaves;
         const bool ok = t < kt;
-        s.q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0, 0);
+        s.q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0, kStreamLoad);
         s.m[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
     }
 }

@@ -46,15 +46,15 @@ __device__ __forceinline__ MetaRaw<G, ASYM> load_meta(__amdgpu_buffer_rsrc_t srs
     MetaRaw<G, ASYM> m;
     if constexpr (G == 128) {
         const uint32_t so = idx < 0 ? kBufferOob : (uint32_t)(idx & ~1) * 2;
-        m.s[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
+        m.s[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, kStreamLoad);
     }
     if constexpr (G == 64) {
         const uint32_t so = idx < 0 ? kBufferOob : (uint32_t)idx * 4;
-        m.s[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
+        m.s[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, kStreamLoad);
     }
     if constexpr (G == 32) {
         const uint32_t so = idx < 0 ? kBufferOob : (uint32_t)idx * 8;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(srs, so, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(srs, so, 0, kStreamLoad);
         m.s[0] = v[0];
         m.s[1] = v[1];
     }
@@ -64,7 +64,7 @@ __device__ __forceinline__ MetaRaw<G, ASYM> load_meta(__amdgpu_buffer_rsrc_t srs
         if constexpr (G == 128) zo = idx < 0 ? kBufferOob : (uint32_t)(idx & ~3);
         if constexpr (G == 64) zo = idx < 0 ? kBufferOob : (uint32_t)(idx & ~1) * 2;
         if constexpr (G == 32) zo = idx < 0 ? kBufferOob : (uint32_t)idx * 4;
-        m.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zo, 0, 0);
+        m.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zo, 0, kStreamLoad);
     }
     (void)GPT;
     return m;
@@ -127,6 +127,78 @@ __device__ __forceinline__ void tile_product(const u4 &q, const MetaRaw<G, ASYM>
         if (i % MPG == MPG - 1) {
 #pragma unroll
             for (int j = 0; j < MR; ++j) acc[j] += sc[g] * c[j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Offset-split product.  Masking a code into the low mantissa nibble of fp16
+// 1024.0 (0x6400) gives 1024 + q exactly; masking it into the next nibble of
+// fp16 64.0 (0x5400, where one unit is 1/16) gives 64 + q exactly.  Each dword
+// of codes becomes an MFMA operand v with one shift and four mask-or
+// operations: v = 1024 + q at K offsets 0, 1, 4, 5 and 64 + q at 2, 3, 6, 7.
+// The zero point enters as a second operand p of the same shape (1024 + z or
+// 64 + z), multiplied with the same activations by a second MFMA chain, so
+//   sum x (q - z) = (x . v) - (x . p).
+// Both chains see the same activations in the same order; where q = z the
+// operands are identical and the difference is exactly zero.  p does not
+// depend on the codes: for symmetric weights it is a constant register, for
+// asymmetric ones it is built once per group from the row's zero point.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMagicLo = 0x64006400u;   // fp16 1024.0 in both halves
+constexpr uint32_t kMagicHi = 0x54005400u;   // fp16 64.0 in both halves
+
+// 8 codes of one dword -> 1024 + q (K offsets 0, 1, 4, 5), 64 + q (2, 3, 6, 7)
+__device__ __forceinline__ h8 unpack8_split(uint32_t w, uint32_t mlo, uint32_t mhi)
+{
+    const uint32_t w8 = w >> 8;
+    const u4 v = {(w & 0x000F000Fu) | mlo, (w & 0x00F000F0u) | mhi, (w8 & 0x000F000Fu) | mlo,
+                  (w8 & 0x00F000F0u) | mhi};
+    return __builtin_bit_cast(h8, v);
+}
+
+// the offset operand of zero point z: 1024 + z and 64 + z in the same slots
+__device__ __forceinline__ h8 offset8(int z)
+{
+    const _Float16 lo = (_Float16)(1024.0f + (float)z);   // exact: integers below 2048
+    const _Float16 hi = (_Float16)(64.0f + (float)z);
+    return h8{lo, lo, hi, hi, lo, lo, hi, hi};
+}
+
+// One 1 KiB tile, offset-split.  psym: the offset operand of the symmetric
+// zero point 8, kept in registers by the caller.
+template <int G, bool ASYM, int MR>
+__device__ __forceinline__ void tile_product_split(const u4 &q, const MetaRaw<G, ASYM> &mr, const h8 *a,
+                                                   const h8 &psym, uint32_t mlo, uint32_t mhi, f4 &acc)
+{
+    constexpr int MPG = G / 32;                      // MFMAs per group
+    const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const int r = (int)(threadIdx.x & 15);
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    f4 cv = zero4, cp = zero4;
+    h8 p = psym;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = i / MPG;
+        if constexpr (ASYM) {
+            if (i % MPG == 0) {
+                uint32_t zb;
+                if constexpr (G == 128) zb = mr.z >> (8 * (r & 3));
+                else if constexpr (G == 64) zb = mr.z >> (16 * (r & 1) + 8 * g);
+                else zb = mr.z >> (8 * g);
+                p = offset8((int)(int8_t)(uint8_t)zb);
+            }
+        }
+        const h8 v = unpack8_split(wd[i], mlo, mhi);
+        cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], v, (i % MPG == 0) ? zero4 : cv, 0, 0, 0);
+        cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], p, (i % MPG == 0) ? zero4 : cp, 0, 0, 0);
+        if (i % MPG == MPG - 1) {
+            uint16_t hb;
+            if constexpr (G == 128) hb = (uint16_t)(mr.s[0] >> (16 * (r & 1)));
+            else hb = (uint16_t)(mr.s[g / 2] >> (16 * (g & 1)));
+            const float sc = (float)__builtin_bit_cast(_Float16, hb);
+#pragma unroll
+            for (int j = 0; j < MR; ++j) acc[j] = __builtin_fmaf(sc, cv[j] - cp[j], acc[j]);
         }
     }
 }

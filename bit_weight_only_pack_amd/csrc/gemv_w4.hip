@@ -60,7 +60,7 @@ void gemv_w4_kernel(const GemvBatch b)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // the problem of this workgroup (wave-uniform scan of at most 8 entries)
     int pi = 0;
-    while (pi + 1 < b.count && (int)blockIdx.x >= b.p[pi + 1].strip_begin) ++pi;
+    while (pi + 1 < b.count && (int)blockIdx.x >= b.p[pi + 1].wg_begin) ++pi;
     const GemvProblem &pr = b.p[pi];
     const uint8_t *codes = pr.codes, *scales = pr.scales, *zeros = pr.zeros;
     const _Float16 *x = pr.x;
@@ -70,7 +70,7 @@ void gemv_w4_kernel(const GemvBatch b)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const int strip = (int)blockIdx.x - pr.strip_begin;
+    const int strip = (int)blockIdx.x - pr.wg_begin;
     const int r = lane & 15;                         // B column (weight row) and A row (token)
     const int kq = lane >> 4;                        // 8-K slice inside each 32-K MFMA block
     const int xrow = x_row_halfs(ct);
@@ -98,7 +98,7 @@ void gemv_w4_kernel(const GemvBatch b)
         for (int u = 0; u < P; ++u) {
             const int t = b0 + wave + u * W;
             const bool ok = t < ktiles;
-            q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0, 0);
+            q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0, kStreamLoad);
             mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
         }
         const int rend = min(b0 + W * P, ktiles);
@@ -165,6 +165,197 @@ void gemv_w4_kernel(const GemvBatch b)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel (every decode shape): the workgroup's whole activation
+// block sits in LDS, so nothing waits behind the weight stream.
+//   1. x goes to LDS first, by LDS-direct loads (1 KiB per wave instruction).
+//      Rows are padded to whole 1 KiB chunks, so every chunk lies in one row,
+//      and the 16-byte blocks of row m are XOR-swizzled by m & 15 so the up
+//      to 16 A rows of an MFMA operand fall in different banks.
+//   2. Each wave then issues the weight and metadata loads of its K tiles (a
+//      contiguous run of the strip), tile by tile.
+//   3. A wait for the x part only (issued first; vector loads retire in
+//      order) and one barrier.
+//   4. Tiles in issue order, each waiting only for its own loads; the
+//      offset-split product (two MFMA chains per group, see gemv_tile.hpp).
+//   5. Fixed-order cross-wave sum through LDS, fp16 RNE store.
+// ---------------------------------------------------------------------------
+constexpr int kV2MaxLds = 80 * 1024;               // two workgroups still fit a compute unit's 160 KiB
+
+struct V2Lds {
+    int rowp;                                        // 16-byte blocks per LDS row of x
+    int red, total;
+};
+__host__ __device__ inline V2Lds v2_lds(int M, int kt, int W, int MR)
+{
+    V2Lds l;
+    l.rowp = (int)round_up((int64_t)kt * 16, 64);
+    l.red = M * l.rowp * 16;
+    l.total = l.red + W * MR * 64 * 4;
+    return l;
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// a workgroup barrier without the vmcnt(0) that __syncthreads implies
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int G, bool ASYM, int MR, int T>
+__global__ __launch_bounds__(1024)
+void gemv_w4_v2_kernel(const GemvBatch b)
+{
+    constexpr int GPT = 128 / G;
+    constexpr int NW = T * (ASYM ? 3 : 2);          // weight + metadata loads per wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int pi = 0;
+    while (pi + 1 < b.count && (int)blockIdx.x >= b.p[pi + 1].wg_begin) ++pi;
+    const GemvProblem &pr = b.p[pi];
+    const int M = b.M, N = pr.N, K = pr.K, kt = pr.ktiles;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    const int strip = (int)blockIdx.x - pr.wg_begin;
+    const int r = lane & 15, kq = lane >> 4;
+    const int tw = (kt + W - 1) / W;                 // K tiles per wave (<= T)
+    const int t0 = wave * tw;
+    const V2Lds L = v2_lds(M, kt, W, MR);
+    float *red = reinterpret_cast<float *>(smem + L.red);
+
+    // 1. activations -> LDS: chunk cc of row m holds blocks 64 cc .. 64 cc + 63
+    //    of the row; block jj of row m holds x[m][8 (jj ^ (m & 15)) ..]
+    {
+        const auto xrs = buffer_rsrc(pr.x, (uint32_t)(M * K * 2));
+        const int cpr = L.rowp >> 6;
+        for (int m = 0; m < M; ++m) {
+            for (int cc = wave; cc < cpr; cc += W) {
+                const int j = (cc * 64 + lane) ^ (m & 15);
+                lds_dma16(xrs, smem + (m * cpr + cc) * 1024, j * 8 < K ? (uint32_t)((m * K + j * 8) * 2) : kBufferOob);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. weights and metadata of this wave's tiles
+    u4 q[T];
+    MetaRaw<G, ASYM> mr[T];
+    {
+        const int64_t tiles0 = (int64_t)strip * kt;
+        const auto crs = buffer_rsrc(pr.codes + tiles0 * 1024, (uint32_t)kt * 1024);
+        const auto srs = buffer_rsrc(pr.scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+        const auto zrs = buffer_rsrc(ASYM ? pr.zeros + tiles0 * 16 * GPT : pr.scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+            const int t = t0 + u;
+            const bool ok = u < tw && t < kt;
+            q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
+                                                         kStreamLoad);
+            mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+            __builtin_amdgcn_sched_barrier(0);       // keep the loads in tile order
+        }
+    }
+
+    // 3. x in LDS everywhere
+    wait_vm<NW>();
+    wg_barrier();
+
+    // 4. products, tile by tile in load order
+    uint32_t mlo = kMagicLo, mhi = kMagicHi;
+    asm volatile("" : "+v"(mlo), "+v"(mhi));         // in registers: each mask-or is one operation
+    h8 psym = offset8(8);
+    {
+        u4 pw = __builtin_bit_cast(u4, psym);
+        asm volatile("" : "+v"(pw));                 // materialised once, outside the tile loop
+        psym = __builtin_bit_cast(h8, pw);
+    }
+    const int xr = r < M ? r : M - 1;                // A row r reads token min(r, M-1)
+    const _Float16 *xa[4];                           // A fragment i of this wave's first tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * L.rowp + t0 * 16 + ((i * 4 + kq) ^ (xr & 15))) * 8;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        if (u < tw && t0 + u < kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            h8 a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const h8 *>(xa[i] + u * 128);
+            u4 qv = q[u];
+            asm volatile("" : "+v"(qv));
+            MetaRaw<G, ASYM> mv = mr[u];
+            pin_meta<G, ASYM>(mv);
+            tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
+        }
+    }
+
+    // 5. fixed-order cross-wave sum, fp16 RNE store
+    if (W > 1) {
+#pragma unroll
+        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                float v = red[j * 64 + lane];
+                for (int w = 1; w < W; ++w) v += red[(w * MR + j) * 64 + lane];
+                acc[j] = v;
+            }
+        }
+    }
+    if (wave == 0) {
+        const int n = strip * 16 + r;
+#pragma unroll
+        for (int j = 0; j < MR; ++j) {
+            const int m = kq * 4 + j;
+            if (m < M && n < N) pr.y[(int64_t)m * N + n] = (_Float16)acc[j];
+        }
+    }
+}
+
+template <int G, bool ASYM, int MR, int T>
+hipError_t launch_v2_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    auto k = gemv_w4_v2_kernel<G, ASYM, MR, T>;
+    if (lds > 64 * 1024) {                           // above the default dynamic LDS limit
+        static bool raised = false;
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kV2MaxLds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    k<<<grid, block, lds, st>>>(b);
+    return hipGetLastError();
+}
+
+template <int G, bool ASYM, int MR>
+hipError_t launch_v2_t(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    if (T <= 1) return launch_v2_k<G, ASYM, MR, 1>(grid, block, lds, st, b);
+    if (T <= 2) return launch_v2_k<G, ASYM, MR, 2>(grid, block, lds, st, b);
+    if (T <= 4) return launch_v2_k<G, ASYM, MR, 4>(grid, block, lds, st, b);
+    return launch_v2_k<G, ASYM, MR, 8>(grid, block, lds, st, b);
+}
+
+template <int G, bool ASYM>
+hipError_t launch_v2(int MR, int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    if (MR == 1) return launch_v2_t<G, ASYM, 1>(T, grid, block, lds, st, b);
+    if (MR == 2) return launch_v2_t<G, ASYM, 2>(T, grid, block, lds, st, b);
+    return launch_v2_t<G, ASYM, 4>(T, grid, block, lds, st, b);
+}
+
 template <int G, bool ASYM, int MR>
 hipError_t launch_p(int P, dim3 grid, dim3 block, size_t lds, hipStream_t s, const GemvBatch &b)
 {
@@ -203,20 +394,46 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
         p.N = (int)L[i].N;
         p.K = (int)L[i].K;
         p.ktiles = (int)L[i].ktiles;
-        p.strip_begin = (int)strips;
         strips += L[i].strips;
         if (L[i].ktiles > kt) kt = L[i].ktiles;
     }
     b.count = count;
     b.M = M;
     if (strips == 0) return hipSuccess;
+    const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const int G = L[0].G;
+    const bool asym = L[0].asym;
     // waves per workgroup: enough that each wave holds at most 4 tiles (8 for
     // long K), capped at 16 waves
     int W = (int)((kt + 3) / 4);
     if (W < 1) W = 1;
     if (W > 16) W = 16;
-    const int P = (int)((kt + W - 1) / W) <= 4 ? 4 : 8;
-    const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const int64_t T = (kt + W - 1) / W;
+    for (int i = 0, wg = 0; i < count; ++i) {        // one workgroup per strip
+        b.p[i].wg_begin = wg;
+        wg += (int)L[i].strips;
+    }
+    const dim3 grid((unsigned)strips), block((unsigned)(W * 64));
+
+    // streaming kernel whenever the x block fits
+    if (T <= 8) {
+        const V2Lds lay = v2_lds(M, (int)kt, W, MR);
+        if (lay.total <= kV2MaxLds) {
+            b.ct = 0;
+            const size_t lds = (size_t)lay.total;
+            switch (G) {
+            case 32: return asym ? launch_v2<32, true>(MR, (int)T, grid, block, lds, s, b)
+                                 : launch_v2<32, false>(MR, (int)T, grid, block, lds, s, b);
+            case 64: return asym ? launch_v2<64, true>(MR, (int)T, grid, block, lds, s, b)
+                                 : launch_v2<64, false>(MR, (int)T, grid, block, lds, s, b);
+            default: return asym ? launch_v2<128, true>(MR, (int)T, grid, block, lds, s, b)
+                                 : launch_v2<128, false>(MR, (int)T, grid, block, lds, s, b);
+            }
+        }
+    }
+
+    // round-based kernel: activations staged in chunks of K tiles
+    const int P = T <= 4 ? 4 : 8;
     // activation chunk: every K tile of a round when it fits the LDS budget
     const int64_t round_tiles = (int64_t)W * P;
     int64_t ct = kt < round_tiles ? kt : round_tiles;
@@ -224,11 +441,10 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
     if (ct < 1) ct = 1;
     b.ct = (int)ct;
     const size_t lds = (size_t)gemv_lds_bytes(M, (int)ct, W, MR);
-    const dim3 grid((unsigned)strips), block((unsigned)(W * 64));
-    switch (L[0].G) {
-    case 32: return L[0].asym ? launch_gm<32, true>(MR, P, grid, block, lds, s, b) : launch_gm<32, false>(MR, P, grid, block, lds, s, b);
-    case 64: return L[0].asym ? launch_gm<64, true>(MR, P, grid, block, lds, s, b) : launch_gm<64, false>(MR, P, grid, block, lds, s, b);
-    default: return L[0].asym ? launch_gm<128, true>(MR, P, grid, block, lds, s, b) : launch_gm<128, false>(MR, P, grid, block, lds, s, b);
+    switch (G) {
+    case 32: return asym ? launch_gm<32, true>(MR, P, grid, block, lds, s, b) : launch_gm<32, false>(MR, P, grid, block, lds, s, b);
+    case 64: return asym ? launch_gm<64, true>(MR, P, grid, block, lds, s, b) : launch_gm<64, false>(MR, P, grid, block, lds, s, b);
+    default: return asym ? launch_gm<128, true>(MR, P, grid, block, lds, s, b) : launch_gm<128, false>(MR, P, grid, block, lds, s, b);
     }
 }
 

@@ -23,6 +23,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 constexpr uint32_t kBufferOob = 0x80000000u;   // an offset past any descriptor used here
+// Cache policy of loads that stream data read once (packed weights): the
+// non-temporal hint, so streaming lines do not displace reused ones.
+constexpr int kStreamLoad = 2;
 
 constexpr int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
@@ -93,7 +96,7 @@ struct GemvProblem {
     const uint8_t *codes, *scales, *zeros;
     const _Float16 *x;
     _Float16 *y;
-    int N, K, ktiles, strip_begin;
+    int N, K, ktiles, wg_begin;          // wg_begin: first workgroup of the problem
 };
 struct GemvBatch {
     GemvProblem p[kMaxGemvBatch];
