@@ -203,5 +203,32 @@ __device__ __forceinline__ void tile_product_split(const u4 &q, const MetaRaw<G,
     }
 }
 
+// Batch-1 symmetric form: the offset terms of the tile's groups come in
+// precomputed (off[g], valid in the lanes that hold C row 0), so only the
+// code chain runs here.
+template <int G>
+__device__ __forceinline__ void tile_product_pre(const u4 &q, const MetaRaw<G, false> &mr, const h8 *a,
+                                                 const float *off, uint32_t mlo, uint32_t mhi, f4 &acc)
+{
+    constexpr int MPG = G / 32;
+    const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const int r = (int)(threadIdx.x & 15);
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    f4 cv = zero4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = i / MPG;
+        const h8 v = unpack8_split(wd[i], mlo, mhi);
+        cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], v, (i % MPG == 0) ? zero4 : cv, 0, 0, 0);
+        if (i % MPG == MPG - 1) {
+            uint16_t hb;
+            if constexpr (G == 128) hb = (uint16_t)(mr.s[0] >> (16 * (r & 1)));
+            else hb = (uint16_t)(mr.s[g / 2] >> (16 * (g & 1)));
+            const float sc = (float)__builtin_bit_cast(_Float16, hb);
+            acc[0] = __builtin_fmaf(sc, cv[0] - off[g], acc[0]);
+        }
+    }
+}
+
 }  // namespace tile
 }  // namespace lowbit

@@ -58,10 +58,9 @@ void gemv_w4_kernel(const GemvBatch b)
 {
     constexpr int GPT = 128 / G;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // the problem of this workgroup (wave-uniform scan of at most 8 entries)
-    int pi = 0;
-    while (pi + 1 < b.count && (int)blockIdx.x >= b.p[pi + 1].wg_begin) ++pi;
-    const GemvProblem &pr = b.p[pi];
+    // the problem of this workgroup is blockIdx.y; strips past its end exit
+    const GemvProblem &pr = b.p[blockIdx.y];
+    if ((int)blockIdx.x >= pr.strips) return;
     const uint8_t *codes = pr.codes, *scales = pr.scales, *zeros = pr.zeros;
     const _Float16 *x = pr.x;
     _Float16 *y = pr.y;
@@ -70,7 +69,7 @@ void gemv_w4_kernel(const GemvBatch b)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const int strip = (int)blockIdx.x - pr.wg_begin;
+    const int strip = (int)blockIdx.x;
     const int r = lane & 15;                         // B column (weight row) and A row (token)
     const int kq = lane >> 4;                        // 8-K slice inside each 32-K MFMA block
     const int xrow = x_row_halfs(ct);
@@ -210,23 +209,70 @@ __device__ __forceinline__ void wait_vm()
 // a workgroup barrier without the vmcnt(0) that __syncthreads implies
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int G, bool ASYM, int MR, int T>
-__global__ __launch_bounds__(1024)
+// Occupancy targets: batch-1 symmetric with up to 4 tiles per wave keeps 8
+// waves per SIMD (64 VGPRs), so four 8-wave workgroups share a compute unit;
+// other forms with up to 4 tiles per wave 6; 8 tiles per wave (16-wave
+// workgroups, one per compute unit) 4.
+template <int G, bool ASYM, int MR, int T, int NP>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
 void gemv_w4_v2_kernel(const GemvBatch b)
 {
     constexpr int GPT = 128 / G;
     constexpr int NW = T * (ASYM ? 3 : 2);          // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    int pi = 0;
-    while (pi + 1 < b.count && (int)blockIdx.x >= b.p[pi + 1].wg_begin) ++pi;
-    const GemvProblem &pr = b.p[pi];
-    const int M = b.M, N = pr.N, K = pr.K, kt = pr.ktiles;
+    // One round of kernel-argument reads.  NP = 1: the one problem.  NP = 4:
+    // the problems' strips are laid end to end over blockIdx.x and the fields
+    // of all four are read at once, then selected.  NP = 8: blockIdx.y is the
+    // problem and strips past its end exit.  Every field is made live right
+    // away (empty asm), so the scalar loads go out together.
+    if constexpr (NP == 4) {
+        // all four problems' pointers and sizes live before the selection
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const GemvProblem &q = b.p[i];
+            asm volatile("" ::"s"(q.codes), "s"(q.scales), "s"(q.zeros), "s"(q.x), "s"(q.y), "s"(q.N), "s"(q.K),
+                         "s"(q.ktiles), "s"(q.strips), "s"(q.tw));
+        }
+        asm volatile("" ::"s"(b.first[1]), "s"(b.first[2]), "s"(b.first[3]), "s"(b.M), "s"(b.W));
+    }
+    int pi, strip;
+    if constexpr (NP == 1) {
+        pi = 0;
+        strip = (int)blockIdx.x;
+    } else if constexpr (NP == 4) {
+        const int bx = (int)blockIdx.x, f1 = b.first[1], f2 = b.first[2], f3 = b.first[3];
+        pi = (bx >= f1 ? 1 : 0) + (bx >= f2 ? 1 : 0) + (bx >= f3 ? 1 : 0);
+        strip = bx - (pi == 0 ? 0 : pi == 1 ? f1 : pi == 2 ? f2 : f3);
+    } else {
+        pi = (int)blockIdx.y;
+        strip = (int)blockIdx.x;
+    }
+    auto field = [&](auto get) {
+        if constexpr (NP == 4) {
+            const auto v0 = get(b.p[0]), v1 = get(b.p[1]), v2 = get(b.p[2]), v3 = get(b.p[3]);
+            return pi == 0 ? v0 : pi == 1 ? v1 : pi == 2 ? v2 : v3;
+        } else {
+            return get(b.p[pi]);
+        }
+    };
+    const uint8_t *codes = field([](const GemvProblem &q) { return q.codes; });
+    const uint8_t *scales = field([](const GemvProblem &q) { return q.scales; });
+    const uint8_t *zeros = field([](const GemvProblem &q) { return q.zeros; });
+    const _Float16 *xg = field([](const GemvProblem &q) { return q.x; });
+    _Float16 *yp = field([](const GemvProblem &q) { return q.y; });
+    int N = field([](const GemvProblem &q) { return q.N; });
+    int K = field([](const GemvProblem &q) { return q.K; });
+    int kt = field([](const GemvProblem &q) { return q.ktiles; });
+    int nst = field([](const GemvProblem &q) { return q.strips; });
+    int tw = field([](const GemvProblem &q) { return q.tw; });
+    int M = b.M, W = b.W;
+    asm volatile("" : "+s"(codes), "+s"(scales), "+s"(xg), "+s"(yp), "+s"(N), "+s"(K), "+s"(kt), "+s"(nst),
+                 "+s"(tw), "+s"(M), "+s"(W));
+    if constexpr (ASYM) asm volatile("" : "+s"(zeros));
+    if (strip >= nst) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int W = blockDim.x >> 6;
-    const int strip = (int)blockIdx.x - pr.wg_begin;
     const int r = lane & 15, kq = lane >> 4;
-    const int tw = (kt + W - 1) / W;                 // K tiles per wave (<= T)
     const int t0 = wave * tw;
     const V2Lds L = v2_lds(M, kt, W, MR);
     float *red = reinterpret_cast<float *>(smem + L.red);
@@ -234,7 +280,7 @@ void gemv_w4_v2_kernel(const GemvBatch b)
     // 1. activations -> LDS: chunk cc of row m holds blocks 64 cc .. 64 cc + 63
     //    of the row; block jj of row m holds x[m][8 (jj ^ (m & 15)) ..]
     {
-        const auto xrs = buffer_rsrc(pr.x, (uint32_t)(M * K * 2));
+        const auto xrs = buffer_rsrc(xg, (uint32_t)(M * K * 2));
         const int cpr = L.rowp >> 6;
         for (int m = 0; m < M; ++m) {
             for (int cc = wave; cc < cpr; cc += W) {
@@ -250,9 +296,9 @@ void gemv_w4_v2_kernel(const GemvBatch b)
     MetaRaw<G, ASYM> mr[T];
     {
         const int64_t tiles0 = (int64_t)strip * kt;
-        const auto crs = buffer_rsrc(pr.codes + tiles0 * 1024, (uint32_t)kt * 1024);
-        const auto srs = buffer_rsrc(pr.scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
-        const auto zrs = buffer_rsrc(ASYM ? pr.zeros + tiles0 * 16 * GPT : pr.scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+        const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
+        const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+        const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
 #pragma unroll
         for (int u = 0; u < T; ++u) {
             const int t = t0 + u;
@@ -283,10 +329,35 @@ void gemv_w4_v2_kernel(const GemvBatch b)
     for (int i = 0; i < 4; ++i)
         xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * L.rowp + t0 * 16 + ((i * 4 + kq) ^ (xr & 15))) * 8;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Batch-1 symmetric weights: the offset chain x . p does not depend on
+    // the codes or the weight row, so one MFMA chain serves several tiles.
+    // Its A rows 0..3 carry K blocks of different (tile, group) pairs
+    // instead of copies of the one token: row j = (tile u0 + j / GPT, group
+    // j % GPT), and C row j (lane / 16 == 0, element j) is that group's offset
+    // term, computed exactly as the per-tile chain would compute it.
+    constexpr bool PRE = !ASYM && MR == 1;
+    constexpr int TPS = 4 / GPT;                     // tiles per offset set
+    constexpr int MPG = G / 32;
+    f4 cps = {0.f, 0.f, 0.f, 0.f};
+    const int tvalid = min(tw, kt - t0);             // this wave's real tiles (>= 1 when it has work)
 #pragma unroll
     for (int u = 0; u < T; ++u) {
-        if (u < tw && t0 + u < kt) {
+        if (u < tvalid) {
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PRE) {
+                if (u % TPS == 0) {
+                    const int rr = r < 4 ? r : 0;
+                    const int tu = min(u + rr / GPT, tvalid - 1);
+                    const int g = rr % GPT;
+                    const _Float16 *xb = reinterpret_cast<const _Float16 *>(smem) + ((t0 + tu) * 16 + g * MPG * 4 + kq) * 8;
+#pragma unroll
+                    for (int i = 0; i < MPG; ++i) {
+                        const h8 ab = *reinterpret_cast<const h8 *>(xb + i * 32);
+                        cps = __builtin_amdgcn_mfma_f32_16x16x32_f16(ab, psym, i == 0 ? f4{0.f, 0.f, 0.f, 0.f} : cps,
+                                                                     0, 0, 0);
+                    }
+                }
+            }
             h8 a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const h8 *>(xa[i] + u * 128);
@@ -294,11 +365,19 @@ void gemv_w4_v2_kernel(const GemvBatch b)
             asm volatile("" : "+v"(qv));
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
-            tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
+            if constexpr (PRE) {
+                float off[GPT];
+#pragma unroll
+                for (int g = 0; g < GPT; ++g) off[g] = cps[(u % TPS) * GPT + g];
+                tile_product_pre<G>(qv, mv, a, off, mlo, mhi, acc);
+            } else {
+                tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
+            }
         }
     }
 
-    // 5. fixed-order cross-wave sum, fp16 RNE store
+    // 5. fixed-order cross-wave sum (all partials read at once, added in wave
+    //    order), fp16 RNE store
     if (W > 1) {
 #pragma unroll
         for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
@@ -306,8 +385,13 @@ void gemv_w4_v2_kernel(const GemvBatch b)
         if (wave == 0) {
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
+                float part[16];
+#pragma unroll
+                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
                 float v = red[j * 64 + lane];
-                for (int w = 1; w < W; ++w) v += red[(w * MR + j) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < 16; ++w)
+                    if (w < W) v += part[w];
                 acc[j] = v;
             }
         }
@@ -317,15 +401,15 @@ void gemv_w4_v2_kernel(const GemvBatch b)
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
             const int m = kq * 4 + j;
-            if (m < M && n < N) pr.y[(int64_t)m * N + n] = (_Float16)acc[j];
+            if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[j];
         }
     }
 }
 
-template <int G, bool ASYM, int MR, int T>
-hipError_t launch_v2_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+template <int G, bool ASYM, int MR, int T, int NP>
+hipError_t launch_v2_np(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
-    auto k = gemv_w4_v2_kernel<G, ASYM, MR, T>;
+    auto k = gemv_w4_v2_kernel<G, ASYM, MR, T, NP>;
     if (lds > 64 * 1024) {                           // above the default dynamic LDS limit
         static bool raised = false;
         if (!raised) {
@@ -339,10 +423,17 @@ hipError_t launch_v2_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const 
     return hipGetLastError();
 }
 
+template <int G, bool ASYM, int MR, int T>
+hipError_t launch_v2_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    if (b.count == 1) return launch_v2_np<G, ASYM, MR, T, 1>(grid, block, lds, st, b);
+    if (b.count <= 4) return launch_v2_np<G, ASYM, MR, T, 4>(grid, block, lds, st, b);
+    return launch_v2_np<G, ASYM, MR, T, 8>(grid, block, lds, st, b);
+}
+
 template <int G, bool ASYM, int MR>
 hipError_t launch_v2_t(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
-    if (T <= 1) return launch_v2_k<G, ASYM, MR, 1>(grid, block, lds, st, b);
     if (T <= 2) return launch_v2_k<G, ASYM, MR, 2>(grid, block, lds, st, b);
     if (T <= 4) return launch_v2_k<G, ASYM, MR, 4>(grid, block, lds, st, b);
     return launch_v2_k<G, ASYM, MR, 8>(grid, block, lds, st, b);
@@ -394,11 +485,13 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
         p.N = (int)L[i].N;
         p.K = (int)L[i].K;
         p.ktiles = (int)L[i].ktiles;
+        p.strips = (int)L[i].strips;
         strips += L[i].strips;
         if (L[i].ktiles > kt) kt = L[i].ktiles;
     }
     b.count = count;
     b.M = M;
+    b.W = 0;
     if (strips == 0) return hipSuccess;
     const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
     const int G = L[0].G;
@@ -409,11 +502,20 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
     if (W < 1) W = 1;
     if (W > 16) W = 16;
     const int64_t T = (kt + W - 1) / W;
-    for (int i = 0, wg = 0; i < count; ++i) {        // one workgroup per strip
-        b.p[i].wg_begin = wg;
-        wg += (int)L[i].strips;
+    int64_t max_strips = 0;
+    for (int i = 0; i < kMaxGemvBatch; ++i) b.first[i] = 0x7FFFFFFF;
+    for (int i = 0, f = 0; i < count; ++i) {
+        b.p[i].tw = (int)((L[i].ktiles + W - 1) / W);
+        b.first[i] = f;
+        f += (int)L[i].strips;
+        if (L[i].strips > max_strips) max_strips = L[i].strips;
     }
-    const dim3 grid((unsigned)strips), block((unsigned)(W * 64));
+    b.W = W;
+    // one workgroup per strip.  The streaming kernel lays up to 4 problems end
+    // to end over blockIdx.x; otherwise (and in the round-based kernel)
+    // blockIdx.x = strip and blockIdx.y = problem.
+    const dim3 grid((unsigned)max_strips, (unsigned)count), block((unsigned)(W * 64));
+    const dim3 grid_flat((unsigned)strips);
 
     // streaming kernel whenever the x block fits
     if (T <= 8) {
@@ -421,13 +523,14 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
         if (lay.total <= kV2MaxLds) {
             b.ct = 0;
             const size_t lds = (size_t)lay.total;
+            const dim3 g2 = count <= 4 ? grid_flat : grid;
             switch (G) {
-            case 32: return asym ? launch_v2<32, true>(MR, (int)T, grid, block, lds, s, b)
-                                 : launch_v2<32, false>(MR, (int)T, grid, block, lds, s, b);
-            case 64: return asym ? launch_v2<64, true>(MR, (int)T, grid, block, lds, s, b)
-                                 : launch_v2<64, false>(MR, (int)T, grid, block, lds, s, b);
-            default: return asym ? launch_v2<128, true>(MR, (int)T, grid, block, lds, s, b)
-                                 : launch_v2<128, false>(MR, (int)T, grid, block, lds, s, b);
+            case 32: return asym ? launch_v2<32, true>(MR, (int)T, g2, block, lds, s, b)
+                                 : launch_v2<32, false>(MR, (int)T, g2, block, lds, s, b);
+            case 64: return asym ? launch_v2<64, true>(MR, (int)T, g2, block, lds, s, b)
+                                 : launch_v2<64, false>(MR, (int)T, g2, block, lds, s, b);
+            default: return asym ? launch_v2<128, true>(MR, (int)T, g2, block, lds, s, b)
+                                 : launch_v2<128, false>(MR, (int)T, g2, block, lds, s, b);
             }
         }
     }

@@ -90,17 +90,21 @@ hipError_t launch_w4_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *c
 hipError_t launch_w4_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s);
 
 // A batch of independent GEMVs with the same format, M and group size, run by
-// one launch (problems laid end to end over the grid, one strip per workgroup).
+// one launch (one workgroup per 16-row strip; blockIdx.y picks the problem).
 constexpr int kMaxGemvBatch = 8;
 struct GemvProblem {
     const uint8_t *codes, *scales, *zeros;
     const _Float16 *x;
     _Float16 *y;
-    int N, K, ktiles, wg_begin;          // wg_begin: first workgroup of the problem
+    int N, K, ktiles, strips;
+    int tw;                              // K tiles per wave of the streaming kernel
+    int pad;
 };
 struct GemvBatch {
     GemvProblem p[kMaxGemvBatch];
+    int first[kMaxGemvBatch];            // first workgroup of each problem when laid end to end
     int count, M, ct;
+    int W;                               // waves per workgroup
 };
 hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
                                 const _Float16 *const *x, _Float16 *const *y, hipStream_t s);
