@@ -185,10 +185,14 @@ struct V2Lds {
     int rowp;                                        // 16-byte blocks per LDS row of x
     int red, total;
 };
-__host__ __device__ inline V2Lds v2_lds(int M, int kt, int W, int MR)
+// 16-byte blocks per K tile in LDS: 16, or 20 for the batch-1 symmetric form,
+// whose shared offset chain reads the same block of four consecutive tiles at
+// once (the 64-byte pad puts those reads in different banks)
+__host__ __device__ constexpr int v2_tile_blocks(bool asym, int MR) { return !asym && MR == 1 ? 20 : 16; }
+__host__ __device__ inline V2Lds v2_lds(int M, int kt, int W, int MR, bool asym)
 {
     V2Lds l;
-    l.rowp = (int)round_up((int64_t)kt * 16, 64);
+    l.rowp = (int)round_up((int64_t)kt * v2_tile_blocks(asym, MR), 64);
     l.red = M * l.rowp * 16;
     l.total = l.red + W * MR * 64 * 4;
     return l;
@@ -274,18 +278,23 @@ void gemv_w4_v2_kernel(const GemvBatch b)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, kq = lane >> 4;
     const int t0 = wave * tw;
-    const V2Lds L = v2_lds(M, kt, W, MR);
+    constexpr int TB = v2_tile_blocks(ASYM, MR);
+    const V2Lds L = v2_lds(M, kt, W, MR, ASYM);
     float *red = reinterpret_cast<float *>(smem + L.red);
 
     // 1. activations -> LDS: chunk cc of row m holds blocks 64 cc .. 64 cc + 63
-    //    of the row; block jj of row m holds x[m][8 (jj ^ (m & 15)) ..]
+    //    of the row; block b < 16 of tile t of row m holds
+    //    x[m][128 t + 8 (b ^ (m & 15)) ..], blocks 16..TB-1 are zero padding
     {
         const auto xrs = buffer_rsrc(xg, (uint32_t)(M * K * 2));
         const int cpr = L.rowp >> 6;
         for (int m = 0; m < M; ++m) {
             for (int cc = wave; cc < cpr; cc += W) {
-                const int j = (cc * 64 + lane) ^ (m & 15);
-                lds_dma16(xrs, smem + (m * cpr + cc) * 1024, j * 8 < K ? (uint32_t)((m * K + j * 8) * 2) : kBufferOob);
+                const int jj = cc * 64 + lane;
+                const int t = jj / TB, bb = jj - t * TB;
+                const int j = t * 16 + (bb ^ (m & 15));
+                const bool ok = bb < 16 && j * 8 < K;
+                lds_dma16(xrs, smem + (m * cpr + cc) * 1024, ok ? (uint32_t)((m * K + j * 8) * 2) : kBufferOob);
             }
         }
     }
@@ -327,7 +336,7 @@ void gemv_w4_v2_kernel(const GemvBatch b)
     const _Float16 *xa[4];                           // A fragment i of this wave's first tile
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * L.rowp + t0 * 16 + ((i * 4 + kq) ^ (xr & 15))) * 8;
+        xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * L.rowp + t0 * TB + ((i * 4 + kq) ^ (xr & 15))) * 8;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     // Batch-1 symmetric weights: the offset chain x . p does not depend on
     // the codes or the weight row, so one MFMA chain serves several tiles.
@@ -349,7 +358,7 @@ void gemv_w4_v2_kernel(const GemvBatch b)
                     const int rr = r < 4 ? r : 0;
                     const int tu = min(u + rr / GPT, tvalid - 1);
                     const int g = rr % GPT;
-                    const _Float16 *xb = reinterpret_cast<const _Float16 *>(smem) + ((t0 + tu) * 16 + g * MPG * 4 + kq) * 8;
+                    const _Float16 *xb = reinterpret_cast<const _Float16 *>(smem) + ((t0 + tu) * TB + g * MPG * 4 + kq) * 8;
 #pragma unroll
                     for (int i = 0; i < MPG; ++i) {
                         const h8 ab = *reinterpret_cast<const h8 *>(xb + i * 32);
@@ -360,7 +369,7 @@ void gemv_w4_v2_kernel(const GemvBatch b)
             }
             h8 a[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const h8 *>(xa[i] + u * 128);
+            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const h8 *>(xa[i] + u * TB * 8);
             u4 qv = q[u];
             asm volatile("" : "+v"(qv));
             MetaRaw<G, ASYM> mv = mr[u];
@@ -519,7 +528,7 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
 
     // streaming kernel whenever the x block fits
     if (T <= 8) {
-        const V2Lds lay = v2_lds(M, (int)kt, W, MR);
+        const V2Lds lay = v2_lds(M, (int)kt, W, MR, asym);
         if (lay.total <= kV2MaxLds) {
             b.ct = 0;
             const size_t lds = (size_t)lay.total;
