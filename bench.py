@@ -240,7 +240,7 @@ def bench_decode(args, torch, lb, synth):
         per_group = None
     else:
         med = time_launches(torch, lb, fmt, M, G, launches, stream, args.kernel_reps)
-        n_launch, kernel = len(launches), "gemv_w4_kernel<G=128,sym,M=1>"
+        n_launch, kernel = len(launches), "gemv_w4_v2_kernel<G=128,sym,M=1>"
         groups = {}
         for L, t in zip(launches, med):
             groups.setdefault("+".join(L["names"]), []).append((t, L["bytes"]))
