@@ -185,7 +185,7 @@ def time_launches(torch, lb, fmt, M, G, launches, stream, reps):
 def read_traffic(name):
     """HBM bytes per launch measured with rocprofv3 counters, if recorded."""
     path = os.path.join(ROOT, "profiles", name)
-    if os.path.exists(path):
+    if name and os.path.exists(path):
         for line in open(path):
             if line.startswith("traffic_bytes_per_launch:"):
                 return float(line.split(":")[1])
@@ -274,8 +274,8 @@ def bench_decode(args, torch, lb, synth):
         "gpu_ms_per_step": round(gpu_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic("w4_gemv_decode_step_traffic.txt" if mode != "chain"
-                                             else "w4_gemv_chain_decode_step_traffic.txt"),
+                     "traffic": read_traffic({"batched": "w4_gemv_decode_step_traffic.txt",
+                                              "chain": "w4_gemv_chain_decode_step_traffic.txt"}.get(mode, "")),
                      "kernel": kernel, "bytes_per_launch": round(bytes_per_launch),
                      "avg_launch_us": round(avg_launch_us, 3)},
     }
