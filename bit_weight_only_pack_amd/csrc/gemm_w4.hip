@@ -12,18 +12,18 @@
 //     waves; each wave owns TN 16-column strips of the weight and reads its B
 //     operands straight from the packed 16 x 128 tiles, already in the lane
 //     order of v_mfma_f32_16x16x32_{bf16,f16}: no LDS traffic for B.
-//   * Weights stay exact.  fp16 activations: B = q - z, formed exactly in
-//     packed fp16 (as in the GEMV).  bf16 activations: gfx950 has no packed
-//     bf16 add, so B = 128 + q (one mask+or with the bf16 constant 128.0, exact)
-//     and the bias is removed with the row sums of the activations:
-//       sum_k a (q - z) = sum_k a (128 + q) - (128 + z) * sum_k a
-//     The row sums of each quantization group are taken (v_dot2_f32_bf16,
-//     fp32) while the A tile is staged.
-//   * Scales in fp32 with one accumulator set: before the MFMAs of group g
-//     the accumulator (held in units of the previous group's scale) is
-//     rescaled per column by s_prev / s_g and the group's bias correction is
-//     added; the epilogue multiplies by the last scale.  A zero scale keeps
-//     the unit and zeroes that column's operands for the group.
+//   * Weights stay exact, in offset form.  The B operand holds each code
+//     plus a constant, made by masking it into the mantissa of a power of
+//     two: bf16 activations 128 + q (mask-or with bf16 128.0); fp16
+//     activations 1024 + q and 64 + q (fp16 1024.0 and 64.0, one unit 1/16
+//     there, as in the GEMV).  The zero point enters as an operand p of the
+//     same shape (128 + z, or 1024 + z / 64 + z), and per group
+//       sum_k a (q - z) = sum_k a v  -  sum_k a p
+//     is one MFMA chain over v started from the chain of a against -p (one
+//     chain per row block for symmetric weights, where p is a constant; one
+//     per column block for asymmetric ones).
+//   * Scales in fp32: each group's chain starts fresh and is added to the
+//     accumulator with one FMA by the column's scale (a zero scale adds 0).
 //   * Split-K over workgroups when the output tiles alone cannot fill the
 //     256 CUs: fp32 partial tiles go to a workspace and a second kernel adds
 //     them in a fixed order (deterministic) and rounds to the output type.
@@ -36,19 +36,25 @@ namespace {
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
-template <typename T>
-__device__ __forceinline__ T bitcast_u32(uint32_t v) { return __builtin_bit_cast(T, v); }
-
-// 8 codes -> 8 exact fp16 values q - z (packed layout of lowbit_internal.hpp)
-__device__ __forceinline__ h8 unpack_f16(uint32_t w, uint32_t magic, h2 blo, h2 bhi)
+// 8 codes -> exact fp16 offset values: 1024 + q at K offsets 0, 1, 4, 5 (mask
+// into 1024.0) and 64 + q at 2, 3, 6, 7 (mask into 64.0, where one unit is 1/16)
+__device__ __forceinline__ u4 unpack_f16_split(uint32_t w, uint32_t mlo, uint32_t mhi)
 {
-    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const uint32_t w8 = w >> 8;
-    const h2 p0 = bitcast_u32<h2>((w & 0x000F000Fu) | magic) + blo;
-    const h2 p1 = __builtin_elementwise_fma(bitcast_u32<h2>((w & 0x00F000F0u) | magic), sixteenth, bhi);
-    const h2 p2 = bitcast_u32<h2>((w8 & 0x000F000Fu) | magic) + blo;
-    const h2 p3 = __builtin_elementwise_fma(bitcast_u32<h2>((w8 & 0x00F000F0u) | magic), sixteenth, bhi);
-    return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    return u4{(w & 0x000F000Fu) | mlo, (w & 0x00F000F0u) | mhi, (w8 & 0x000F000Fu) | mlo, (w8 & 0x00F000F0u) | mhi};
+}
+
+// the negated offset operand of zero point z, same slots as the unpack
+__device__ __forceinline__ u4 neg_offset(bool bf16, int z)
+{
+    if (bf16) {
+        const uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)(-128.0f - (float)z));   // exact: |128 + z| < 256
+        const uint32_t d = h | (h << 16);
+        return u4{d, d, d, d};
+    }
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(-1024.0f - (float)z));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(-64.0f - (float)z));
+    return u4{lo | (lo << 16), hi | (hi << 16), lo | (lo << 16), hi | (hi << 16)};
 }
 
 // 8 codes -> 8 exact bf16 values 128 + q (element j = K offset j)
@@ -84,9 +90,6 @@ struct GemmArgs {
 //   scale / zero-point blocks of those tiles.
 // Each wave issues the same fixed set of load instructions per stage, so
 // "stage k has landed" is a vmcnt count; a barrier then publishes it.
-// bf16 activations: the row sums of each quantization group come from one
-// more MFMA per A operand against a B of ones, in the same accumulator layout
-// as the products (no LDS round trip for them).
 constexpr int kV2Waves = 8;
 constexpr int kV2BM = 128, kV2BN = 256;
 constexpr int kV2Stages = 3;
@@ -198,13 +201,12 @@ void gemm_w4_v2_kernel(GemmArgs p)
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-    float unit[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) unit[j] = 1.0f;
 
-    uint32_t magic = A_BF16 ? 0x43004300u : 0x64006400u;   // 128.0 (bf16) / 1024.0 (fp16)
-    asm volatile("" : "+v"(magic));
-    const u4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 x 8
+    uint32_t mlo = A_BF16 ? 0x43004300u : 0x64006400u;   // 128.0 (bf16) / 1024.0 (fp16)
+    uint32_t mhi = 0x54005400u;                          // 64.0 (fp16)
+    asm volatile("" : "+v"(mlo), "+v"(mhi));             // in registers: each mask-or is one operation
+    u4 psym = neg_offset(A_BF16, 8);
+    asm volatile("" : "+v"(psym));
 
     // prologue: stages 0 .. kV2Stages-2
 #pragma unroll
@@ -226,86 +228,62 @@ void gemm_w4_v2_kernel(GemmArgs p)
 
 #pragma unroll
         for (int g = 0; g < GPT; ++g) {
-            float ratio[TN], bz[TN];
-            bool zcol[TN];
-            bool anyzero = false;
+            float sc[TN];
+            u4 pneg[TN];
 #pragma unroll
             for (int nb = 0; nb < TN; ++nb) {
                 const int s = wn * 4 + nb;             // strip in the tile; its loader wave = s / 2
                 const uint8_t *ms = sm + (s >> 1) * 256 + (s & 1) * 32 * GPT;
-                const float sc = (float)*reinterpret_cast<const _Float16 *>(ms + (r16 * GPT + g) * 2);
-                int z = 8;
+                sc[nb] = (float)*reinterpret_cast<const _Float16 *>(ms + (r16 * GPT + g) * 2);
                 if constexpr (ASYM) {
                     const uint8_t *mz = sm + kV2MStage + (s >> 1) * 256 + (s & 1) * 16 * GPT;
-                    z = (int)*reinterpret_cast<const int8_t *>(mz + r16 * GPT + g);
+                    pneg[nb] = neg_offset(A_BF16, (int)*reinterpret_cast<const int8_t *>(mz + r16 * GPT + g));
                 }
-                zcol[nb] = (sc == 0.0f);
-                anyzero |= zcol[nb];
-                ratio[nb] = zcol[nb] ? 1.0f : unit[nb] * __builtin_amdgcn_rcpf(sc);
-                unit[nb] = zcol[nb] ? unit[nb] : sc;
-                bz[nb] = zcol[nb] ? 0.0f : -(128.0f + (float)z);
-                if constexpr (!A_BF16) bz[nb] = (float)z;   // (fp16 path: z goes into the unpack)
             }
-            const bool wave_zero = __builtin_amdgcn_ballot_w64(anyzero) != 0;
+            // the group's B operands in offset form
+            u4 bv[SPG][TN];
 #pragma unroll
-            for (int mb = 0; mb < TM; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < TN; ++nb) acc[mb][nb] = acc[mb][nb] * ratio[nb];
-
-            f4 rs[TM];
-#pragma unroll
-            for (int mb = 0; mb < TM; ++mb) rs[mb] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ss = 0; ss < SPG; ++ss) {
-                const int ks = g * SPG + ss;           // 32-K step inside the tile
-                u4 bops[TN];
+            for (int ss = 0; ss < SPG; ++ss)
 #pragma unroll
                 for (int nb = 0; nb < TN; ++nb) {
-                    const uint32_t w = bq[nb][ks];
-                    if constexpr (A_BF16) {
-                        bops[nb] = unpack_bf16_biased(w, magic);
-                    } else {
-                        const int z = (int)bz[nb];
-                        const _Float16 lo = (_Float16)(-1024.0f - (float)z);
-                        const _Float16 hi = (_Float16)(-64.0f - (float)z);
-                        bops[nb] = __builtin_bit_cast(u4, unpack_f16(w, magic, h2{lo, lo}, h2{hi, hi}));
+                    const uint32_t w = bq[nb][g * SPG + ss];
+                    bv[ss][nb] = A_BF16 ? unpack_bf16_biased(w, mlo) : unpack_f16_split(w, mlo, mhi);
+                }
+            auto mfma = [&](const u4 &a, const u4 &b, const f4 &c) __attribute__((always_inline)) {
+                if constexpr (A_BF16)
+                    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a),
+                                                                   __builtin_bit_cast(bf8v, b), c, 0, 0, 0);
+                else
+                    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
+                                                                  __builtin_bit_cast(h8, b), c, 0, 0, 0);
+            };
+#pragma unroll
+            for (int mb = 0; mb < TM; ++mb) {
+                const int row = wm * 64 + mb * 16 + r16;
+                u4 av[SPG];
+#pragma unroll
+                for (int ss = 0; ss < SPG; ++ss) {
+                    const int chunk = ((g * SPG + ss) * 4 + kq) ^ (row & 15);
+                    av[ss] = *reinterpret_cast<const u4 *>(sa + row * 256 + chunk * 16);
+                }
+                // - sum_k a p over the group: shared by the row block (symmetric)
+                f4 off = f4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (!ASYM) {
+#pragma unroll
+                    for (int ss = 0; ss < SPG; ++ss) off = mfma(av[ss], psym, off);
+                }
+#pragma unroll
+                for (int nb = 0; nb < TN; ++nb) {
+                    f4 c = off;
+                    if constexpr (ASYM) {
+#pragma unroll
+                        for (int ss = 0; ss < SPG; ++ss) c = mfma(av[ss], pneg[nb], ss == 0 ? f4{0.f, 0.f, 0.f, 0.f} : c);
                     }
+#pragma unroll
+                    for (int ss = 0; ss < SPG; ++ss) c = mfma(av[ss], bv[ss][nb], c);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[mb][nb][i] = __builtin_fmaf(sc[nb], c[i], acc[mb][nb][i]);
                 }
-                // a column with a zero scale takes no part in this group (rare:
-                // a wave-uniform branch, kept out of the common path)
-                if (__builtin_expect(wave_zero, 0)) {
-                    asm volatile("" ::: "memory");
-#pragma unroll
-                    for (int nb = 0; nb < TN; ++nb)
-                        if (zcol[nb]) bops[nb] = u4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int mb = 0; mb < TM; ++mb) {
-                    const int row = wm * 64 + mb * 16 + r16;
-                    const int chunk = (ks * 4 + kq) ^ (row & 15);
-                    const u4 av = *reinterpret_cast<const u4 *>(sa + row * 256 + chunk * 16);
-#pragma unroll
-                    for (int nb = 0; nb < TN; ++nb) {
-                        if constexpr (A_BF16)
-                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf8v, av), __builtin_bit_cast(bf8v, bops[nb]), acc[mb][nb], 0, 0, 0);
-                        else
-                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                __builtin_bit_cast(h8, av), __builtin_bit_cast(h8, bops[nb]), acc[mb][nb], 0, 0, 0);
-                    }
-                    if constexpr (A_BF16)
-                        rs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
-                                                                         __builtin_bit_cast(bf8v, ones), rs[mb], 0, 0, 0);
-                }
-            }
-            // bf16: remove the bias (128 + z) of this group, in the group's units
-            if constexpr (A_BF16) {
-#pragma unroll
-                for (int mb = 0; mb < TM; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < TN; ++nb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = __builtin_fmaf(rs[mb][i], bz[nb], acc[mb][nb][i]);
             }
         }
     }
@@ -314,8 +292,8 @@ void gemm_w4_v2_kernel(GemmArgs p)
     // before this workgroup's LDS can be handed to another one
     v2_wait_vm<0>();
 
-    // epilogue: back to real units; C layout of the 16x16 MFMA: lane holds
-    // column (lane % 16) and rows 4*(lane / 16) + i of each block
+    // epilogue; C layout of the 16x16 MFMA: lane holds column (lane % 16) and
+    // rows 4*(lane / 16) + i of each block
 #pragma unroll
     for (int mb = 0; mb < TM; ++mb)
 #pragma unroll
@@ -325,7 +303,7 @@ void gemm_w4_v2_kernel(GemmArgs p)
                 const int m = m0 + wm * 64 + mb * 16 + kq * 4 + i;
                 const int n = n0 + wn * 64 + nb * 16 + r16;
                 if (m < p.M && n < p.N) {
-                    const float v = acc[mb][nb][i] * unit[nb];
+                    const float v = acc[mb][nb][i];
                     const int64_t o = (int64_t)m * p.N + n;
                     if (p.splits > 1)
                         p.part[(int64_t)split * p.M * p.N + o] = v;
