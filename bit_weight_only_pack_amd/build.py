@@ -24,6 +24,8 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INCLUDE, "-I" + CSRC,
+    # kernel arguments of scalar type (up to 16 dwords) arrive preloaded in SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

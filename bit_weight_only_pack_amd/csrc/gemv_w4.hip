@@ -217,63 +217,16 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // waves per SIMD (64 VGPRs), so four 8-wave workgroups share a compute unit;
 // other forms with up to 4 tiles per wave 6; 8 tiles per wave (16-wave
 // workgroups, one per compute unit) 4.
-template <int G, bool ASYM, int MR, int T, int NP>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
-void gemv_w4_v2_kernel(const GemvBatch b)
+// The streaming kernel's work for one strip, once its problem's fields are
+// known (in scalar registers).
+template <int G, bool ASYM, int MR, int T>
+__device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_t *scales, const uint8_t *zeros,
+                                              const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M,
+                                              int W, int strip)
 {
     constexpr int GPT = 128 / G;
     constexpr int NW = T * (ASYM ? 3 : 2);          // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // One round of kernel-argument reads.  NP = 1: the one problem.  NP = 4:
-    // the problems' strips are laid end to end over blockIdx.x and the fields
-    // of all four are read at once, then selected.  NP = 8: blockIdx.y is the
-    // problem and strips past its end exit.  Every field is made live right
-    // away (empty asm), so the scalar loads go out together.
-    if constexpr (NP == 4) {
-        // all four problems' pointers and sizes live before the selection
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const GemvProblem &q = b.p[i];
-            asm volatile("" ::"s"(q.codes), "s"(q.scales), "s"(q.zeros), "s"(q.x), "s"(q.y), "s"(q.N), "s"(q.K),
-                         "s"(q.ktiles), "s"(q.strips), "s"(q.tw));
-        }
-        asm volatile("" ::"s"(b.first[1]), "s"(b.first[2]), "s"(b.first[3]), "s"(b.M), "s"(b.W));
-    }
-    int pi, strip;
-    if constexpr (NP == 1) {
-        pi = 0;
-        strip = (int)blockIdx.x;
-    } else if constexpr (NP == 4) {
-        const int bx = (int)blockIdx.x, f1 = b.first[1], f2 = b.first[2], f3 = b.first[3];
-        pi = (bx >= f1 ? 1 : 0) + (bx >= f2 ? 1 : 0) + (bx >= f3 ? 1 : 0);
-        strip = bx - (pi == 0 ? 0 : pi == 1 ? f1 : pi == 2 ? f2 : f3);
-    } else {
-        pi = (int)blockIdx.y;
-        strip = (int)blockIdx.x;
-    }
-    auto field = [&](auto get) {
-        if constexpr (NP == 4) {
-            const auto v0 = get(b.p[0]), v1 = get(b.p[1]), v2 = get(b.p[2]), v3 = get(b.p[3]);
-            return pi == 0 ? v0 : pi == 1 ? v1 : pi == 2 ? v2 : v3;
-        } else {
-            return get(b.p[pi]);
-        }
-    };
-    const uint8_t *codes = field([](const GemvProblem &q) { return q.codes; });
-    const uint8_t *scales = field([](const GemvProblem &q) { return q.scales; });
-    const uint8_t *zeros = field([](const GemvProblem &q) { return q.zeros; });
-    const _Float16 *xg = field([](const GemvProblem &q) { return q.x; });
-    _Float16 *yp = field([](const GemvProblem &q) { return q.y; });
-    int N = field([](const GemvProblem &q) { return q.N; });
-    int K = field([](const GemvProblem &q) { return q.K; });
-    int kt = field([](const GemvProblem &q) { return q.ktiles; });
-    int nst = field([](const GemvProblem &q) { return q.strips; });
-    int tw = field([](const GemvProblem &q) { return q.tw; });
-    int M = b.M, W = b.W;
-    asm volatile("" : "+s"(codes), "+s"(scales), "+s"(xg), "+s"(yp), "+s"(N), "+s"(K), "+s"(kt), "+s"(nst),
-                 "+s"(tw), "+s"(M), "+s"(W));
-    if constexpr (ASYM) asm volatile("" : "+s"(zeros));
-    if (strip >= nst) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, kq = lane >> 4;
@@ -416,19 +369,96 @@ void gemv_w4_v2_kernel(const GemvBatch b)
 }
 
 template <int G, bool ASYM, int MR, int T, int NP>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
+void gemv_w4_v2_kernel(const GemvBatch b)
+{
+    // One round of kernel-argument reads.  NP = 4:
+    // the problems' strips are laid end to end over blockIdx.x and the fields
+    // of all four are read at once, then selected.  NP = 8: blockIdx.y is the
+    // problem and strips past its end exit.  Every field is made live right
+    // away (empty asm), so the scalar loads go out together.
+    if constexpr (NP == 4) {
+        // all four problems' pointers and sizes live before the selection
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const GemvProblem &q = b.p[i];
+            asm volatile("" ::"s"(q.codes), "s"(q.scales), "s"(q.zeros), "s"(q.x), "s"(q.y), "s"(q.N), "s"(q.K),
+                         "s"(q.ktiles), "s"(q.strips), "s"(q.tw));
+        }
+        asm volatile("" ::"s"(b.first[1]), "s"(b.first[2]), "s"(b.first[3]), "s"(b.M), "s"(b.W));
+    }
+    int pi, strip;
+    if constexpr (NP == 4) {
+        const int bx = (int)blockIdx.x, f1 = b.first[1], f2 = b.first[2], f3 = b.first[3];
+        pi = (bx >= f1 ? 1 : 0) + (bx >= f2 ? 1 : 0) + (bx >= f3 ? 1 : 0);
+        strip = bx - (pi == 0 ? 0 : pi == 1 ? f1 : pi == 2 ? f2 : f3);
+    } else {
+        pi = (int)blockIdx.y;
+        strip = (int)blockIdx.x;
+    }
+    auto field = [&](auto get) {
+        if constexpr (NP == 4) {
+            const auto v0 = get(b.p[0]), v1 = get(b.p[1]), v2 = get(b.p[2]), v3 = get(b.p[3]);
+            return pi == 0 ? v0 : pi == 1 ? v1 : pi == 2 ? v2 : v3;
+        } else {
+            return get(b.p[pi]);
+        }
+    };
+    const uint8_t *codes = field([](const GemvProblem &q) { return q.codes; });
+    const uint8_t *scales = field([](const GemvProblem &q) { return q.scales; });
+    const uint8_t *zeros = field([](const GemvProblem &q) { return q.zeros; });
+    const _Float16 *xg = field([](const GemvProblem &q) { return q.x; });
+    _Float16 *yp = field([](const GemvProblem &q) { return q.y; });
+    int N = field([](const GemvProblem &q) { return q.N; });
+    int K = field([](const GemvProblem &q) { return q.K; });
+    int kt = field([](const GemvProblem &q) { return q.ktiles; });
+    int nst = field([](const GemvProblem &q) { return q.strips; });
+    int tw = field([](const GemvProblem &q) { return q.tw; });
+    int M = b.M, W = b.W;
+    asm volatile("" : "+s"(codes), "+s"(scales), "+s"(xg), "+s"(yp), "+s"(N), "+s"(K), "+s"(kt), "+s"(nst),
+                 "+s"(tw), "+s"(M), "+s"(W));
+    if constexpr (ASYM) asm volatile("" : "+s"(zeros));
+    if (strip >= nst) return;
+    gemv_v2_strip<G, ASYM, MR, T>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, strip);
+}
+
+// One problem: every field is a kernel argument of its own (16 dwords), so
+// the hardware preloads them into scalar registers before the first
+// instruction and the first load needs no kernel-argument read.
+template <int G, bool ASYM, int MR, int T>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
+void gemv_w4_v2_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
+                       int kt, int tw, int M, int W, const uint8_t *zeros)
+{
+    gemv_v2_strip<G, ASYM, MR, T>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
+}
+
+// raises a kernel's dynamic LDS limit when a launch needs more than the default
+// (`raised` belongs to the caller's instantiation, i.e. to one kernel)
+inline hipError_t v2_lds_limit(const void *k, size_t lds, bool &raised)
+{
+    if (lds <= 64 * 1024 || raised) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kV2MaxLds);
+    if (e == hipSuccess) raised = true;
+    return e;
+}
+
+template <int G, bool ASYM, int MR, int T, int NP>
 hipError_t launch_v2_np(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
-    auto k = gemv_w4_v2_kernel<G, ASYM, MR, T, NP>;
-    if (lds > 64 * 1024) {                           // above the default dynamic LDS limit
-        static bool raised = false;
-        if (!raised) {
-            const hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kV2MaxLds);
-            if (e != hipSuccess) return e;
-            raised = true;
-        }
+    static bool raised = false;
+    if constexpr (NP == 1) {
+        auto k = gemv_w4_v2_single<G, ASYM, MR, T>;
+        const hipError_t e = v2_lds_limit((const void *)k, lds, raised);
+        if (e != hipSuccess) return e;
+        const GemvProblem &p = b.p[0];
+        k<<<grid, block, lds, st>>>(p.codes, p.scales, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W, p.zeros);
+    } else {
+        auto k = gemv_w4_v2_kernel<G, ASYM, MR, T, NP>;
+        const hipError_t e = v2_lds_limit((const void *)k, lds, raised);
+        if (e != hipSuccess) return e;
+        k<<<grid, block, lds, st>>>(b);
     }
-    k<<<grid, block, lds, st>>>(b);
     return hipGetLastError();
 }
 
