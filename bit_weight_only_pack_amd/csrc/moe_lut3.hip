@@ -412,25 +412,46 @@ void moe_lut3_gemm_kernel(MoeArgs p)
 // The same product as moe_lut3_gemm_kernel for passes whose activation rows
 // fit in LDS.  One workgroup of 8 waves per (expert, group of column tiles):
 // each pass stages its activation rows and block scales in LDS once, then
-// every wave walks its two strips of each tile of the group along K; the
-// weight stream runs D - 1 K steps ahead of the MFMAs in a ring of register
-// slots that continues from one tile into the next (unrolled so that no slot
-// is copied while its loads are in flight), and it is the only vector-memory
-// traffic of the loop.
-constexpr int kGWaves = 8;                          // waves per workgroup
-constexpr int kGTileStrips = kGWaves * kStripsPerWave;   // 16 strips = 256 columns per tile
+// every wave walks its strip of each tile of the group along K; the weight
+// stream runs D - 1 K steps ahead of the MFMAs in a ring of register slots
+// that continues from one tile into the next (unrolled so that no slot is
+// copied while its loads are in flight), and it is the only vector-memory
+// traffic of the loop: finished tiles go to an LDS output block, which is
+// written out once per pass.  (A store inside the loop would be the last
+// vector-memory operation before the next loads; reusing its registers
+// would make the compiler wait for it, and so for every load in flight.)
+constexpr int kGWaves = 16;                         // waves per workgroup
+constexpr int kGSPW = 1;                            // strips per wave
+constexpr int kGTileStrips = kGWaves * kGSPW;       // 16 strips = 256 columns per tile
 constexpr int kLdsRowPad = 16;                      // bytes added to each staged row (rows fall in different banks)
 
 struct WSlot {
-    uint32_t w[kStripsPerWave][3];
-    u4 cbk[kStripsPerWave];
-    uint32_t bscale[kStripsPerWave];
+    uint32_t w[kGSPW][3];
+    u4 cbk[kGSPW];
+    uint32_t bscale[kGSPW];
 };
 
-__host__ __device__ inline int moe_lds_bytes(int MB, int K)
+// K rounded up to whole 128-K steps: a staged row holds the zero-filled tail
+// of its last step, which the MFMAs of that step read (times zero weights;
+// bytes left unwritten could hold E4M3 NaN patterns)
+__host__ __device__ constexpr int moe_kpad(int K) { return (K + 127) / 128 * 128; }
+
+// LDS of one workgroup: activation rows, their block scales, slot ids, then
+// the bf16 output block of the group's tiles
+struct MoeLds {
+    int s_off, sid_off, out_off, bytes;
+};
+__host__ __device__ inline MoeLds moe_lds_layout(int MB, int K, int tiles)
 {
-    return MB * 16 * (K + kLdsRowPad) + MB * 16 * (K / 32) + MB * 16 * 4;
+    MoeLds l;
+    l.s_off = MB * 16 * (moe_kpad(K) + kLdsRowPad);
+    l.sid_off = l.s_off + MB * 16 * (K / 32);
+    l.out_off = (l.sid_off + MB * 16 * 4 + 15) & ~15;
+    l.bytes = l.out_off + tiles * MB * 16 * kGTileStrips * 16 * 2;
+    return l;
 }
+// the staging part alone (rows, scales, slot ids): what decides the pass size
+__host__ __device__ inline int moe_lds_bytes(int MB, int K) { return moe_lds_layout(MB, K, 0).bytes; }
 
 struct MoeGroupArgs {
     MoeArgs m;
@@ -467,10 +488,13 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
     }
 
     const int K = p.K, ksteps = p.ksteps, k_chunks = K / 32;
-    const int astride = K + kLdsRowPad;
+    const int astride = moe_kpad(K) + kLdsRowPad;
+    const MoeLds lay = moe_lds_layout(MB, K, ga.tiles_per_group);
     uint8_t *a_lds = smem;                                     // [MB*16][astride]
-    uint8_t *s_lds = smem + MB * 16 * astride;                 // [MB*16][k_chunks]
-    int *sid_lds = reinterpret_cast<int *>(s_lds + MB * 16 * k_chunks);   // [MB*16]
+    uint8_t *s_lds = smem + lay.s_off;                         // [MB*16][k_chunks]
+    int *sid_lds = reinterpret_cast<int *>(smem + lay.sid_off);   // [MB*16]
+    uint16_t *o_lds = reinterpret_cast<uint16_t *>(smem + lay.out_off);   // [tile][MB*16][256] bf16
+    constexpr int kTileCols = kGTileStrips * 16;
 
     // weight descriptors over the local expert's units (strips past N read zeros)
     const int64_t eunit0 = (int64_t)local * p.strips * ksteps;
@@ -489,8 +513,8 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
         const int ti = g / ksteps, t = g - ti * ksteps;
         const bool live = g < total;
 #pragma unroll
-        for (int j = 0; j < kStripsPerWave; ++j) {
-            const int s = (tile0 + ti) * kGTileStrips + wave * kStripsPerWave + j;
+        for (int j = 0; j < kGSPW; ++j) {
+            const int s = (tile0 + ti) * kGTileStrips + wave * kGSPW + j;
             const bool ok = live && s < p.strips;
             const uint32_t unit = (uint32_t)(s * ksteps + t);
             const auto iv = __builtin_amdgcn_raw_buffer_load_b96(irs, ok ? unit * 768 + lane * 12 : kBufferOob, 0, 0);
@@ -526,19 +550,23 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
         const int ssid = sid_lds[srow];
         const bool srow_ok = ssid < p.num_valid;
         const uint32_t arow_off = srow_ok ? (uint32_t)(ssid / p.a_row_div) : 0u;
-        const int chunks = K / 16;
+        const int chunks = moe_kpad(K) / 16;                  // 16-byte chunks per staged row
+        const int kchunks = K / 16;                            // of which these hold data
         for (int c0 = 0; c0 < chunks; c0 += kBatch * kTpr) {
             u4 v[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int c = c0 + sl + u * kTpr;
                 v[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    ars, srow_ok && c < chunks ? arow_off * (uint32_t)K + c * 16 : kBufferOob, 0, 0);
+                    ars, srow_ok && c < kchunks ? arow_off * (uint32_t)K + c * 16 : kBufferOob, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int c = c0 + sl + u * kTpr;
-                if (c < chunks) *reinterpret_cast<u4 *>(a_lds + srow * astride + c * 16) = v[u];
+                if (c < chunks)
+                    *reinterpret_cast<u4 *>(a_lds + srow * astride + c * 16) = v[u];
+                else
+                    asm volatile("" ::"v"(v[u]));      // consumed on every path: nothing stays pending
             }
         }
         for (int c0 = 0; c0 < k_chunks; c0 += kBatch * kTpr) {
@@ -552,16 +580,23 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int c = c0 + sl + u * kTpr;
-                if (c < k_chunks) s_lds[srow * k_chunks + c] = (uint8_t)v[u];
+                if (c < k_chunks)
+                    s_lds[srow * k_chunks + c] = (uint8_t)v[u];
+                else
+                    asm volatile("" ::"v"(v[u]));
             }
         }
+        // every staging load has landed (they were issued after the ring's
+        // first loads, so this waits for those too): the streaming loop below
+        // starts with nothing in flight but its own ring
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
         __syncthreads();
 
-        f4 acc[MB][kStripsPerWave];
+        f4 acc[MB][kGSPW];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int j = 0; j < kStripsPerWave; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < kGSPW; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
 
         // 2. stream the weights D - 1 pairs ahead (the first D - 1 are in flight)
         int ti = 0, t = 0;                                     // the pair being computed
@@ -571,7 +606,7 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
                 const int k_lo = t * 128 + 16 * kg;
                 const int kc = t * 4 + kg;                     // this lane supplies block kc's scale
 #pragma unroll
-                for (int j = 0; j < kStripsPerWave; ++j) {
+                for (int j = 0; j < kGSPW; ++j) {
                     const i8v b = lut3_decode(wcur.w[j][0], wcur.w[j][1], wcur.w[j][2], wcur.cbk[j].x,
                                               wcur.cbk[j].y, wcur.cbk[j].z, wcur.cbk[j].w);
                     const int bs = (int)((wcur.bscale[j] >> (8 * exsel)) & 0xffu);
@@ -590,24 +625,23 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
                     }
                 }
                 if (t == ksteps - 1) {
-                    // 3. tile done: lane holds column (lane % 16), rows 4*(lane/16) + i of each block
+                    // 3. tile done: lane holds column (lane % 16), rows 4*(lane/16) + i
+                    //    of each block; rounded to bf16 into the LDS output block
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
                         if (mb >= nmb) continue;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int sid = sid_lds[mb * 16 + kg * 4 + i];
 #pragma unroll
-                            for (int j = 0; j < kStripsPerWave; ++j) {
-                                const int n = ((tile0 + ti) * kGTileStrips + wave * kStripsPerWave + j) * 16 + r16;
-                                if (sid < p.num_valid && n < p.N) {
-                                    const __bf16 v = (__bf16)acc[mb][j][i];
-                                    p.out[(int64_t)sid * p.N + n] = __builtin_bit_cast(uint16_t, v);
-                                }
+                            for (int j = 0; j < kGSPW; ++j) {
+                                const int c = (wave * kGSPW + j) * 16 + r16;
+                                const __bf16 v = (__bf16)acc[mb][j][i];
+                                o_lds[(ti * MB * 16 + mb * 16 + kg * 4 + i) * kTileCols + c] =
+                                    __builtin_bit_cast(uint16_t, v);
                             }
                         }
 #pragma unroll
-                        for (int j = 0; j < kStripsPerWave; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
+                        for (int j = 0; j < kGSPW; ++j) acc[mb][j] = f4{0.f, 0.f, 0.f, 0.f};
                     }
                 }
                 // advance (arithmetic, not a branch: keeps both counters in registers)
@@ -624,6 +658,25 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
         }
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) step(g + d, wsl[d], wsl[(d + D - 1) % D]);
+
+        // 4. the pass's output rows, 16 bytes per thread and step
+        __syncthreads();
+        constexpr int kChunksPerRow = kTileCols / 8;
+        for (int idx = threadIdx.x; idx < ntl * nmb * 16 * kChunksPerRow; idx += kGWaves * 64) {
+            const int cc = idx % kChunksPerRow;
+            const int rr = idx / kChunksPerRow;                // tile * nmb * 16 + row
+            const int tl = rr / (nmb * 16), row = rr - tl * nmb * 16;
+            const int sid = sid_lds[row];
+            const int n = (tile0 + tl) * kTileCols + cc * 8;
+            if (sid >= p.num_valid || n >= p.N) continue;
+            const uint16_t *src = o_lds + (tl * MB * 16 + row) * kTileCols + cc * 8;
+            uint16_t *dst = p.out + (int64_t)sid * p.N + n;
+            if (n + 8 <= p.N && (p.N & 7) == 0) {
+                *reinterpret_cast<u4 *>(dst) = *reinterpret_cast<const u4 *>(src);
+            } else {
+                for (int q = 0; q < 8 && n + q < p.N; ++q) dst[q] = src[q];
+            }
+        }
     }
 }
 
@@ -709,6 +762,7 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
     // Activation rows in LDS when a pass of 32 rows (or 16) fits in 80 KB;
     // otherwise the kernel that reads activations straight from memory.
     constexpr int kMaxLds = 80 * 1024;
+    constexpr int kMaxGroupLds = 150 * 1024;
     const int mb = moe_lds_bytes(2, p.K) <= kMaxLds ? 2 : (moe_lds_bytes(1, p.K) <= kMaxLds ? 1 : 0);
     if (mb > 0) {
         // workgroups of 8 waves over groups of 256-column tiles: about 256
@@ -719,9 +773,12 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
         ga.gtiles = (int)((L.strips + kGTileStrips - 1) / kGTileStrips);
         const int64_t want = (E_global * (int64_t)ga.gtiles + 255) / 256;     // tiles per workgroup for ~256
         ga.tiles_per_group = (int)std::max<int64_t>(1, std::min<int64_t>(want, ga.gtiles));
+        // the group's output block has to fit the LDS as well
+        while (ga.tiles_per_group > 1 && moe_lds_layout(mb, p.K, ga.tiles_per_group).bytes > kMaxGroupLds)
+            --ga.tiles_per_group;
         ga.n_groups = (ga.gtiles + ga.tiles_per_group - 1) / ga.tiles_per_group;
         const unsigned gblocks = (unsigned)((int64_t)E_global * ga.n_groups);
-        const int lds = moe_lds_bytes(mb, p.K);
+        const int lds = moe_lds_layout(mb, p.K, ga.tiles_per_group).bytes;
         auto k = mb == 2 ? moe_lut3_gemm_lds_kernel<2, 5> : moe_lut3_gemm_lds_kernel<1, 5>;
         hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
