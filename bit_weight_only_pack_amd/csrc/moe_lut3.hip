@@ -474,6 +474,11 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
     if (ntl <= 0) return;
     const int row0 = p.expert_offsets[e], row1 = p.expert_offsets[e + 1];
     if (row0 >= row1) return;                                  // no slot routed here
+    // the first pass's slot ids go out together with the local-expert read
+    // (both need only row0), so the weight stream can start one round trip
+    // earlier
+    int sid_first = p.num_valid;
+    if ((int)threadIdx.x < min(MB * 16, row1 - row0)) sid_first = p.sorted_ids[row0 + threadIdx.x];
     const int local = p.block_expert[row0 / p.block_m];
     const int col0 = tile0 * kGTileStrips * 16, col1 = min(p.N, (tile0 + ntl) * kGTileStrips * 16);
 
@@ -536,12 +541,16 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
         //    overlap, and the staging loads go out 8 per thread before any
         //    LDS store
         __syncthreads();                                       // previous pass done with the LDS rows
-        for (int i = threadIdx.x; i < MB * 16; i += kGWaves * 64)
-            sid_lds[i] = i < nmb * 16 ? p.sorted_ids[pass + i] : p.num_valid;
-        __syncthreads();                                       // (waits for every outstanding load)
         WSlot wsl[D];
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) load_w(wsl[d], d);
+        static_assert(MB * 16 <= kGWaves * 64, "one slot id per thread");
+        if ((int)threadIdx.x < MB * 16) {
+            const int i = (int)threadIdx.x;
+            sid_lds[i] = pass == row0 ? (i < nmb * 16 ? sid_first : p.num_valid)
+                                      : (i < nmb * 16 ? p.sorted_ids[pass + i] : p.num_valid);
+        }
+        __syncthreads();
         // thread -> (row, lane in row): every thread stages 16-byte chunks of one row
         constexpr int kRows = MB * 16;
         constexpr int kTpr = kGWaves * 64 / kRows;            // threads per staged row
