@@ -162,3 +162,27 @@ def test_moe_gemm_full_workload_sampled(proj):
     else:
         ref = _ref(d, aq[slots], as_[slots], 1, topk[toks], None)
     assert_close(bf16_bits_to_f64(got[slots]), bf16_bits_to_f64(ref), proj)
+
+
+def test_moe_gemm_k_tail_reads_no_stale_lds():
+    """K not a multiple of 128: the last K step's MFMAs also read the staged
+    activation bytes past K (against zero weights).  Those bytes must be
+    zeros written by the kernel, not whatever an earlier kernel left in LDS:
+    a first launch stages activations that are all 0xFF (an E4M3 NaN) on
+    every compute unit, then the K = 64 and K = 192 cases must still match
+    the oracle and be finite."""
+    T, E, top_k, N, K = 256, 128, 8, 256, 2048
+    d = synth.lut3_weights(E, N, K, workload_id=412)
+    topk = synth.moe_routing(T, E, top_k, workload_id=412)
+    aq = np.full((T, K), 0xFF, np.uint8)
+    as_ = np.full((T, K // 32), 127, np.uint8)
+    run_moe(d, aq, as_, top_k, topk, E)                    # poisons LDS; its output is NaN by design
+    for (T2, E2, k2, N2, K2, gate_up) in [(3, 4, 2, 8, 64, True), (3, 4, 2, 24, 192, False)]:
+        d2 = synth.lut3_weights(E2, N2, K2, workload_id=410, part=N2 + K2)
+        topk2 = synth.moe_routing(T2, E2, k2, workload_id=410, layer=T2)
+        rows = T2 if gate_up else T2 * k2
+        aq2, as2 = synth.mxfp8_activations(rows, K2, workload_id=410, part=K2)
+        div = k2 if gate_up else 1
+        got = run_moe(d2, aq2, as2, div, topk2, E2)
+        ref = _ref(d2, aq2, as2, div, topk2, None)
+        assert_close(bf16_bits_to_f64(got), bf16_bits_to_f64(ref), "after stale LDS, K=%d" % K2)
