@@ -18,8 +18,9 @@
  *            matmul).
  *   [ARM]    "Low Bit ARM kernels" (GPU MODE lecture 38 notes), section on
  *            group-wise quantization (symmetric / asymmetric, fp16 scale plus
- *            int8 zero point per group, group sizes 32/64/128) and the section
- *            on decode = GEMV, prefill = GEMM.
+ *            int8 zero point per group, group sizes 32/64/128), the section
+ *            on decode = GEMV, prefill = GEMM, and the measurements section
+ *            (4-bit weights with dynamic INT8 activations, group 32).
  *   [LUT-B]  "vLLM PR #62759 analysis: decoding LUT-B MoE weights directly in
  *            Rubin tensor cores with MXFP8 activations", sections "Format"
  *            (3-bit index, E4M3 codebook per 8 output channels x 64 K, one
@@ -367,6 +368,76 @@ void orc_moe_gemm(const uint8_t *idx, const uint8_t *cb, const uint8_t *ex,
             if (out_bf16) out_bf16[sid * N + n] = orc_double_to_bf16(acc);
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* W4A8: the same INT4 weights against dynamically quantized INT8            */
+/* activations ([ARM] measurements section: 4-bit weights with dynamic INT8  */
+/* activations, group size 32; the inner loop keeps unpacked weights as int8 */
+/* and feeds int8 matrix-multiply instructions with int32 accumulation).    */
+/* ------------------------------------------------------------------------ */
+
+/* Per-token dynamic INT8 quantization of fp16 activations.
+ * The page names the scheme only.  Readings: one scale per token row,
+ * symmetric, codes in [-127, 127], the row's largest magnitude mapping to
+ * 127.  The decisions that produce integers are taken in binary32, the
+ * precision the GPU takes them in, with every operation correctly rounded:
+ *   amax = max_k |x[m][k]|                 (exact)
+ *   inv  = fl32(127 / amax)
+ *   q    = rint(fl32(x[m][k] * inv))       (ties to even; |q| <= 127 always,
+ *                                           clamped for clarity)
+ *   s    = fl32(amax / 127)                (the dequantization scale)
+ * A row of zeros gets s = 0 and all codes 0.  x must be finite. */
+void orc_quant_act_i8(const uint16_t *x, int64_t M, int64_t K, int8_t *xq, float *sx)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf((float)orc_f16_to_double(x[m * K + k]));
+            if (v > amax) amax = v;
+        }
+        float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+        sx[m] = amax / 127.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = (float)orc_f16_to_double(x[m * K + k]) * inv;
+            float r = rintf(t);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            xq[m * K + k] = (int8_t)r;
+        }
+    }
+}
+
+/* y[m][n] = sum_k (s[m] * xq[m][k]) * w[n][k]:  the INT4 weights of
+ * orc_w4_dequant against the dequantized INT8 activations of
+ * orc_quant_act_i8.  Every term is exact in double (s: 24 significant bits,
+ * xq: 8, w: 19); the sum runs in ascending k in double and is rounded to
+ * nearest even into fp16 (y_out, may be NULL). */
+void orc_w4a8_matmul(const uint16_t *x, int64_t M, int64_t N, int64_t K, int G,
+                     const uint8_t *qweight, const uint16_t *scales, const int8_t *zeros,
+                     double *y64, uint16_t *y_out)
+{
+    int8_t *xq = (int8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
+    float *sx = (float *)malloc((size_t)(M > 0 ? M : 1) * sizeof(float));
+    if (!xq || !sx) { free(xq); free(sx); return; }
+    orc_quant_act_i8(x, M, K, xq, sx);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t byte = qweight[n * (K / 2) + k / 2];
+                int q = (k % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
+                int z = w4_zero(zeros, n, k, K, G);
+                double s = orc_f16_to_double(scales[n * (K / G) + k / G]);
+                double w = (double)(q - z) * s;
+                double a = (double)sx[m] * (double)xq[m * K + k];
+                acc += a * w;
+            }
+            if (y64) y64[m * N + n] = acc;
+            if (y_out) y_out[m * N + n] = orc_double_to_f16(acc);
+        }
+    free(xq);
+    free(sx);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -59,6 +59,8 @@ def _declare(lib):
         "orc_lut3_dequant": [_p, _p, _p, _i64, _i64, _i64, _p],
         "orc_moe_align": [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _i64],
         "orc_moe_gemm": [_p, _p, _p, _i64, _i64, _i64, _p, _p, _i64, _p, _i64, _i64, _p, _p, _p],
+        "orc_quant_act_i8": [_p, _i64, _i64, _p, _p],
+        "orc_w4a8_matmul": [_p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _p],
         "orc_f16_array_to_double": [_p, _i64, _p],
         "orc_bf16_array_to_double": [_p, _i64, _p],
         "orc_double_array_to_f16": [_p, _i64, _p],
@@ -194,6 +196,32 @@ class Oracle:
                                    _ptr(r), r.size, _ptr(y64), _ptr(yb), od)
         return y64, yb
 
+    # ---------------------------------------------------------------- W4A8
+    def quant_act_i8(self, x):
+        """fp16 x [M][K] -> (codes int8 [M][K], scales float32 [M]): per-token
+        symmetric INT8, decisions in binary32."""
+        xb = _f16_bits(x)
+        M, K = xb.shape
+        xq = np.empty((M, K), np.int8)
+        sx = np.empty(M, np.float32)
+        self._lib.orc_quant_act_i8(_ptr(xb), M, K, _ptr(xq), _ptr(sx))
+        return xq, sx
+
+    def w4a8_matmul(self, x, qweight, scales, zeros, group_size):
+        """INT4 weights x dynamically quantized INT8 activations.
+        Returns (y64 float64 [M][N], y_bits uint16 fp16 [M][N])."""
+        xb = _f16_bits(x)
+        M, K = xb.shape
+        q = _c(qweight, np.uint8)
+        N = q.shape[0]
+        assert q.shape == (N, K // 2)
+        s = _f16_bits(scales)
+        z = None if zeros is None else _c(zeros, np.int8)
+        y64 = np.empty((M, N), np.float64)
+        yb = np.empty((M, N), np.uint16)
+        self._lib.orc_w4a8_matmul(_ptr(xb), M, N, K, group_size, _ptr(q), _ptr(s), _ptr(z), _ptr(y64), _ptr(yb))
+        return y64, yb
+
     # ---------------------------------------------------------------- LUT3 MoE
     def lut3_dequant(self, idx, cb, ex):
         """idx u8 [E][N][K] (0..7), cb u8 [E][N/8][K/64][8], ex u8 [E][N/8][K/64] -> float64 [E][N][K]."""
@@ -291,6 +319,14 @@ def w4_matmul_rows(*a, **k):
     return _get().w4_matmul_rows(*a, **k)
 
 
+def quant_act_i8(*a, **k):
+    return _get().quant_act_i8(*a, **k)
+
+
+def w4a8_matmul(*a, **k):
+    return _get().w4a8_matmul(*a, **k)
+
+
 def lut3_dequant(*a, **k):
     return _get().lut3_dequant(*a, **k)
 
@@ -312,4 +348,4 @@ def default():
     return _get()
 
 
-__all__ = ["build", "build_variant", "source_text", "Oracle", "default", "f16_to_double", "bf16_to_double", "double_to_f16", "double_to_bf16", "e4m3_to_double", "ue8m0_to_double", "w4_unpack", "w4_dequant", "w4_matmul", "w4_matmul_rows", "lut3_dequant", "moe_align", "moe_gemm", "version"]
+__all__ = ["build", "build_variant", "source_text", "Oracle", "default", "f16_to_double", "bf16_to_double", "double_to_f16", "double_to_bf16", "e4m3_to_double", "ue8m0_to_double", "w4_unpack", "w4_dequant", "w4_matmul", "w4_matmul_rows", "quant_act_i8", "w4a8_matmul", "lut3_dequant", "moe_align", "moe_gemm", "version"]

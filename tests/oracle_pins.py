@@ -362,6 +362,139 @@ def check_rows_subset(o):
     assert np.array_equal(r64, y64[rows]) and np.array_equal(rb, yb[rows])
 
 
+# ------------------------------------------------------------------ W4A8: dynamic INT8 activations
+def check_quant_closed_forms(o):
+    """A row whose largest magnitude is 127 * 2^e makes 127 / amax = 2^-e and
+    amax / 127 = 2^e exact, so each code is the nearest integer to x / 2^e,
+    ties to even (Python's round), with no rounding anywhere else."""
+    for e in (-4, 0, 3):
+        ints = np.arange(-127, 128)
+        halves = np.arange(-126, 127) + 0.5
+        for vals, expect in ((ints, ints),
+                             (np.append(halves, 127), np.append([round(h) for h in halves], 127))):
+            x = (vals * 2.0 ** e).astype(np.float16)
+            assert np.array_equal(x.astype(np.float64), vals * 2.0 ** e)
+            xq, sx = o.quant_act_i8(x[None, :])
+            assert float(sx[0]) == 2.0 ** e, e
+            assert np.array_equal(xq[0].astype(np.int64), np.asarray(expect, np.int64)), e
+
+
+def check_quant_properties(o):
+    """Invariants of per-token symmetric quantization on rows of very
+    different magnitudes: scale = amax / 127 to one binary32 rounding, the
+    largest magnitude maps to +-127, codes keep the sign and order of x and
+    lie within half a step (plus the binary32 roundings) of x / s; rows are
+    quantized independently; scaling a row by 2^j scales s by 2^j and keeps
+    the codes; a zero row gives s = 0 and zero codes."""
+    r = np.random.default_rng(31)
+    mags = np.array([[0.01], [1.0], [30.0], [1000.0], [1e-3], [3.0]])
+    x = (r.standard_normal((6, 384)) * mags).astype(np.float16)
+    x[5, 17] = -np.float16(40.0)                     # a negative row maximum
+    xq, sx = o.quant_act_i8(x)
+    xd = x.astype(np.float64)
+    for m in range(x.shape[0]):
+        amax = np.max(np.abs(xd[m]))
+        s = float(sx[m])
+        assert abs(s - amax / 127) <= 2.0 ** -23 * amax / 127, m
+        k = int(np.argmax(np.abs(xd[m])))
+        assert int(xq[m, k]) == (127 if xd[m, k] > 0 else -127), m
+        q = xq[m].astype(np.int64)
+        assert np.all(np.abs(q) <= 127)
+        assert np.all(np.sign(q) * np.sign(xd[m]) >= 0), m
+        order = np.argsort(xd[m], kind="stable")
+        assert np.all(np.diff(q[order]) >= 0), m
+        assert np.all(np.abs(xd[m] - s * q) <= s * (0.5 + 3e-5)), m
+    for m in range(x.shape[0]):
+        q1, s1 = o.quant_act_i8(x[m:m + 1])
+        assert np.array_equal(q1[0], xq[m]) and s1[0] == sx[m], m
+    for j in (-2, 3):
+        xs = (xd[1:3] * 2.0 ** j).astype(np.float16)
+        assert np.array_equal(xs.astype(np.float64), xd[1:3] * 2.0 ** j)
+        qj, sj = o.quant_act_i8(xs)
+        assert np.array_equal(qj, xq[1:3]) and np.array_equal(sj.astype(np.float64), sx[1:3].astype(np.float64) * 2.0 ** j)
+    qz, sz = o.quant_act_i8(np.zeros((2, 64), np.float16))
+    assert np.all(qz == 0) and np.all(sz == 0)
+
+
+def _check_w4a8_bruteforce_case(o, M, N, K, G, asym, seed):
+    r = np.random.default_rng(seed)
+    codes = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = r.uniform(0.002, 0.05, size=(N, K // G)).astype(np.float16)
+    z = r.integers(-128, 128, size=(N, K // G)).astype(np.int8) if asym else None
+    x = (r.standard_normal((M, K)) * 2).astype(np.float16)
+    xq, sx = o.quant_act_i8(x)
+    sf = [_frac_f16(row) for row in s.view(np.uint16)]
+    xf = [[F(float(sx[m])) * int(v) for v in xq[m]] for m in range(M)]
+    exact = _exact_matmul(xf, codes, z, sf, G)
+    y64, yb = o.w4a8_matmul(x, _pack_codes(codes), s, z, G)
+    for m in range(M):
+        for n in range(N):
+            e, mag = exact[m][n]
+            assert abs(F(float(y64[m, n])) - e) <= (K + 1) * F(1, 2 ** 53) * mag, ("sum", M, N, K, G, m, n)
+            assert yb[m, n] == _np_f16_bits([float(e)])[0], ("rounding", M, N, K, G, m, n)
+
+
+def check_w4a8_bruteforce(o):
+    """The W4A8 product of the oracle's (separately pinned) INT8 codes and
+    scales against exact rationals."""
+    _check_w4a8_bruteforce_case(o, 1, 5, 64, 32, False, 41)
+    _check_w4a8_bruteforce_case(o, 3, 6, 128, 32, True, 42)
+    _check_w4a8_bruteforce_case(o, 2, 4, 256, 128, True, 43)
+    _check_w4a8_bruteforce_case(o, 4, 3, 192, 64, False, 44)
+
+
+def check_w4a8_numpy(o):
+    """W4A8 product == numpy float64 matmul of the dequantized activations
+    (s * codes) and the (pinned) dequantized weights."""
+    r = np.random.default_rng(45)
+    for (M, N, K, G, asym) in ((1, 64, 512, 32, True), (8, 40, 384, 128, False), (3, 24, 256, 64, True)):
+        codes, q, s, z = _random_w4(r, N, K, G, asym)
+        x = r.standard_normal((M, K)).astype(np.float16)
+        xq, sx = o.quant_act_i8(x)
+        ref = (sx.astype(np.float64)[:, None] * xq.astype(np.float64)) @ o.w4_dequant(q, s, z, G).astype(np.float64).T
+        y64, _ = o.w4a8_matmul(x, q, s, z, G)
+        err = np.max(np.abs(y64 - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-12, ("numpy", M, N, K, G, err)
+
+
+def check_w4a8_on_grid_equals_w4a16(o):
+    """Activations already on their quantization grid (row maximum 127 * 2^e,
+    every value a multiple of 2^e) dequantize to themselves, so the W4A8
+    product equals the W4A16 product bit for bit."""
+    r = np.random.default_rng(46)
+    N, K, G = 24, 256, 32
+    codes, q, s, z = _random_w4(r, N, K, G, True)
+    for e in (-5, -1):
+        j = r.integers(-127, 128, size=(2, K))
+        j[:, 7] = (127, -127)
+        x = (j * 2.0 ** e).astype(np.float16)
+        y8, b8 = o.w4a8_matmul(x, q, s, z, G)
+        y16, b16 = o.w4_matmul(x, "f16", q, s, z, G, "f16")
+        assert np.array_equal(y8, y16) and np.array_equal(b8, b16), e
+
+
+def check_w4a8_special(o):
+    """x = 127 e_k: scale 1, code 127 at k, so y = RNE_fp16(127 w[:, k]);
+    codes at the zero point give 0; a zero activation row gives 0."""
+    r = np.random.default_rng(47)
+    N, K, G = 32, 128, 32
+    codes, q, s, z = _random_w4(r, N, K, G, True)
+    W = o.w4_dequant(q, s, z, G).astype(np.float64)
+    for k in (0, 5, 127):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 127
+        y64, yb = o.w4a8_matmul(x, q, s, z, G)
+        assert np.array_equal(y64[0], 127 * W[:, k]), k
+        assert np.array_equal(yb[0], _np_f16_bits(127 * W[:, k])), k
+    zc = np.repeat(z.astype(np.uint8), G, axis=1)
+    x = r.standard_normal((2, K)).astype(np.float16)
+    y64, _ = o.w4a8_matmul(x, _pack_codes(zc), s, z, G)
+    assert np.all(y64 == 0.0)
+    x[1] = 0
+    y64, yb = o.w4a8_matmul(x, q, s, z, G)
+    assert np.all(y64[1] == 0.0) and np.all(yb[1] == 0)
+
+
 # ------------------------------------------------------------------ LUT3 / MXFP8 / MoE
 def check_lut3_hand(o):
     g = _golden("lut3_hand_example.json")
@@ -495,5 +628,7 @@ ALL_CHECKS = [
     check_hand_bytes, check_sixteen_codes, check_dequant_exact_all_scales, check_fp16_tie, check_gemv_2x4,
     check_bruteforce_tiny, check_bruteforce_tiny_gemv_workload, check_numpy_matmul, check_one_hot,
     check_codes_at_zero_point, check_pow2_scaling, check_k_split, check_rows_subset,
+    check_quant_closed_forms, check_quant_properties, check_w4a8_bruteforce, check_w4a8_numpy,
+    check_w4a8_on_grid_equals_w4a16, check_w4a8_special,
     check_lut3_hand, check_lut3_bruteforce, check_moe_bruteforce, check_moe_numpy, check_moe_align,
 ]

@@ -31,6 +31,18 @@ MUTANTS = [
     ("ties away from zero", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     ("bf16 encode exponent", "((E + 127) << 7)", "((E + 126) << 7)"),
     ("fp16 overflow saturates", "if (isinf(r)) return sign | 0x7c00;", "if (isinf(r)) return sign | 0x7bff;"),
+    ("activation codes scaled to 128", "127.0f / amax", "128.0f / amax"),
+    ("activation ties away from zero", "float r = rintf(t);", "float r = roundf(t);"),
+    ("activation codes truncated", "float r = rintf(t);", "float r = truncf(t);"),
+    ("activation maximum over a column", "fabsf((float)orc_f16_to_double(x[m * K + k]))",
+     "fabsf((float)orc_f16_to_double(x[k * M + m]))"),
+    ("activation maximum without magnitude", "float v = fabsf((float)orc_f16_to_double(x[m * K + k]));",
+     "float v = (float)orc_f16_to_double(x[m * K + k]);"),
+    ("activation scale dropped", "double a = (double)sx[m] * (double)xq[m * K + k];",
+     "double a = (double)xq[m * K + k];"),
+    ("activation scale of row 0", "double a = (double)sx[m] * (double)xq[m * K + k];",
+     "double a = (double)sx[0] * (double)xq[m * K + k];"),
+    ("dequantization scale amax / 128", "sx[m] = amax / 127.0f;", "sx[m] = amax / 128.0f;"),
     ("E4M3 subnormal", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("E4M3 bias", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
     ("E4M3 NaN treated as a number", "if (e == 15 && m == 7)\n        return NAN;", "if (e == 16)\n        return NAN;"),
