@@ -28,6 +28,7 @@ LOWBIT_BF16 = 1
 
 LOWBIT_OP_GEMV = 0
 LOWBIT_OP_GEMM = 1
+LOWBIT_OP_GEMV_W4A8 = 2
 
 _lib = None
 
@@ -61,6 +62,10 @@ SIGNATURES = {
     "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lowbit_gemv_batched": (_i, [_i, _i, _i, _i, _vp, _vp]),
+    "lowbit_quant_act_i8": (_i, [_i, _i, _vp, _vp, _vp, _vp]),
+    "lowbit_gemv_w4a8": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lowbit_gemv_w4a8_batched_workspace_bytes": (_sz, [_i, _i, _i, _i, _vp]),
+    "lowbit_gemv_w4a8_batched": (_i, [_i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "lowbit_gemv_chain_bytes": (_sz, [_i, _i]),
     "lowbit_gemv_chain_init": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, ctypes.c_uint, _vp, _sz, _vp]),
     "lowbit_gemv_chain_run": (_i, [_vp, _vp]),
@@ -190,6 +195,26 @@ def lowbit_gemv_batched(fmt, M, group_size, count, problems, stream=None):
     """problems: a ctypes array from make_gemv_problems (host memory)."""
     return lib().lowbit_gemv_batched(fmt, M, group_size, count, ctypes.cast(problems, ctypes.c_void_p),
                                      _stream(stream))
+
+
+def lowbit_quant_act_i8(M, K, x, xq, x_scale, stream=None):
+    return lib().lowbit_quant_act_i8(M, K, _ptr(x), _ptr(xq), _ptr(x_scale), _stream(stream))
+
+
+def lowbit_gemv_w4a8(fmt, M, N, K, group_size, packed, x, y, workspace=None, ws_bytes=0, stream=None):
+    return lib().lowbit_gemv_w4a8(fmt, M, N, K, group_size, _ptr(packed), _ptr(x), _ptr(y), _ptr(workspace),
+                                  ws_bytes, _stream(stream))
+
+
+def lowbit_gemv_w4a8_batched_workspace_bytes(fmt, M, group_size, count, problems):
+    return lib().lowbit_gemv_w4a8_batched_workspace_bytes(fmt, M, group_size, count,
+                                                          ctypes.cast(problems, ctypes.c_void_p))
+
+
+def lowbit_gemv_w4a8_batched(fmt, M, group_size, count, problems, workspace=None, ws_bytes=0, stream=None):
+    """problems: a ctypes array from make_gemv_problems (host memory)."""
+    return lib().lowbit_gemv_w4a8_batched(fmt, M, group_size, count, ctypes.cast(problems, ctypes.c_void_p),
+                                          _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def lowbit_gemv_chain_bytes(count, stages):

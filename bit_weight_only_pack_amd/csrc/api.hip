@@ -170,6 +170,13 @@ size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_si
     if (!is_w4(fmt) || check_w4_shape(fmt, N, K, group_size) != LOWBIT_OK || M < 0) return 0;
     if (op == LOWBIT_OP_GEMV) return gemv_w4_workspace(M, N, K, group_size);
     if (op == LOWBIT_OP_GEMM) return gemm_w4_workspace(M, N, K, group_size);
+    if (op == LOWBIT_OP_GEMV_W4A8) {
+        if (M == 0 || N == 0) return 0;
+        const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
+        size_t ws = 0;
+        gemv_w4a8_plan(&L, 1, M, &ws);
+        return ws;
+    }
     return 0;
 }
 
@@ -215,6 +222,96 @@ int lowbit_gemv_batched(int fmt, int M, int group_size, int count, const lowbit_
         ++n;
     }
     return hip_status(launch_gemv_w4_batch(L, n, M, packed, x, y, (hipStream_t)stream));
+}
+
+int lowbit_quant_act_i8(int M, int K, const void *x, int8_t *xq, float *x_scale, void *stream)
+{
+    if (M < 0 || K < 0 || K % 8 != 0) return LOWBIT_E_INVALID_ARG;
+    if (M == 0) return LOWBIT_OK;
+    if (x_scale == nullptr || (K > 0 && (x == nullptr || xq == nullptr))) return LOWBIT_E_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(xq) % 8 != 0)
+        return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)M * K >= ((int64_t)1 << 31)) return LOWBIT_E_UNSUPPORTED;
+    return hip_status(launch_quant_act_i8(M, K, static_cast<const _Float16 *>(x), xq, x_scale, (hipStream_t)stream));
+}
+
+namespace {
+
+// Shared by the single and batched W4A8 entry points: validates the
+// problems, keeps the non-empty ones, checks the plan and the workspace.
+int w4a8_prepare(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems, void *workspace,
+                 size_t ws_bytes, W4Layout *L, const uint8_t **packed, const _Float16 **x, _Float16 **y, int *n_out)
+{
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        const lowbit_gemv_problem &p = problems[i];
+        int st = check_w4_shape(fmt, p.N, p.K, group_size);
+        if (st != LOWBIT_OK) return st;
+        if (p.N == 0) continue;
+        if (p.packed == nullptr || p.y == nullptr || (p.K > 0 && p.x == nullptr)) return LOWBIT_E_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(p.x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+        L[n] = w4_layout(p.N, p.K, group_size, fmt == LOWBIT_W4_ASYM);
+        packed[n] = static_cast<const uint8_t *>(p.packed);
+        x[n] = static_cast<const _Float16 *>(p.x);
+        y[n] = static_cast<_Float16 *>(p.y);
+        ++n;
+    }
+    *n_out = n;
+    if (n == 0) return LOWBIT_OK;
+    size_t need = 0;
+    const int mode = gemv_w4a8_plan(L, n, M, &need);
+    if (mode < 0) return LOWBIT_E_UNSUPPORTED;
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LOWBIT_E_WORKSPACE;
+    if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return LOWBIT_E_INVALID_ARG;
+    return LOWBIT_OK;
+}
+
+}  // namespace
+
+int lowbit_gemv_w4a8(int fmt, int M, int N, int K, int group_size, const void *packed, const void *x, void *y,
+                     void *workspace, size_t ws_bytes, void *stream)
+{
+    int st = check_w4_shape(fmt, N, K, group_size);
+    if (st != LOWBIT_OK) return st;
+    if (M < 0) return LOWBIT_E_INVALID_ARG;
+    if (M > 16) return LOWBIT_E_UNSUPPORTED;
+    if (M == 0 || N == 0) return LOWBIT_OK;
+    lowbit_gemv_problem p = {packed, x, y, N, K};
+    return lowbit_gemv_w4a8_batched(fmt, M, group_size, 1, &p, workspace, ws_bytes, stream);
+}
+
+size_t lowbit_gemv_w4a8_batched_workspace_bytes(int fmt, int M, int group_size, int count,
+                                                const lowbit_gemv_problem *problems)
+{
+    if (count <= 0 || count > kMaxGemvBatch || M <= 0 || M > 16 || problems == nullptr) return 0;
+    W4Layout L[kMaxGemvBatch];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        if (check_w4_shape(fmt, problems[i].N, problems[i].K, group_size) != LOWBIT_OK) return 0;
+        if (problems[i].N == 0) continue;
+        L[n++] = w4_layout(problems[i].N, problems[i].K, group_size, fmt == LOWBIT_W4_ASYM);
+    }
+    if (n == 0) return 0;
+    size_t ws = 0;
+    gemv_w4a8_plan(L, n, M, &ws);
+    return ws;
+}
+
+int lowbit_gemv_w4a8_batched(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems,
+                             void *workspace, size_t ws_bytes, void *stream)
+{
+    if (count < 0 || M < 0) return LOWBIT_E_INVALID_ARG;
+    if (count > kMaxGemvBatch || M > 16) return LOWBIT_E_UNSUPPORTED;
+    if (count == 0 || M == 0) return LOWBIT_OK;
+    if (problems == nullptr) return LOWBIT_E_INVALID_ARG;
+    W4Layout L[kMaxGemvBatch];
+    const uint8_t *packed[kMaxGemvBatch];
+    const _Float16 *x[kMaxGemvBatch];
+    _Float16 *y[kMaxGemvBatch];
+    int n = 0;
+    int st = w4a8_prepare(fmt, M, group_size, count, problems, workspace, ws_bytes, L, packed, x, y, &n);
+    if (st != LOWBIT_OK || n == 0) return st;
+    return hip_status(launch_gemv_w4a8_batch(L, n, M, packed, x, y, workspace, (hipStream_t)stream));
 }
 
 size_t lowbit_gemv_chain_bytes(int count, int stages)

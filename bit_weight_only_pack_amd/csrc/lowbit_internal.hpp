@@ -109,6 +109,15 @@ struct GemvBatch {
 hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
                                 const _Float16 *const *x, _Float16 *const *y, hipStream_t s);
 
+// W4A8 GEMV (gemv_w4a8.hip): dynamic per-token INT8 activations.
+// gemv_w4a8_plan: 0 = the launch quantizes activations itself, 1 = needs a
+// workspace of *ws_bytes for the prepared activation blocks, -1 = no kernel
+// for this batch.
+int gemv_w4a8_plan(const W4Layout *L, int count, int M, size_t *ws_bytes);
+hipError_t launch_gemv_w4a8_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
+                                  const _Float16 *const *x, _Float16 *const *y, void *ws, hipStream_t s);
+hipError_t launch_quant_act_i8(int M, int K, const _Float16 *x, int8_t *xq, float *sx, hipStream_t s);
+
 // A chain of dependent GEMV stages run by one persistent launch
 // (gemv_chain.hip).  Device buffer: counters, then the ChainProb table, then
 // the per-stage arrival counts.

@@ -61,8 +61,9 @@ extern "C" {
 #define LOWBIT_BF16  1
 
 /* ---- operations (for lowbit_workspace_bytes) ---------------------------- */
-#define LOWBIT_OP_GEMV  0
-#define LOWBIT_OP_GEMM  1
+#define LOWBIT_OP_GEMV       0
+#define LOWBIT_OP_GEMM       1
+#define LOWBIT_OP_GEMV_W4A8  2
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *lowbit_strerror(int status);
@@ -170,6 +171,57 @@ typedef struct lowbit_gemv_problem {
  */
 int lowbit_gemv_batched(int fmt, int M, int group_size, int count,
                         const lowbit_gemv_problem *problems, void *stream);
+
+/*
+ * Dynamic per-token INT8 quantization of activations ("Low Bit ARM kernels",
+ * measurements section: 4-bit weights run with dynamic INT8 activations; the
+ * page names the scheme, the rounding below is this library's definition).
+ * For each token row m, in binary32 with correctly rounded operations:
+ *   amax = max_k |x[m][k]|,  inv = 127 / amax,  x_scale[m] = amax / 127,
+ *   xq[m][k] = round-to-nearest-even(x[m][k] * inv)   (in [-127, 127])
+ * A row of zeros gives x_scale 0 and codes 0.  x must be finite.
+ *   x       : f16 [M][K], 16-byte aligned; K % 8 == 0
+ *   xq      : i8  [M][K] (output), 8-byte aligned
+ *   x_scale : f32 [M]    (output)
+ * This is the quantization lowbit_gemv_w4a8 applies internally; it is
+ * exported as a building block and test hook.
+ */
+int lowbit_quant_act_i8(int M, int K, const void *x, int8_t *xq, float *x_scale, void *stream);
+
+/*
+ * W4A8 decode GEMV / small-batch product: W4 weights against dynamically
+ * quantized INT8 activations on the int8 matrix cores ("Low Bit ARM kernels":
+ * 4-bit weights with dynamic INT8 activations, group size 32; unpacked weights
+ * kept as int8 and fed to int8 matrix-multiply instructions with int32
+ * accumulation):
+ *   y[m][n] = x_scale[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - z)
+ * with xq, x_scale as lowbit_quant_act_i8 defines them; the inner sums are
+ * exact int32, the scales are applied in fp32, y is rounded to nearest even
+ * into fp16.  Arguments as lowbit_gemv (same packed blob).
+ *   M         : 0..16 rows; K <= 16384 (else LOWBIT_E_UNSUPPORTED)
+ *   workspace : >= lowbit_workspace_bytes(LOWBIT_OP_GEMV_W4A8, ...) bytes,
+ *               256-byte aligned; 0 (no workspace) whenever the launch can
+ *               quantize the activations itself, which holds at M = 1 for
+ *               every K and at M <= 4 for K <= 4096.  Larger activation
+ *               blocks are quantized into the workspace by a first kernel.
+ */
+int lowbit_gemv_w4a8(int fmt, int M, int N, int K, int group_size, const void *packed, const void *x, void *y,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of lowbit_gemv_w4a8_batched for these problems (HOST
+ * array, read during the call); 0 when none is needed or the batch is invalid. */
+size_t lowbit_gemv_w4a8_batched_workspace_bytes(int fmt, int M, int group_size, int count,
+                                                const lowbit_gemv_problem *problems);
+
+/*
+ * Up to 8 independent W4A8 GEMVs in one launch (same fmt, M and group_size),
+ * each with exactly the result of lowbit_gemv_w4a8: the batched form for
+ * projections that share a layer input (q/k/v, gate/up), as
+ * lowbit_gemv_batched.  workspace: >= lowbit_gemv_w4a8_batched_workspace_bytes
+ * (may be NULL when that is 0).
+ */
+int lowbit_gemv_w4a8_batched(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems,
+                             void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * A chain of dependent GEMV stages executed by ONE persistent launch: a whole

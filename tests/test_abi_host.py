@@ -157,3 +157,33 @@ def test_gemv_batched_argument_checks():
     nul = lb.make_gemv_problems([(FAKE, FAKE, None, 64, 256)])
     assert lb.lowbit_gemv_batched(SYM, 1, 32, 1, nul) == E_ARG
     assert lb.lowbit_gemv_batched(SYM, 17, 32, 1, probs) == E_UNS
+
+
+def test_w4a8_argument_checks_and_workspace_plan():
+    """W4A8: shape limits, the workspace rule (none when the launch quantizes
+    the activations itself) and the activation-quantization checks, all
+    decided on the host before anything is enqueued."""
+    OP = lb.LOWBIT_OP_GEMV_W4A8
+    assert lb.lowbit_workspace_bytes(OP, ASYM, 1, 14336, 4096, 32) == 0       # M=1: fused for every K
+    assert lb.lowbit_workspace_bytes(OP, ASYM, 1, 4096, 14336, 32) == 0
+    assert lb.lowbit_workspace_bytes(OP, SYM, 4, 4096, 4096, 128) == 0
+    ws8 = lb.lowbit_workspace_bytes(OP, ASYM, 8, 4096, 14336, 32)
+    # codes (M*K bytes) + code sums (K/G groups x 8 slots x 4 bytes) + scales, whole KiB
+    assert ws8 == -(-(8 * 14336 + (14336 // 32) * 8 * 4 + 64) // 1024) * 1024
+    assert lb.lowbit_gemv_w4a8(ASYM, 8, 4096, 14336, 32, FAKE, FAKE, FAKE, None, 0) == E_WS
+    assert lb.lowbit_gemv_w4a8(ASYM, 8, 4096, 14336, 32, FAKE, FAKE, FAKE, FAKE, ws8 - 1) == E_WS
+    assert lb.lowbit_gemv_w4a8(SYM, 1, 64, 16384 + 128, 128, FAKE, FAKE, FAKE, None, 0) == E_UNS   # K > 16384
+    assert lb.lowbit_gemv_w4a8(SYM, 17, 64, 256, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS
+    assert lb.lowbit_gemv_w4a8(SYM, 1, 64, 250, 32, FAKE, FAKE, FAKE, None, 0) == E_ARG
+    assert lb.lowbit_gemv_w4a8(SYM, 1, 64, 256, 32, FAKE, FAKE + 2, FAKE, None, 0) == E_ARG
+    assert lb.lowbit_gemv_w4a8(SYM, 0, 64, 256, 32, None, None, None, None, 0) == lb.LOWBIT_OK
+    assert lb.lowbit_quant_act_i8(2, 12, FAKE, FAKE, FAKE) == E_ARG          # K % 8
+    assert lb.lowbit_quant_act_i8(2, 16, FAKE + 4, FAKE, FAKE) == E_ARG      # x alignment
+    assert lb.lowbit_quant_act_i8(2, 16, FAKE, FAKE, None) == E_ARG
+    assert lb.lowbit_quant_act_i8(0, 16, None, None, None) == lb.LOWBIT_OK
+    probs = lb.make_gemv_problems([(FAKE, FAKE, FAKE, 4096, 4096)] * 3)
+    assert lb.lowbit_gemv_w4a8_batched_workspace_bytes(SYM, 1, 128, 3, probs) == 0
+    wsb = lb.lowbit_gemv_w4a8_batched_workspace_bytes(SYM, 8, 32, 3, probs)
+    assert wsb == 3 * lb.lowbit_workspace_bytes(OP, SYM, 8, 4096, 4096, 32) > 0
+    assert lb.lowbit_gemv_w4a8_batched(SYM, 8, 32, 3, probs, FAKE, wsb - 1) == E_WS
+    assert lb.lowbit_gemv_w4a8_batched(SYM, 1, 32, 9, probs, None, 0) == E_UNS
