@@ -21,6 +21,8 @@ Other workloads (--workload), one JSON line each:
                 zero points U{0..15}, M in {1, 2, 4, 8}, 1% outlier channels x20
   prefill     : W4 GEMM, M in {512, 2048, 8192}, (K, N) in {(4096, 14336),
                 (14336, 4096)}, bf16 in/out, symmetric G=128
+  decode-w4a8 : the decode-asym step with dynamic per-token INT8 activations
+                (W4A8 on the int8 matrix cores), M in {1, 2, 4, 8}
   moe         : 3-bit LUT-codebook MoE, 128 experts, top-8 over 256 tokens,
                 gate/up K=2048 N=1536 and down K=768 N=2048, MXFP8 activations
 
@@ -159,10 +161,15 @@ def time_graph(torch, graph, stream, steps, warmup):
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
-def time_launches(torch, lb, fmt, M, G, launches, stream, reps):
+def time_launches(torch, lb, fmt, M, G, launches, stream, reps, call=None):
     """Each launch bracketed by its own HIP event pair on the launch stream,
     queued behind a bounded spin kernel so no host gap falls inside a pair.
-    Returns the median duration (us) of every launch over `reps` passes."""
+    Returns the median duration (us) of every launch over `reps` passes.
+    call(L, stream_handle) -> status issues one launch (default: the W4A16
+    batched GEMV)."""
+    if call is None:
+        def call(L, st):
+            return lb.lowbit_gemv_batched(fmt, M, G, L["count"], L["probs"], st)
     per = []
     with torch.cuda.stream(stream):
         for _ in range(reps):
@@ -172,7 +179,7 @@ def time_launches(torch, lb, fmt, M, G, launches, stream, reps):
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                st = lb.lowbit_gemv_batched(fmt, M, G, L["count"], L["probs"], stream.cuda_stream)
+                st = call(L, stream.cuda_stream)
                 b.record(stream)
                 if st != 0:
                     raise lb.LowbitError(st)
@@ -192,8 +199,9 @@ def read_traffic(name):
     return None
 
 
-def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0):
-    """The CPU oracle on the first `layers` layers of the same step (single thread)."""
+def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0, a8=False):
+    """The CPU oracle on the first `layers` layers of the same step (single
+    thread); a8: the W4A8 product (dynamic INT8 activations)."""
     import oracle
     projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
     t_total = 0.0
@@ -208,7 +216,10 @@ def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0
                 w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
                                      layer=layer, part=pid)
                 t0 = time.perf_counter()
-                oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
+                if a8:
+                    oracle.w4a8_matmul(x, w["qweight"], w["scales"], w["zeros"], G)
+                else:
+                    oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
                 t_total += time.perf_counter() - t0
                 nbytes += w4_bytes(K, N, M, G, asym)
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
@@ -308,6 +319,73 @@ def bench_decode_asym(args, torch, lb, synth):
             "dtype": "f16", "data": "synthetic", "vs_baseline": None,
             "config": {"workload": "llama3-8b-w4-asym-g32-decode-step", "M": [1, 2, 4, 8], "group_size": G},
             "per_M": res}
+
+
+def run_step_a8(lb, fmt, M, G, launches, ws, wsb, stream):
+    for L in launches:
+        st = lb.lowbit_gemv_w4a8_batched(fmt, M, G, L["count"], L["probs"], ws, wsb, stream)
+        if st != 0:
+            raise lb.LowbitError(st)
+
+
+def bench_decode_w4a8(args, torch, lb, synth):
+    """The 224-GEMV step with W4A8 (dynamic per-token INT8 activations, the
+    ARM pages' recipe: asymmetric INT4, group size 32) at M = 1, 2, 4, 8; one
+    shared workspace serves every launch of the step (they run in stream
+    order).  The W4A16 step of the same weights and inputs at M = 1 is timed
+    beside it."""
+    G, asym, wid = 32, True, 2
+    res = {}
+    m1 = None
+    for M in (1, 2, 4, 8):
+        fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=True, outlier_frac=0.01)
+        step_bytes = sum(L["bytes"] for L in launches)
+        wsb = max(lb.lowbit_gemv_w4a8_batched_workspace_bytes(fmt, M, G, L["count"], L["probs"]) for L in launches)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.Stream()
+        graph = capture(torch, lambda: run_step_a8(lb, fmt, M, G, launches, ws, wsb, stream.cuda_stream), stream)
+        ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
+
+        def call(L, st):
+            return lb.lowbit_gemv_w4a8_batched(fmt, M, G, L["count"], L["probs"], ws, wsb, st)
+        med = time_launches(torch, lb, fmt, M, G, launches, stream, 2, call)
+        groups = {}
+        for L, t in zip(launches, med):
+            groups.setdefault("+".join(L["names"]), []).append(t)
+        res["M=%d" % M] = dict(ms_per_step=round(ms, 4), GBps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                               tokens_per_s=round(M * 1e3 / ms, 1), bytes_per_step=step_bytes,
+                               workspace_bytes=wsb, kernel_sum_ms=round(float(med.sum()) / 1e3, 4),
+                               per_launch_us={k: round(float(np.mean(v)), 2) for k, v in groups.items()})
+        if M == 1:
+            g16 = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
+            ms16, _ = time_graph(torch, g16, stream, args.steps, args.warmup)
+            res["M=1"]["w4a16_same_step_ms"] = round(ms16, 4)
+            del g16
+            m1 = dict(ms=ms, gpu_ms=gpu_ms, bytes=step_bytes, n=len(launches))
+        del graph, keep, launches, ws
+        torch.cuda.empty_cache()
+    avg_us = m1["gpu_ms"] * 1e3 / m1["n"]
+    bpl = m1["bytes"] / m1["n"]
+    ach = bpl / (avg_us * 1e-6) / 1e9
+    out = {"metric": "W4A8 (dynamic INT8 activations) decode step effective HBM GB/s",
+           "value": res["M=1"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res["M=1"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "i8 x u4 (int32 accumulate), fp32 scales, f16 out",
+           "data": "synthetic (seeded; asymmetric INT4 G=32, zero points U{0..15}, N(0,1) fp16 inputs with 1% "
+                   "outlier channels x20)",
+           "config": {"workload": "llama3-8b-w4a8-asym-g32-decode-step", "M": [1, 2, 4, 8], "group_size": G,
+                      "launches_per_step": m1["n"]},
+           "tokens_per_s": res["M=1"]["tokens_per_s"],
+           "pct_of_hbm_peak": round(100 * res["M=1"]["GBps"] / HBM_PEAK_GBPS, 2),
+           "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "gemv_w4a8 (fused quantization, G=32, asym, M=1)", "bytes_per_launch": round(bpl),
+                        "avg_launch_us": round(avg_us, 3)},
+           "per_M": res}
+    if args.cpu_layers > 0:
+        out["cpu_baseline"] = cpu_baseline_decode(synth, 3 * args.cpu_layers, 1, G, asym, wid, outlier_frac=0.01,
+                                                  a8=True)
+    return out
 
 
 def bench_prefill(args, torch, lb, synth):
@@ -438,7 +516,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "decode-asym", "prefill", "moe"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode-asym", "decode-w4a8", "prefill", "moe"])
     ap.add_argument("--mode", default="batched", choices=["chain", "batched", "unfused"],
                     help="decode: chain = the whole step as one persistent launch with stage dependencies; "
                          "batched = one launch per group of GEMVs sharing an input (4 per layer); "
@@ -465,8 +544,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "prefill": bench_prefill,
-          "moe": bench_moe}[args.workload]
+    fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "decode-w4a8": bench_decode_w4a8,
+          "prefill": bench_prefill, "moe": bench_moe}[args.workload]
     print(json.dumps(fn(args, torch, lb, synth)), flush=True)
 
 

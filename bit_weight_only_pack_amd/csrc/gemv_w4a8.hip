@@ -22,11 +22,11 @@
 //     the 8 codes in the byte order of the unpacked weights (K offsets 0 4 1 5
 //     2 6 3 7), then the code sums per (group, token), then the per-token
 //     scales.  The tile loop reads only this block, from LDS.
-//   * Fused form: each workgroup stages its problem's fp16 x in LDS and
-//     builds the block itself (every workgroup computes the same codes), so
-//     a projection costs one launch.  When the block and the staging do not
-//     fit, quant_act_kernel writes the block to a workspace first and the
-//     GEMV copies it into LDS.
+//   * Fused form (one token): each workgroup stages its problem's fp16 x in
+//     LDS and builds the block itself (every workgroup computes the same
+//     codes), so a projection costs one launch.  From two tokens on,
+//     quant_act_kernel writes the block to a workspace once and the GEMV
+//     copies it into LDS (cheaper than re-quantizing in every workgroup).
 //   * Schedule of the W4A16 streaming GEMV: one workgroup per 16-row strip,
 //     waves split K into runs of at most 8 tiles, every weight load issued up
 //     front with the non-temporal hint, fixed-order cross-wave sum.
@@ -62,22 +62,21 @@ __host__ __device__ inline A8Block a8_block(int M, int kt, int G)
     return b;
 }
 
-// LDS of the GEMV: the block, then (fused) 1 KiB of per-wave maxima, then a
-// region shared by the fp16 staging of x (fused) and the cross-wave sums.
+// LDS of the GEMV: the block, the cross-wave sums, then (fused) 1 KiB of
+// per-wave maxima and the fp16 staging of x.  The sums do not share the
+// staging: a wave that has finished its tiles writes its partial sums while
+// slower waves may still be quantizing from the staging.
 struct A8Lds {
-    int amx, xf, red, total;
+    int red, amx, xf, total;
 };
 __host__ __device__ inline A8Lds a8_lds(int M, int K, int kt, int G, int W, int MR, bool fused)
 {
     const A8Block b = a8_block(M, kt, G);
     A8Lds l;
-    l.amx = b.bytes;
-    const int after = fused ? b.bytes + 1024 : b.bytes;
-    l.xf = after;
-    l.red = after;
-    const int xf = fused ? M * (int)round_up(K, 512) * 2 : 0;
-    const int red = W * MR * 64 * 4;
-    l.total = after + (xf > red ? xf : red);
+    l.red = b.bytes;
+    l.amx = l.red + W * MR * 64 * 4;
+    l.xf = fused ? l.amx + 1024 : l.amx;
+    l.total = l.xf + (fused ? M * (int)round_up(K, 512) * 2 : 0);
     return l;
 }
 
@@ -98,33 +97,82 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // this wave's LDS writes done, then a workgroup barrier (weight loads stay in flight)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// one activation code: round to nearest even of x * inv in binary32
-__device__ __forceinline__ int a8_code(_Float16 x, float inv)
+// Codes of 8 activations, as the low bytes of fl32(fl32(x * inv) + 1.5 * 2^23):
+// the product is rounded to binary32 first (as the definition does), then the
+// add rounds it to an integer, ties to even, in the unit place of [2^23, 2^24);
+// |x * inv| <= 127.00002, so the integer is the code and no clamp is needed
+// (its bits are 0x4B400000 + code, whose low byte is the code's byte).
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+constexpr float kRoundMagic = 12582912.0f;           // 1.5 * 2^23
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+
+__device__ __forceinline__ void a8_codes8(h8 v, float inv, uint32_t *bits)
 {
-    float t = __builtin_rintf(__fmul_rn((float)x, inv));
-    t = __builtin_fminf(__builtin_fmaxf(t, -127.f), 127.f);
-    return (int)t;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float t = __fmul_rn((float)v[i], inv);
+        asm volatile("" : "+v"(t));                   // two roundings: no fused multiply-add
+        bits[i] = __builtin_bit_cast(uint32_t, t + kRoundMagic);
+    }
 }
 
-// 8 codes (K offsets 0..7) -> the two dwords of the block, bytes ordered by
-// K offsets 0 4 1 5 | 2 6 3 7 (the byte order of the unpacked weight dword)
-__device__ __forceinline__ uint2 a8_pack(const int *c)
+// the block's two dwords of 8 codes: bytes ordered by K offsets 0 4 1 5 | 2 6 3 7
+// (the byte order of the unpacked weight dword); v_perm_b32 picks byte 0 of
+// two sources per half-word
+__device__ __forceinline__ uint2 a8_pack(const uint32_t *b)
 {
-    const uint32_t d0 = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[4] & 0xFF) << 8) | ((uint32_t)(c[1] & 0xFF) << 16) |
-                        ((uint32_t)(c[5] & 0xFF) << 24);
-    const uint32_t d1 = (uint32_t)(c[2] & 0xFF) | ((uint32_t)(c[6] & 0xFF) << 8) | ((uint32_t)(c[3] & 0xFF) << 16) |
-                        ((uint32_t)(c[7] & 0xFF) << 24);
-    return make_uint2(d0, d1);
+    // selector bytes: 0 = byte 0 of the second operand, 4 = byte 0 of the first
+    const uint32_t p04 = __builtin_amdgcn_perm(b[4], b[0], 0x0C0C0400u);   // [c0, c4, 0, 0]
+    const uint32_t p15 = __builtin_amdgcn_perm(b[5], b[1], 0x04000C0Cu);   // [0, 0, c1, c5]
+    const uint32_t p26 = __builtin_amdgcn_perm(b[6], b[2], 0x0C0C0400u);
+    const uint32_t p37 = __builtin_amdgcn_perm(b[7], b[3], 0x04000C0Cu);
+    return make_uint2(p04 | p15, p26 | p37);
 }
 
-// Sum of v over aligned groups of `n` lanes (n a power of two <= 16); every
-// lane of a group must be active.
+// largest magnitude of 8 fp16 values as fp16 bits (non-negative fp16 bit
+// patterns order as unsigned integers), folded into m
+__device__ __forceinline__ us2 a8_absmax8(h8 v, us2 m)
+{
+    const u4 w = __builtin_bit_cast(u4, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
+    return m;
+}
+
+// Cross-lane steps on the DPP path (no LDS round trip): swap lanes within
+// pairs and within halves of each quad, mirror each half-row (8 lanes) and
+// each row (16 lanes).
+__device__ __forceinline__ int dpp_pair(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_quad(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_half_mirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false); }
+
+// Sum of v over aligned groups of `n` lanes (n = 4, 8 or 16); every lane of
+// a group must be active.  After each step every lane of the combined span
+// holds the span's sum.
 template <int n>
 __device__ __forceinline__ int seg_sum(int v)
 {
-#pragma unroll
-    for (int o = 1; o < n; o <<= 1) v += __shfl_xor(v, o);
+    static_assert(n == 4 || n == 8 || n == 16, "group of 4, 8 or 16 lanes");
+    v += dpp_pair(v);
+    v += dpp_quad(v);
+    if constexpr (n >= 8) v += dpp_half_mirror(v);
+    if constexpr (n >= 16) v += dpp_mirror(v);
     return v;
+}
+
+// Maximum of a non-negative float over the wave (all lanes active): the bit
+// patterns of non-negative floats order as integers.
+__device__ __forceinline__ float wave_max_nonneg(float a)
+{
+    int v = __builtin_bit_cast(int, a);
+    v = max(v, dpp_pair(v));
+    v = max(v, dpp_quad(v));
+    v = max(v, dpp_half_mirror(v));
+    v = max(v, dpp_mirror(v));
+    const int r = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                      max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+    return __builtin_bit_cast(float, r);
 }
 
 // Quantizes 8-K blocks kb of token m into the activation block `blk`
@@ -133,13 +181,12 @@ __device__ __forceinline__ int seg_sum(int v)
 template <int G>
 __device__ __forceinline__ void a8_put(uint8_t *blk, const A8Block &B, int M, int m, int kb, h8 v, float inv)
 {
-    int c[8];
-    int sum = 0;
+    uint32_t c[8];
+    a8_codes8(v, inv, c);
+    uint32_t usum = 0u - 8u * kRoundMagicBits;       // sum of codes = sum of bits - 8 * magic (mod 2^32)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        c[i] = a8_code(v[i], inv);
-        sum += c[i];
-    }
+    for (int i = 0; i < 8; ++i) usum += c[i];
+    int sum = (int)usum;
     *reinterpret_cast<uint2 *>(blk + B.img + ((int64_t)kb * M + m) * 8) = a8_pack(c);
     sum = seg_sum<G / 8>(sum);
     if ((threadIdx.x & (G / 8 - 1)) == 0)
@@ -163,7 +210,6 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
     const int t0 = wave * tw;
     const A8Block B = a8_block(M, kt, G);
     const A8Lds L = a8_lds(M, K, kt, G, W, MR, FUSED);
-    const int nthr = W * 64;
 
     // 1. activations -> LDS (fused: fp16 x, rows padded to whole KiB; else
     //    the prepared block), by LDS-direct loads issued before the weights
@@ -206,35 +252,35 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
     wg_barrier();
 
     if constexpr (FUSED) {
-        // 4. per-token maximum magnitude: per wave, then across waves
+        // 4. per-token maximum magnitude: each wave over the 8-K blocks of its
+        //    own tiles (zero padding past K included), then across waves
         float *amx = reinterpret_cast<float *>(smem + L.amx);
         const int xrow = (int)round_up(K, 512) * 2;
+        const int kb0 = t0 * 16, kb1 = (t0 + max(min(tw, kt - t0), 0)) * 16;
         for (int m = 0; m < M; ++m) {
-            float a = 0.f;
-            for (int c = threadIdx.x; c < K / 8; c += nthr) {
-                const h8 v = *reinterpret_cast<const h8 *>(smem + L.xf + m * xrow + c * 16);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf((float)v[i]));
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o));
+            us2 mm = {0, 0};
+            for (int kb = kb0 + lane; kb < kb1; kb += 64)
+                mm = a8_absmax8(*reinterpret_cast<const h8 *>(smem + L.xf + m * xrow + kb * 16), mm);
+            const unsigned short mh = mm.x > mm.y ? mm.x : mm.y;
+            float a = (float)__builtin_bit_cast(_Float16, mh);
+            a = wave_max_nonneg(a);
             if (lane == 0) amx[wave * 16 + m] = a;
         }
         lds_barrier();
-        // 5. codes, code sums and scales into the block (zero padding past K
-        //    quantizes to code 0)
-        const int KB = kt * 16;
+        // 5. each wave writes the codes and code sums its own tiles read (its
+        //    LDS writes precede its reads: a wave's LDS instructions execute
+        //    in order), wave 0 the scales it applies at the end
         for (int m = 0; m < M; ++m) {
             float a = amx[m];
             for (int w = 1; w < W; ++w) a = __builtin_fmaxf(a, amx[w * 16 + m]);
             const float inv = a > 0.f ? __fdiv_rn(127.f, a) : 0.f;
-            for (int kb = threadIdx.x; kb < KB; kb += nthr) {
+            for (int kb = kb0 + lane; kb < kb1; kb += 64) {
                 const h8 v = *reinterpret_cast<const h8 *>(smem + L.xf + m * xrow + kb * 16);
                 a8_put<G>(smem, B, M, m, kb, v, inv);
             }
-            if (threadIdx.x == 0) reinterpret_cast<float *>(smem + B.sx)[m] = __fdiv_rn(a, 127.f);
+            if (wave == 0 && lane == 0) reinterpret_cast<float *>(smem + B.sx)[m] = __fdiv_rn(a, 127.f);
         }
-        lds_barrier();
+        __builtin_amdgcn_wave_barrier();
     }
 
     // 6. products, tile by tile in load order
@@ -256,6 +302,22 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
             const uint32_t wd[4] = {qv.x, qv.y, qv.z, qv.w};
+            int xs1[GPT];                            // MR == 1: the tile's GPT code sums, one read
+            if constexpr (MR == 1) {
+                const int *xs = xsum + t * GPT * MS;
+                if constexpr (GPT == 4) {
+                    if (MS == 1) {
+                        const i4v v4 = *reinterpret_cast<const i4v *>(xs);
+                        xs1[0] = v4.x; xs1[1] = v4.y; xs1[2] = v4.z; xs1[3] = v4.w;
+                    } else {
+#pragma unroll
+                        for (int g = 0; g < GPT; ++g) xs1[g] = xs[g * MS];
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < GPT; ++g) xs1[g] = xs[g * MS];
+                }
+            }
             i4v c = zero4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -267,7 +329,9 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
                     const int g = i / MPG;
                     const int *xs = xsum + (t * GPT + g) * MS;
                     int xv[MR];
-                    if constexpr (MR == 4) {
+                    if constexpr (MR == 1) {
+                        xv[0] = xs1[g];
+                    } else if constexpr (MR == 4) {
                         const i4v v4 = *reinterpret_cast<const i4v *>(xs);
                         xv[0] = v4.x; xv[1] = v4.y; xv[2] = v4.z; xv[3] = v4.w;
                     } else {
@@ -334,19 +398,48 @@ void gemv_w4a8_single(const uint8_t *codes, const uint8_t *scales, const void *x
     a8_strip<G, ASYM, MR, T, FUSED>(codes, scales, zeros, xin, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
 }
 
-// Up to 8 problems laid end to end over blockIdx.x (b.first[i] = first
-// workgroup of problem i; unused entries hold INT_MAX).
-template <int G, bool ASYM, int MR, int T, bool FUSED>
+// Problems laid end to end over blockIdx.x (b.first[i] = first workgroup of
+// problem i; unused entries hold INT_MAX).  NP = 4: every field of the four
+// problems is read in one round of scalar loads and selected afterwards (a
+// dependent second round would delay the first HBM load); NP = 8: the
+// problem is found first, then its fields are read.
+template <int G, bool ASYM, int MR, int T, bool FUSED, int NP>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : 6)))
 void gemv_w4a8_batch(const GemvBatch b)
 {
     const int bx = (int)blockIdx.x;
-    int pi = 0;
+    if constexpr (NP == 4) {
 #pragma unroll
-    for (int i = 1; i < kMaxGemvBatch; ++i) pi += bx >= b.first[i] ? 1 : 0;
-    const GemvProblem &p = b.p[pi];
-    a8_strip<G, ASYM, MR, T, FUSED>(p.codes, p.scales, p.zeros, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W,
-                                     bx - b.first[pi]);
+        for (int i = 0; i < 4; ++i) {
+            const GemvProblem &q = b.p[i];
+            asm volatile("" ::"s"(q.codes), "s"(q.scales), "s"(q.zeros), "s"(q.x), "s"(q.y), "s"(q.N), "s"(q.K),
+                         "s"(q.ktiles), "s"(q.tw));
+        }
+        asm volatile("" ::"s"(b.first[1]), "s"(b.first[2]), "s"(b.first[3]), "s"(b.M), "s"(b.W));
+        const int f1 = b.first[1], f2 = b.first[2], f3 = b.first[3];
+        const int pi = (bx >= f1 ? 1 : 0) + (bx >= f2 ? 1 : 0) + (bx >= f3 ? 1 : 0);
+        auto field = [&](auto get) {
+            const auto v0 = get(b.p[0]), v1 = get(b.p[1]), v2 = get(b.p[2]), v3 = get(b.p[3]);
+            return pi == 0 ? v0 : pi == 1 ? v1 : pi == 2 ? v2 : v3;
+        };
+        const int strip = bx - (pi == 0 ? 0 : pi == 1 ? f1 : pi == 2 ? f2 : f3);
+        a8_strip<G, ASYM, MR, T, FUSED>(field([](const GemvProblem &q) { return q.codes; }),
+                                         field([](const GemvProblem &q) { return q.scales; }),
+                                         field([](const GemvProblem &q) { return q.zeros; }),
+                                         field([](const GemvProblem &q) { return (const void *)q.x; }),
+                                         field([](const GemvProblem &q) { return q.y; }),
+                                         field([](const GemvProblem &q) { return q.N; }),
+                                         field([](const GemvProblem &q) { return q.K; }),
+                                         field([](const GemvProblem &q) { return q.ktiles; }),
+                                         field([](const GemvProblem &q) { return q.tw; }), b.M, b.W, strip);
+    } else {
+        int pi = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxGemvBatch; ++i) pi += bx >= b.first[i] ? 1 : 0;
+        const GemvProblem &p = b.p[pi];
+        a8_strip<G, ASYM, MR, T, FUSED>(p.codes, p.scales, p.zeros, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W,
+                                         bx - b.first[pi]);
+    }
 }
 
 // Writes activation blocks (IMAGE) or canonical codes [M][K] + scales [M].
@@ -367,14 +460,10 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
     const int M = qb.M, K = qb.K[pi], kt = qb.kt[pi];
     const _Float16 *xr = qb.x[pi] + (int64_t)m * K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float a = 0.f;
-    for (int c = threadIdx.x; c < K / 8; c += 256) {
-        const h8 v = *reinterpret_cast<const h8 *>(xr + c * 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf((float)v[i]));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o));
+    us2 mm = {0, 0};
+    for (int c = threadIdx.x; c < K / 8; c += 256) mm = a8_absmax8(*reinterpret_cast<const h8 *>(xr + c * 8), mm);
+    float a = (float)__builtin_bit_cast(_Float16, (unsigned short)(mm.x > mm.y ? mm.x : mm.y));
+    a = wave_max_nonneg(a);
     if (lane == 0) wmax[wave] = a;
     __syncthreads();
     a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
@@ -393,10 +482,12 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
         uint8_t *o = qb.out[pi] + (int64_t)m * K;
         for (int c = threadIdx.x; c < K / 8; c += 256) {
             const h8 v = *reinterpret_cast<const h8 *>(xr + c * 8);
-            uint32_t d[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) d[i / 4] |= (uint32_t)(a8_code(v[i], inv) & 0xFF) << (8 * (i % 4));
-            *reinterpret_cast<uint2 *>(o + c * 8) = make_uint2(d[0], d[1]);
+            uint32_t b[8];
+            a8_codes8(v, inv, b);
+            // natural K order: bytes 0..3 and 4..7
+            const uint32_t d0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+            const uint32_t d1 = __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[6], 0x04000C0Cu);
+            *reinterpret_cast<uint2 *>(o + c * 8) = make_uint2(d0, d1);
         }
         if (threadIdx.x == 0) qb.sx[pi][m] = s;
     }
@@ -437,7 +528,10 @@ A8Plan a8_plan(const W4Layout *L, int count, int M)
         p.ws_off[i] = off;
         off += align256(a8_block(M, (int)L[i].ktiles, L[i].G).bytes);
     }
-    if (fused <= kA8FusedMaxLds) {
+    // The fused form pays the quantization once per workgroup (a launch has
+    // hundreds to thousands): worth it at M = 1, where a separate launch costs
+    // more; from M = 2 one quantization kernel plus a block copy is faster.
+    if (M == 1 && fused <= kA8FusedMaxLds) {
         p.mode = 0;
         p.lds = (size_t)fused;
     } else if (split <= kA8MaxLds) {
@@ -468,9 +562,15 @@ hipError_t a8_launch_k(const GemvBatch &b, dim3 grid, dim3 block, size_t lds, hi
         if (e != hipSuccess) return e;
         const GemvProblem &p = b.p[0];
         k<<<grid, block, lds, st>>>(p.codes, p.scales, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W, p.zeros);
+    } else if (b.count <= 4) {
+        static bool raised = false;
+        auto k = gemv_w4a8_batch<G, ASYM, MR, T, FUSED, 4>;
+        const hipError_t e = a8_lds_limit((const void *)k, lds, raised);
+        if (e != hipSuccess) return e;
+        k<<<grid, block, lds, st>>>(b);
     } else {
         static bool raised = false;
-        auto k = gemv_w4a8_batch<G, ASYM, MR, T, FUSED>;
+        auto k = gemv_w4a8_batch<G, ASYM, MR, T, FUSED, 8>;
         const hipError_t e = a8_lds_limit((const void *)k, lds, raised);
         if (e != hipSuccess) return e;
         k<<<grid, block, lds, st>>>(b);

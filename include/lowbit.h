@@ -200,10 +200,10 @@ int lowbit_quant_act_i8(int M, int K, const void *x, int8_t *xq, float *x_scale,
  * into fp16.  Arguments as lowbit_gemv (same packed blob).
  *   M         : 0..16 rows; K <= 16384 (else LOWBIT_E_UNSUPPORTED)
  *   workspace : >= lowbit_workspace_bytes(LOWBIT_OP_GEMV_W4A8, ...) bytes,
- *               256-byte aligned; 0 (no workspace) whenever the launch can
- *               quantize the activations itself, which holds at M = 1 for
- *               every K and at M <= 4 for K <= 4096.  Larger activation
- *               blocks are quantized into the workspace by a first kernel.
+ *               256-byte aligned; 0 (no workspace) at M = 1, where the
+ *               launch quantizes the activations itself.  From M = 2 a first
+ *               kernel quantizes them into the workspace (one pass instead of
+ *               one per workgroup).
  */
 int lowbit_gemv_w4a8(int fmt, int M, int N, int K, int group_size, const void *packed, const void *x, void *y,
                      void *workspace, size_t ws_bytes, void *stream);

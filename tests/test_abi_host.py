@@ -166,7 +166,7 @@ def test_w4a8_argument_checks_and_workspace_plan():
     OP = lb.LOWBIT_OP_GEMV_W4A8
     assert lb.lowbit_workspace_bytes(OP, ASYM, 1, 14336, 4096, 32) == 0       # M=1: fused for every K
     assert lb.lowbit_workspace_bytes(OP, ASYM, 1, 4096, 14336, 32) == 0
-    assert lb.lowbit_workspace_bytes(OP, SYM, 4, 4096, 4096, 128) == 0
+    assert lb.lowbit_workspace_bytes(OP, SYM, 2, 4096, 4096, 128) > 0         # from M = 2: quantized once, into the workspace
     ws8 = lb.lowbit_workspace_bytes(OP, ASYM, 8, 4096, 14336, 32)
     # codes (M*K bytes) + code sums (K/G groups x 8 slots x 4 bytes) + scales, whole KiB
     assert ws8 == -(-(8 * 14336 + (14336 // 32) * 8 * 4 + 64) // 1024) * 1024

@@ -80,8 +80,8 @@ def test_quant_act_ties_and_grid():
     (1, 512, 4096, 128, False),
     (2, 64, 1536, 64, True),
     (3, 200, 2048, 32, True),
-    (4, 96, 4096, 128, True),          # fused, 4 token rows
-    (8, 80, 4096, 32, False),          # activation block through the workspace
+    (4, 96, 4096, 128, True),          # 4 token rows (workspace)
+    (8, 80, 4096, 32, False),
     (2, 48, 14336, 32, True),          # workspace, long K
     (16, 32, 1024, 64, False),
     (1, 16, 16384, 128, True),         # the longest K (8 tiles per wave)
@@ -147,7 +147,7 @@ def test_gemv_w4a8_llama3_8b_shapes_m1(proj):
 @pytest.mark.parametrize("proj", ["q", "gate", "down"])
 @pytest.mark.parametrize("M", [2, 4, 8])
 def test_gemv_w4a8_llama3_8b_shapes_batch(proj, M):
-    """M = 2, 4, 8 at full size (fused or workspace front end); a seeded
+    """M = 2, 4, 8 at full size (workspace front end); a seeded
     sample of 128 weight rows against the oracle."""
     _, K, N = next(p for p in synth.LLAMA3_8B_PROJS if p[0] == proj)
     pid = [p[0] for p in synth.LLAMA3_8B_PROJS].index(proj)
@@ -178,7 +178,7 @@ def test_gemv_w4a8_batched_matches_single_bitexact(M):
     yd = [torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda") for _, N in shapes]
     probs = lb.make_gemv_problems([(packs[i], xd[i], yd[i], shapes[i][1], shapes[i][0]) for i in range(len(shapes))])
     wsb = lb.lowbit_gemv_w4a8_batched_workspace_bytes(lb.LOWBIT_W4_ASYM, M, 32, len(shapes), probs)
-    assert (wsb > 0) == (M == 8)
+    assert (wsb > 0) == (M > 1)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
     lb.check(lb.lowbit_gemv_w4a8_batched(lb.LOWBIT_W4_ASYM, M, 32, len(shapes), probs, ws, wsb))
     torch.cuda.synchronize()
