@@ -441,6 +441,140 @@ void orc_w4a8_matmul(const uint16_t *x, int64_t M, int64_t N, int64_t K, int G,
 }
 
 /* ------------------------------------------------------------------------ */
+/* The MoE layer around the two grouped GEMMs: SiLU(gate) * up, MXFP8       */
+/* re-quantization of the result, router-weighted combine of the experts'   */
+/* outputs.  The page (section "Emulation path") runs the experts on MXFP8  */
+/* activations quantized before each GEMM; it does not spell these steps    */
+/* out, so each reading is stated where it is used.                        */
+/* ------------------------------------------------------------------------ */
+
+/* double -> OCP E4M3 byte (1 sign, 4 exponent bits with bias 7, 3 fraction
+ * bits; largest finite 448), round to nearest even, saturating: magnitudes
+ * that round above 448 give 448 (the MX conversion clamps to the largest
+ * normal; E4M3 has no infinity).  NaN -> 0x7F. */
+uint8_t orc_double_to_e4m3(double v)
+{
+    if (isnan(v)) return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double r = round_to_format(fabs(v), 4, -6, 448.0);
+    if (isinf(r)) r = 448.0;
+    if (r < ldexp(1.0, -6))                          /* subnormal or zero: r / 2^-9 */
+        return sign | (uint8_t)(r / ldexp(1.0, -9));
+    int ex;
+    frexp(r, &ex);
+    int E = ex - 1;                                  /* r in [2^E, 2^(E+1)), -6 <= E <= 8 */
+    int frac = (int)(r / ldexp(1.0, E - 3)) - 8;     /* 0..7 */
+    return sign | (uint8_t)(((E + 7) << 3) | frac);
+}
+
+/* MXFP8 quantization (OCP MX: one shared power-of-two scale per 32
+ * consecutive elements of a row, elements in E4M3).  Reading: the shared
+ * exponent is floor(log2(amax)) - 8, 8 being the exponent of E4M3's largest
+ * value, clamped to the UE8M0 range [-127, 127]; each element becomes the
+ * saturating round-to-nearest-even E4M3 of x / 2^e; an all-zero block gets
+ * exponent 0 (byte 127).  x: bf16 bits [R][K], K % 32 == 0; q: u8 [R][K];
+ * s: u8 [R][K/32] (UE8M0 = e + 127). */
+void orc_mxfp8_quant(const uint16_t *x, int64_t R, int64_t K, uint8_t *q, uint8_t *s)
+{
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t b = 0; b < K / 32; ++b) {
+            double amax = 0.0;
+            for (int64_t k = 32 * b; k < 32 * b + 32; ++k) {
+                double v = fabs(orc_bf16_to_double(x[r * K + k]));
+                if (v > amax) amax = v;
+            }
+            int e = 0;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);                    /* amax = m * 2^ex, m in [0.5, 1) */
+                e = (ex - 1) - 8;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            s[r * (K / 32) + b] = (uint8_t)(e + 127);
+            for (int64_t k = 32 * b; k < 32 * b + 32; ++k)
+                q[r * K + k] = orc_double_to_e4m3(ldexp(orc_bf16_to_double(x[r * K + k]), -e));
+        }
+}
+
+/* 2^t in binary32 by a stated algorithm (the layer's SiLU uses it on both
+ * sides, so the E4M3 codes that follow compare bit for bit): n = rint(t)
+ * (ties to even), f = t - n (exact, |f| <= 1/2), 2^f = e^(f ln 2) by its
+ * Taylor polynomial through degree 7 evaluated in Horner form with
+ * correctly rounded fused multiply-adds, then scaled by 2^n.  t is first
+ * clamped to [-100, 100], so every result is a normal binary32 number.  The
+ * coefficients are (ln 2)^k / k! rounded to binary32. */
+static float exp2_f32(float t)
+{
+    static const double LN2 = 0.693147180559945309417232121458;
+    if (t > 100.0f) t = 100.0f;
+    if (t < -100.0f) t = -100.0f;
+    float n = rintf(t);
+    float f = t - n;
+    float c[8];
+    double term = 1.0;
+    for (int k = 0; k < 8; ++k) {                    /* (ln 2)^k / k! */
+        c[k] = (float)term;
+        term = term * LN2 / (double)(k + 1);
+    }
+    float p = c[7];
+    for (int k = 6; k >= 0; --k) p = fmaf(p, f, c[k]);
+    return ldexpf(p, (int)n);
+}
+
+/* SiLU(g) = g / (1 + e^-g), in binary32: e^-g = 2^(fl32(-g * fl32(log2 e)))
+ * by exp2_f32, then fl32(1 + e), fl32(1 / that), fl32(g * that). */
+float orc_silu_f32(float g)
+{
+    const float LOG2E = 1.44269504088896340736f;
+    float t = -g * LOG2E;
+    float e = exp2_f32(t);
+    float sig = 1.0f / (1.0f + e);
+    return g * sig;
+}
+
+/* act[r][j] = RNE_bf16( fl32( SiLU(gate) * up ) ), gate = gu[r][j],
+ * up = gu[r][I + j] (the gate/up GEMM stacks the two projections along N:
+ * columns 0..I-1 gate, I..2I-1 up).  gu, act: bf16 bits. */
+void orc_silu_mul_bf16(const uint16_t *gu, int64_t R, int64_t I, uint16_t *act)
+{
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t j = 0; j < I; ++j) {
+            float g = (float)orc_bf16_to_double(gu[r * 2 * I + j]);
+            float u = (float)orc_bf16_to_double(gu[r * 2 * I + I + j]);
+            float a = orc_silu_f32(g) * u;
+            act[r * I + j] = orc_double_to_bf16((double)a);
+        }
+}
+
+/* Router-weighted combine of the routed experts' outputs:
+ *   y64[t][h] = sum_{j < top_k} w[t][j] * out[t * top_k + j][h]
+ * in double, ascending j (every product is exact: 24 + 8 significant bits),
+ * y_bf16 = RNE_bf16(y64).  A slot of an expert that is not local has a zero
+ * row in `out` and adds nothing.  out: bf16 bits [T*top_k][H]; w: f32. */
+void orc_moe_combine(const uint16_t *out, const float *w, int64_t T, int64_t top_k, int64_t H,
+                     double *y64, uint16_t *y_bf16)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < top_k; ++j)
+                acc += (double)w[t * top_k + j] * orc_bf16_to_double(out[(t * top_k + j) * H + h]);
+            if (y64) y64[t * H + h] = acc;
+            if (y_bf16) y_bf16[t * H + h] = orc_double_to_bf16(acc);
+        }
+}
+
+void orc_silu_f32_array(const float *g, int64_t n, float *out)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_silu_f32(g[i]); }
+
+void orc_exp2_f32_array(const float *t, int64_t n, float *out)
+{ for (int64_t i = 0; i < n; ++i) out[i] = exp2_f32(t[i]); }
+
+void orc_double_array_to_e4m3(const double *v, int64_t n, uint8_t *out)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_double_to_e4m3(v[i]); }
+
+/* ------------------------------------------------------------------------ */
 /* Array forms of the format conversions (one call per array, for tests).   */
 /* ------------------------------------------------------------------------ */
 

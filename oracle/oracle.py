@@ -61,6 +61,12 @@ def _declare(lib):
         "orc_moe_gemm": [_p, _p, _p, _i64, _i64, _i64, _p, _p, _i64, _p, _i64, _i64, _p, _p, _p],
         "orc_quant_act_i8": [_p, _i64, _i64, _p, _p],
         "orc_w4a8_matmul": [_p, _i64, _i64, _i64, _int, _p, _p, _p, _p, _p],
+        "orc_mxfp8_quant": [_p, _i64, _i64, _p, _p],
+        "orc_silu_mul_bf16": [_p, _i64, _i64, _p],
+        "orc_moe_combine": [_p, _p, _i64, _i64, _i64, _p, _p],
+        "orc_silu_f32_array": [_p, _i64, _p],
+        "orc_exp2_f32_array": [_p, _i64, _p],
+        "orc_double_array_to_e4m3": [_p, _i64, _p],
         "orc_f16_array_to_double": [_p, _i64, _p],
         "orc_bf16_array_to_double": [_p, _i64, _p],
         "orc_double_array_to_f16": [_p, _i64, _p],
@@ -266,6 +272,73 @@ class Oracle:
                              _ptr(t), T, top_k, _ptr(m), _ptr(y64), _ptr(ob))
         return y64, ob
 
+    # ---------------------------------------------------------------- MoE layer
+    def double_to_e4m3(self, v):
+        v = _c(v, np.float64).ravel()
+        out = np.empty(v.size, np.uint8)
+        self._lib.orc_double_array_to_e4m3(_ptr(v), v.size, _ptr(out))
+        return out
+
+    def exp2_f32(self, t):
+        t = _c(t, np.float32).ravel()
+        out = np.empty(t.size, np.float32)
+        self._lib.orc_exp2_f32_array(_ptr(t), t.size, _ptr(out))
+        return out
+
+    def silu_f32(self, g):
+        g = _c(g, np.float32).ravel()
+        out = np.empty(g.size, np.float32)
+        self._lib.orc_silu_f32_array(_ptr(g), g.size, _ptr(out))
+        return out
+
+    def mxfp8_quant(self, x_bf16):
+        """bf16 bits [R][K] -> (E4M3 bytes [R][K], UE8M0 bytes [R][K/32])."""
+        x = _c(x_bf16, np.uint16)
+        R, K = x.shape
+        assert K % 32 == 0
+        q = np.empty((R, K), np.uint8)
+        sc = np.empty((R, K // 32), np.uint8)
+        self._lib.orc_mxfp8_quant(_ptr(x), R, K, _ptr(q), _ptr(sc))
+        return q, sc
+
+    def silu_mul_bf16(self, gu_bf16):
+        """bf16 bits [R][2I] (gate | up) -> bf16 bits [R][I]."""
+        gu = _c(gu_bf16, np.uint16)
+        R, I2 = gu.shape
+        act = np.empty((R, I2 // 2), np.uint16)
+        self._lib.orc_silu_mul_bf16(_ptr(gu), R, I2 // 2, _ptr(act))
+        return act
+
+    def silu_mul_quant(self, gu_bf16):
+        """SiLU(gate) * up, then MXFP8: -> (E4M3 [R][I], UE8M0 [R][I/32])."""
+        return self.mxfp8_quant(self.silu_mul_bf16(gu_bf16))
+
+    def moe_combine(self, out_bf16, w, top_k):
+        """out bf16 bits [T*top_k][H], w f32 [T][top_k] -> (y64 [T][H], y bf16 bits [T][H])."""
+        o = _c(out_bf16, np.uint16)
+        ww = _c(w, np.float32)
+        T = ww.shape[0]
+        H = o.shape[1]
+        assert ww.shape == (T, top_k) and o.shape[0] == T * top_k
+        y64 = np.empty((T, H), np.float64)
+        yb = np.empty((T, H), np.uint16)
+        self._lib.orc_moe_combine(_ptr(o), _ptr(ww), T, top_k, H, _ptr(y64), _ptr(yb))
+        return y64, yb
+
+    def moe_layer(self, w13, w2, x_bf16, topk_ids, topk_w, expert_map=None):
+        """The whole layer, step by step: MXFP8 of the hidden rows, gate/up
+        grouped GEMM (row of slot sid = sid / top_k), SiLU(gate) * up and
+        MXFP8, down grouped GEMM (row = sid), router-weighted combine.
+        w13 / w2: dicts of idx, cb, ex (canonical LUT3 arrays).  Returns a dict
+        of every intermediate and the output (y64, y bf16 bits)."""
+        top_k = topk_ids.shape[1]
+        xq, xs = self.mxfp8_quant(x_bf16)
+        _, gu = self.moe_gemm(w13["idx"], w13["cb"], w13["ex"], xq, xs, top_k, topk_ids, expert_map)
+        aq, as_ = self.silu_mul_quant(gu)
+        _, out = self.moe_gemm(w2["idx"], w2["cb"], w2["ex"], aq, as_, 1, topk_ids, expert_map)
+        y64, yb = self.moe_combine(out, topk_w, top_k)
+        return dict(xq=xq, xs=xs, gate_up=gu, aq=aq, as_=as_, down=out, y64=y64, y=yb)
+
     def version(self):
         return self._lib.orc_version()
 
@@ -339,6 +412,38 @@ def moe_gemm(*a, **k):
     return _get().moe_gemm(*a, **k)
 
 
+def double_to_e4m3(*a, **k):
+    return _get().double_to_e4m3(*a, **k)
+
+
+def exp2_f32(*a, **k):
+    return _get().exp2_f32(*a, **k)
+
+
+def silu_f32(*a, **k):
+    return _get().silu_f32(*a, **k)
+
+
+def mxfp8_quant(*a, **k):
+    return _get().mxfp8_quant(*a, **k)
+
+
+def silu_mul_bf16(*a, **k):
+    return _get().silu_mul_bf16(*a, **k)
+
+
+def silu_mul_quant(*a, **k):
+    return _get().silu_mul_quant(*a, **k)
+
+
+def moe_combine(*a, **k):
+    return _get().moe_combine(*a, **k)
+
+
+def moe_layer(*a, **k):
+    return _get().moe_layer(*a, **k)
+
+
 def version(*a, **k):
     return _get().version(*a, **k)
 
@@ -348,4 +453,4 @@ def default():
     return _get()
 
 
-__all__ = ["build", "build_variant", "source_text", "Oracle", "default", "f16_to_double", "bf16_to_double", "double_to_f16", "double_to_bf16", "e4m3_to_double", "ue8m0_to_double", "w4_unpack", "w4_dequant", "w4_matmul", "w4_matmul_rows", "quant_act_i8", "w4a8_matmul", "lut3_dequant", "moe_align", "moe_gemm", "version"]
+__all__ = ["build", "build_variant", "source_text", "Oracle", "default", "f16_to_double", "bf16_to_double", "double_to_f16", "double_to_bf16", "e4m3_to_double", "ue8m0_to_double", "w4_unpack", "w4_dequant", "w4_matmul", "w4_matmul_rows", "quant_act_i8", "w4a8_matmul", "lut3_dequant", "moe_align", "moe_gemm", "double_to_e4m3", "exp2_f32", "silu_f32", "mxfp8_quant", "silu_mul_bf16", "silu_mul_quant", "moe_combine", "moe_layer", "version"]

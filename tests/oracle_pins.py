@@ -622,6 +622,177 @@ def check_moe_align(o):
         assert pos == P
 
 
+# ------------------------------------------------------------------ MoE layer: SiLU * up, MXFP8, combine
+def _torch_to_e4m3(v):
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def _torch_to_bf16_bits(v):
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def check_e4m3_encode(o):
+    """Every finite E4M3 value encodes to its own byte; values between
+    neighbours round to nearest even as torch's float8_e4m3fn conversion does;
+    magnitudes above 448 saturate to 448 (0x7E); the hand bytes of the page
+    notes (0x38 = 1, 0x40 = 2, 0xC4 = -3, 0x7E = 448, 0x01 = 2^-9)."""
+    b = np.array([i for i in range(256) if (i & 0x7F) != 0x7F], np.uint8)
+    vals = _torch_e4m3_to_f64(b)
+    assert np.array_equal(o.double_to_e4m3(vals), b)
+    r = np.random.default_rng(51)
+    v = np.concatenate([r.uniform(-448, 448, 4000), r.uniform(-0.02, 0.02, 2000),
+                        (vals[:-1] + vals[1:]) / 2])                       # midpoints: ties
+    v = v[np.abs(v) <= 448].astype(np.float32).astype(np.float64)
+    assert np.array_equal(o.double_to_e4m3(v), _torch_to_e4m3(v))
+    assert np.all(o.double_to_e4m3(np.array([448.5, 464.0, 479.9, 480, 1e6])) == 0x7E)
+    assert np.all(o.double_to_e4m3(np.array([-500.0, -1e9])) == 0xFE)
+    assert o.double_to_e4m3(np.array([1.0, 2.0, -3.0, 448.0, 2.0 ** -9])).tolist() == [0x38, 0x40, 0xC4, 0x7E, 0x01]
+
+
+def check_mxfp8_quant(o):
+    """MXFP8 of bf16 rows: a block of E4M3 values times 2^j whose largest
+    magnitude lies in [256, 448] keeps its bytes exactly with exponent byte
+    127 + j; random blocks decode to within half an E4M3 step of x (largest
+    element saturated at 448 * 2^e at most); the largest magnitude lands in
+    [256, 448] after scaling; a zero block gets byte 127 and zero codes;
+    blocks are independent."""
+    r = np.random.default_rng(52)
+    good = np.array([i for i in range(256) if (i & 0x7F) != 0x7F], np.uint8)
+    gv = _torch_e4m3_to_f64(good)
+    for j in (-20, -3, 0, 5):
+        codes = r.choice(good, size=(3, 64))
+        codes[:, 0] = 0x7E                                     # 448 in every block of row 0..2
+        codes[:, 32] = 0xF8                                    # -256 in the second block
+        x = _torch_e4m3_to_f64(codes) * 2.0 ** j
+        xb = _torch_to_bf16_bits(x)
+        assert np.array_equal(o.bf16_to_double(xb).reshape(x.shape), x)   # exact in bf16
+        q, sc = o.mxfp8_quant(xb)
+        assert np.array_equal(sc, np.full((3, 2), 127 + j, np.uint8)), j
+        assert np.array_equal(q, codes), j
+    x = r.standard_normal((5, 128)) * np.array([[1e-3], [1.0], [30.0], [1e4], [1.0]])
+    x[4, 32:64] = 0.0
+    xb = _torch_to_bf16_bits(x)
+    xd = o.bf16_to_double(xb).reshape(x.shape)
+    q, sc = o.mxfp8_quant(xb)
+    assert sc[4, 1] == 127 and np.all(q[4, 32:64] == 0)
+    dec = _torch_e4m3_to_f64(q) * np.ldexp(1.0, sc.astype(np.int64) - 127).repeat(32, axis=1)
+    blocks = np.abs(xd).reshape(5, 4, 32)
+    amax = blocks.max(axis=2)
+    scaled_max = (amax / np.ldexp(1.0, sc.astype(np.int64) - 127))[amax > 0]
+    assert np.all((scaled_max >= 256) & (scaled_max < 512))
+    step = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(xd), 1e-300))).astype(np.int64) - 3)
+    sub = np.ldexp(1.0, sc.astype(np.int64) - 127 - 9).repeat(32, axis=1)           # E4M3 subnormal step
+    cap = 448 * np.ldexp(1.0, sc.astype(np.int64) - 127).repeat(32, axis=1)
+    err = np.abs(dec - np.clip(xd, -cap, cap))
+    assert np.all(err <= np.maximum(step, sub) / 2 * (1 + 1e-12))
+    for rr in range(5):
+        q1, s1 = o.mxfp8_quant(xb[rr:rr + 1])
+        assert np.array_equal(q1[0], q[rr]) and np.array_equal(s1[0], sc[rr])
+
+
+def check_silu(o):
+    """The stated 2^t routine is exact at integers and within 1 ulp of 2^t;
+    SiLU is within (4 + |t| ln2) binary32 ulp of g / (1 + e^-g) (libm,
+    double), t = g log2(e) -- rounding log2(e) and then t to binary32 moves
+    the exponent by up to 2 |t| 2^-24 -- and exactly 0 at 0; SiLU(g) * up rounds to the bf16
+    nearest the double product except where binary32 rounding decides a near
+    tie (at most 1 bf16 ulp away)."""
+    import math
+    k = np.arange(-100, 101).astype(np.float32)
+    assert np.array_equal(o.exp2_f32(k).astype(np.float64), 2.0 ** k.astype(np.float64))
+    t = np.linspace(-99.5, 99.5, 200001).astype(np.float32)
+    ref = np.exp2(t.astype(np.float64))
+    e = o.exp2_f32(t).astype(np.float64)
+    assert np.all(np.abs(e - ref) <= ref * 2.0 ** -23)
+    g = np.concatenate([np.linspace(-60, 60, 100001), [0.0]]).astype(np.float32)
+    gd = g.astype(np.float64)
+    ref = np.array([v / (1.0 + math.exp(-v)) for v in gd])
+    sv = o.silu_f32(g).astype(np.float64)
+    mask = np.abs(ref) > 1e-30
+    ulps = 4 + np.abs(gd) * np.log2(np.e) * np.log(2)
+    assert np.all((np.abs(sv - ref) <= ulps * np.abs(ref) * 2.0 ** -23)[mask])
+    assert sv[-1] == 0.0
+    r = np.random.default_rng(53)
+    gu = _torch_to_bf16_bits(r.standard_normal((64, 256)) * 3)
+    act = o.silu_mul_bf16(gu)
+    gud = o.bf16_to_double(gu).reshape(64, 256)
+    exact = np.array([[gud[i, j] / (1 + math.exp(-gud[i, j])) * gud[i, 128 + j] for j in range(128)] for i in range(64)])
+    ref_bits = o.double_to_bf16(exact.ravel()).reshape(64, 128)
+    same = act == ref_bits
+    assert same.mean() > 0.995
+    ad = o.bf16_to_double(act).reshape(64, 128)
+    rd = o.bf16_to_double(ref_bits).reshape(64, 128)
+    assert np.all(np.abs(ad - rd)[~same] <= np.abs(rd[~same]) * 2.0 ** -7)
+    # gate is the first half: gate = 20 gives SiLU ~ 20, gate = -20 gives ~ 0
+    u = r.standard_normal(128)
+    for gate, factor in ((20.0, 20.0), (-20.0, 0.0)):
+        gu2 = _torch_to_bf16_bits(np.concatenate([np.full(128, gate), u])[None, :])
+        a2 = o.bf16_to_double(o.silu_mul_bf16(gu2)).ravel()
+        ud = o.bf16_to_double(gu2).ravel()[128:]
+        assert np.allclose(a2, factor * ud, rtol=1e-2, atol=1e-6), gate
+
+
+def check_moe_combine(o):
+    """Combine: one-hot router weights return the chosen slot's row exactly;
+    general weights equal a numpy float64 weighted sum; a slot with a zero
+    row adds nothing."""
+    r = np.random.default_rng(54)
+    T, k, H = 7, 4, 96
+    out = _torch_to_bf16_bits(r.standard_normal((T * k, H)))
+    od = o.bf16_to_double(out).reshape(T * k, H)
+    w = np.zeros((T, k), np.float32)
+    pick = r.integers(0, k, T)
+    w[np.arange(T), pick] = 1.0
+    y64, yb = o.moe_combine(out, w, k)
+    assert np.array_equal(yb, out[np.arange(T) * k + pick])
+    w = r.dirichlet(np.ones(k), T).astype(np.float32)
+    y64, yb = o.moe_combine(out, w, k)
+    ref = np.einsum("tj,tjh->th", w.astype(np.float64), od.reshape(T, k, H))
+    assert np.max(np.abs(y64 - ref)) <= 1e-15 * np.max(np.abs(ref))
+    out2 = out.copy()
+    out2[3 * k + 1] = 0
+    y2, _ = o.moe_combine(out2, w, k)
+    ref2 = ref.copy()
+    ref2[3] -= w[3, 1] * od[3 * k + 1]
+    assert np.max(np.abs(y2 - ref2)) <= 1e-15 * np.max(np.abs(ref))
+
+
+def _tiny_moe(seed, T=5, E=4, top_k=2, H=64, I=64):
+    d13 = synth.lut3_weights(E, 2 * I, H, workload_id=90, layer=seed, part=0)
+    d2 = synth.lut3_weights(E, H, I, workload_id=90, layer=seed, part=1)
+    r = np.random.default_rng(seed)
+    x = _torch_to_bf16_bits(r.standard_normal((T, H)))
+    topk = np.stack([r.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = r.dirichlet(np.ones(top_k), T).astype(np.float32)
+    return d13, d2, x, topk, w
+
+
+def check_moe_layer_wiring(o):
+    """The layer's composition: every expert non-local gives y = 0; one-hot
+    router weights give the chosen slot's down row; permuting tokens permutes
+    the output rows bit for bit; a token routed twice to one expert gets
+    (w1 + w2) times that expert's row."""
+    d13, d2, x, topk, w = _tiny_moe(55)
+    T, top_k = topk.shape
+    res = o.moe_layer(d13, d2, x, topk, w, expert_map=np.full(4, -1, np.int32))
+    assert np.all(res["y64"] == 0)
+    w1 = np.zeros_like(w)
+    w1[:, 1] = 1.0
+    res = o.moe_layer(d13, d2, x, topk, w1)
+    assert np.array_equal(res["y"], res["down"][np.arange(T) * top_k + 1])
+    perm = np.array([3, 0, 4, 2, 1])
+    a = o.moe_layer(d13, d2, x, topk, w)
+    b = o.moe_layer(d13, d2, x[perm], topk[perm], w[perm])
+    assert np.array_equal(b["y64"], a["y64"][perm]) and np.array_equal(b["y"], a["y"][perm])
+    t2 = topk.copy()
+    t2[:, 1] = t2[:, 0]
+    c = o.moe_layer(d13, d2, x, t2, w)
+    row = o.bf16_to_double(c["down"]).reshape(T * top_k, -1)[np.arange(T) * top_k]
+    assert np.array_equal(c["y64"], (w[:, 0].astype(np.float64) + w[:, 1])[:, None] * row)
+
+
 ALL_CHECKS = [
     check_f16_decode, check_f16_encode, check_bf16_decode, check_bf16_encode,
     check_e4m3_decode, check_ue8m0_decode,
@@ -631,4 +802,5 @@ ALL_CHECKS = [
     check_quant_closed_forms, check_quant_properties, check_w4a8_bruteforce, check_w4a8_numpy,
     check_w4a8_on_grid_equals_w4a16, check_w4a8_special,
     check_lut3_hand, check_lut3_bruteforce, check_moe_bruteforce, check_moe_numpy, check_moe_align,
+    check_e4m3_encode, check_mxfp8_quant, check_silu, check_moe_combine, check_moe_layer_wiring,
 ]

@@ -43,6 +43,16 @@ MUTANTS = [
     ("activation scale of row 0", "double a = (double)sx[m] * (double)xq[m * K + k];",
      "double a = (double)sx[0] * (double)xq[m * K + k];"),
     ("dequantization scale amax / 128", "sx[m] = amax / 127.0f;", "sx[m] = amax / 128.0f;"),
+    ("SiLU of -g", "float t = -g * LOG2E;", "float t = g * LOG2E;"),
+    ("exp polynomial one degree short", "for (int k = 6; k >= 0; --k) p = fmaf(p, f, c[k]);",
+     "for (int k = 5; k >= 0; --k) p = fmaf(p, f, c[k]);"),
+    ("gate and up swapped", "float g = (float)orc_bf16_to_double(gu[r * 2 * I + j]);",
+     "float g = (float)orc_bf16_to_double(gu[r * 2 * I + I + j]);"),
+    ("MXFP8 exponent offset 7", "e = (ex - 1) - 8;", "e = (ex - 1) - 7;"),
+    ("E4M3 encode saturates to NaN", "if (isinf(r)) r = 448.0;", "if (isinf(r)) r = 480.0;"),
+    ("zero block exponent", "            int e = 0;\n            if (amax > 0.0) {", "            int e = -127;\n            if (amax > 0.0) {"),
+    ("combine weight of slot 0", "acc += (double)w[t * top_k + j] *", "acc += (double)w[t * top_k] *"),
+    ("combine row order", "orc_bf16_to_double(out[(t * top_k + j) * H + h])", "orc_bf16_to_double(out[(j * T + t) * H + h])"),
     ("E4M3 subnormal", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("E4M3 bias", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
     ("E4M3 NaN treated as a number", "if (e == 15 && m == 7)\n        return NAN;", "if (e == 16)\n        return NAN;"),
