@@ -23,8 +23,10 @@ Other workloads (--workload), one JSON line each:
                 (14336, 4096)}, bf16 in/out, symmetric G=128
   decode-w4a8 : the decode-asym step with dynamic per-token INT8 activations
                 (W4A8 on the int8 matrix cores), M in {1, 2, 4, 8}
-  moe         : 3-bit LUT-codebook MoE, 128 experts, top-8 over 256 tokens,
-                gate/up K=2048 N=1536 and down K=768 N=2048, MXFP8 activations
+  moe         : a whole 3-bit LUT-codebook MoE layer, 128 experts, top-8 over
+                256 tokens, hidden 2048, intermediate 768: MXFP8 of the hidden
+                rows, alignment, gate/up GEMM, SiLU*up -> MXFP8, down GEMM,
+                router-weighted combine
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -429,86 +431,112 @@ def bench_prefill(args, torch, lb, synth):
 
 
 def bench_moe(args, torch, lb, synth):
-    """One MoE layer's grouped GEMMs: routing alignment (once, shared by both
-    GEMMs), then the gate/up and the down GEMM, captured as one graph.  The
-    down GEMM reads its own synthetic MXFP8 activations (the SiLU and
-    re-quantisation between the two are not part of this path)."""
-    T, E, top_k, bm = 256, 128, 8, 16
+    """One whole MoE layer, step by step through the C ABI and captured as one
+    graph: MXFP8 of the hidden rows, routing alignment, gate/up grouped GEMM,
+    SiLU(gate) * up re-quantized to MXFP8, down grouped GEMM, router-weighted
+    combine (the same kernels lowbit_moe_layer enqueues).  The dominant
+    kernel's roofline entry is the gate/up GEMM's."""
+    T, E, top_k, bm, H, I = 256, 128, 8, 16, 2048, 768
     L3 = lb.LOWBIT_LUT3_E4M3
-    topk = torch.from_numpy(synth.moe_routing(T, E, top_k, workload_id=4)).cuda()
-    cap = T * top_k + E * (bm - 1)
+    S = T * top_k
+    topk_np = synth.moe_routing(T, E, top_k, workload_id=4)
+    w_np = synth.moe_topk_weights(T, E, top_k, workload_id=4)
+    x_np = synth.activations_bf16(T, H, workload_id=4, part=2)
+    topk = torch.from_numpy(topk_np).cuda()
+    wts = torch.from_numpy(w_np).cuda()
+    x = torch.from_numpy(x_np.view(np.int16)).cuda()
+    cap = S + E * (bm - 1)
     ids = torch.empty(cap, dtype=torch.int32, device="cuda")
     offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     blk = torch.empty(cap // bm, dtype=torch.int32, device="cuda")
     npp = torch.empty(1, dtype=torch.int32, device="cuda")
+    xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
+    gu = torch.empty((S, 2 * I), dtype=torch.int16, device="cuda")
+    aq = torch.empty((S, I), dtype=torch.uint8, device="cuda")
+    as_ = torch.empty((S, I // 32), dtype=torch.uint8, device="cuda")
+    down = torch.empty((S, H), dtype=torch.int16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     stream = torch.cuda.Stream()
-    projs = {}
-    for proj, (K, N, div, part) in (("gate_up", (2048, 1536, top_k, 0)), ("down", (768, 2048, 1, 1))):
+    packs = {}
+    weights = {}
+    for name, (N, K, part) in (("w13", (2 * I, H, 0)), ("w2", (H, I, 1))):
         d = synth.lut3_weights(E, N, K, workload_id=4, part=part)
         nb = lb.lowbit_packed_bytes(L3, E, N, K, 0)
         packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
         lb.check(lb.lowbit_pack_weights(L3, E, N, K, 0, torch.from_numpy(d["idx"]).cuda(),
                                         torch.from_numpy(d["cb"]).cuda(), torch.from_numpy(d["ex"]).cuda(), packed,
                                         nb))
-        del d
-        rows = T if div == top_k else T * top_k
-        aq, as_ = synth.mxfp8_activations(rows, K, workload_id=4, part=part)
-        aq, as_ = torch.from_numpy(aq).cuda(), torch.from_numpy(as_).cuda()
-        out = torch.empty((T * top_k, N), dtype=torch.int16, device="cuda")
-        projs[proj] = dict(K=K, N=N, div=div, rows=rows, packed=packed, nb=nb, aq=aq, as_=as_, out=out,
-                           bytes=nb + aq.numel() + as_.numel() + out.numel() * 2)
-
-    def align():
-        lb.check(lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, stream.cuda_stream))
-
-    def gemm(q):
-        lb.check(lb.lowbit_moe_gemm(L3, E, q["N"], q["K"], q["packed"], E, q["aq"], q["as_"], q["rows"], q["div"],
-                                    ids, offs, blk, T * top_k, bm, q["out"], stream.cuda_stream))
+        packs[name] = (packed, nb)
+        weights[name] = d
+    st = stream.cuda_stream
+    steps = [
+        ("quant_x", lambda: lb.lowbit_mxfp8_quant(x, T, H, xq, xs, st), T * H * 2 + T * H + T * H // 32),
+        ("align", lambda: lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, st), S * 4),
+        ("gate_up", lambda: lb.lowbit_moe_gemm(L3, E, 2 * I, H, packs["w13"][0], E, xq, xs, T, top_k, ids, offs, blk,
+                                               S, bm, gu, st),
+         packs["w13"][1] + T * H + T * H // 32 + S * 2 * I * 2),
+        ("silu_mul_quant", lambda: lb.lowbit_moe_silu_mul_quant(gu, S, I, aq, as_, st), S * 2 * I * 2 + S * I + S * I // 32),
+        ("down", lambda: lb.lowbit_moe_gemm(L3, E, H, I, packs["w2"][0], E, aq, as_, S, 1, ids, offs, blk, S, bm, down,
+                                            st),
+         packs["w2"][1] + S * I + S * I // 32 + S * H * 2),
+        ("combine", lambda: lb.lowbit_moe_combine(down, wts, T, top_k, H, y, st), S * H * 2 + S * 4 + T * H * 2),
+    ]
 
     def layer():
-        align()
-        gemm(projs["gate_up"])
-        gemm(projs["down"])
+        for _, fn, _ in steps:
+            lb.check(fn())
     graph = capture(torch, layer, stream)
     ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
-    # per-kernel durations: each launch between its own event pair, queued behind a bounded spin
-    per = {"align": [], "gate_up": [], "down": []}
+    per = {name: [] for name, _, _ in steps}
     with torch.cuda.stream(stream):
         for _ in range(5):
             evs = []
             torch.cuda._sleep(20_000_000)
-            for name, fn in (("align", align), ("gate_up", lambda: gemm(projs["gate_up"])),
-                             ("down", lambda: gemm(projs["down"]))):
+            for name, fn, _ in steps:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                fn()
+                lb.check(fn())
                 b.record(stream)
                 evs.append((name, a, b))
             torch.cuda.synchronize()
             for name, a, b in evs:
                 per[name].append(a.elapsed_time(b) * 1e3)
     us = {k: float(np.median(v)) for k, v in per.items()}
-    layer_bytes = projs["gate_up"]["bytes"] + projs["down"]["bytes"]
+    nbytes = {name: b for name, _, b in steps}
+    layer_bytes = sum(nbytes.values())
     gbps = layer_bytes / (ms * 1e-3) / 1e9
-    gu = projs["gate_up"]
-    gu_gbps = gu["bytes"] / (us["gate_up"] * 1e-6) / 1e9
-    return {"metric": "3-bit LUT MoE layer grouped GEMMs (align + gate/up + down) effective HBM GB/s",
-            "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "fp8 (MXFP8 x LUT3 E4M3)", "data": "synthetic",
-            "config": {"workload": "lut3-moe-layer-256tok-128e-top8", "tokens": T, "experts": E, "top_k": top_k,
-                       "block_m": bm, "gate_up_KxN": [2048, 1536], "down_KxN": [768, 2048],
-                       "bytes_per_layer": layer_bytes},
-            "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-            "gpu_ms_per_step": round(gpu_ms, 4),
-            "roofline": {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "kernel": "moe_lut3_gemm_lds_kernel (gate/up)", "bytes_per_launch": gu["bytes"],
-                         "avg_launch_us": round(us["gate_up"], 3)},
-            "per_kernel_us": {k: round(v, 2) for k, v in us.items()},
-            "per_kernel_GBps": {"gate_up": round(gu_gbps, 1),
-                                "down": round(projs["down"]["bytes"] / (us["down"] * 1e-6) / 1e9, 1)}}
+    gu_gbps = nbytes["gate_up"] / (us["gate_up"] * 1e-6) / 1e9
+    out = {"metric": "3-bit LUT MoE layer (MXFP8 in, align, gate/up, SiLU*up MXFP8, down, combine) effective HBM GB/s",
+           "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8 (MXFP8 x LUT3 E4M3), fp32 accumulate, bf16 in/out",
+           "data": "synthetic (seeded; N(0,1) router logits -> softmax top-8, N(0,1) bf16 hidden rows)",
+           "config": {"workload": "lut3-moe-layer-256tok-128e-top8", "tokens": T, "experts": E, "top_k": top_k,
+                      "block_m": bm, "hidden": H, "intermediate": I, "bytes_per_layer": layer_bytes},
+           "tokens_per_s": round(T * 1e3 / ms, 1),
+           "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+           "gpu_ms_per_step": round(gpu_ms, 4),
+           "roofline": {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "moe_lut3_gemm_lds_kernel (gate/up)", "bytes_per_launch": nbytes["gate_up"],
+                        "avg_launch_us": round(us["gate_up"], 3)},
+           "per_kernel_us": {k: round(v, 2) for k, v in us.items()},
+           "per_kernel_GBps": {k: round(nbytes[k] / (us[k] * 1e-6) / 1e9, 1) for k in us if k != "align"}}
+    if args.cpu_layers > 0:
+        import oracle
+        tok = np.arange(0, T, T // 16)
+        t0 = time.perf_counter()
+        oracle.moe_layer(weights["w13"], weights["w2"], x_np[tok], topk_np[tok], w_np[tok])
+        dt = time.perf_counter() - t0
+        full = dt * T / len(tok)
+        out["cpu_baseline"] = {"value": round(layer_bytes / full / 1e9, 5), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "%d of %d tokens (the whole layer on them), one thread, %.1f s; layer time "
+                                         "extrapolated by token count" % (len(tok), T, dt),
+                               "tokens_per_s": round(len(tok) / dt, 3)}
+    return out
 
 
 def main():

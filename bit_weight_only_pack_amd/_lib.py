@@ -73,6 +73,11 @@ SIGNATURES = {
     "lowbit_gemm": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "lowbit_moe_align": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lowbit_moe_gemm": (_i, [_i, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
+    "lowbit_mxfp8_quant": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "lowbit_moe_silu_mul_quant": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "lowbit_moe_combine": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+    "lowbit_moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "lowbit_moe_layer": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -181,6 +186,29 @@ def lowbit_moe_gemm(fmt, E_local, N, K, packed, E, a_e4m3, a_ue8m0, a_rows, a_ro
     return lib().lowbit_moe_gemm(fmt, E_local, N, K, _ptr(packed), E, _ptr(a_e4m3), _ptr(a_ue8m0), a_rows,
                                  a_row_div, _ptr(sorted_ids), _ptr(expert_offsets), _ptr(block_expert), num_valid,
                                  block_m, _ptr(out), _stream(stream))
+
+
+def lowbit_mxfp8_quant(x, R, K, q, scale, stream=None):
+    return lib().lowbit_mxfp8_quant(_ptr(x), R, K, _ptr(q), _ptr(scale), _stream(stream))
+
+
+def lowbit_moe_silu_mul_quant(gate_up, R, I, q, scale, stream=None):
+    return lib().lowbit_moe_silu_mul_quant(_ptr(gate_up), R, I, _ptr(q), _ptr(scale), _stream(stream))
+
+
+def lowbit_moe_combine(expert_out, topk_weights, T, top_k, H, y, stream=None):
+    return lib().lowbit_moe_combine(_ptr(expert_out), _ptr(topk_weights), T, top_k, H, _ptr(y), _stream(stream))
+
+
+def lowbit_moe_layer_workspace_bytes(T, top_k, E, H, I, block_m):
+    return lib().lowbit_moe_layer_workspace_bytes(T, top_k, E, H, I, block_m)
+
+
+def lowbit_moe_layer(w13, w2, E_local, E, H, I, x, topk_ids, topk_weights, T, top_k, expert_map, block_m, y,
+                     workspace, ws_bytes, stream=None):
+    return lib().lowbit_moe_layer(_ptr(w13), _ptr(w2), E_local, E, H, I, _ptr(x), _ptr(topk_ids),
+                                  _ptr(topk_weights), T, top_k, _ptr(expert_map), block_m, _ptr(y), _ptr(workspace),
+                                  ws_bytes, _stream(stream))
 
 
 def make_gemv_problems(problems):

@@ -488,4 +488,99 @@ int lowbit_moe_gemm(int fmt, int E_local, int N, int K, const void *packed, int 
                                       static_cast<uint16_t *>(out), (hipStream_t)stream));
 }
 
+int lowbit_mxfp8_quant(const void *x, int R, int K, uint8_t *q, uint8_t *scale, void *stream)
+{
+    if (R < 0 || K < 0 || K % 32 != 0) return LOWBIT_E_INVALID_ARG;
+    if (R == 0 || K == 0) return LOWBIT_OK;
+    if (x == nullptr || q == nullptr || scale == nullptr) return LOWBIT_E_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 8 != 0)
+        return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)R * K >= ((int64_t)1 << 31)) return LOWBIT_E_UNSUPPORTED;
+    return hip_status(launch_mxfp8_rows(static_cast<const uint16_t *>(x), R, K, false, q, scale, (hipStream_t)stream));
+}
+
+int lowbit_moe_silu_mul_quant(const void *gate_up, int R, int I, uint8_t *q, uint8_t *scale, void *stream)
+{
+    if (R < 0 || I < 0 || I % 32 != 0) return LOWBIT_E_INVALID_ARG;
+    if (R == 0 || I == 0) return LOWBIT_OK;
+    if (gate_up == nullptr || q == nullptr || scale == nullptr) return LOWBIT_E_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(gate_up) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 8 != 0)
+        return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)R * 2 * I >= ((int64_t)1 << 31)) return LOWBIT_E_UNSUPPORTED;
+    return hip_status(launch_mxfp8_rows(static_cast<const uint16_t *>(gate_up), R, I, true, q, scale,
+                                        (hipStream_t)stream));
+}
+
+int lowbit_moe_combine(const void *expert_out, const float *topk_weights, int T, int top_k, int H, void *y,
+                       void *stream)
+{
+    if (T < 0 || top_k < 0 || H < 0 || H % 8 != 0) return LOWBIT_E_INVALID_ARG;
+    if (T == 0 || H == 0) return LOWBIT_OK;
+    if (y == nullptr || (top_k > 0 && (expert_out == nullptr || topk_weights == nullptr)))
+        return LOWBIT_E_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(expert_out) % 16 != 0 || reinterpret_cast<uintptr_t>(y) % 16 != 0)
+        return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)T * top_k * H >= ((int64_t)1 << 31)) return LOWBIT_E_UNSUPPORTED;
+    return hip_status(launch_moe_combine(static_cast<const uint16_t *>(expert_out), topk_weights, T, top_k, H,
+                                         static_cast<uint16_t *>(y), (hipStream_t)stream));
+}
+
+namespace {
+int moe_layer_check(int E_local, int E, int H, int I, int T, int top_k, int block_m)
+{
+    if (E_local < 0 || E <= 0 || H <= 0 || I <= 0 || T < 0 || top_k <= 0 || block_m <= 0) return LOWBIT_E_INVALID_ARG;
+    if (H % 64 != 0 || I % 64 != 0) return LOWBIT_E_INVALID_ARG;     // both GEMMs' K is a multiple of 64
+    if (E > 1024 || block_m % 16 != 0 || block_m > 4096) return LOWBIT_E_UNSUPPORTED;
+    const MoeLayerWs w = moe_layer_ws(T, top_k, E, H, I, block_m);
+    if (w.capacity >= ((int64_t)1 << 31) || w.bytes >= ((int64_t)1 << 40) ||
+        (int64_t)T * top_k * 2 * I >= ((int64_t)1 << 31) || (int64_t)T * top_k * H >= ((int64_t)1 << 31))
+        return LOWBIT_E_UNSUPPORTED;
+    if (check_lut3_shape(E_local, 2 * I, H) != LOWBIT_OK || check_lut3_shape(E_local, H, I) != LOWBIT_OK)
+        return LOWBIT_E_UNSUPPORTED;
+    return LOWBIT_OK;
+}
+}  // namespace
+
+size_t lowbit_moe_layer_workspace_bytes(int T, int top_k, int E, int H, int I, int block_m)
+{
+    if (moe_layer_check(0, E, H, I, T, top_k, block_m) != LOWBIT_OK) return 0;
+    return (size_t)moe_layer_ws(T, top_k, E, H, I, block_m).bytes;
+}
+
+int lowbit_moe_layer(const void *w13, const void *w2, int E_local, int E, int H, int I, const void *x,
+                     const int32_t *topk_ids, const float *topk_weights, int T, int top_k, const int32_t *expert_map,
+                     int block_m, void *y, void *workspace, size_t ws_bytes, void *stream)
+{
+    int st = moe_layer_check(E_local, E, H, I, T, top_k, block_m);
+    if (st != LOWBIT_OK) return st;
+    if (T == 0) return LOWBIT_OK;
+    if (x == nullptr || topk_ids == nullptr || topk_weights == nullptr || y == nullptr || workspace == nullptr ||
+        (E_local > 0 && (w13 == nullptr || w2 == nullptr)))
+        return LOWBIT_E_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(y) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return LOWBIT_E_INVALID_ARG;
+    const MoeLayerWs w = moe_layer_ws(T, top_k, E, H, I, block_m);
+    if (ws_bytes < (size_t)w.bytes) return LOWBIT_E_WORKSPACE;
+    const hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint8_t *xq = ws + w.xq, *xs = ws + w.xs, *aq = ws + w.aq, *as = ws + w.as;
+    int32_t *sorted = reinterpret_cast<int32_t *>(ws + w.sorted), *offs = reinterpret_cast<int32_t *>(ws + w.offsets);
+    int32_t *blk = reinterpret_cast<int32_t *>(ws + w.blocks), *npp = reinterpret_cast<int32_t *>(ws + w.npp);
+    uint16_t *gu = reinterpret_cast<uint16_t *>(ws + w.gate_up), *down = reinterpret_cast<uint16_t *>(ws + w.down);
+    const int slots = T * top_k;
+    hipError_t e = launch_mxfp8_rows(static_cast<const uint16_t *>(x), T, H, false, xq, xs, s);
+    if (e == hipSuccess)
+        e = launch_moe_align(topk_ids, slots, E, block_m, expert_map, sorted, offs, blk, npp, (int)w.capacity, s);
+    if (e == hipSuccess)
+        e = launch_moe_gemm(lut3_layout(E_local, 2 * I, H), static_cast<const uint8_t *>(w13), E, xq, xs, T, top_k,
+                            sorted, offs, blk, slots, block_m, gu, s);
+    if (e == hipSuccess) e = launch_mxfp8_rows(gu, slots, I, true, aq, as, s);
+    if (e == hipSuccess)
+        e = launch_moe_gemm(lut3_layout(E_local, H, I), static_cast<const uint8_t *>(w2), E, aq, as, slots, 1, sorted,
+                            offs, blk, slots, block_m, down, s);
+    if (e == hipSuccess) e = launch_moe_combine(down, topk_weights, T, top_k, H, static_cast<uint16_t *>(y), s);
+    return hip_status(e);
+}
+
 }  // extern "C"

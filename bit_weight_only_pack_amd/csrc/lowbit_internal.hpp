@@ -190,6 +190,33 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
                            const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
                            uint16_t *out, hipStream_t s);
 
+// The MoE layer around the grouped GEMMs (moe_layer.hip)
+hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t R, int K, bool silu, uint8_t *q, uint8_t *scale,
+                             hipStream_t s);
+hipError_t launch_moe_combine(const uint16_t *out, const float *w, int T, int top_k, int H, uint16_t *y,
+                              hipStream_t s);
+struct MoeLayerWs {
+    int64_t xq, xs, sorted, offsets, blocks, npp, gate_up, aq, as, down, bytes, capacity;
+};
+inline MoeLayerWs moe_layer_ws(int T, int top_k, int E, int H, int I, int block_m)
+{
+    MoeLayerWs w;
+    const int64_t slots = (int64_t)T * top_k;
+    w.capacity = slots + (int64_t)E * (block_m - 1);
+    w.xq = 0;
+    w.xs = align256(w.xq + (int64_t)T * H);
+    w.sorted = align256(w.xs + (int64_t)T * (H / 32));
+    w.offsets = align256(w.sorted + w.capacity * 4);
+    w.blocks = align256(w.offsets + (int64_t)(E + 1) * 4);
+    w.npp = align256(w.blocks + (w.capacity / block_m + 1) * 4);
+    w.gate_up = align256(w.npp + 4);
+    w.aq = align256(w.gate_up + slots * 2 * I * 2);
+    w.as = align256(w.aq + slots * I);
+    w.down = align256(w.as + slots * (I / 32));
+    w.bytes = align256(w.down + slots * H * 2);
+    return w;
+}
+
 size_t gemm_w4_workspace(int M, int64_t N, int64_t K, int G);
 hipError_t launch_gemm_w4(const W4Layout &L, int M, const uint8_t *packed, const void *a, int a_bf16, void *c,
                           int c_bf16, void *ws, size_t ws_bytes, hipStream_t s);

@@ -104,6 +104,18 @@ def moe_routing(T, E, top_k, *, workload_id=0, layer=0):
     return np.ascontiguousarray(order[:, :top_k].astype(np.int32))
 
 
+def moe_topk_weights(T, E, top_k, *, workload_id=0, layer=0):
+    """Router weights of the experts moe_routing picks (same logits): softmax
+    probabilities in float64, the chosen top_k renormalized to sum 1, cast to
+    float32.  Returns float32 [T][top_k] in the order of moe_routing's ids."""
+    logits = rng(workload_id, T_ROUTER, layer).standard_normal((T, E)).astype(np.float32).astype(np.float64)
+    order = np.argsort(-logits.astype(np.float32), axis=1, kind="stable")[:, :top_k]
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    pk = np.take_along_axis(p, order, axis=1)
+    return np.ascontiguousarray((pk / pk.sum(axis=1, keepdims=True)).astype(np.float32))
+
+
 def lut3_weights(E, N, K, *, exp_range=(120, 124), workload_id=0, layer=0, part=0):
     """3-bit LUT-codebook experts.
     idx u8 [E][N][K] uniform 0..7; codebook u8 (E4M3 bytes) [E][N/8][K/64][8]

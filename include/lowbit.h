@@ -360,6 +360,69 @@ int lowbit_moe_gemm(int fmt, int E_local, int N, int K, const void *packed, int 
                     const int32_t *block_expert, int num_valid, int block_m, void *out,
                     void *stream);
 
+/*
+ * MXFP8 quantization of bf16 rows (OCP MX as the "vLLM PR #62759 analysis"
+ * uses it, section "Format"/"Emulation path": E4M3 elements with one UE8M0
+ * scale per 32 consecutive elements).  Per 32-block of a row: e =
+ * floor(log2(max |x|)) - 8 (8 = exponent of E4M3's largest value 448),
+ * clamped to [-127, 127], 0 for an all-zero block; scale byte = e + 127;
+ * element = round-to-nearest-even E4M3 of x / 2^e, saturated at +-448.
+ *   x     : bf16 [R][K], 16-byte aligned, K % 32 == 0
+ *   q     : u8 (E4M3) [R][K] (output), 8-byte aligned
+ *   scale : u8 (UE8M0) [R][K/32] (output)
+ * The hidden states go through this before the gate/up grouped GEMM.
+ */
+int lowbit_mxfp8_quant(const void *x, int R, int K, uint8_t *q, uint8_t *scale, void *stream);
+
+/*
+ * SiLU(gate) * up of the gate/up grouped GEMM output, re-quantized to MXFP8
+ * for the down GEMM (the expert MLP of the MoE layer; the page's emulation
+ * quantizes the activations before each expert GEMM).
+ *   gate_up : bf16 [R][2I] (lowbit_moe_gemm output of the stacked gate and up
+ *             projections: columns 0..I-1 gate, I..2I-1 up), 16-byte aligned
+ *   q, scale: as lowbit_mxfp8_quant for K = I (I % 32 == 0)
+ * act = RNE_bf16(SiLU(g) * u) in binary32, SiLU(g) = g / (1 + e^-g) with e^-g
+ * evaluated as 2^t, t = -g * log2(e), by a fixed binary32 algorithm (n =
+ * rint(t), 2^(t-n) by its Taylor polynomial through degree 7 in Horner form
+ * with fused multiply-adds, t clamped to [-100, 100]), then MXFP8 of act.
+ */
+int lowbit_moe_silu_mul_quant(const void *gate_up, int R, int I, uint8_t *q, uint8_t *scale, void *stream);
+
+/*
+ * Router-weighted combine of the routed experts' outputs:
+ *   y[t][h] = RNE_bf16( sum_{j < top_k} topk_weights[t][j] * expert_out[t*top_k + j][h] )
+ * in fp32, j ascending.  Slots of experts that are not local have zero rows
+ * (lowbit_moe_gemm) and add nothing.
+ *   expert_out   : bf16 [T*top_k][H], 16-byte aligned; H % 8 == 0
+ *   topk_weights : f32 [T][top_k]
+ *   y            : bf16 [T][H] (output), 16-byte aligned
+ */
+int lowbit_moe_combine(const void *expert_out, const float *topk_weights, int T, int top_k, int H, void *y,
+                       void *stream);
+
+/* Workspace bytes of lowbit_moe_layer (0 for an invalid shape). */
+size_t lowbit_moe_layer_workspace_bytes(int T, int top_k, int E, int H, int I, int block_m);
+
+/*
+ * One whole MoE layer with 3-bit LUT-codebook experts and MXFP8 activations
+ * ("vLLM PR #62759 analysis": format, A gather, expert parallelism, emulation
+ * path), enqueued as six kernels: MXFP8 of x, routing alignment, gate/up
+ * grouped GEMM, SiLU(gate) * up with MXFP8, down grouped GEMM, combine.
+ *   w13      : lowbit_pack_weights(LOWBIT_LUT3_E4M3, E_local, 2I, H, ...) --
+ *              each expert's gate (rows 0..I-1) and up (rows I..2I-1) stacked
+ *   w2       : lowbit_pack_weights(LOWBIT_LUT3_E4M3, E_local, H, I, ...)
+ *   E        : global experts (routing ids are in [0, E)); expert_map as in
+ *              lowbit_moe_align (NULL = all local)
+ *   x        : bf16 [T][H] hidden states, 16-byte aligned; H % 64 == 0, I % 64 == 0
+ *   topk_ids : i32 [T][top_k]; topk_weights: f32 [T][top_k]
+ *   y        : bf16 [T][H] (output), 16-byte aligned
+ *   workspace: >= lowbit_moe_layer_workspace_bytes(T, top_k, E, H, I, block_m),
+ *              256-byte aligned; block_m a multiple of 16
+ */
+int lowbit_moe_layer(const void *w13, const void *w2, int E_local, int E, int H, int I, const void *x,
+                     const int32_t *topk_ids, const float *topk_weights, int T, int top_k, const int32_t *expert_map,
+                     int block_m, void *y, void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

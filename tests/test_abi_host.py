@@ -187,3 +187,26 @@ def test_w4a8_argument_checks_and_workspace_plan():
     assert wsb == 3 * lb.lowbit_workspace_bytes(OP, SYM, 8, 4096, 4096, 32) > 0
     assert lb.lowbit_gemv_w4a8_batched(SYM, 8, 32, 3, probs, FAKE, wsb - 1) == E_WS
     assert lb.lowbit_gemv_w4a8_batched(SYM, 1, 32, 9, probs, None, 0) == E_UNS
+
+
+def test_moe_layer_argument_checks():
+    """The MoE layer entry points validate on the host: block sizes of the
+    MXFP8 rows (K % 32), the layer's K multiples of 64, workspace size and
+    alignment, null pointers; empty calls return OK without touching memory."""
+    assert lb.lowbit_mxfp8_quant(FAKE, 4, 48, FAKE, FAKE) == E_ARG                # K % 32
+    assert lb.lowbit_mxfp8_quant(FAKE + 8, 4, 64, FAKE, FAKE) == E_ARG            # x alignment
+    assert lb.lowbit_mxfp8_quant(None, 0, 64, None, None) == lb.LOWBIT_OK
+    assert lb.lowbit_moe_silu_mul_quant(FAKE, 4, 40, FAKE, FAKE) == E_ARG         # I % 32
+    assert lb.lowbit_moe_silu_mul_quant(FAKE, 4, 64, None, FAKE) == E_ARG
+    assert lb.lowbit_moe_combine(FAKE, FAKE, 4, 2, 60, FAKE) == E_ARG             # H % 8
+    assert lb.lowbit_moe_combine(None, None, 0, 2, 64, None) == lb.LOWBIT_OK
+    wsb = lb.lowbit_moe_layer_workspace_bytes(256, 8, 128, 2048, 768, 16)
+    slots = 256 * 8
+    assert wsb >= slots * (2 * 768 * 2 + 768 + 768 // 32 + 2048 * 2) + 256 * (2048 + 2048 // 32)
+    assert lb.lowbit_moe_layer_workspace_bytes(256, 8, 128, 2000, 768, 16) == 0   # H % 64
+    assert lb.lowbit_moe_layer_workspace_bytes(256, 8, 128, 2048, 768, 24) == 0   # block_m % 16
+    args = (FAKE, FAKE, 128, 128, 2048, 768, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE)
+    assert lb.lowbit_moe_layer(*args, FAKE, wsb - 1) == E_WS
+    assert lb.lowbit_moe_layer(*args, FAKE + 128, wsb) == E_ARG                   # workspace alignment
+    assert lb.lowbit_moe_layer(FAKE, FAKE, 128, 128, 2048, 704, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE,
+                               FAKE, wsb) == E_ARG                                  # I % 64
