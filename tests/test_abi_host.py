@@ -208,5 +208,5 @@ def test_moe_layer_argument_checks():
     args = (FAKE, FAKE, 128, 128, 2048, 768, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE)
     assert lb.lowbit_moe_layer(*args, FAKE, wsb - 1) == E_WS
     assert lb.lowbit_moe_layer(*args, FAKE + 128, wsb) == E_ARG                   # workspace alignment
-    assert lb.lowbit_moe_layer(FAKE, FAKE, 128, 128, 2048, 704, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE,
+    assert lb.lowbit_moe_layer(FAKE, FAKE, 128, 128, 2048, 736, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE,
                                FAKE, wsb) == E_ARG                                  # I % 64
