@@ -339,7 +339,7 @@ def bench_decode_w4a8(args, torch, lb, synth):
     G, asym, wid = 32, True, 2
     res = {}
     m1 = None
-    for M in (1, 2, 4, 8):
+    for M in [int(v) for v in args.m_list.split(",")]:
         fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=True, outlier_frac=0.01)
         step_bytes = sum(L["bytes"] for L in launches)
         wsb = max(lb.lowbit_gemv_w4a8_batched_workspace_bytes(fmt, M, G, L["count"], L["probs"]) for L in launches)
@@ -375,7 +375,8 @@ def bench_decode_w4a8(args, torch, lb, synth):
            "vs_baseline": None, "dtype": "i8 x u4 (int32 accumulate), fp32 scales, f16 out",
            "data": "synthetic (seeded; asymmetric INT4 G=32, zero points U{0..15}, N(0,1) fp16 inputs with 1% "
                    "outlier channels x20)",
-           "config": {"workload": "llama3-8b-w4a8-asym-g32-decode-step", "M": [1, 2, 4, 8], "group_size": G,
+           "config": {"workload": "llama3-8b-w4a8-asym-g32-decode-step", "M": [int(v) for v in args.m_list.split(",")],
+                      "group_size": G,
                       "launches_per_step": m1["n"]},
            "tokens_per_s": res["M=1"]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res["M=1"]["GBps"] / HBM_PEAK_GBPS, 2),
@@ -552,6 +553,7 @@ def main():
                          "unfused = one launch per GEMV (7 per layer)")
     ap.add_argument("--cpu-layers", type=int, default=4, help="decode: layers the CPU oracle runs (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
+    ap.add_argument("--m-list", default="1,2,4,8", help="decode-w4a8: token counts to run (must include 1)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (a kernel of known traffic for counter runs)")
     args = ap.parse_args()
