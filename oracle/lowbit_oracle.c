@@ -265,6 +265,55 @@ void orc_w4_matmul_rows(const uint16_t *x, int x_dtype, int64_t K, int64_t N, in
 }
 
 /* ------------------------------------------------------------------------ */
+/* Uniform b-bit codes, b = 1..8 ([ARM] the 1-8 bit kernel table: one       */
+/* unpack routine per bit width; group-wise quantization as for INT4).       */
+/* ------------------------------------------------------------------------ */
+
+/* Zero point of a b-bit weight: symmetric 2^(b-1) (the midpoint of the
+ * unsigned code range, as z = 8 is for 4 bits), asymmetric the int8 zero
+ * point of the group. */
+static int wb_zero(const int8_t *zeros, int bits, int64_t n, int64_t k, int64_t K, int G)
+{
+    if (zeros == NULL) return 1 << (bits - 1);
+    return (int)zeros[n * (K / G) + k / G];
+}
+
+/* w[n][k] = (q[n][k] - z) * s[n][k/G] with q = codes[n][k] (one code per
+ * byte, q < 2^bits); exact in binary32 (|q - z| <= 383 needs 9 bits, an fp16
+ * scale 11). */
+void orc_wb_dequant(const uint8_t *codes, const uint16_t *scales, const int8_t *zeros, int bits,
+                    int64_t N, int64_t K, int G, float *w_out)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int q = codes[n * K + k];
+            int z = wb_zero(zeros, bits, n, k, K, G);
+            double s = orc_f16_to_double(scales[n * (K / G) + k / G]);
+            w_out[n * K + k] = (float)((double)(q - z) * s);
+        }
+}
+
+/* y[m][n] = sum_k x[m][k] * w[n][k], x fp16, ascending k in double (every
+ * product exact), y_out fp16 RNE (may be NULL). */
+void orc_wb_matmul(const uint16_t *x, int64_t M, int64_t N, int64_t K, int G, int bits,
+                   const uint8_t *codes, const uint16_t *scales, const int8_t *zeros,
+                   double *y64, uint16_t *y_out)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                int q = codes[n * K + k];
+                int z = wb_zero(zeros, bits, n, k, K, G);
+                double s = orc_f16_to_double(scales[n * (K / G) + k / G]);
+                acc += orc_f16_to_double(x[m * K + k]) * ((double)(q - z) * s);
+            }
+            if (y64) y64[m * N + n] = acc;
+            if (y_out) y_out[m * N + n] = orc_double_to_f16(acc);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* 3-bit LUT-codebook MoE with MXFP8 activations.                           */
 /* ------------------------------------------------------------------------ */
 

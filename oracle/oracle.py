@@ -57,6 +57,8 @@ def _declare(lib):
         "orc_w4_matmul": [_p, _int, _i64, _i64, _i64, _int, _p, _p, _p, _p, _p, _int],
         "orc_w4_matmul_rows": [_p, _int, _i64, _i64, _int, _p, _p, _p, _p, _i64, _p, _p, _int],
         "orc_lut3_dequant": [_p, _p, _p, _i64, _i64, _i64, _p],
+        "orc_wb_dequant": [_p, _p, _p, _int, _i64, _i64, _int, _p],
+        "orc_wb_matmul": [_p, _i64, _i64, _i64, _int, _int, _p, _p, _p, _p, _p],
         "orc_moe_align": [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _i64],
         "orc_moe_gemm": [_p, _p, _p, _i64, _i64, _i64, _p, _p, _i64, _p, _i64, _i64, _p, _p, _p],
         "orc_quant_act_i8": [_p, _i64, _i64, _p, _p],
@@ -200,6 +202,32 @@ class Oracle:
         yb = np.empty((r.size, N), np.uint16)
         self._lib.orc_w4_matmul_rows(_ptr(xb), xd, K, N, group_size, _ptr(q), _ptr(s), _ptr(z),
                                    _ptr(r), r.size, _ptr(y64), _ptr(yb), od)
+        return y64, yb
+
+    # ---------------------------------------------------------------- b-bit codes
+    def wb_dequant(self, codes, scales, zeros, bits, group_size):
+        """codes u8 [N][K] (< 2^bits) -> float32 [N][K], w = (q - z) * s, exact."""
+        c = _c(codes, np.uint8)
+        N, K = c.shape
+        assert int(c.max(initial=0)) < (1 << bits)
+        s = _f16_bits(scales)
+        z = None if zeros is None else _c(zeros, np.int8)
+        out = np.empty((N, K), np.float32)
+        self._lib.orc_wb_dequant(_ptr(c), _ptr(s), _ptr(z), bits, N, K, group_size, _ptr(out))
+        return out
+
+    def wb_matmul(self, x, codes, scales, zeros, bits, group_size):
+        """fp16 x [M][K] against b-bit weights -> (y64 [M][N], y fp16 bits [M][N])."""
+        xb = _f16_bits(x)
+        M, K = xb.shape
+        c = _c(codes, np.uint8)
+        N = c.shape[0]
+        assert c.shape == (N, K)
+        s = _f16_bits(scales)
+        z = None if zeros is None else _c(zeros, np.int8)
+        y64 = np.empty((M, N), np.float64)
+        yb = np.empty((M, N), np.uint16)
+        self._lib.orc_wb_matmul(_ptr(xb), M, N, K, group_size, bits, _ptr(c), _ptr(s), _ptr(z), _ptr(y64), _ptr(yb))
         return y64, yb
 
     # ---------------------------------------------------------------- W4A8
@@ -346,8 +374,7 @@ class Oracle:
 def _get():
     global _default
     if _default is None:
-        if not os.path.exists(_LIB):
-            build()
+        build()                      # compiles when the library is missing or older than the source
         _default = Oracle(_LIB)
     return _default
 
@@ -390,6 +417,14 @@ def w4_matmul(*a, **k):
 
 def w4_matmul_rows(*a, **k):
     return _get().w4_matmul_rows(*a, **k)
+
+
+def wb_dequant(*a, **k):
+    return _get().wb_dequant(*a, **k)
+
+
+def wb_matmul(*a, **k):
+    return _get().wb_matmul(*a, **k)
 
 
 def quant_act_i8(*a, **k):
@@ -453,4 +488,4 @@ def default():
     return _get()
 
 
-__all__ = ["build", "build_variant", "source_text", "Oracle", "default", "f16_to_double", "bf16_to_double", "double_to_f16", "double_to_bf16", "e4m3_to_double", "ue8m0_to_double", "w4_unpack", "w4_dequant", "w4_matmul", "w4_matmul_rows", "quant_act_i8", "w4a8_matmul", "lut3_dequant", "moe_align", "moe_gemm", "double_to_e4m3", "exp2_f32", "silu_f32", "mxfp8_quant", "silu_mul_bf16", "silu_mul_quant", "moe_combine", "moe_layer", "version"]
+__all__ = ["build", "build_variant", "source_text", "Oracle", "default", "f16_to_double", "bf16_to_double", "double_to_f16", "double_to_bf16", "e4m3_to_double", "ue8m0_to_double", "w4_unpack", "w4_dequant", "w4_matmul", "w4_matmul_rows", "wb_dequant", "wb_matmul", "quant_act_i8", "w4a8_matmul", "lut3_dequant", "moe_align", "moe_gemm", "double_to_e4m3", "exp2_f32", "silu_f32", "mxfp8_quant", "silu_mul_bf16", "silu_mul_quant", "moe_combine", "moe_layer", "version"]

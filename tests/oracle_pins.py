@@ -362,6 +362,90 @@ def check_rows_subset(o):
     assert np.array_equal(r64, y64[rows]) and np.array_equal(rb, yb[rows])
 
 
+# ------------------------------------------------------------------ b-bit codes (1..8)
+def _random_wb(r, N, K, G, bits, asym):
+    codes = r.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    s = r.uniform(0.002, 0.02, size=(N, K // G)).astype(np.float16)
+    z = r.integers(-128, 128, size=(N, K // G)).astype(np.int8) if asym else None
+    return codes, s, z
+
+
+def check_wb_equals_w4_at_four_bits(o):
+    """At 4 bits the b-bit definition is the INT4 one: dequantized weights and
+    products equal the (separately pinned) W4 oracle's bit for bit, symmetric
+    (z = 2^3 = 8) and asymmetric."""
+    r = np.random.default_rng(61)
+    for asym in (False, True):
+        codes, s, z = _random_wb(r, 24, 256, 32, 4, asym)
+        q = _pack_codes(codes)
+        assert np.array_equal(o.wb_dequant(codes, s, z, 4, 32), o.w4_dequant(q, s, z, 32))
+        x = r.standard_normal((3, 256)).astype(np.float16)
+        a = o.wb_matmul(x, codes, s, z, 4, 32)
+        b = o.w4_matmul(x, "f16", q, s, z, 32, "f16")
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), asym
+
+
+def check_wb_dequant_closed_form(o):
+    """Every code of every width against (q - z) * s in exact rationals, with
+    z = 2^(b-1) (symmetric) and int8 zero points over the full range."""
+    r = np.random.default_rng(62)
+    for bits in range(1, 9):
+        n = 1 << bits
+        K = 32 * ((n + 31) // 32)
+        codes = (np.arange(K) % n).astype(np.uint8)[None, :].repeat(3, axis=0)
+        s = np.array([[0.01], [0.0625], [-3.5]], np.float16).repeat(K // 32, axis=1)
+        for z in (None, r.integers(-128, 128, size=(3, K // 32)).astype(np.int8)):
+            W = o.wb_dequant(codes, s, z, bits, 32)
+            for i in range(3):
+                for k in range(K):
+                    zz = (1 << (bits - 1)) if z is None else int(z[i, k // 32])
+                    assert F(float(W[i, k])) == (int(codes[i, k]) - zz) * F(float(s[i, k // 32])), (bits, i, k)
+
+
+def check_wb_bruteforce(o):
+    """b-bit products against exact rationals for several widths, group
+    sizes, both zero-point forms."""
+    r = np.random.default_rng(63)
+    for bits, G, asym, M, N, K in ((1, 32, False, 2, 5, 64), (2, 64, True, 1, 6, 128), (3, 32, True, 3, 4, 96),
+                                   (5, 128, False, 1, 3, 256), (6, 32, True, 2, 4, 64), (7, 64, False, 1, 5, 128),
+                                   (8, 32, True, 2, 3, 64)):
+        codes, s, z = _random_wb(r, N, K, G, bits, asym)
+        x = (r.standard_normal((M, K)) * 2).astype(np.float16)
+        xf = [[F(float(v)) for v in row] for row in x.astype(np.float64)]
+        sf = [_frac_f16(row) for row in s.view(np.uint16)]
+        y64, yb = o.wb_matmul(x, codes, s, z, bits, G)
+        for m in range(M):
+            for nn in range(N):
+                acc, mag = F(0), F(0)
+                for k in range(K):
+                    zz = (1 << (bits - 1)) if z is None else int(z[nn, k // G])
+                    t = xf[m][k] * (int(codes[nn, k]) - zz) * sf[nn][k // G]
+                    acc += t
+                    mag += abs(t)
+                assert abs(F(float(y64[m, nn])) - acc) <= (K + 1) * F(1, 2 ** 53) * mag, (bits, m, nn)
+                assert yb[m, nn] == _np_f16_bits([float(acc)])[0], (bits, m, nn)
+
+
+def check_wb_numpy_and_special(o):
+    """numpy float64 matmul of the pinned dequantized W; codes at the
+    symmetric zero point give exactly 0; a one-hot x gives the weight column."""
+    r = np.random.default_rng(64)
+    for bits in (2, 3, 6):
+        codes, s, z = _random_wb(r, 40, 384, 128, bits, True)
+        x = r.standard_normal((4, 384)).astype(np.float16)
+        ref = x.astype(np.float64) @ o.wb_dequant(codes, s, z, bits, 128).astype(np.float64).T
+        y64, _ = o.wb_matmul(x, codes, s, z, bits, 128)
+        assert np.max(np.abs(y64 - ref)) <= 1e-12 * np.max(np.abs(ref)), bits
+        mid = np.full((8, 128), 1 << (bits - 1), np.uint8)
+        y64, _ = o.wb_matmul(x[:, :128], mid, s[:8, :1], None, bits, 128)
+        assert np.all(y64 == 0), bits
+        W = o.wb_dequant(codes, s, z, bits, 128)
+        e = np.zeros((1, 384), np.float16)
+        e[0, 77] = 1
+        y64, yb = o.wb_matmul(e, codes, s, z, bits, 128)
+        assert np.array_equal(y64[0], W[:, 77].astype(np.float64)), bits
+
+
 # ------------------------------------------------------------------ W4A8: dynamic INT8 activations
 def check_quant_closed_forms(o):
     """A row whose largest magnitude is 127 * 2^e makes 127 / amax = 2^-e and
@@ -799,6 +883,7 @@ ALL_CHECKS = [
     check_hand_bytes, check_sixteen_codes, check_dequant_exact_all_scales, check_fp16_tie, check_gemv_2x4,
     check_bruteforce_tiny, check_bruteforce_tiny_gemv_workload, check_numpy_matmul, check_one_hot,
     check_codes_at_zero_point, check_pow2_scaling, check_k_split, check_rows_subset,
+    check_wb_equals_w4_at_four_bits, check_wb_dequant_closed_form, check_wb_bruteforce, check_wb_numpy_and_special,
     check_quant_closed_forms, check_quant_properties, check_w4a8_bruteforce, check_w4a8_numpy,
     check_w4a8_on_grid_equals_w4a16, check_w4a8_special,
     check_lut3_hand, check_lut3_bruteforce, check_moe_bruteforce, check_moe_numpy, check_moe_align,

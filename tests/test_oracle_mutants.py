@@ -31,6 +31,11 @@ MUTANTS = [
     ("ties away from zero", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     ("bf16 encode exponent", "((E + 127) << 7)", "((E + 126) << 7)"),
     ("fp16 overflow saturates", "if (isinf(r)) return sign | 0x7c00;", "if (isinf(r)) return sign | 0x7bff;"),
+    ("b-bit symmetric zero point 2^b", "if (zeros == NULL) return 1 << (bits - 1);", "if (zeros == NULL) return 1 << bits;"),
+    ("b-bit code index transposed", "            int q = codes[n * K + k];\n            int z = wb_zero(zeros, bits, n, k, K, G);\n            double s = orc_f16_to_double(scales[n * (K / G) + k / G]);\n            w_out",
+     "            int q = codes[k * N + n];\n            int z = wb_zero(zeros, bits, n, k, K, G);\n            double s = orc_f16_to_double(scales[n * (K / G) + k / G]);\n            w_out"),
+    ("b-bit product uses the zero point of group 0", "                int z = wb_zero(zeros, bits, n, k, K, G);\n                double s = orc_f16_to_double(scales[n * (K / G) + k / G]);\n                acc +=",
+     "                int z = wb_zero(zeros, bits, n, 0, K, G);\n                double s = orc_f16_to_double(scales[n * (K / G) + k / G]);\n                acc +="),
     ("activation codes scaled to 128", "127.0f / amax", "128.0f / amax"),
     ("activation ties away from zero", "float r = rintf(t);", "float r = roundf(t);"),
     ("activation codes truncated", "float r = rintf(t);", "float r = truncf(t);"),
