@@ -23,6 +23,13 @@ LOWBIT_W4_SYM = 0
 LOWBIT_W4_ASYM = 1
 LOWBIT_LUT3_E4M3 = 2
 
+
+
+def LOWBIT_UINT(bits, asym=False):
+    """Format id of uniform b-bit codes (the C macro of the same name)."""
+    return 16 + 2 * bits + (1 if asym else 0)
+
+
 LOWBIT_F16 = 0
 LOWBIT_BF16 = 1
 

@@ -34,6 +34,30 @@ int check_w4_shape(int fmt, int N, int K, int G)
     return LOWBIT_OK;
 }
 
+// dense group-wise formats: INT4 (nibble-packed canonical codes) and uniform
+// b-bit codes (one code per byte)
+bool is_dense(int fmt) { return is_w4(fmt) || is_uint_fmt(fmt); }
+
+int check_dense_shape(int fmt, int N, int K, int G)
+{
+    if (is_uint_fmt(fmt)) {
+        const int bits = uint_bits(fmt);
+        if (bits < 1 || bits > 8) return LOWBIT_E_UNSUPPORTED;
+        return check_w4_shape(uint_asym(fmt) ? LOWBIT_W4_ASYM : LOWBIT_W4_SYM, N, K, G);
+    }
+    return check_w4_shape(fmt, N, K, G);
+}
+
+bool dense_asym(int fmt) { return is_uint_fmt(fmt) ? uint_asym(fmt) : fmt == LOWBIT_W4_ASYM; }
+
+W4Layout dense_layout(int fmt, int64_t N, int64_t K, int G)
+{
+    return is_uint_fmt(fmt) ? wb_layout(N, K, G, uint_bits(fmt), uint_asym(fmt)) : w4_layout(N, K, G, fmt == LOWBIT_W4_ASYM);
+}
+
+// canonical code bytes of one matrix: two codes per byte for INT4, one otherwise
+int64_t dense_code_bytes(int fmt, int64_t N, int64_t K) { return is_uint_fmt(fmt) ? N * K : N * (K / 2); }
+
 bool is_lut3(int fmt) { return fmt == LOWBIT_LUT3_E4M3; }
 
 int check_lut3_shape(int E, int N, int K)
@@ -68,9 +92,9 @@ int lowbit_version(void) { return 1; }
 size_t lowbit_packed_bytes(int fmt, int E, int N, int K, int group_size)
 {
     if (E < 0) return 0;
-    if (is_w4(fmt)) {
-        if (check_w4_shape(fmt, N, K, group_size) != LOWBIT_OK) return 0;
-        return (size_t)E * (size_t)w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM).bytes;
+    if (is_dense(fmt)) {
+        if (check_dense_shape(fmt, N, K, group_size) != LOWBIT_OK) return 0;
+        return (size_t)E * (size_t)dense_layout(fmt, N, K, group_size).bytes;
     }
     if (is_lut3(fmt)) {
         if (check_lut3_shape(E, N, K) != LOWBIT_OK) return 0;
@@ -95,23 +119,24 @@ int lowbit_pack_weights(int fmt, int E, int N, int K, int group_size, const void
                                            static_cast<const uint8_t *>(zeros), static_cast<uint8_t *>(packed),
                                            (hipStream_t)stream));
     }
-    if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
-    int st = check_w4_shape(fmt, N, K, group_size);
+    if (!is_dense(fmt)) return LOWBIT_E_UNSUPPORTED;
+    int st = check_dense_shape(fmt, N, K, group_size);
     if (st != LOWBIT_OK) return st;
-    const bool asym = fmt == LOWBIT_W4_ASYM;
+    const bool asym = dense_asym(fmt);
     if (asym != (zeros != nullptr)) return LOWBIT_E_INVALID_ARG;
-    const W4Layout L = w4_layout(N, K, group_size, asym);
+    const W4Layout L = dense_layout(fmt, N, K, group_size);
     if (packed_bytes < (size_t)E * (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
     if (E == 0) return LOWBIT_OK;
     if (packed == nullptr) return LOWBIT_E_INVALID_ARG;
     if ((int64_t)N * K > 0 && (codes == nullptr || scales == nullptr)) return LOWBIT_E_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t ncode = (int64_t)N * (K / 2), nmeta = (int64_t)N * (K / group_size);
+    const int64_t ncode = dense_code_bytes(fmt, N, K), nmeta = (int64_t)N * (K / group_size);
     for (int e = 0; e < E; ++e) {
-        hipError_t err = launch_w4_pack(
-            L, static_cast<const uint8_t *>(codes) + e * ncode, static_cast<const uint16_t *>(scales) + e * nmeta,
-            asym ? static_cast<const int8_t *>(zeros) + e * nmeta : nullptr,
-            static_cast<uint8_t *>(packed) + (int64_t)e * L.bytes, s);
+        const uint8_t *c = static_cast<const uint8_t *>(codes) + e * ncode;
+        const uint16_t *sc = static_cast<const uint16_t *>(scales) + e * nmeta;
+        const int8_t *z = asym ? static_cast<const int8_t *>(zeros) + e * nmeta : nullptr;
+        uint8_t *dst = static_cast<uint8_t *>(packed) + (int64_t)e * L.bytes;
+        hipError_t err = is_w4(fmt) ? launch_w4_pack(L, c, sc, z, dst, s) : launch_wb_pack(L, c, sc, z, dst, s);
         if (err != hipSuccess) return hip_status(err);
     }
     return LOWBIT_OK;
@@ -132,22 +157,23 @@ int lowbit_unpack_weights(int fmt, int E, int N, int K, int group_size, const vo
                                              static_cast<uint8_t *>(scales), static_cast<uint8_t *>(zeros),
                                              (hipStream_t)stream));
     }
-    if (!is_w4(fmt)) return LOWBIT_E_UNSUPPORTED;
-    int st = check_w4_shape(fmt, N, K, group_size);
+    if (!is_dense(fmt)) return LOWBIT_E_UNSUPPORTED;
+    int st = check_dense_shape(fmt, N, K, group_size);
     if (st != LOWBIT_OK) return st;
-    const bool asym = fmt == LOWBIT_W4_ASYM;
+    const bool asym = dense_asym(fmt);
     if (asym != (zeros != nullptr)) return LOWBIT_E_INVALID_ARG;
-    const W4Layout L = w4_layout(N, K, group_size, asym);
+    const W4Layout L = dense_layout(fmt, N, K, group_size);
     if (packed_bytes < (size_t)E * (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
     if (E == 0 || (int64_t)N * K == 0) return LOWBIT_OK;
     if (packed == nullptr || codes == nullptr || scales == nullptr) return LOWBIT_E_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t ncode = (int64_t)N * (K / 2), nmeta = (int64_t)N * (K / group_size);
+    const int64_t ncode = dense_code_bytes(fmt, N, K), nmeta = (int64_t)N * (K / group_size);
     for (int e = 0; e < E; ++e) {
-        hipError_t err = launch_w4_unpack(
-            L, static_cast<const uint8_t *>(packed) + (int64_t)e * L.bytes,
-            static_cast<uint8_t *>(codes) + e * ncode, static_cast<uint16_t *>(scales) + e * nmeta,
-            asym ? static_cast<int8_t *>(zeros) + e * nmeta : nullptr, s);
+        const uint8_t *src = static_cast<const uint8_t *>(packed) + (int64_t)e * L.bytes;
+        uint8_t *c = static_cast<uint8_t *>(codes) + e * ncode;
+        uint16_t *sc = static_cast<uint16_t *>(scales) + e * nmeta;
+        int8_t *z = asym ? static_cast<int8_t *>(zeros) + e * nmeta : nullptr;
+        hipError_t err = is_w4(fmt) ? launch_w4_unpack(L, src, c, sc, z, s) : launch_wb_unpack(L, src, c, sc, z, s);
         if (err != hipSuccess) return hip_status(err);
     }
     return LOWBIT_OK;
@@ -156,18 +182,21 @@ int lowbit_unpack_weights(int fmt, int E, int N, int K, int group_size, const vo
 int lowbit_dequant(int fmt, int N, int K, int group_size, const void *packed, size_t packed_bytes,
                    float *w_out, void *stream)
 {
-    int st = check_w4_shape(fmt, N, K, group_size);
+    int st = check_dense_shape(fmt, N, K, group_size);
     if (st != LOWBIT_OK) return st;
-    const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
+    const W4Layout L = dense_layout(fmt, N, K, group_size);
     if (packed_bytes < (size_t)L.bytes) return LOWBIT_E_WORKSPACE;
     if ((int64_t)N * K == 0) return LOWBIT_OK;
     if (packed == nullptr || w_out == nullptr) return LOWBIT_E_INVALID_ARG;
-    return hip_status(launch_w4_dequant(L, static_cast<const uint8_t *>(packed), w_out, (hipStream_t)stream));
+    const uint8_t *src = static_cast<const uint8_t *>(packed);
+    return hip_status(is_w4(fmt) ? launch_w4_dequant(L, src, w_out, (hipStream_t)stream)
+                                 : launch_wb_dequant(L, src, w_out, (hipStream_t)stream));
 }
 
 size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_size)
 {
-    if (!is_w4(fmt) || check_w4_shape(fmt, N, K, group_size) != LOWBIT_OK || M < 0) return 0;
+    if (!is_dense(fmt) || check_dense_shape(fmt, N, K, group_size) != LOWBIT_OK || M < 0) return 0;
+    if (!is_w4(fmt)) return 0;                        // b-bit GEMV: no workspace
     if (op == LOWBIT_OP_GEMV) return gemv_w4_workspace(M, N, K, group_size);
     if (op == LOWBIT_OP_GEMM) return gemm_w4_workspace(M, N, K, group_size);
     if (op == LOWBIT_OP_GEMV_W4A8) {
@@ -183,6 +212,10 @@ size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_si
 int lowbit_gemv(int fmt, int M, int N, int K, int group_size, const void *packed, const void *x,
                 void *y, void *workspace, size_t ws_bytes, void *stream)
 {
+    if (is_uint_fmt(fmt)) {
+        lowbit_gemv_problem p = {packed, x, y, N, K};
+        return lowbit_gemv_batched(fmt, M, group_size, 1, &p, stream);
+    }
     int st = check_w4_shape(fmt, N, K, group_size);
     if (st != LOWBIT_OK) return st;
     if (M < 0) return LOWBIT_E_INVALID_ARG;
@@ -208,18 +241,24 @@ int lowbit_gemv_batched(int fmt, int M, int group_size, int count, const lowbit_
     const _Float16 *x[kMaxGemvBatch];
     _Float16 *y[kMaxGemvBatch];
     int n = 0;
+    int64_t kt_max = 0;
     for (int i = 0; i < count; ++i) {
         const lowbit_gemv_problem &p = problems[i];
-        int st = check_w4_shape(fmt, p.N, p.K, group_size);
+        int st = check_dense_shape(fmt, p.N, p.K, group_size);
         if (st != LOWBIT_OK) return st;
         if (p.N == 0) continue;                        // nothing to compute for this one
         if (p.packed == nullptr || p.y == nullptr || (p.K > 0 && p.x == nullptr)) return LOWBIT_E_INVALID_ARG;
         if (reinterpret_cast<uintptr_t>(p.x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
-        L[n] = w4_layout(p.N, p.K, group_size, fmt == LOWBIT_W4_ASYM);
+        L[n] = dense_layout(fmt, p.N, p.K, group_size);
+        kt_max = L[n].ktiles > kt_max ? L[n].ktiles : kt_max;
         packed[n] = static_cast<const uint8_t *>(p.packed);
         x[n] = static_cast<const _Float16 *>(p.x);
         y[n] = static_cast<_Float16 *>(p.y);
         ++n;
+    }
+    if (is_uint_fmt(fmt)) {
+        if (n > 0 && gemv_wb_lds(M, kt_max) == 0) return LOWBIT_E_UNSUPPORTED;
+        return hip_status(launch_gemv_wb_batch(L, n, M, packed, x, y, (hipStream_t)stream));
     }
     return hip_status(launch_gemv_w4_batch(L, n, M, packed, x, y, (hipStream_t)stream));
 }

@@ -1,0 +1,383 @@
+// gemv_wb.hip -- decode GEMV / small-batch product with uniform b-bit codes,
+// b = 1..8 ("Low Bit ARM kernels": one unpack routine per bit width from 1 to
+// 8 bits in a bit-width x tile table, group-wise fp16 scales, symmetric or
+// with an int8 zero point; fewer bits, fewer weight bytes to stream at decode).
+//
+//   y[m][n] = sum_k x[m][k] * (q[n][k] - z) * s[n][k / G],  z = 2^(b-1) or int8
+//
+// MI355X design: the W4 streaming GEMV's schedule (one workgroup per 16-row
+// strip, waves split K, x staged in LDS by LDS-direct loads, every weight load
+// issued up front with the non-temporal hint, fixed-order cross-wave sum, fp16
+// RNE) with the codes split into 4-, 2- and 1-bit planes (lowbit_internal.hpp).
+// A shift and a mask of a plane dword give two codes in the two 16-bit halves;
+// or-ed together and into fp16 1024.0 they form 1024 + q exactly (q <= 255),
+// which feeds the offset-split product of gemv_tile.hpp: x.(1024 + q) -
+// x.(1024 + z) by two MFMA chains over the same activations, so codes equal
+// to the zero point give exactly zero.
+#include "lowbit_internal.hpp"
+#include "gemv_tile.hpp"
+
+namespace lowbit {
+
+namespace {
+
+using namespace tile;
+
+constexpr int kWbMaxLds = 160 * 1024;
+
+__host__ __device__ inline int wb_rowp(int kt) { return (int)round_up((int64_t)kt * 16, 64); }
+__host__ __device__ inline int wb_lds(int M, int kt, int W, int MR) { return M * wb_rowp(kt) * 16 + W * MR * 64 * 4; }
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// the planes of one lane's tile, as loaded
+template <int BITS>
+struct WbTile {
+    static constexpr int N4 = BITS / 4, N2 = (BITS % 4) >= 2 ? 1 : 0, N1 = BITS & 1;
+    u4 a[N4 > 0 ? N4 : 1];
+    uint2 b;
+    uint32_t c;
+};
+
+template <int BITS>
+__device__ __forceinline__ WbTile<BITS> load_wb(__amdgpu_buffer_rsrc_t rs, bool ok, uint32_t base)
+{
+    using TT = WbTile<BITS>;
+    TT w;
+#pragma unroll
+    for (int p = 0; p < TT::N4; ++p)
+        w.a[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + 16 * p : kBufferOob, 0, kStreamLoad);
+    if constexpr (TT::N2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? base + 16 * TT::N4 : kBufferOob, 0, kStreamLoad);
+        w.b = make_uint2(v[0], v[1]);
+    }
+    if constexpr (TT::N1)
+        w.c = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? base + 16 * TT::N4 + 8 * TT::N2 : kBufferOob, 0, kStreamLoad);
+    return w;
+}
+
+template <int BITS>
+__device__ __forceinline__ void pin_wb(WbTile<BITS> &w)
+{
+    using TT = WbTile<BITS>;
+#pragma unroll
+    for (int p = 0; p < TT::N4; ++p) asm volatile("" : "+v"(w.a[p]));
+    if constexpr (TT::N2) asm volatile("" : "+v"(w.b.x), "+v"(w.b.y));
+    if constexpr (TT::N1) asm volatile("" : "+v"(w.c));
+}
+
+// MFMA block i (K offsets 0..7 of the lane's 8-K slice) -> 8 fp16 1024 + q
+template <int BITS>
+__device__ __forceinline__ h8 wb_operand(const WbTile<BITS> &w, int i, uint32_t magic)
+{
+    using TT = WbTile<BITS>;
+    u4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t r = magic;
+        if constexpr (TT::N4 >= 1) r |= (w.a[0][i] >> (4 * q)) & 0x000F000Fu;
+        if constexpr (TT::N4 >= 2) r |= ((w.a[1][i] >> (4 * q)) & 0x000F000Fu) << 4;
+        if constexpr (TT::N2) {
+            const uint32_t bw = (i >> 1) ? w.b.y : w.b.x;
+            r |= ((bw >> (2 * (4 * (i & 1) + q))) & 0x00030003u) << (4 * TT::N4);
+        }
+        if constexpr (TT::N1) r |= ((w.c >> (4 * i + q)) & 0x00010001u) << (4 * TT::N4 + 2 * TT::N2);
+        v[q] = r;
+    }
+    return __builtin_bit_cast(h8, v);
+}
+
+// offset operand of zero point z: 1024 + z in every half
+__device__ __forceinline__ h8 wb_offset(int z)
+{
+    const _Float16 o = (_Float16)(1024.0f + (float)z);   // exact: integers below 2048
+    return h8{o, o, o, o, o, o, o, o};
+}
+
+template <int BITS, int G, bool ASYM, int MR, int T>
+__device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *scales, const uint8_t *zeros,
+                                         const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M, int W,
+                                         int strip)
+{
+    using TT = WbTile<BITS>;
+    constexpr int GPT = 128 / G;
+    constexpr int MPG = G / 32;
+    constexpr int NLD = TT::N4 + TT::N2 + TT::N1;           // code loads per tile
+    constexpr int NW = T * (NLD + (ASYM ? 2 : 1));           // weight + metadata loads per wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, kq = lane >> 4;
+    const int t0 = wave * tw;
+    const int rowp = wb_rowp(kt);
+    float *red = reinterpret_cast<float *>(smem + M * rowp * 16);
+
+    // 1. x -> LDS: block bb of tile t of row m holds x[m][128 t + 8 (bb ^ (m & 15)) ..]
+    {
+        const auto xrs = buffer_rsrc(xg, (uint32_t)(M * K * 2));
+        const int cpr = rowp >> 6;
+        for (int m = 0; m < M; ++m)
+            for (int cc = wave; cc < cpr; cc += W) {
+                const int jj = cc * 64 + lane;
+                const int t = jj >> 4, bb = jj & 15;
+                const int j = t * 16 + (bb ^ (m & 15));
+                lds_dma16(xrs, smem + (m * cpr + cc) * 1024, j * 8 < K ? (uint32_t)((m * K + j * 8) * 2) : kBufferOob);
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. codes and metadata of this wave's tiles
+    TT q[T];
+    MetaRaw<G, ASYM> mr[T];
+    {
+        const int64_t tiles0 = (int64_t)strip * kt;
+        const auto crs = buffer_rsrc(codes + tiles0 * 256 * BITS, (uint32_t)kt * 256 * BITS);
+        const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+        const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+            const int t = t0 + u;
+            const bool ok = u < tw && t < kt;
+            q[u] = load_wb<BITS>(crs, ok, (uint32_t)(t * 64 + lane) * 4 * BITS);
+            mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // 3. x in LDS everywhere
+    wait_vm<NW>();
+    asm volatile("s_barrier" ::: "memory");
+
+    // 4. products, tile by tile in load order
+    uint32_t magic = 0x64006400u;                    // fp16 1024.0 in both halves
+    asm volatile("" : "+v"(magic));
+    h8 psym = wb_offset(1 << (BITS - 1));
+    {
+        u4 pw = __builtin_bit_cast(u4, psym);
+        asm volatile("" : "+v"(pw));
+        psym = __builtin_bit_cast(h8, pw);
+    }
+    const int xr = r < M ? r : M - 1;
+    const _Float16 *xa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * rowp + t0 * 16 + ((i * 4 + kq) ^ (xr & 15))) * 8;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const int tvalid = min(tw, kt - t0);
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        if (u < tvalid) {
+            __builtin_amdgcn_sched_barrier(0);
+            TT w = q[u];
+            pin_wb<BITS>(w);
+            MetaRaw<G, ASYM> mv = mr[u];
+            pin_meta<G, ASYM>(mv);
+            f4 cv = zero4, cp = zero4;
+            h8 p = psym;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int g = i / MPG;
+                if constexpr (ASYM) {
+                    if (i % MPG == 0) {
+                        uint32_t zb;
+                        if constexpr (G == 128) zb = mv.z >> (8 * (r & 3));
+                        else if constexpr (G == 64) zb = mv.z >> (16 * (r & 1) + 8 * g);
+                        else zb = mv.z >> (8 * g);
+                        p = wb_offset((int)(int8_t)(uint8_t)zb);
+                    }
+                }
+                const h8 a = *reinterpret_cast<const h8 *>(xa[i] + u * 128);
+                const h8 v = wb_operand<BITS>(w, i, magic);
+                cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, v, (i % MPG == 0) ? zero4 : cv, 0, 0, 0);
+                cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p, (i % MPG == 0) ? zero4 : cp, 0, 0, 0);
+                if (i % MPG == MPG - 1) {
+                    uint16_t hb;
+                    if constexpr (G == 128) hb = (uint16_t)(mv.s[0] >> (16 * (r & 1)));
+                    else hb = (uint16_t)(mv.s[g / 2] >> (16 * (g & 1)));
+                    const float sc = (float)__builtin_bit_cast(_Float16, hb);
+#pragma unroll
+                    for (int j = 0; j < MR; ++j) acc[j] = __builtin_fmaf(sc, cv[j] - cp[j], acc[j]);
+                }
+            }
+        }
+    }
+
+    // 5. fixed-order cross-wave sum, fp16 RNE store
+    if (W > 1) {
+#pragma unroll
+        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                float part[16];
+#pragma unroll
+                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
+                float v = red[j * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < 16; ++w)
+                    if (w < W) v += part[w];
+                acc[j] = v;
+            }
+        }
+    }
+    if (wave == 0) {
+        const int n = strip * 16 + r;
+#pragma unroll
+        for (int j = 0; j < MR; ++j) {
+            const int m = kq * 4 + j;
+            if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[j];
+        }
+    }
+}
+
+template <int BITS, int G, bool ASYM, int MR, int T>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : 6)))
+void gemv_wb_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
+                    int kt, int tw, int M, int W, const uint8_t *zeros)
+{
+    wb_strip<BITS, G, ASYM, MR, T>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
+}
+
+// problems laid end to end over blockIdx.x (b.first[i] = first workgroup of
+// problem i; unused entries hold INT_MAX)
+template <int BITS, int G, bool ASYM, int MR, int T>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : 6)))
+void gemv_wb_batch(const GemvBatch b)
+{
+    const int bx = (int)blockIdx.x;
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGemvBatch; ++i) pi += bx >= b.first[i] ? 1 : 0;
+    const GemvProblem &p = b.p[pi];
+    wb_strip<BITS, G, ASYM, MR, T>(p.codes, p.scales, p.zeros, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W,
+                                   bx - b.first[pi]);
+}
+
+inline hipError_t wb_lds_limit(const void *k, size_t lds, bool &raised)
+{
+    if (lds <= 64 * 1024 || raised) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kWbMaxLds);
+    if (e == hipSuccess) raised = true;
+    return e;
+}
+
+template <int BITS, int G, bool ASYM, int MR, int T>
+hipError_t wb_launch_k(const GemvBatch &b, dim3 grid, dim3 block, size_t lds, hipStream_t st)
+{
+    if (b.count == 1) {
+        static bool raised = false;
+        auto k = gemv_wb_single<BITS, G, ASYM, MR, T>;
+        const hipError_t e = wb_lds_limit((const void *)k, lds, raised);
+        if (e != hipSuccess) return e;
+        const GemvProblem &p = b.p[0];
+        k<<<grid, block, lds, st>>>(p.codes, p.scales, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W, p.zeros);
+    } else {
+        static bool raised = false;
+        auto k = gemv_wb_batch<BITS, G, ASYM, MR, T>;
+        const hipError_t e = wb_lds_limit((const void *)k, lds, raised);
+        if (e != hipSuccess) return e;
+        k<<<grid, block, lds, st>>>(b);
+    }
+    return hipGetLastError();
+}
+
+template <int BITS, int G, bool ASYM>
+hipError_t wb_launch_mt(int MR, int T, const GemvBatch &b, dim3 grid, dim3 block, size_t lds, hipStream_t st)
+{
+    if (MR == 1) return T <= 4 ? wb_launch_k<BITS, G, ASYM, 1, 4>(b, grid, block, lds, st)
+                               : wb_launch_k<BITS, G, ASYM, 1, 8>(b, grid, block, lds, st);
+    return T <= 4 ? wb_launch_k<BITS, G, ASYM, 4, 4>(b, grid, block, lds, st)
+                  : wb_launch_k<BITS, G, ASYM, 4, 8>(b, grid, block, lds, st);
+}
+
+template <int BITS>
+hipError_t wb_launch_bits(int G, bool asym, int MR, int T, const GemvBatch &b, dim3 grid, dim3 block, size_t lds,
+                          hipStream_t st)
+{
+    switch (G) {
+    case 32: return asym ? wb_launch_mt<BITS, 32, true>(MR, T, b, grid, block, lds, st)
+                         : wb_launch_mt<BITS, 32, false>(MR, T, b, grid, block, lds, st);
+    case 64: return asym ? wb_launch_mt<BITS, 64, true>(MR, T, b, grid, block, lds, st)
+                         : wb_launch_mt<BITS, 64, false>(MR, T, b, grid, block, lds, st);
+    default: return asym ? wb_launch_mt<BITS, 128, true>(MR, T, b, grid, block, lds, st)
+                         : wb_launch_mt<BITS, 128, false>(MR, T, b, grid, block, lds, st);
+    }
+}
+
+}  // namespace
+
+// LDS the b-bit GEMV needs for M rows over the widest problem (0 if it has
+// no kernel for it: more than 8 tiles per wave or more than 160 KiB)
+size_t gemv_wb_lds(int M, int64_t kt_max)
+{
+    int W = (int)((kt_max + 3) / 4);
+    W = W < 1 ? 1 : (W > 16 ? 16 : W);
+    const int64_t T = (kt_max + W - 1) / W;
+    const int MR = M == 1 ? 1 : 4;
+    const int64_t lds = wb_lds(M, (int)kt_max, W, MR);
+    return (T > 8 || lds > kWbMaxLds) ? 0 : (size_t)lds;
+}
+
+hipError_t launch_gemv_wb_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
+                                const _Float16 *const *x, _Float16 *const *y, hipStream_t s)
+{
+    if (M == 0 || count == 0) return hipSuccess;
+    GemvBatch b;
+    int64_t strips = 0, kt = 0;
+    for (int i = 0; i < count; ++i) kt = L[i].ktiles > kt ? L[i].ktiles : kt;
+    int W = (int)((kt + 3) / 4);
+    W = W < 1 ? 1 : (W > 16 ? 16 : W);
+    const int T = (int)((kt + W - 1) / W);
+    const int MR = M == 1 ? 1 : 4;
+    const size_t lds = (size_t)wb_lds(M, (int)kt, W, MR);
+    if (T > 8 || lds > (size_t)kWbMaxLds) return hipErrorInvalidValue;   // rejected by the caller first
+    for (int i = 0; i < kMaxGemvBatch; ++i) b.first[i] = 0x7FFFFFFF;
+    for (int i = 0; i < count; ++i) {
+        GemvProblem &p = b.p[i];
+        p.codes = packed[i] + L[i].codes_off;
+        p.scales = packed[i] + L[i].scales_off;
+        p.zeros = L[i].asym ? packed[i] + L[i].zeros_off : nullptr;
+        p.x = x[i];
+        p.y = y[i];
+        p.N = (int)L[i].N;
+        p.K = (int)L[i].K;
+        p.ktiles = (int)L[i].ktiles;
+        p.strips = (int)L[i].strips;
+        p.tw = (int)((L[i].ktiles + W - 1) / W);
+        p.pad = 0;
+        b.first[i] = (int)strips;
+        strips += L[i].strips;
+    }
+    b.count = count;
+    b.M = M;
+    b.ct = 0;
+    b.W = W;
+    if (strips == 0) return hipSuccess;
+    const dim3 grid((unsigned)strips), block((unsigned)(W * 64));
+    const int G = L[0].G;
+    const bool asym = L[0].asym;
+    switch (L[0].bits) {
+    case 1: return wb_launch_bits<1>(G, asym, MR, T, b, grid, block, lds, s);
+    case 2: return wb_launch_bits<2>(G, asym, MR, T, b, grid, block, lds, s);
+    case 3: return wb_launch_bits<3>(G, asym, MR, T, b, grid, block, lds, s);
+    case 4: return wb_launch_bits<4>(G, asym, MR, T, b, grid, block, lds, s);
+    case 5: return wb_launch_bits<5>(G, asym, MR, T, b, grid, block, lds, s);
+    case 6: return wb_launch_bits<6>(G, asym, MR, T, b, grid, block, lds, s);
+    case 7: return wb_launch_bits<7>(G, asym, MR, T, b, grid, block, lds, s);
+    default: return wb_launch_bits<8>(G, asym, MR, T, b, grid, block, lds, s);
+    }
+}
+
+}  // namespace lowbit

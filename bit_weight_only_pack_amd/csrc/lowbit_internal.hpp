@@ -53,32 +53,54 @@ constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
 // end are padding: codes 0, scales 0, zeros 0.  Every section starts at a
 // 256-byte boundary.
 // ---------------------------------------------------------------------------
+//
+// Uniform b-bit codes (b = 1..8, formats LOWBIT_UINT) use the same tiles,
+// with 256 * b bytes per tile: lane l owns b consecutive dwords holding its
+// 32 codes (MFMA block i = 0..3, K offset j = 0..7) split into bit planes,
+// b = 4 n4 + 2 n2 + n1 (n4 <= 2, n2, n1 <= 1):
+//   n4 dwords per 4-bit plane (code bits 4p..4p+3 of plane p): dword i in the
+//     INT4 nibble slots above, so (w >> 4q) & 0x000F000F = K offsets 2q, 2q+1;
+//   2 dwords for the 2-bit plane (code bits 4 n4, +1): dword i / 2, the pair q
+//     of block i at bits 2 (4 (i & 1) + q) and 16 + 2 (4 (i & 1) + q);
+//   1 dword for the 1-bit plane (code bit 4 n4 + 2 n2): pair q of block i at
+//     bits 4 i + q and 16 + 4 i + q.
+// A shift and a mask therefore give two codes in the two 16-bit halves, ready
+// to be or-ed into fp16 1024.0.  At b = 4 the layout is the INT4 one.
+// ---------------------------------------------------------------------------
 struct W4Layout {
     int64_t N, K;
     int G;
     bool asym;
+    int bits;            // code width: 4 for the INT4 formats, 1..8 for LOWBIT_UINT
     int64_t strips;      // ceil(N / 16)
     int64_t ktiles;      // ceil(K / 128)
     int64_t codes_off, scales_off, zeros_off, bytes;
 };
 
-inline W4Layout w4_layout(int64_t N, int64_t K, int G, bool asym)
+inline W4Layout wb_layout(int64_t N, int64_t K, int G, int bits, bool asym)
 {
     W4Layout L;
-    L.N = N; L.K = K; L.G = G; L.asym = asym;
+    L.N = N; L.K = K; L.G = G; L.asym = asym; L.bits = bits;
     L.strips = (N + 15) / 16;
     L.ktiles = (K + 127) / 128;
     const int64_t tiles = L.strips * L.ktiles;
     const int64_t gpt = 128 / G;
     L.codes_off = 0;
-    L.scales_off = align256(tiles * 1024);
+    L.scales_off = align256(tiles * 256 * bits);
     L.zeros_off = align256(L.scales_off + tiles * 16 * gpt * 2);
     L.bytes = align256(L.zeros_off + (asym ? tiles * 16 * gpt : 0));
     return L;
 }
+inline W4Layout w4_layout(int64_t N, int64_t K, int G, bool asym) { return wb_layout(N, K, G, 4, asym); }
 
 // slot of the code of K offset j (0..7) inside a packed dword
 __host__ __device__ constexpr int w4_slot(int j) { return (j & 1) * 4 + (j >> 1); }
+
+// LOWBIT_UINT(bits, asym) = 16 + 2 * bits + asym
+constexpr int kUintBase = 16;
+inline bool is_uint_fmt(int fmt) { return fmt >= kUintBase + 2 && fmt <= kUintBase + 17; }
+inline int uint_bits(int fmt) { return (fmt - kUintBase) / 2; }
+inline bool uint_asym(int fmt) { return ((fmt - kUintBase) & 1) != 0; }
 
 // ---------------------------------------------------------------------------
 // Launchers (enqueue only; argument validation happens in api.hip).
@@ -88,6 +110,15 @@ hipError_t launch_w4_pack(const W4Layout &L, const uint8_t *codes, const uint16_
 hipError_t launch_w4_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *codes,
                             uint16_t *scales, int8_t *zeros, hipStream_t s);
 hipError_t launch_w4_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s);
+// b-bit codes (canonical: one code per byte, [N][K])
+hipError_t launch_wb_pack(const W4Layout &L, const uint8_t *codes, const uint16_t *scales, const int8_t *zeros,
+                          uint8_t *packed, hipStream_t s);
+hipError_t launch_wb_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *codes, uint16_t *scales,
+                            int8_t *zeros, hipStream_t s);
+hipError_t launch_wb_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s);
+hipError_t launch_gemv_wb_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
+                                const _Float16 *const *x, _Float16 *const *y, hipStream_t s);
+size_t gemv_wb_lds(int M, int64_t kt_max);    // 0: no kernel for this M and K
 
 // A batch of independent GEMVs with the same format, M and group size, run by
 // one launch (one workgroup per 16-row strip; blockIdx.y picks the problem).

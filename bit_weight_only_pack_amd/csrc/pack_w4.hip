@@ -1,5 +1,6 @@
-// pack_w4.hip -- offline re-pack of INT4 group-wise weights into the tiled
-// device layout, its inverse, and the fp32 dequant test hook.
+// pack_w4.hip -- offline re-pack of INT4 (and uniform b-bit) group-wise
+// weights into the tiled device layout, its inverse, and the fp32 dequant
+// test hook.
 //
 // Canonical input ("Low Bit Metal Kernels", int4_matmul step 2): row n of the
 // weight holds K codes, two per byte, the low nibble being the even K index.
@@ -134,7 +135,189 @@ __global__ void w4_dequant_kernel(const uint32_t *__restrict__ codes, const _Flo
     }
 }
 
+// ---- uniform b-bit codes: bit planes (layout in lowbit_internal.hpp) ----
+struct WbPlanes {
+    int n4, n2, n1;
+};
+__host__ __device__ inline WbPlanes wb_planes(int bits) { return WbPlanes{bits / 4, (bits % 4) >= 2 ? 1 : 0, bits & 1}; }
+
+// position of code bit `plane bit` for (block i, K offset j) inside the lane's
+// dwords: returns dword index and bit position
+__device__ inline void wb_bit(const WbPlanes &P, int i, int j, int cb, int &dw, int &pos)
+{
+    const int q = j >> 1, h = (j & 1) * 16;
+    if (cb < 4 * P.n4) {                                   // a 4-bit plane
+        dw = (cb / 4) * 4 + i;
+        pos = 4 * w4_slot(j) + (cb & 3);
+    } else if (P.n2 && cb < 4 * P.n4 + 2) {                // the 2-bit plane
+        dw = 4 * P.n4 + i / 2;
+        pos = h + 2 * (4 * (i & 1) + q) + (cb - 4 * P.n4);
+    } else {                                               // the 1-bit plane
+        dw = 4 * P.n4 + 2 * P.n2;
+        pos = h + 4 * i + q;
+    }
+}
+
+// one thread per (tile, lane): its 32 codes -> `bits` dwords
+__global__ void wb_pack_codes(const uint8_t *__restrict__ codes, uint32_t *__restrict__ out, int64_t N, int64_t K,
+                              int64_t ktiles, int bits, int64_t total)
+{
+    const int64_t d = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (d >= total) return;
+    const int64_t tile = d >> 6;
+    const int lane = (int)(d & 63);
+    const int64_t s = tile / ktiles, t = tile % ktiles;
+    const int64_t n = s * 16 + (lane & 15);
+    const WbPlanes P = wb_planes(bits);
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i) {
+        const int64_t kb = t * 128 + i * 32 + (lane >> 4) * 8;
+        if (n >= N || kb >= K) continue;                   // K % 32 == 0: the 8 codes are inside the row
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t c = codes[n * K + kb + j];
+            for (int cb = 0; cb < bits; ++cb) {
+                int dw, pos;
+                wb_bit(P, i, j, cb, dw, pos);
+                w[dw] |= ((c >> cb) & 1u) << pos;
+            }
+        }
+    }
+    for (int k = 0; k < bits; ++k) out[d * bits + k] = w[k];
+}
+
+__global__ void wb_unpack_codes(const uint32_t *__restrict__ in, uint8_t *__restrict__ codes, int64_t N, int64_t K,
+                                int64_t ktiles, int bits, int64_t total)
+{
+    const int64_t d = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (d >= total) return;
+    const int64_t tile = d >> 6;
+    const int lane = (int)(d & 63);
+    const int64_t s = tile / ktiles, t = tile % ktiles;
+    const int64_t n = s * 16 + (lane & 15);
+    const WbPlanes P = wb_planes(bits);
+    uint32_t w[8];
+    for (int k = 0; k < bits; ++k) w[k] = in[d * bits + k];
+    for (int i = 0; i < 4; ++i) {
+        const int64_t kb = t * 128 + i * 32 + (lane >> 4) * 8;
+        if (n >= N || kb >= K) continue;
+        for (int j = 0; j < 8; ++j) {
+            uint32_t c = 0;
+            for (int cb = 0; cb < bits; ++cb) {
+                int dw, pos;
+                wb_bit(P, i, j, cb, dw, pos);
+                c |= ((w[dw] >> pos) & 1u) << cb;
+            }
+            codes[n * K + kb + j] = (uint8_t)c;
+        }
+    }
+}
+
+// fp32 dequant, one thread per (tile, lane): w = (q - z) * s exact in fp32
+__global__ void wb_dequant_kernel(const uint32_t *__restrict__ in, const _Float16 *__restrict__ scales,
+                                  const int8_t *__restrict__ zeros, float *__restrict__ wout, int64_t N, int64_t K,
+                                  int G, int64_t ktiles, int bits, int64_t total)
+{
+    const int64_t d = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (d >= total) return;
+    const int64_t tile = d >> 6;
+    const int lane = (int)(d & 63);
+    const int r = lane & 15;
+    const int64_t s = tile / ktiles, t = tile % ktiles;
+    const int64_t n = s * 16 + r;
+    const WbPlanes P = wb_planes(bits);
+    const int gpt = 128 / G;
+    uint32_t w[8];
+    for (int k = 0; k < bits; ++k) w[k] = in[d * bits + k];
+    for (int i = 0; i < 4; ++i) {
+        const int64_t kb = t * 128 + i * 32 + (lane >> 4) * 8;
+        if (n >= N || kb >= K) continue;
+        const int64_t meta = (tile * 16 + r) * gpt + (i * 32) / G;
+        const float sc = (float)scales[meta];
+        const int z = zeros ? (int)zeros[meta] : (1 << (bits - 1));
+        for (int j = 0; j < 8; ++j) {
+            int c = 0;
+            for (int cb = 0; cb < bits; ++cb) {
+                int dw, pos;
+                wb_bit(P, i, j, cb, dw, pos);
+                c |= (int)((w[dw] >> pos) & 1u) << cb;
+            }
+            wout[n * K + kb + j] = (float)(c - z) * sc;
+        }
+    }
+}
+
+// zero-fill of the alignment gaps between sections
+void fill_gaps(const W4Layout &L, uint8_t *packed, hipStream_t s)
+{
+    const int64_t tiles = L.strips * L.ktiles;
+    const int64_t gpt = 128 / L.G;
+    const int64_t gaps[3][2] = {{L.codes_off + tiles * 256 * L.bits, L.scales_off},
+                                {L.scales_off + tiles * 16 * gpt * 2, L.zeros_off},
+                                {L.zeros_off + (L.asym ? tiles * 16 * gpt : 0), L.bytes}};
+    for (auto &g : gaps)
+        if (g[1] > g[0])
+            fill_zero<<<blocks_for(g[1] - g[0]), kThreads, 0, s>>>(packed + g[0], g[1] - g[0]);
+}
+
+void pack_meta(const W4Layout &L, const uint16_t *scales, const int8_t *zeros, uint8_t *packed, hipStream_t s)
+{
+    const int64_t nm = L.strips * L.ktiles * 16 * (128 / L.G);
+    if (nm == 0) return;
+    w4_pack_meta<uint16_t><<<blocks_for(nm), kThreads, 0, s>>>(
+        scales, reinterpret_cast<uint16_t *>(packed + L.scales_off), L.N, L.K, L.G, L.ktiles, nm);
+    if (L.asym)
+        w4_pack_meta<int8_t><<<blocks_for(nm), kThreads, 0, s>>>(
+            zeros, reinterpret_cast<int8_t *>(packed + L.zeros_off), L.N, L.K, L.G, L.ktiles, nm);
+}
+
+void unpack_meta(const W4Layout &L, const uint8_t *packed, uint16_t *scales, int8_t *zeros, hipStream_t s)
+{
+    const int64_t nm = L.strips * L.ktiles * 16 * (128 / L.G);
+    if (nm == 0) return;
+    w4_unpack_meta<uint16_t><<<blocks_for(nm), kThreads, 0, s>>>(
+        reinterpret_cast<const uint16_t *>(packed + L.scales_off), scales, L.N, L.K, L.G, L.ktiles, nm);
+    if (L.asym)
+        w4_unpack_meta<int8_t><<<blocks_for(nm), kThreads, 0, s>>>(
+            reinterpret_cast<const int8_t *>(packed + L.zeros_off), zeros, L.N, L.K, L.G, L.ktiles, nm);
+}
+
 }  // namespace
+
+hipError_t launch_wb_pack(const W4Layout &L, const uint8_t *codes, const uint16_t *scales, const int8_t *zeros,
+                          uint8_t *packed, hipStream_t s)
+{
+    const int64_t nl = L.strips * L.ktiles * 64;
+    if (nl > 0) {
+        wb_pack_codes<<<blocks_for(nl), kThreads, 0, s>>>(codes, reinterpret_cast<uint32_t *>(packed + L.codes_off),
+                                                          L.N, L.K, L.ktiles, L.bits, nl);
+        pack_meta(L, scales, zeros, packed, s);
+    }
+    fill_gaps(L, packed, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_wb_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *codes, uint16_t *scales,
+                            int8_t *zeros, hipStream_t s)
+{
+    const int64_t nl = L.strips * L.ktiles * 64;
+    if (nl == 0) return hipSuccess;
+    wb_unpack_codes<<<blocks_for(nl), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(packed + L.codes_off),
+                                                        codes, L.N, L.K, L.ktiles, L.bits, nl);
+    unpack_meta(L, packed, scales, zeros, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_wb_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s)
+{
+    const int64_t nl = L.strips * L.ktiles * 64;
+    if (nl == 0) return hipSuccess;
+    wb_dequant_kernel<<<blocks_for(nl), kThreads, 0, s>>>(
+        reinterpret_cast<const uint32_t *>(packed + L.codes_off),
+        reinterpret_cast<const _Float16 *>(packed + L.scales_off),
+        L.asym ? reinterpret_cast<const int8_t *>(packed + L.zeros_off) : nullptr, w, L.N, L.K, L.G, L.ktiles,
+        L.bits, nl);
+    return hipGetLastError();
+}
 
 hipError_t launch_w4_pack(const W4Layout &L, const uint8_t *codes, const uint16_t *scales,
                           const int8_t *zeros, uint8_t *packed, hipStream_t s)

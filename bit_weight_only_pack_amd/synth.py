@@ -59,6 +59,20 @@ def w4_weights(N, K, group_size, *, asym=False, scale_range=(0.002, 0.01), zero_
     return dict(qweight=qweight, scales=scales, zeros=zeros)
 
 
+def wb_weights(N, K, group_size, bits, *, asym=False, scale_range=(0.002, 0.01), workload_id=0, layer=0, part=0):
+    """Uniform b-bit weights (b = 1..8): codes u8 [N][K] uniform in [0, 2^b)
+    (one per byte), scales fp16 [N][K/G] uniform in scale_range, zeros int8
+    [N][K/G] uniform in [0, 2^b) clipped to 127 (asymmetric) or None."""
+    codes = rng(workload_id, T_CODES, layer, part).integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    lo, hi = scale_range
+    scales = rng(workload_id, T_SCALES, layer, part).uniform(lo, hi, size=(N, K // group_size)).astype(np.float16)
+    zeros = None
+    if asym:
+        zeros = np.minimum(rng(workload_id, T_ZEROS, layer, part).integers(0, 1 << bits, size=(N, K // group_size)),
+                           127).astype(np.int8)
+    return dict(codes=codes, scales=scales, zeros=zeros)
+
+
 def outlier_channels(K, frac=0.01, workload_id=0, layer=0, part=0):
     """round(frac*K) distinct channel indices chosen by seed (sorted)."""
     n = int(round(frac * K))

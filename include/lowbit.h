@@ -55,6 +55,11 @@ extern "C" {
 #define LOWBIT_W4_ASYM    1  /* INT4 codes, fp16 scale + int8 zero point / group */
 #define LOWBIT_LUT3_E4M3  2  /* 3-bit index into an 8-entry E4M3 codebook per
                                 8 outputs x 64 K tile, one UE8M0 exponent per tile */
+/* Uniform b-bit codes, b = 1..8 ("Low Bit ARM kernels": one unpack routine per
+ * bit width 1-8), fp16 scale per group, zero point 2^(b-1) (asym = 0) or an
+ * int8 zero point per group (asym = 1):  w = (q - z) * s, 0 <= q < 2^b.
+ * Canonical codes are one per byte (bits above b are ignored). */
+#define LOWBIT_UINT(bits, asym) (16 + 2 * (bits) + ((asym) ? 1 : 0))
 
 /* ---- activation / output element types --------------------------------- */
 #define LOWBIT_F16   0
@@ -98,6 +103,10 @@ size_t lowbit_packed_bytes(int fmt, int E, int N, int K, int group_size);
  *   scales : f16 [E][N][K/group_size]
  *   zeros  : i8  [E][N][K/group_size] for LOWBIT_W4_ASYM; must be NULL for
  *            LOWBIT_W4_SYM (zero point 8)
+ * LOWBIT_UINT(bits, asym) (same group sizes and shape rules as W4):
+ *   codes  : u8  [E][N][K]    one code per weight, 0 <= q < 2^bits
+ *   scales : f16 [E][N][K/group_size]
+ *   zeros  : i8  [E][N][K/group_size] when asym, else NULL (zero point 2^(bits-1))
  * LOWBIT_LUT3_E4M3 (group_size ignored, N % 8 == 0, K % 64 == 0):
  *   codes  : u8  [E][N][K]           one index 0..7 per weight
  *   scales : u8  [E][N/8][K/64][8]   E4M3 codebook of each 8 x 64 tile
@@ -120,9 +129,9 @@ int lowbit_unpack_weights(int fmt, int E, int N, int K, int group_size,
                           void *codes, void *scales, void *zeros, void *stream);
 
 /*
- * Dequantize one packed W4 matrix to fp32 (test hook):
+ * Dequantize one packed W4 or LOWBIT_UINT matrix to fp32 (test hook):
  *   w[n][k] = (q[n][k] - z) * s[n][k / group_size],  w_out f32 [N][K].
- * The product is exact in fp32 (|q - z| <= 143 has 8 significant bits, an
+ * The product is exact in fp32 (|q - z| <= 383 has 9 significant bits, an
  * fp16 scale 11), so the result is bit-identical to any exact evaluation.
  */
 int lowbit_dequant(int fmt, int N, int K, int group_size,
@@ -139,7 +148,9 @@ size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_si
  * Kernels", int4_matmul; "Low Bit ARM kernels", decode = GEMV):
  *   y[m][n] = sum_k x[m][k] * (q[n][k] - z) * s[n][k / group_size]
  * accumulated in fp32, rounded to nearest even into fp16.
- *   fmt     : LOWBIT_W4_SYM or LOWBIT_W4_ASYM
+ *   fmt     : LOWBIT_W4_SYM, LOWBIT_W4_ASYM or LOWBIT_UINT(bits, asym)
+ *             (b-bit codes: M * round_up(K, 512) halfs of x must fit 160 KiB
+ *             of LDS and K <= 16384, else LOWBIT_E_UNSUPPORTED)
  *   M       : 0..16 rows (tokens); larger M -> LOWBIT_E_UNSUPPORTED (use lowbit_gemm)
  *   packed  : blob from lowbit_pack_weights(fmt, 1, N, K, group_size, ...)
  *   x       : f16 [M][K], 16-byte aligned

@@ -210,3 +210,23 @@ def test_moe_layer_argument_checks():
     assert lb.lowbit_moe_layer(*args, FAKE + 128, wsb) == E_ARG                   # workspace alignment
     assert lb.lowbit_moe_layer(FAKE, FAKE, 128, 128, 2048, 736, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE,
                                FAKE, wsb) == E_ARG                                  # I % 64
+
+
+def test_uint_formats_host_rules():
+    """b-bit formats: packed size = tiles x 256 x bits + sections; invalid
+    widths and shapes rejected before any launch."""
+    for bits in range(1, 9):
+        tiles = (64 // 16) * (512 // 128)
+        assert lb.lowbit_packed_bytes(lb.LOWBIT_UINT(bits), 1, 64, 512, 128) == \
+            -(-tiles * 256 * bits // 256) * 256 + tiles * 16 * 2
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_UINT(4), 1, 64, 512, 128) == lb.lowbit_packed_bytes(SYM, 1, 64, 512, 128)
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_UINT(9), 1, 64, 512, 128) == 0
+    assert lb.lowbit_packed_bytes(lb.LOWBIT_UINT(3), 1, 64, 500, 128) == 0
+    f3 = lb.LOWBIT_UINT(3, True)
+    nb = lb.lowbit_packed_bytes(f3, 1, 64, 512, 32)
+    assert lb.lowbit_pack_weights(f3, 1, 64, 512, 32, FAKE, FAKE, None, FAKE, nb) == E_ARG    # asym needs zeros
+    assert lb.lowbit_gemv(f3, 17, 64, 512, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS
+    assert lb.lowbit_gemv(f3, 16, 64, 16384, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS            # x over the LDS budget
+    assert lb.lowbit_gemv(f3, 1, 64, 16384 + 128, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS       # > 8 tiles per wave
+    assert lb.lowbit_gemm(f3, 64, 64, 512, 32, FAKE, FAKE, lb.LOWBIT_BF16, FAKE, lb.LOWBIT_BF16, None, 0) == E_UNS
+    assert lb.lowbit_gemv_w4a8(f3, 1, 64, 512, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS
