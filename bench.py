@@ -23,6 +23,8 @@ Other workloads (--workload), one JSON line each:
                 (14336, 4096)}, bf16 in/out, symmetric G=128
   decode-w4a8 : the decode-asym step with dynamic per-token INT8 activations
                 (W4A8 on the int8 matrix cores), M in {1, 2, 4, 8}
+  decode-bits : the decode step with uniform b-bit weights (--bits, default
+                2,3,8; symmetric, G=128, M=1)
   moe         : a whole 3-bit LUT-codebook MoE layer, 128 experts, top-8 over
                 256 tokens, hidden 2048, intermediate 768: MXFP8 of the hidden
                 rows, alignment, gate/up GEMM, SiLU*up -> MXFP8, down GEMM,
@@ -391,6 +393,107 @@ def bench_decode_w4a8(args, torch, lb, synth):
     return out
 
 
+def wb_bytes(K, N, M, G, bits):
+    """Bytes a b-bit product must move at least once: codes (b/8 B/weight),
+    fp16 scales, fp16 input and output rows (symmetric: no zero points)."""
+    return N * K * bits // 8 + N * (K // G) * 2 + M * K * 2 + M * N * 2
+
+
+def build_step_wb(lb, synth, torch, bits, G, workload_id):
+    """The 224-GEMV step with uniform b-bit weights (symmetric), packed on the
+    GPU layer by layer; batched launches as in build_step."""
+    M = 1
+    fmt = lb.LOWBIT_UINT(bits)
+    projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
+    launches, keep = [], []
+    for layer in range(LAYERS):
+        for group in GROUPS_FUSED:
+            pid0, K0, _ = projs[group[0]]
+            x = torch.from_numpy(synth.activations_f16(M, K0, workload_id=workload_id, layer=layer, part=pid0)).cuda()
+            items = []
+            for name in group:
+                pid, K, N = projs[name]
+                w = synth.wb_weights(N, K, G, bits, workload_id=workload_id, layer=layer, part=pid)
+                nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
+                packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+                codes = torch.from_numpy(w["codes"]).cuda()
+                scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
+                lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, None, packed, nb))
+                y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                items.append((packed, x, y, N, K))
+                del codes, scales, w
+            keep.append(items)
+            launches.append(dict(names=group, probs=lb.make_gemv_problems(items), count=len(items),
+                                 bytes=sum(wb_bytes(K, N, M, G, bits) for (_, _, _, N, K) in items)))
+        torch.cuda.synchronize()
+    return fmt, launches, keep
+
+
+def bench_decode_bits(args, torch, lb, synth):
+    """The 8B decode step (M = 1, symmetric, G = 128) with uniform b-bit
+    weights for each b of --bits; fewer bits stream fewer bytes."""
+    G, M, wid = 128, 1, 6
+    res = {}
+    ref = None
+    for bits in [int(v) for v in args.bits.split(",")]:
+        fmt, launches, keep = build_step_wb(lb, synth, torch, bits, G, wid)
+        step_bytes = sum(L["bytes"] for L in launches)
+        stream = torch.cuda.Stream()
+        graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
+        ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
+        med = time_launches(torch, lb, fmt, M, G, launches, stream, 2)
+        groups = {}
+        for L, t in zip(launches, med):
+            groups.setdefault("+".join(L["names"]), []).append(t)
+        res["b=%d" % bits] = dict(ms_per_step=round(ms, 4), GBps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                                  tokens_per_s=round(1e3 / ms, 1), bytes_per_step=step_bytes,
+                                  bytes_per_weight=bits / 8 + 2 / G,
+                                  per_launch_us={k: round(float(np.mean(v)), 2) for k, v in groups.items()})
+        if ref is None or bits == 3:
+            n = len(launches)
+            ref = dict(bits=bits, gpu_ms=gpu_ms, bytes=step_bytes, n=n)
+        del graph, keep, launches
+        torch.cuda.empty_cache()
+    avg_us = ref["gpu_ms"] * 1e3 / ref["n"]
+    bpl = ref["bytes"] / ref["n"]
+    ach = bpl / (avg_us * 1e-6) / 1e9
+    key = "b=%d" % ref["bits"]
+    out = {"metric": "b-bit decode step effective HBM GB/s and tokens/s at 8B shapes", "value": res[key]["GBps"],
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res[key]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic (seeded; uniform b-bit codes, U[0.002,0.01] fp16 scales, N(0,1) fp16 inputs)",
+           "config": {"workload": "llama3-8b-uint-decode-step", "bits": [int(v) for v in args.bits.split(",")],
+                      "value_bits": ref["bits"], "M": M, "group_size": G, "launches_per_step": ref["n"]},
+           "tokens_per_s": res[key]["tokens_per_s"],
+           "pct_of_hbm_peak": round(100 * res[key]["GBps"] / HBM_PEAK_GBPS, 2),
+           "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "gemv_wb (b=%d, G=128, sym, M=1)" % ref["bits"], "bytes_per_launch": round(bpl),
+                        "avg_launch_us": round(avg_us, 3)},
+           "per_bits": res}
+    if args.cpu_layers > 0:
+        import oracle
+        projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
+        t_total, nbytes = 0.0, 0
+        for group in GROUPS_FUSED:
+            pid0, K0, _ = projs[group[0]]
+            x = synth.activations_f16(M, K0, workload_id=wid, layer=0, part=pid0)
+            for name in group:
+                pid, K, N = projs[name]
+                w = synth.wb_weights(N, K, G, ref["bits"], workload_id=wid, layer=0, part=pid)
+                t0 = time.perf_counter()
+                oracle.wb_matmul(x, w["codes"], w["scales"], None, ref["bits"], G)
+                t_total += time.perf_counter() - t0
+                nbytes += wb_bytes(K, N, M, G, ref["bits"])
+        out["cpu_baseline"] = {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "layer 0 of the step at b=%d (7 GEMVs, %.1f MB), one thread, %.1f s"
+                                         % (ref["bits"], nbytes / 1e6, t_total),
+                               "tokens_per_s": round(1 / LAYERS / t_total, 6)}
+    return out
+
+
 def bench_prefill(args, torch, lb, synth):
     fmt, G = lb.LOWBIT_W4_SYM, 128
     res = {}
@@ -546,7 +649,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-asym", "decode-w4a8", "prefill", "moe"])
+                    choices=["decode", "decode-asym", "decode-w4a8", "decode-bits", "prefill", "moe"])
     ap.add_argument("--mode", default="batched", choices=["chain", "batched", "unfused"],
                     help="decode: chain = the whole step as one persistent launch with stage dependencies; "
                          "batched = one launch per group of GEMVs sharing an input (4 per layer); "
@@ -554,6 +657,7 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=4, help="decode: layers the CPU oracle runs (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
     ap.add_argument("--m-list", default="1,2,4,8", help="decode-w4a8: token counts to run (must include 1)")
+    ap.add_argument("--bits", default="2,3,8", help="decode-bits: code widths to run (1..8)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (a kernel of known traffic for counter runs)")
     args = ap.parse_args()
@@ -575,7 +679,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "decode-w4a8": bench_decode_w4a8,
-          "prefill": bench_prefill, "moe": bench_moe}[args.workload]
+          "decode-bits": bench_decode_bits, "prefill": bench_prefill, "moe": bench_moe}[args.workload]
     print(json.dumps(fn(args, torch, lb, synth)), flush=True)
 
 
