@@ -257,7 +257,7 @@ int lowbit_gemv_batched(int fmt, int M, int group_size, int count, const lowbit_
         ++n;
     }
     if (is_uint_fmt(fmt)) {
-        if (n > 0 && gemv_wb_lds(M, kt_max) == 0) return LOWBIT_E_UNSUPPORTED;
+        if (n > 0 && gemv_wb_lds(M, kt_max, uint_asym(fmt)) == 0) return LOWBIT_E_UNSUPPORTED;
         return hip_status(launch_gemv_wb_batch(L, n, M, packed, x, y, (hipStream_t)stream));
     }
     return hip_status(launch_gemv_w4_batch(L, n, M, packed, x, y, (hipStream_t)stream));

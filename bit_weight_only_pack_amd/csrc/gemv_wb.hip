@@ -12,7 +12,8 @@
 // A shift and a mask of a plane dword give two codes in the two 16-bit halves;
 // or-ed together and into fp16 1024.0 they form 1024 + q exactly (q <= 255),
 // which feeds the offset-split product of gemv_tile.hpp: x.(1024 + q) -
-// x.(1024 + z) by two MFMA chains over the same activations, so codes equal
+// x.(1024 + z) by two MFMA chains over the same activations (at batch 1 with
+// symmetric weights one chain of offsets serves four tiles), so codes equal
 // to the zero point give exactly zero.
 #include "lowbit_internal.hpp"
 #include "gemv_tile.hpp"
@@ -25,8 +26,16 @@ using namespace tile;
 
 constexpr int kWbMaxLds = 160 * 1024;
 
-__host__ __device__ inline int wb_rowp(int kt) { return (int)round_up((int64_t)kt * 16, 64); }
-__host__ __device__ inline int wb_lds(int M, int kt, int W, int MR) { return M * wb_rowp(kt) * 16 + W * MR * 64 * 4; }
+// 16-byte blocks per K tile of a row of x in LDS: 16, or 20 for the batch-1
+// symmetric form, whose shared offset chain reads the same block of four
+// consecutive tiles at once (the 64-byte pad puts those reads in different
+// banks)
+__host__ __device__ constexpr int wb_tile_blocks(bool pre) { return pre ? 20 : 16; }
+__host__ __device__ inline int wb_rowp(int kt, bool pre) { return (int)round_up((int64_t)kt * wb_tile_blocks(pre), 64); }
+__host__ __device__ inline int wb_lds(int M, int kt, int W, int MR, bool pre)
+{
+    return M * wb_rowp(kt, pre) * 16 + W * MR * 64 * 4;
+}
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t *lds, uint32_t off)
 {
@@ -49,20 +58,24 @@ struct WbTile {
     uint32_t c;
 };
 
+// tile base byte offset `base`; each plane is a lane-major region of the tile
 template <int BITS>
-__device__ __forceinline__ WbTile<BITS> load_wb(__amdgpu_buffer_rsrc_t rs, bool ok, uint32_t base)
+__device__ __forceinline__ WbTile<BITS> load_wb(__amdgpu_buffer_rsrc_t rs, bool ok, uint32_t base, int lane)
 {
     using TT = WbTile<BITS>;
     TT w;
 #pragma unroll
     for (int p = 0; p < TT::N4; ++p)
-        w.a[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + 16 * p : kBufferOob, 0, kStreamLoad);
+        w.a[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + 1024 * p + lane * 16 : kBufferOob, 0,
+                                                       kStreamLoad);
     if constexpr (TT::N2) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? base + 16 * TT::N4 : kBufferOob, 0, kStreamLoad);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? base + 1024 * TT::N4 + lane * 8 : kBufferOob, 0,
+                                                            kStreamLoad);
         w.b = make_uint2(v[0], v[1]);
     }
     if constexpr (TT::N1)
-        w.c = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? base + 16 * TT::N4 + 8 * TT::N2 : kBufferOob, 0, kStreamLoad);
+        w.c = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, ok ? base + 1024 * TT::N4 + 512 * TT::N2 + lane * 4 : kBufferOob, 0, kStreamLoad);
     return w;
 }
 
@@ -76,24 +89,35 @@ __device__ __forceinline__ void pin_wb(WbTile<BITS> &w)
     if constexpr (TT::N1) asm volatile("" : "+v"(w.c));
 }
 
-// MFMA block i (K offsets 0..7 of the lane's 8-K slice) -> 8 fp16 1024 + q
-template <int BITS>
-__device__ __forceinline__ h8 wb_operand(const WbTile<BITS> &w, int i, uint32_t magic)
+// the bits of a plane that sit at position `src` of each 16-bit half, moved to
+// position `dst`: one shift (none when equal) and a mask
+template <int SRC, int DST, uint32_t MASK>
+__device__ __forceinline__ uint32_t plane_bits(uint32_t w)
+{
+    if constexpr (SRC > DST) return (w >> (SRC - DST)) & (MASK << DST);
+    else if constexpr (SRC < DST) return (w << (DST - SRC)) & (MASK << DST);
+    else return w & (MASK << DST);
+}
+
+// MFMA block I (K offsets 0..7 of the lane's 8-K slice), pair Q -> two fp16
+// 1024 + q: each plane's pair, shifted into place, or-ed into 1024.0
+template <int BITS, int I, int Q>
+__device__ __forceinline__ uint32_t wb_pair(const WbTile<BITS> &w, uint32_t magic)
 {
     using TT = WbTile<BITS>;
-    u4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t r = magic;
-        if constexpr (TT::N4 >= 1) r |= (w.a[0][i] >> (4 * q)) & 0x000F000Fu;
-        if constexpr (TT::N4 >= 2) r |= ((w.a[1][i] >> (4 * q)) & 0x000F000Fu) << 4;
-        if constexpr (TT::N2) {
-            const uint32_t bw = (i >> 1) ? w.b.y : w.b.x;
-            r |= ((bw >> (2 * (4 * (i & 1) + q))) & 0x00030003u) << (4 * TT::N4);
-        }
-        if constexpr (TT::N1) r |= ((w.c >> (4 * i + q)) & 0x00010001u) << (4 * TT::N4 + 2 * TT::N2);
-        v[q] = r;
-    }
+    uint32_t r = magic;
+    if constexpr (TT::N4 >= 1) r |= plane_bits<4 * Q, 0, 0x000F000Fu>(w.a[0][I]);
+    if constexpr (TT::N4 >= 2) r |= plane_bits<4 * Q, 4, 0x000F000Fu>(w.a[1][I]);
+    if constexpr (TT::N2) r |= plane_bits<2 * (4 * (I & 1) + Q), 4 * TT::N4, 0x00030003u>((I >> 1) ? w.b.y : w.b.x);
+    if constexpr (TT::N1) r |= plane_bits<4 * I + Q, 4 * TT::N4 + 2 * TT::N2, 0x00010001u>(w.c);
+    return r;
+}
+
+template <int BITS, int I>
+__device__ __forceinline__ h8 wb_operand(const WbTile<BITS> &w, uint32_t magic)
+{
+    const u4 v = {wb_pair<BITS, I, 0>(w, magic), wb_pair<BITS, I, 1>(w, magic), wb_pair<BITS, I, 2>(w, magic),
+                  wb_pair<BITS, I, 3>(w, magic)};
     return __builtin_bit_cast(h8, v);
 }
 
@@ -112,6 +136,9 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     using TT = WbTile<BITS>;
     constexpr int GPT = 128 / G;
     constexpr int MPG = G / 32;
+    constexpr bool PRE = !ASYM && MR == 1;                  // shared offset chain (batch 1, symmetric)
+    constexpr int TB = wb_tile_blocks(PRE);
+    constexpr int TPS = 4 / GPT;                            // tiles per offset set
     constexpr int NLD = TT::N4 + TT::N2 + TT::N1;           // code loads per tile
     constexpr int NW = T * (NLD + (ASYM ? 2 : 1));           // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -119,19 +146,21 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, kq = lane >> 4;
     const int t0 = wave * tw;
-    const int rowp = wb_rowp(kt);
+    const int rowp = wb_rowp(kt, PRE);
     float *red = reinterpret_cast<float *>(smem + M * rowp * 16);
 
-    // 1. x -> LDS: block bb of tile t of row m holds x[m][128 t + 8 (bb ^ (m & 15)) ..]
+    // 1. x -> LDS: block bb < 16 of tile t of row m holds
+    //    x[m][128 t + 8 (bb ^ (m & 15)) ..], blocks 16..TB-1 are zero padding
     {
         const auto xrs = buffer_rsrc(xg, (uint32_t)(M * K * 2));
         const int cpr = rowp >> 6;
         for (int m = 0; m < M; ++m)
             for (int cc = wave; cc < cpr; cc += W) {
                 const int jj = cc * 64 + lane;
-                const int t = jj >> 4, bb = jj & 15;
+                const int t = jj / TB, bb = jj - t * TB;
                 const int j = t * 16 + (bb ^ (m & 15));
-                lds_dma16(xrs, smem + (m * cpr + cc) * 1024, j * 8 < K ? (uint32_t)((m * K + j * 8) * 2) : kBufferOob);
+                const bool ok = bb < 16 && j * 8 < K;
+                lds_dma16(xrs, smem + (m * cpr + cc) * 1024, ok ? (uint32_t)((m * K + j * 8) * 2) : kBufferOob);
             }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -148,7 +177,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
         for (int u = 0; u < T; ++u) {
             const int t = t0 + u;
             const bool ok = u < tw && t < kt;
-            q[u] = load_wb<BITS>(crs, ok, (uint32_t)(t * 64 + lane) * 4 * BITS);
+            q[u] = load_wb<BITS>(crs, ok, (uint32_t)t * 256 * BITS, lane);
             mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -171,18 +200,40 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     const _Float16 *xa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * rowp + t0 * 16 + ((i * 4 + kq) ^ (xr & 15))) * 8;
+        xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * rowp + t0 * TB + ((i * 4 + kq) ^ (xr & 15))) * 8;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // batch 1, symmetric: x . p does not depend on the codes or the weight
+    // row, so one MFMA chain computes it for several tiles, its A rows 0..3
+    // carrying the K blocks of (tile u0 + j / GPT, group j % GPT); C row j is
+    // exactly what a per-tile chain would give (same products, same order)
+    f4 cps = zero4;
     const int tvalid = min(tw, kt - t0);
 #pragma unroll
     for (int u = 0; u < T; ++u) {
         if (u < tvalid) {
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PRE) {
+                if (u % TPS == 0) {
+                    const int rr = r < 4 ? r : 0;
+                    const int tu = min(u + rr / GPT, tvalid - 1);
+                    const int g = rr % GPT;
+                    const _Float16 *xb = reinterpret_cast<const _Float16 *>(smem) + ((t0 + tu) * TB + g * MPG * 4 + kq) * 8;
+#pragma unroll
+                    for (int i = 0; i < MPG; ++i)
+                        cps = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8 *>(xb + i * 32), psym,
+                                                                     i == 0 ? zero4 : cps, 0, 0, 0);
+                }
+            }
             TT w = q[u];
             pin_wb<BITS>(w);
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
+            h8 vs[4];
+            vs[0] = wb_operand<BITS, 0>(w, magic);
+            vs[1] = wb_operand<BITS, 1>(w, magic);
+            vs[2] = wb_operand<BITS, 2>(w, magic);
+            vs[3] = wb_operand<BITS, 3>(w, magic);
             f4 cv = zero4, cp = zero4;
             h8 p = psym;
 #pragma unroll
@@ -197,17 +248,20 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
                         p = wb_offset((int)(int8_t)(uint8_t)zb);
                     }
                 }
-                const h8 a = *reinterpret_cast<const h8 *>(xa[i] + u * 128);
-                const h8 v = wb_operand<BITS>(w, i, magic);
-                cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, v, (i % MPG == 0) ? zero4 : cv, 0, 0, 0);
-                cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p, (i % MPG == 0) ? zero4 : cp, 0, 0, 0);
+                const h8 a = *reinterpret_cast<const h8 *>(xa[i] + u * TB * 8);
+                cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, vs[i], (i % MPG == 0) ? zero4 : cv, 0, 0, 0);
+                if constexpr (!PRE) cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p, (i % MPG == 0) ? zero4 : cp, 0, 0, 0);
                 if (i % MPG == MPG - 1) {
                     uint16_t hb;
                     if constexpr (G == 128) hb = (uint16_t)(mv.s[0] >> (16 * (r & 1)));
                     else hb = (uint16_t)(mv.s[g / 2] >> (16 * (g & 1)));
                     const float sc = (float)__builtin_bit_cast(_Float16, hb);
+                    if constexpr (PRE) {
+                        acc[0] = __builtin_fmaf(sc, cv[0] - cps[(u % TPS) * GPT + g], acc[0]);
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < MR; ++j) acc[j] = __builtin_fmaf(sc, cv[j] - cp[j], acc[j]);
+                        for (int j = 0; j < MR; ++j) acc[j] = __builtin_fmaf(sc, cv[j] - cp[j], acc[j]);
+                    }
                 }
             }
         }
@@ -243,7 +297,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
 }
 
 template <int BITS, int G, bool ASYM, int MR, int T>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : 6)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1 && BITS <= 4) ? 8 : 6)))
 void gemv_wb_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
                     int kt, int tw, int M, int W, const uint8_t *zeros)
 {
@@ -253,7 +307,7 @@ void gemv_wb_single(const uint8_t *codes, const uint8_t *scales, const _Float16 
 // problems laid end to end over blockIdx.x (b.first[i] = first workgroup of
 // problem i; unused entries hold INT_MAX)
 template <int BITS, int G, bool ASYM, int MR, int T>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : 6)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1 && BITS <= 4) ? 8 : 6)))
 void gemv_wb_batch(const GemvBatch b)
 {
     const int bx = (int)blockIdx.x;
@@ -320,13 +374,13 @@ hipError_t wb_launch_bits(int G, bool asym, int MR, int T, const GemvBatch &b, d
 
 // LDS the b-bit GEMV needs for M rows over the widest problem (0 if it has
 // no kernel for it: more than 8 tiles per wave or more than 160 KiB)
-size_t gemv_wb_lds(int M, int64_t kt_max)
+size_t gemv_wb_lds(int M, int64_t kt_max, bool asym)
 {
     int W = (int)((kt_max + 3) / 4);
     W = W < 1 ? 1 : (W > 16 ? 16 : W);
     const int64_t T = (kt_max + W - 1) / W;
     const int MR = M == 1 ? 1 : 4;
-    const int64_t lds = wb_lds(M, (int)kt_max, W, MR);
+    const int64_t lds = wb_lds(M, (int)kt_max, W, MR, !asym && MR == 1);
     return (T > 8 || lds > kWbMaxLds) ? 0 : (size_t)lds;
 }
 
@@ -341,7 +395,7 @@ hipError_t launch_gemv_wb_batch(const W4Layout *L, int count, int M, const uint8
     W = W < 1 ? 1 : (W > 16 ? 16 : W);
     const int T = (int)((kt + W - 1) / W);
     const int MR = M == 1 ? 1 : 4;
-    const size_t lds = (size_t)wb_lds(M, (int)kt, W, MR);
+    const size_t lds = (size_t)wb_lds(M, (int)kt, W, MR, !L[0].asym && MR == 1);
     if (T > 8 || lds > (size_t)kWbMaxLds) return hipErrorInvalidValue;   // rejected by the caller first
     for (int i = 0; i < kMaxGemvBatch; ++i) b.first[i] = 0x7FFFFFFF;
     for (int i = 0; i < count; ++i) {

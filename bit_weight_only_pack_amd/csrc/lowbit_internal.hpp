@@ -55,17 +55,29 @@ constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
 // ---------------------------------------------------------------------------
 //
 // Uniform b-bit codes (b = 1..8, formats LOWBIT_UINT) use the same tiles,
-// with 256 * b bytes per tile: lane l owns b consecutive dwords holding its
-// 32 codes (MFMA block i = 0..3, K offset j = 0..7) split into bit planes,
-// b = 4 n4 + 2 n2 + n1 (n4 <= 2, n2, n1 <= 1):
-//   n4 dwords per 4-bit plane (code bits 4p..4p+3 of plane p): dword i in the
-//     INT4 nibble slots above, so (w >> 4q) & 0x000F000F = K offsets 2q, 2q+1;
-//   2 dwords for the 2-bit plane (code bits 4 n4, +1): dword i / 2, the pair q
-//     of block i at bits 2 (4 (i & 1) + q) and 16 + 2 (4 (i & 1) + q);
-//   1 dword for the 1-bit plane (code bit 4 n4 + 2 n2): pair q of block i at
-//     bits 4 i + q and 16 + 4 i + q.
+// with 256 * b bytes per tile.  A lane's 32 codes (MFMA block i = 0..3, K
+// offset j = 0..7) are split into bit planes, b = 4 n4 + 2 n2 + n1 (n4 <= 2,
+// n2, n1 <= 1), and each plane is its own region of the tile, lane-major, so
+// every load of a wave is one dense span:
+//   4-bit plane p (code bits 4p..4p+3), 1 KiB at 1024 p: 4 dwords per lane,
+//     dword i in the INT4 nibble slots above, so (w >> 4q) & 0x000F000F holds
+//     K offsets 2q, 2q+1;
+//   2-bit plane (code bits 4 n4, +1), 512 B after the 4-bit planes: 2 dwords
+//     per lane, dword i / 2 holds the pair q of block i at bits
+//     2 (4 (i & 1) + q) and 16 + 2 (4 (i & 1) + q);
+//   1-bit plane (code bit 4 n4 + 2 n2), 256 B last: 1 dword per lane, the
+//     pair q of block i at bits 4 i + q and 16 + 4 i + q.
 // A shift and a mask therefore give two codes in the two 16-bit halves, ready
 // to be or-ed into fp16 1024.0.  At b = 4 the layout is the INT4 one.
+// dword index inside a tile of plane dword k (0..b-1) of lane l
+__host__ __device__ inline int wb_word(int bits, int lane, int k)
+{
+    const int n4 = bits / 4, n2 = (bits % 4) >= 2 ? 1 : 0;
+    if (k < 4 * n4) return (k / 4) * 256 + lane * 4 + (k % 4);
+    k -= 4 * n4;
+    if (k < 2 * n2) return n4 * 256 + lane * 2 + k;
+    return n4 * 256 + n2 * 128 + lane;
+}
 // ---------------------------------------------------------------------------
 struct W4Layout {
     int64_t N, K;
@@ -118,7 +130,7 @@ hipError_t launch_wb_unpack(const W4Layout &L, const uint8_t *packed, uint8_t *c
 hipError_t launch_wb_dequant(const W4Layout &L, const uint8_t *packed, float *w, hipStream_t s);
 hipError_t launch_gemv_wb_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
                                 const _Float16 *const *x, _Float16 *const *y, hipStream_t s);
-size_t gemv_wb_lds(int M, int64_t kt_max);    // 0: no kernel for this M and K
+size_t gemv_wb_lds(int M, int64_t kt_max, bool asym);    // 0: no kernel for this M and K
 
 // A batch of independent GEMVs with the same format, M and group size, run by
 // one launch (one workgroup per 16-row strip; blockIdx.y picks the problem).

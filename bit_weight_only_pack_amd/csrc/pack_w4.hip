@@ -182,7 +182,7 @@ __global__ void wb_pack_codes(const uint8_t *__restrict__ codes, uint32_t *__res
             }
         }
     }
-    for (int k = 0; k < bits; ++k) out[d * bits + k] = w[k];
+    for (int k = 0; k < bits; ++k) out[tile * 64 * bits + wb_word(bits, lane, k)] = w[k];
 }
 
 __global__ void wb_unpack_codes(const uint32_t *__restrict__ in, uint8_t *__restrict__ codes, int64_t N, int64_t K,
@@ -196,7 +196,7 @@ __global__ void wb_unpack_codes(const uint32_t *__restrict__ in, uint8_t *__rest
     const int64_t n = s * 16 + (lane & 15);
     const WbPlanes P = wb_planes(bits);
     uint32_t w[8];
-    for (int k = 0; k < bits; ++k) w[k] = in[d * bits + k];
+    for (int k = 0; k < bits; ++k) w[k] = in[tile * 64 * bits + wb_word(bits, lane, k)];
     for (int i = 0; i < 4; ++i) {
         const int64_t kb = t * 128 + i * 32 + (lane >> 4) * 8;
         if (n >= N || kb >= K) continue;
@@ -227,7 +227,7 @@ __global__ void wb_dequant_kernel(const uint32_t *__restrict__ in, const _Float1
     const WbPlanes P = wb_planes(bits);
     const int gpt = 128 / G;
     uint32_t w[8];
-    for (int k = 0; k < bits; ++k) w[k] = in[d * bits + k];
+    for (int k = 0; k < bits; ++k) w[k] = in[tile * 64 * bits + wb_word(bits, lane, k)];
     for (int i = 0; i < 4; ++i) {
         const int64_t kb = t * 128 + i * 32 + (lane >> 4) * 8;
         if (n >= N || kb >= K) continue;
