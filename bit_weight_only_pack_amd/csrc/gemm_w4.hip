@@ -154,46 +154,48 @@ void gemm_w4_v2_kernel(GemmArgs p)
     const auto zrs = buffer_rsrc(ASYM ? p.zeros : p.scales,
                                  ASYM ? (uint32_t)((int64_t)strips_total * p.ktiles * 16 * GPT) : 0u);
 
-    // issue the loads of K tile kt into stage st (a tile past kt1 loads zeros)
-    auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+    // load `part` of K tile kt into stage st (a tile past kt1 loads zeros):
+    // parts 0-3 the A rows, 4-5 the B strips, 6 the scales, 7 the zero points
+    auto issue_part = [&](int kt, int st, int part) __attribute__((always_inline)) {
         uint8_t *sa = smem + st * SB;
         uint8_t *sb = sa + kV2AStage;
         uint8_t *sm = sb + kV2BStage;
         const bool live = kt < kt1;
-        // A: instruction i of wave w fills LDS rows 4(4w + i) .. +3, lane -> (row, stored chunk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        if (part < 4) {
+            // A: instruction i of wave w fills LDS rows 4(4w + i) .. +3, lane -> (row, stored chunk)
+            const int i = part;
             const int row = (wave * 4 + i) * 4 + (lane >> 4);
             const int pos = lane & 15;
             const int chunk = pos ^ (row & 15);
             const int k = kt * 128 + chunk * 8;
             const bool ok = live && m0 + row < p.M && k < p.K;
             v2_dma<16>(ars, sa + (wave * 4 + i) * 1024,
-                   ok ? (uint32_t)(((int64_t)(m0 + row) * p.K + k) * 2) : kBufferOob);
-        }
-        // B: wave w loads strips 2w, 2w + 1 of the tile's 16
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
+                       ok ? (uint32_t)(((int64_t)(m0 + row) * p.K + k) * 2) : kBufferOob);
+        } else if (part < 6) {
+            // B: wave w loads strips 2w, 2w + 1 of the tile's 16
+            const int j = part - 4;
             const int s = n0 / 16 + wave * 2 + j;
             const bool ok = live && s < strips_total;
             v2_dma<16>(crs, sb + (wave * 2 + j) * 1024,
-                   ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 1024 + lane * 16) : kBufferOob);
-        }
-        // scales of those two strips: 2 x 32*GPT bytes, 4 bytes per lane
-        {
+                       ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 1024 + lane * 16) : kBufferOob);
+        } else if (part == 6) {
+            // scales of those two strips: 2 x 32*GPT bytes, 4 bytes per lane
             const int b = lane * 4, j = b / (32 * GPT), off = b - j * 32 * GPT;
             const int s = n0 / 16 + wave * 2 + j;
             const bool ok = live && j < 2 && s < strips_total;
             v2_dma<4>(srs, sm + wave * 256,
-                   ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 32 * GPT + off) : kBufferOob);
-        }
-        if constexpr (ASYM) {
+                      ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 32 * GPT + off) : kBufferOob);
+        } else if constexpr (ASYM) {
             const int b = lane * 4, j = b / (16 * GPT), off = b - j * 16 * GPT;
             const int s = n0 / 16 + wave * 2 + j;
             const bool ok = live && j < 2 && s < strips_total;
             v2_dma<4>(zrs, sm + kV2MStage + wave * 256,
-                   ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 16 * GPT + off) : kBufferOob);
+                      ok ? (uint32_t)(((int64_t)s * p.ktiles + kt) * 16 * GPT + off) : kBufferOob);
         }
+    };
+    auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int part = 0; part < NDMA; ++part) issue_part(kt, st, part);
     };
 
     f4 acc[TM][TN];
@@ -208,81 +210,199 @@ void gemm_w4_v2_kernel(GemmArgs p)
     u4 psym = neg_offset(A_BF16, 8);
     asm volatile("" : "+v"(psym));
 
-    // prologue: stages 0 .. kV2Stages-2
-#pragma unroll
-    for (int s = 0; s < kV2Stages - 1; ++s) issue(kt0 + s, s);
+    auto mfma = [&](const u4 &a, const u4 &b, const f4 &c) __attribute__((always_inline)) {
+        if constexpr (A_BF16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b),
+                                                           c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c,
+                                                          0, 0, 0);
+    };
 
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int st = (kt - kt0) % kV2Stages;
-        v2_wait_vm<NDMA * (kV2Stages - 2)>();          // this wave's loads of stage st landed
-        v2_barrier();                                  // every wave's; stage (st + 2) % 3 free
-        issue(kt + kV2Stages - 1, (st + kV2Stages - 1) % kV2Stages);
+    if constexpr (G == 128) {
+        // Two phases per K tile.  Memory phase: start the loads of the tile two
+        // steps ahead, read this tile's B codes, scales and A operands from LDS
+        // and unpack B.  Compute phase: the tile's MFMAs, then the blocks' scale
+        // FMAs (written beside the next block's run; the compiler gathers them at
+        // the end of the phase).  The wave group wm = 1 runs one phase behind
+        // wm = 0, and waves w and w + 4 share a SIMD, so on every SIMD one wave
+        // reads and unpacks while the other keeps the matrix core busy; a
+        // barrier closes every phase, and the compute phase runs at raised wave
+        // priority.
+        // Stage (kt + 2) % 3 is refilled in tile kt's memory phase: group 0 read
+        // it two phases earlier, group 1 one phase earlier (its LDS reads
+        // complete before that barrier).  Tile kt + 1 must have landed before
+        // the barrier that opens group 0's next memory phase: group 0 waits for
+        // its loads at the end of its compute phase, group 1 at the end of its
+        // memory phase, each with one tile's loads still in flight.
+        static_assert(kV2Stages == 3, "the phase schedule refills stage (kt + 2) % 3");
+        const int grp = wm;
+        issue(kt0, 0);
+        issue(kt0 + 1, 1);
+        v2_wait_vm<NDMA>();
+        v2_barrier();
+        if (grp == 1) v2_barrier();
 
-        const uint8_t *sa = smem + st * SB;
-        const uint8_t *sb = sa + kV2AStage;
-        const uint8_t *sm = sb + kV2BStage;
-        // this wave's B strips (wn * 4 + nb) and their metadata
-        u4 bq[TN];
+        for (int kt = kt0; kt < kt1; ++kt) {
+            const int st = (kt - kt0) % kV2Stages;
+            issue(kt + 2, (st + 2) % kV2Stages);
+            const uint8_t *sa = smem + st * SB;
+            const uint8_t *sb = sa + kV2AStage;
+            const uint8_t *sm = sb + kV2BStage;
+            u4 bq[TN];
 #pragma unroll
-        for (int nb = 0; nb < TN; ++nb) bq[nb] = *reinterpret_cast<const u4 *>(sb + (wn * 4 + nb) * 1024 + lane * 16);
-
-#pragma unroll
-        for (int g = 0; g < GPT; ++g) {
+            for (int nb = 0; nb < TN; ++nb) bq[nb] = *reinterpret_cast<const u4 *>(sb + (wn * 4 + nb) * 1024 + lane * 16);
             float sc[TN];
-            u4 pneg[TN];
+            u4 pn[TN];                                 // asymmetric: negated offset operands
 #pragma unroll
             for (int nb = 0; nb < TN; ++nb) {
                 const int s = wn * 4 + nb;             // strip in the tile; its loader wave = s / 2
-                const uint8_t *ms = sm + (s >> 1) * 256 + (s & 1) * 32 * GPT;
-                sc[nb] = (float)*reinterpret_cast<const _Float16 *>(ms + (r16 * GPT + g) * 2);
+                const uint8_t *ms = sm + (s >> 1) * 256 + (s & 1) * 32;
+                sc[nb] = (float)*reinterpret_cast<const _Float16 *>(ms + r16 * 2);
                 if constexpr (ASYM) {
-                    const uint8_t *mz = sm + kV2MStage + (s >> 1) * 256 + (s & 1) * 16 * GPT;
-                    pneg[nb] = neg_offset(A_BF16, (int)*reinterpret_cast<const int8_t *>(mz + r16 * GPT + g));
+                    const uint8_t *mz = sm + kV2MStage + (s >> 1) * 256 + (s & 1) * 16;
+                    pn[nb] = neg_offset(A_BF16, (int)*reinterpret_cast<const int8_t *>(mz + r16));
                 }
             }
-            // the group's B operands in offset form
-            u4 bv[SPG][TN];
-#pragma unroll
-            for (int ss = 0; ss < SPG; ++ss)
-#pragma unroll
-                for (int nb = 0; nb < TN; ++nb) {
-                    const uint32_t w = bq[nb][g * SPG + ss];
-                    bv[ss][nb] = A_BF16 ? unpack_bf16_biased(w, mlo) : unpack_f16_split(w, mlo, mhi);
-                }
-            auto mfma = [&](const u4 &a, const u4 &b, const f4 &c) __attribute__((always_inline)) {
-                if constexpr (A_BF16)
-                    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a),
-                                                                   __builtin_bit_cast(bf8v, b), c, 0, 0, 0);
-                else
-                    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
-                                                                  __builtin_bit_cast(h8, b), c, 0, 0, 0);
-            };
+            u4 av[TM][4];
 #pragma unroll
             for (int mb = 0; mb < TM; ++mb) {
                 const int row = wm * 64 + mb * 16 + r16;
-                u4 av[SPG];
 #pragma unroll
-                for (int ss = 0; ss < SPG; ++ss) {
-                    const int chunk = ((g * SPG + ss) * 4 + kq) ^ (row & 15);
-                    av[ss] = *reinterpret_cast<const u4 *>(sa + row * 256 + chunk * 16);
+                for (int j = 0; j < 4; ++j) {
+                    const int chunk = (j * 4 + kq) ^ (row & 15);
+                    av[mb][j] = *reinterpret_cast<const u4 *>(sa + row * 256 + chunk * 16);
                 }
-                // - sum_k a p over the group: shared by the row block (symmetric)
-                f4 off = f4{0.f, 0.f, 0.f, 0.f};
+            }
+            // B operands of the tile's four 32-K steps in offset form
+            u4 bv[4][TN];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int nb = 0; nb < TN; ++nb)
+                    bv[j][nb] = A_BF16 ? unpack_bf16_biased(bq[nb][j], mlo) : unpack_f16_split(bq[nb][j], mlo, mhi);
+            if (grp == 1) v2_wait_vm<NDMA>();
+            __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this phase's LDS reads are done
+            __builtin_amdgcn_sched_barrier(0);
+            v2_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // The matrix core runs at full rate from one wave only on back-to-back
+            // accumulation into the same registers: each 16x16 block's chain over
+            // the tile is one uninterrupted run (sched_barrier keeps the runs
+            // apart).  Symmetric weights: the four row blocks' offset chains go
+            // first, so every block chain starts from a value finished long before.
+            f4 offs[TM];
+#pragma unroll
+            for (int mb = 0; mb < TM; ++mb) {
+                offs[mb] = f4{0.f, 0.f, 0.f, 0.f};
                 if constexpr (!ASYM) {
 #pragma unroll
-                    for (int ss = 0; ss < SPG; ++ss) off = mfma(av[ss], psym, off);
+                    for (int j = 0; j < 4; ++j) offs[mb] = mfma(av[mb][j], psym, offs[mb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            f4 prev = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int blk = 0; blk < TM * TN; ++blk) {
+                const int mb = blk / TN, nb = blk % TN;
+                f4 c = offs[mb];
+                if constexpr (ASYM) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) c = mfma(av[mb][j], pn[nb], j == 0 ? f4{0.f, 0.f, 0.f, 0.f} : c);
                 }
 #pragma unroll
-                for (int nb = 0; nb < TN; ++nb) {
-                    f4 c = off;
-                    if constexpr (ASYM) {
+                for (int j = 0; j < 4; ++j) c = mfma(av[mb][j], bv[j][nb], c);
+                __builtin_amdgcn_sched_barrier(0);
+                if (blk > 0) {
+                    const int pm = (blk - 1) / TN, pnb = (blk - 1) % TN;
 #pragma unroll
-                        for (int ss = 0; ss < SPG; ++ss) c = mfma(av[ss], pneg[nb], ss == 0 ? f4{0.f, 0.f, 0.f, 0.f} : c);
+                    for (int i = 0; i < 4; ++i) acc[pm][pnb][i] = __builtin_fmaf(sc[pnb], prev[i], acc[pm][pnb][i]);
+                }
+                prev = c;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[TM - 1][TN - 1][i] = __builtin_fmaf(sc[TN - 1], prev[i], acc[TM - 1][TN - 1][i]);
+            if (grp == 0) v2_wait_vm<NDMA>();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            v2_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (grp == 0) v2_barrier();
+    } else {
+        // groups of 32 or 64 K: operands for a whole K tile do not fit beside
+        // the per-group metadata in 256 registers; one barrier per K tile
+        // prologue: stages 0 .. kV2Stages-2
+#pragma unroll
+        for (int s = 0; s < kV2Stages - 1; ++s) issue(kt0 + s, s);
+
+        for (int kt = kt0; kt < kt1; ++kt) {
+            const int st = (kt - kt0) % kV2Stages;
+            v2_wait_vm<NDMA * (kV2Stages - 2)>();          // this wave's loads of stage st landed
+            v2_barrier();                                  // every wave's; stage (st + 2) % 3 free
+            issue(kt + kV2Stages - 1, (st + kV2Stages - 1) % kV2Stages);
+
+            const uint8_t *sa = smem + st * SB;
+            const uint8_t *sb = sa + kV2AStage;
+            const uint8_t *sm = sb + kV2BStage;
+            // this wave's B strips (wn * 4 + nb) and their metadata
+            u4 bq[TN];
+#pragma unroll
+            for (int nb = 0; nb < TN; ++nb) bq[nb] = *reinterpret_cast<const u4 *>(sb + (wn * 4 + nb) * 1024 + lane * 16);
+
+#pragma unroll
+            for (int g = 0; g < GPT; ++g) {
+                float sc[TN];
+                u4 pneg[TN];
+#pragma unroll
+                for (int nb = 0; nb < TN; ++nb) {
+                    const int s = wn * 4 + nb;             // strip in the tile; its loader wave = s / 2
+                    const uint8_t *ms = sm + (s >> 1) * 256 + (s & 1) * 32 * GPT;
+                    sc[nb] = (float)*reinterpret_cast<const _Float16 *>(ms + (r16 * GPT + g) * 2);
+                    if constexpr (ASYM) {
+                        const uint8_t *mz = sm + kV2MStage + (s >> 1) * 256 + (s & 1) * 16 * GPT;
+                        pneg[nb] = neg_offset(A_BF16, (int)*reinterpret_cast<const int8_t *>(mz + r16 * GPT + g));
+                    }
+                }
+                // the group's B operands in offset form
+                u4 bv[SPG][TN];
+#pragma unroll
+                for (int ss = 0; ss < SPG; ++ss)
+#pragma unroll
+                    for (int nb = 0; nb < TN; ++nb) {
+                        const uint32_t w = bq[nb][g * SPG + ss];
+                        bv[ss][nb] = A_BF16 ? unpack_bf16_biased(w, mlo) : unpack_f16_split(w, mlo, mhi);
                     }
 #pragma unroll
-                    for (int ss = 0; ss < SPG; ++ss) c = mfma(av[ss], bv[ss][nb], c);
+                for (int mb = 0; mb < TM; ++mb) {
+                    const int row = wm * 64 + mb * 16 + r16;
+                    u4 av[SPG];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[mb][nb][i] = __builtin_fmaf(sc[nb], c[i], acc[mb][nb][i]);
+                    for (int ss = 0; ss < SPG; ++ss) {
+                        const int chunk = ((g * SPG + ss) * 4 + kq) ^ (row & 15);
+                        av[ss] = *reinterpret_cast<const u4 *>(sa + row * 256 + chunk * 16);
+                    }
+                    // - sum_k a p over the group: shared by the row block (symmetric)
+                    f4 off = f4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!ASYM) {
+#pragma unroll
+                        for (int ss = 0; ss < SPG; ++ss) off = mfma(av[ss], psym, off);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < TN; ++nb) {
+                        f4 c = off;
+                        if constexpr (ASYM) {
+#pragma unroll
+                            for (int ss = 0; ss < SPG; ++ss) c = mfma(av[ss], pneg[nb], ss == 0 ? f4{0.f, 0.f, 0.f, 0.f} : c);
+                        }
+#pragma unroll
+                        for (int ss = 0; ss < SPG; ++ss) c = mfma(av[ss], bv[ss][nb], c);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = __builtin_fmaf(sc[nb], c[i], acc[mb][nb][i]);
+                    }
                 }
             }
         }
