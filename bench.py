@@ -535,11 +535,12 @@ def bench_prefill(args, torch, lb, synth):
 
 
 def bench_moe(args, torch, lb, synth):
-    """One whole MoE layer, step by step through the C ABI and captured as one
-    graph: MXFP8 of the hidden rows, routing alignment, gate/up grouped GEMM,
-    SiLU(gate) * up re-quantized to MXFP8, down grouped GEMM, router-weighted
-    combine (the same kernels lowbit_moe_layer enqueues).  The dominant
-    kernel's roofline entry is the gate/up GEMM's."""
+    """One whole MoE layer through lowbit_moe_layer, captured as one graph:
+    MXFP8 of the hidden rows and routing alignment (one launch), gate/up
+    grouped GEMM, SiLU(gate) * up re-quantized to MXFP8, down grouped GEMM,
+    router-weighted combine.  The per-kernel breakdown times the same stages
+    through their own entry points (quant_x and align separately).  The
+    dominant kernel's roofline entry is the gate/up GEMM's."""
     T, E, top_k, bm, H, I = 256, 128, 8, 16, 2048, 768
     L3 = lb.LOWBIT_LUT3_E4M3
     S = T * top_k
@@ -587,9 +588,12 @@ def bench_moe(args, torch, lb, synth):
         ("combine", lambda: lb.lowbit_moe_combine(down, wts, T, top_k, H, y, st), S * H * 2 + S * 4 + T * H * 2),
     ]
 
+    wsb = lb.lowbit_moe_layer_workspace_bytes(T, top_k, E, H, I, bm)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
     def layer():
-        for _, fn, _ in steps:
-            lb.check(fn())
+        lb.check(lb.lowbit_moe_layer(packs["w13"][0], packs["w2"][0], E, E, H, I, x, topk, wts, T, top_k, None, bm,
+                                     y, ws, wsb, st))
     graph = capture(torch, layer, stream)
     ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
     per = {name: [] for name, _, _ in steps}

@@ -608,9 +608,8 @@ int lowbit_moe_layer(const void *w13, const void *w2, int E_local, int E, int H,
     int32_t *blk = reinterpret_cast<int32_t *>(ws + w.blocks), *npp = reinterpret_cast<int32_t *>(ws + w.npp);
     uint16_t *gu = reinterpret_cast<uint16_t *>(ws + w.gate_up), *down = reinterpret_cast<uint16_t *>(ws + w.down);
     const int slots = T * top_k;
-    hipError_t e = launch_mxfp8_rows(static_cast<const uint16_t *>(x), T, H, false, xq, xs, s);
-    if (e == hipSuccess)
-        e = launch_moe_align(topk_ids, slots, E, block_m, expert_map, sorted, offs, blk, npp, (int)w.capacity, s);
+    hipError_t e = launch_moe_prep(static_cast<const uint16_t *>(x), T, H, xq, xs, topk_ids, slots, E, block_m,
+                                   expert_map, sorted, offs, blk, npp, (int)w.capacity, s);
     if (e == hipSuccess)
         e = launch_moe_gemm(lut3_layout(E_local, 2 * I, H), static_cast<const uint8_t *>(w13), E, xq, xs, T, top_k,
                             sorted, offs, blk, slots, block_m, gu, s);

@@ -236,6 +236,12 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
 // The MoE layer around the grouped GEMMs (moe_layer.hip)
 hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t R, int K, bool silu, uint8_t *q, uint8_t *scale,
                              hipStream_t s);
+// the MoE layer's front end in one launch: routing (as launch_moe_align) and
+// the MXFP8 quantization of the hidden states (as launch_mxfp8_rows)
+hipError_t launch_moe_prep(const uint16_t *x, int T, int H, uint8_t *xq, uint8_t *xs, const int32_t *topk_ids,
+                           int num_valid, int E, int block_m, const int32_t *expert_map, int32_t *sorted_ids,
+                           int32_t *expert_offsets, int32_t *block_expert, int32_t *num_post_padded, int capacity,
+                           hipStream_t s);
 hipError_t launch_moe_combine(const uint16_t *out, const float *w, int T, int top_k, int H, uint16_t *y,
                               hipStream_t s);
 struct MoeLayerWs {

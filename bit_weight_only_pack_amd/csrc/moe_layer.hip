@@ -22,6 +22,7 @@
 // four lanes of a quad, so its maximum is two DPP steps; the E4M3 rounding is
 // done in integer arithmetic on the binary32 bits, exactly as defined.
 #include "lowbit_internal.hpp"
+#include "moe_align.hpp"
 
 namespace lowbit {
 
@@ -119,13 +120,12 @@ __device__ __forceinline__ void mx_block_put(const float *v, uint8_t *q, uint8_t
     if (write_scale) *scale = (uint8_t)(e + 127);
 }
 
-// One lane per 8 outputs of a row: rows x (K / 8) lanes.  SILU: the input row
-// is [2K] (gate | up), the output row K = I.
+// Lane t of R x (K / 8) quantizes outputs 8c .. 8c + 7 of row r.  SILU: the
+// input row is [2K] (gate | up), the output row K = I.
 template <bool SILU>
-__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t *x, int64_t R, int K, uint8_t *q,
-                                                         uint8_t *scale)
+__device__ __forceinline__ void mxfp8_row_lane(const uint16_t *x, int64_t R, int K, uint8_t *q, uint8_t *scale,
+                                               int64_t t)
 {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int cpr = K / 8;                           // lanes per row (a multiple of 4: K % 32 == 0)
     if (t >= R * cpr) return;                        // whole quads (R * cpr is a multiple of 4)
     const int64_t r = t / cpr;
@@ -145,6 +145,28 @@ __global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t *x, int6
         for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(g[i]);
     }
     mx_block_put(v, q + r * K + c * 8, scale + r * (K / 32) + c / 4, (c & 3) == 0);
+}
+
+template <bool SILU>
+__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t *x, int64_t R, int K, uint8_t *q,
+                                                         uint8_t *scale)
+{
+    mxfp8_row_lane<SILU>(x, R, K, q, scale, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// The layer's front end in one launch (the two jobs are independent): block 0
+// buckets the routed slots by expert, blocks 1.. quantize the hidden states to
+// MXFP8, 1024 lanes each.
+__global__ __launch_bounds__(kAlignThreads)
+void moe_prep_kernel(const uint16_t *x, int64_t T, int H, uint8_t *xq, uint8_t *xs, const int32_t *topk_ids,
+                     int num_valid, int E, int block_m, const int32_t *expert_map, int32_t *sorted_ids,
+                     int32_t *expert_offsets, int32_t *block_expert, int32_t *num_post_padded, int capacity)
+{
+    if (blockIdx.x == 0)
+        moe_align_block(topk_ids, num_valid, E, block_m, expert_map, sorted_ids, expert_offsets, block_expert,
+                        num_post_padded, capacity);
+    else
+        mxfp8_row_lane<false>(x, T, H, xq, xs, (int64_t)(blockIdx.x - 1) * kAlignThreads + threadIdx.x);
 }
 
 // y[t][h .. h+8) = RNE_bf16(sum_j w[t][j] * out[t*top_k + j][h .. h+8)), fp32,
@@ -182,6 +204,19 @@ hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t R, int K, bool silu, uin
         mxfp8_rows_kernel<true><<<blocks, 256, 0, s>>>(x, R, K, q, scale);
     else
         mxfp8_rows_kernel<false><<<blocks, 256, 0, s>>>(x, R, K, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_prep(const uint16_t *x, int T, int H, uint8_t *xq, uint8_t *xs, const int32_t *topk_ids,
+                           int num_valid, int E, int block_m, const int32_t *expert_map, int32_t *sorted_ids,
+                           int32_t *expert_offsets, int32_t *block_expert, int32_t *num_post_padded, int capacity,
+                           hipStream_t s)
+{
+    const int64_t lanes = (int64_t)T * (H / 8);
+    const unsigned blocks = 1 + (unsigned)((lanes + kAlignThreads - 1) / kAlignThreads);
+    moe_prep_kernel<<<blocks, kAlignThreads, 0, s>>>(x, T, H, xq, xs, topk_ids, num_valid, E, block_m, expert_map,
+                                                      sorted_ids, expert_offsets, block_expert, num_post_padded,
+                                                      capacity);
     return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@
 //   * One workgroup per (expert, 128-column tile) loops over all 16-row
 //     blocks of its expert, so each expert's weights stream from HBM once.
 #include "lowbit_internal.hpp"
+#include "moe_align.hpp"
 
 #include <algorithm>
 
@@ -140,109 +141,14 @@ __global__ void lut3_unpack_meta(const uint8_t *__restrict__ cb_in, const uint8_
 }
 
 // ---------------------------------------------------------------- align
-// Bucket the routed slots by expert (ascending expert, ascending slot id),
-// pad each expert to a multiple of block_m with the sentinel num_valid, and
-// record the expert of every block.  One workgroup of 1024 threads:
-//   1. per-expert counts (LDS histogram) and the exclusive scan of the padded
-//      counts (wave prefix sums, then a prefix over the wave totals);
-//   2. placement, a chunk of slots at a time: every slot sets its bit in its
-//      expert's bitmask of the chunk; a slot's rank among its expert's slots
-//      is the number of set bits below its own plus that expert's count from
-//      earlier chunks -- a stable order with no sequential pass;
-//   3. sentinels in the padding and past the end, block_expert.
-constexpr int kAlignThreads = 1024;
-constexpr int kAlignWaves = kAlignThreads / 64;
-constexpr int kMaxExperts = 1024;
-constexpr int kAlignMaskWords = 8192;             // LDS words for the chunk bitmasks (32 KB)
-
 __global__ __launch_bounds__(kAlignThreads)
 void moe_align_kernel(const int32_t *__restrict__ topk_ids, int num_valid, int E, int block_m,
                       const int32_t *__restrict__ expert_map, int32_t *__restrict__ sorted_ids,
                       int32_t *__restrict__ expert_offsets, int32_t *__restrict__ block_expert,
                       int32_t *__restrict__ num_post_padded, int capacity)
 {
-    __shared__ int counts[kMaxExperts];
-    __shared__ int offs[kMaxExperts + 1];
-    __shared__ int running[kMaxExperts];
-    __shared__ int wave_sum[kAlignWaves];
-    __shared__ uint32_t mask[kAlignMaskWords];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-
-    // 1. counts and padded offsets (thread e owns expert e, E <= 1024)
-    counts[tid] = 0;
-    running[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < num_valid; i += kAlignThreads) {
-        const int e = topk_ids[i];
-        if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
-    }
-    __syncthreads();
-    const int padded = tid < E ? (counts[tid] + block_m - 1) / block_m * block_m : 0;
-    int incl = padded;                                // inclusive prefix inside the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) wave_sum[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wave_sum[w];
-    const int excl = before + incl - padded;
-    if (tid < E) offs[tid] = excl;
-    if (tid == E - 1) offs[E] = excl + padded;
-    __syncthreads();
-    const int total = offs[E];
-    if (tid < E) expert_offsets[tid] = offs[tid];
-    if (tid == 0) {
-        expert_offsets[E] = total;                    // (E may equal the thread count)
-        num_post_padded[0] = total;
-    }
-
-    // 2. stable placement, chunk by chunk: a chunk's bitmask holds
-    //    chunk / 32 words per expert, rows one word longer than that so the
-    //    rows of different experts start in different LDS banks
-    const int words = max(1, min(32, kAlignMaskWords / E - 1));   // words per expert per chunk
-    const int stride = words + 1;
-    const int chunk = words * 32;
-    for (int base = 0; base < num_valid; base += chunk) {
-        for (int i = tid; i < E * stride; i += kAlignThreads) mask[i] = 0;
-        __syncthreads();
-        int e = -1, local = 0;
-        if (tid < chunk && base + tid < num_valid) {
-            e = topk_ids[base + tid];
-            if (e >= 0 && e < E) {
-                local = tid;
-                atomicOr(&mask[e * stride + (local >> 5)], 1u << (local & 31));
-            } else {
-                e = -1;
-            }
-        }
-        __syncthreads();
-        if (e >= 0) {
-            const uint32_t *m = mask + e * stride;
-            int rank = __builtin_popcount(m[local >> 5] & ((1u << (local & 31)) - 1u));
-            for (int w = 0; w < (local >> 5); ++w) rank += __builtin_popcount(m[w]);
-            sorted_ids[offs[e] + running[e] + rank] = base + local;
-        }
-        __syncthreads();
-        if (tid < E) {
-            int c = 0;
-            for (int w = 0; w < words; ++w) c += __builtin_popcount(mask[tid * stride + w]);
-            running[tid] += c;
-        }
-        __syncthreads();
-    }
-
-    // 3. sentinels in each expert's padding and past the end; expert of every block
-    if (tid < E) {
-        for (int p = offs[tid] + counts[tid]; p < offs[tid + 1]; ++p) sorted_ids[p] = num_valid;
-        const int local = expert_map ? expert_map[tid] : tid;
-        for (int b = offs[tid] / block_m; b < offs[tid + 1] / block_m; ++b) block_expert[b] = local;
-    }
-    for (int i = total + tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;
-    for (int b = total / block_m + tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
+    moe_align_block(topk_ids, num_valid, E, block_m, expert_map, sorted_ids, expert_offsets, block_expert,
+                    num_post_padded, capacity);
 }
 
 // ---------------------------------------------------------------- grouped GEMM

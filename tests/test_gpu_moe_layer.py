@@ -168,6 +168,42 @@ def test_moe_layer_full_config_sampled_tokens():
     assert np.array_equal(y, y2)                     # deterministic
 
 
+@pytest.mark.parametrize("T,E,top_k,H,I,local", [(64, 16, 4, 512, 256, False), (300, 160, 6, 256, 128, True)])
+def test_moe_layer_equals_stage_chain(T, E, top_k, H, I, local):
+    """lowbit_moe_layer runs the hidden-state quantization and the routing as
+    one launch; its output is bit-identical to the six stages run one by one
+    through their own entry points.  The second case has 1800 slots (two
+    placement chunks), 160 experts and an expert map."""
+    bm = 16
+    d13, d2, x, topk, w = _layer_case(T, E, top_k, H, I, seed=E + T)
+    emap = np.where(np.arange(E) % 3 != 0, np.arange(E), -1).astype(np.int32) if local else None
+    y_layer = _run_layer(d13, d2, x, topk, w, E, H, I, emap=emap, block_m=bm)
+    S = T * top_k
+    xq, xs = _quant(lb.lowbit_mxfp8_quant, x, T, H)
+    cap = S + E * (bm - 1)
+    ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    blk = torch.empty(cap // bm, dtype=torch.int32, device="cuda")
+    npp = torch.empty(1, dtype=torch.int32, device="cuda")
+    lb.check(lb.lowbit_moe_align(dev(topk), T, top_k, E, bm, None if emap is None else dev(emap), ids, offs, blk,
+                                 npp))
+    gu = torch.zeros((S, 2 * I), dtype=torch.int16, device="cuda")
+    lb.check(lb.lowbit_moe_gemm(lb.LOWBIT_LUT3_E4M3, E, 2 * I, H, _pack(d13, E, 2 * I, H), E, dev(xq), dev(xs), T,
+                                top_k, ids, offs, blk, S, bm, gu))
+    aq = torch.zeros((S, I), dtype=torch.uint8, device="cuda")
+    as_ = torch.zeros((S, I // 32), dtype=torch.uint8, device="cuda")
+    lb.check(lb.lowbit_moe_silu_mul_quant(gu, S, I, aq, as_))
+    down = torch.zeros((S, H), dtype=torch.int16, device="cuda")
+    lb.check(lb.lowbit_moe_gemm(lb.LOWBIT_LUT3_E4M3, E, H, I, _pack(d2, E, H, I), E, aq, as_, S, 1, ids, offs, blk, S,
+                                bm, down))
+    y = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    lb.check(lb.lowbit_moe_combine(down, dev(w), T, top_k, H, y))
+    torch.cuda.synchronize()
+    assert np.array_equal(y_layer, y.cpu().numpy().view(np.uint16))
+    ref = oracle.moe_layer(d13, d2, x, topk, w, expert_map=emap)
+    assert_layer_close(bf16_bits_to_f64(y_layer), bf16_bits_to_f64(ref["y"]), "layer")
+
+
 def test_moe_layer_intermediate_codes():
     """The layer's steps run one by one through the C ABI (MXFP8 of x,
     alignment, gate/up GEMM, SiLU * up with MXFP8): the hidden-state codes are
