@@ -60,6 +60,8 @@ def _ref(w, a_bits, a_dtype, c_dtype, G, rows=None):
     (256, 384, 512, 128, False),
     (64, 256, 4096, 128, False),    # split-K path
     (200, 100, 2048, 32, False),    # ragged N inside one strip, split-K
+    (130, 272, 384, 128, True),     # group of a whole K tile: three tiles, ragged M and N, zero points
+    (33, 528, 256, 128, False),     # group of a whole K tile: two tiles, ragged M and N
 ])
 def test_gemm_parity(M, N, K, G, asym, a_dtype, c_dtype):
     w = synth.w4_weights(N, K, G, asym=asym, workload_id=WL, layer=M, part=N)
