@@ -17,11 +17,12 @@ namespace lowbit {
 //      expert's bitmask of the chunk; a slot's rank among its expert's slots
 //      is the number of set bits below its own plus that expert's count from
 //      earlier chunks -- a stable order with no sequential pass;
-//   3. sentinels in the padding and past the end, block_expert.
+//   3. block_expert (sentinels and empty blocks are written first, in step 0).
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kAlignMaskWords = 8192;             // LDS words for the chunk bitmasks (32 KB)
+constexpr int kAlignIdCache = 4096;               // slot ids kept in LDS (as int16) between the passes
 
 // the body of the align kernel, run by one whole 1024-thread workgroup
 __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk_ids, int num_valid, int E,
@@ -34,19 +35,30 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
     __shared__ int counts[kMaxExperts];
     __shared__ int offs[kMaxExperts + 1];
     __shared__ int running[kMaxExperts];
-    __shared__ int wave_sum[kAlignWaves];
+    __shared__ __attribute__((aligned(16))) int wave_sum[kAlignWaves];
     __shared__ uint32_t mask[kAlignMaskWords];
+    __shared__ int16_t ids[kAlignIdCache];           // slot -> expert (or -1) for the first slots
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+
+    // 0. every sorted position starts as the sentinel and every block as "no
+    //    expert"; placement and step 3 overwrite what they own.  The stores
+    //    complete (vmcnt 0) before the barrier that ends step 1, so no later
+    //    store to the same address can be overtaken by them.
+    for (int i = tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;
+    for (int b = tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
 
     // 1. counts and padded offsets (thread e owns expert e, E <= 1024)
     counts[tid] = 0;
     running[tid] = 0;
     __syncthreads();
     for (int i = tid; i < num_valid; i += kAlignThreads) {
-        const int e = topk_ids[i];
-        if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+        int e = topk_ids[i];
+        if (e < 0 || e >= E) e = -1;
+        if (i < kAlignIdCache) ids[i] = (int16_t)e;
+        if (e >= 0) atomicAdd(&counts[e], 1);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): the step-0 stores are done
     __syncthreads();
     const int padded = tid < E ? (counts[tid] + block_m - 1) / block_m * block_m : 0;
     int incl = padded;                                // inclusive prefix inside the wave
@@ -57,8 +69,13 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
     }
     if (lane == 63) wave_sum[wave] = incl;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wave_sum[w];
+    int before = 0;                                   // totals of the earlier waves
+#pragma unroll
+    for (int q = 0; q < kAlignWaves / 4; ++q) {
+        const int4 v = reinterpret_cast<const int4 *>(wave_sum)[q];
+        before += (4 * q + 0 < wave ? v.x : 0) + (4 * q + 1 < wave ? v.y : 0) + (4 * q + 2 < wave ? v.z : 0) +
+                  (4 * q + 3 < wave ? v.w : 0);
+    }
     const int excl = before + incl - padded;
     if (tid < E) offs[tid] = excl;
     if (tid == E - 1) offs[E] = excl + padded;
@@ -81,7 +98,8 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
         __syncthreads();
         int e = -1, local = 0;
         if (tid < chunk && base + tid < num_valid) {
-            e = topk_ids[base + tid];
+            const int i = base + tid;
+            e = i < kAlignIdCache ? (int)ids[i] : topk_ids[i];
             if (e >= 0 && e < E) {
                 local = tid;
                 atomicOr(&mask[e * stride + (local >> 5)], 1u << (local & 31));
@@ -105,14 +123,11 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
         __syncthreads();
     }
 
-    // 3. sentinels in each expert's padding and past the end; expert of every block
+    // 3. expert of every block (the sentinels were written in step 0)
     if (tid < E) {
-        for (int p = offs[tid] + counts[tid]; p < offs[tid + 1]; ++p) sorted_ids[p] = num_valid;
         const int local = expert_map ? expert_map[tid] : tid;
         for (int b = offs[tid] / block_m; b < offs[tid + 1] / block_m; ++b) block_expert[b] = local;
     }
-    for (int i = total + tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;
-    for (int b = total / block_m + tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
 }
 
 }  // namespace lowbit
