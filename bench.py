@@ -538,9 +538,12 @@ def bench_moe(args, torch, lb, synth):
     """One whole MoE layer through lowbit_moe_layer, captured as one graph:
     MXFP8 of the hidden rows and routing alignment (one launch), gate/up
     grouped GEMM, SiLU(gate) * up re-quantized to MXFP8, down grouped GEMM,
-    router-weighted combine.  The per-kernel breakdown times the same stages
-    through their own entry points (quant_x and align separately).  The
-    dominant kernel's roofline entry is the gate/up GEMM's."""
+    router-weighted combine.  Two distinct weight sets (together larger than
+    the MALL) alternate: one graph replay runs the layer on each, and the
+    reported step is one layer.  The per-kernel breakdown times the same
+    stages through their own entry points (quant_x and align separately),
+    alternating the sets as well.  The dominant kernel's roofline entry is
+    the gate/up GEMM's."""
     T, E, top_k, bm, H, I = 256, 128, 8, 16, 2048, 768
     L3 = lb.LOWBIT_LUT3_E4M3
     S = T * top_k
@@ -563,45 +566,56 @@ def bench_moe(args, torch, lb, synth):
     down = torch.empty((S, H), dtype=torch.int16, device="cuda")
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     stream = torch.cuda.Stream()
-    packs = {}
+    # two distinct weight sets (2 x 237 MB, more than the 256 MB MALL), used
+    # alternately, so the timed layers read their experts from HBM
+    packs = [{}, {}]
     weights = {}
-    for name, (N, K, part) in (("w13", (2 * I, H, 0)), ("w2", (H, I, 1))):
-        d = synth.lut3_weights(E, N, K, workload_id=4, part=part)
-        nb = lb.lowbit_packed_bytes(L3, E, N, K, 0)
-        packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        lb.check(lb.lowbit_pack_weights(L3, E, N, K, 0, torch.from_numpy(d["idx"]).cuda(),
-                                        torch.from_numpy(d["cb"]).cuda(), torch.from_numpy(d["ex"]).cuda(), packed,
-                                        nb))
-        packs[name] = (packed, nb)
-        weights[name] = d
+    for ws_id in range(2):
+        for name, (N, K, part) in (("w13", (2 * I, H, 0)), ("w2", (H, I, 1))):
+            d = synth.lut3_weights(E, N, K, workload_id=4, layer=ws_id, part=part)
+            nb = lb.lowbit_packed_bytes(L3, E, N, K, 0)
+            packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            lb.check(lb.lowbit_pack_weights(L3, E, N, K, 0, torch.from_numpy(d["idx"]).cuda(),
+                                            torch.from_numpy(d["cb"]).cuda(), torch.from_numpy(d["ex"]).cuda(),
+                                            packed, nb))
+            packs[ws_id][name] = (packed, nb)
+            if ws_id == 0:
+                weights[name] = d
     st = stream.cuda_stream
-    steps = [
-        ("quant_x", lambda: lb.lowbit_mxfp8_quant(x, T, H, xq, xs, st), T * H * 2 + T * H + T * H // 32),
-        ("align", lambda: lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, st), S * 4),
-        ("gate_up", lambda: lb.lowbit_moe_gemm(L3, E, 2 * I, H, packs["w13"][0], E, xq, xs, T, top_k, ids, offs, blk,
-                                               S, bm, gu, st),
-         packs["w13"][1] + T * H + T * H // 32 + S * 2 * I * 2),
-        ("silu_mul_quant", lambda: lb.lowbit_moe_silu_mul_quant(gu, S, I, aq, as_, st), S * 2 * I * 2 + S * I + S * I // 32),
-        ("down", lambda: lb.lowbit_moe_gemm(L3, E, H, I, packs["w2"][0], E, aq, as_, S, 1, ids, offs, blk, S, bm, down,
-                                            st),
-         packs["w2"][1] + S * I + S * I // 32 + S * H * 2),
-        ("combine", lambda: lb.lowbit_moe_combine(down, wts, T, top_k, H, y, st), S * H * 2 + S * 4 + T * H * 2),
-    ]
+
+    def stages(pk):
+        return [
+            ("quant_x", lambda: lb.lowbit_mxfp8_quant(x, T, H, xq, xs, st), T * H * 2 + T * H + T * H // 32),
+            ("align", lambda: lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, st), S * 4),
+            ("gate_up", lambda: lb.lowbit_moe_gemm(L3, E, 2 * I, H, pk["w13"][0], E, xq, xs, T, top_k, ids, offs, blk,
+                                                   S, bm, gu, st),
+             pk["w13"][1] + T * H + T * H // 32 + S * 2 * I * 2),
+            ("silu_mul_quant", lambda: lb.lowbit_moe_silu_mul_quant(gu, S, I, aq, as_, st),
+             S * 2 * I * 2 + S * I + S * I // 32),
+            ("down", lambda: lb.lowbit_moe_gemm(L3, E, H, I, pk["w2"][0], E, aq, as_, S, 1, ids, offs, blk, S, bm, down,
+                                                st),
+             pk["w2"][1] + S * I + S * I // 32 + S * H * 2),
+            ("combine", lambda: lb.lowbit_moe_combine(down, wts, T, top_k, H, y, st), S * H * 2 + S * 4 + T * H * 2),
+        ]
+    steps_by_set = [stages(packs[0]), stages(packs[1])]
+    steps = steps_by_set[0]
 
     wsb = lb.lowbit_moe_layer_workspace_bytes(T, top_k, E, H, I, bm)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
 
-    def layer():
-        lb.check(lb.lowbit_moe_layer(packs["w13"][0], packs["w2"][0], E, E, H, I, x, topk, wts, T, top_k, None, bm,
-                                     y, ws, wsb, st))
-    graph = capture(torch, layer, stream)
-    ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
+    def layer_pair():
+        for pk in packs:
+            lb.check(lb.lowbit_moe_layer(pk["w13"][0], pk["w2"][0], E, E, H, I, x, topk, wts, T, top_k, None, bm,
+                                         y, ws, wsb, st))
+    graph = capture(torch, layer_pair, stream)
+    ms2, gpu_ms2 = time_graph(torch, graph, stream, args.steps, args.warmup)
+    ms, gpu_ms = ms2 / 2, gpu_ms2 / 2                           # per layer
     per = {name: [] for name, _, _ in steps}
     with torch.cuda.stream(stream):
-        for _ in range(5):
+        for rep in range(6):
             evs = []
             torch.cuda._sleep(20_000_000)
-            for name, fn, _ in steps:
+            for name, fn, _ in steps_by_set[rep % 2]:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -617,12 +631,13 @@ def bench_moe(args, torch, lb, synth):
     gbps = layer_bytes / (ms * 1e-3) / 1e9
     gu_gbps = nbytes["gate_up"] / (us["gate_up"] * 1e-6) / 1e9
     out = {"metric": "3-bit LUT MoE layer (MXFP8 in, align, gate/up, SiLU*up MXFP8, down, combine) effective HBM GB/s",
-           "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "fp8 (MXFP8 x LUT3 E4M3), fp32 accumulate, bf16 in/out",
+           "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": 2 * args.steps,
+           "warmup": 2 * args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8 (MXFP8 x LUT3 E4M3), fp32 accumulate, bf16 in/out",
            "data": "synthetic (seeded; N(0,1) router logits -> softmax top-8, N(0,1) bf16 hidden rows)",
            "config": {"workload": "lut3-moe-layer-256tok-128e-top8", "tokens": T, "experts": E, "top_k": top_k,
-                      "block_m": bm, "hidden": H, "intermediate": I, "bytes_per_layer": layer_bytes},
+                      "block_m": bm, "hidden": H, "intermediate": I, "bytes_per_layer": layer_bytes,
+                      "weight_sets": 2, "layers_per_replay": 2},
            "tokens_per_s": round(T * 1e3 / ms, 1),
            "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
            "gpu_ms_per_step": round(gpu_ms, 4),
