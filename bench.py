@@ -520,17 +520,35 @@ def bench_prefill(args, torch, lb, synth):
             ms, _ = time_graph(torch, graph, stream, max(3, args.steps // 5), 2)
             flop = 2.0 * M * N * K
             tf = flop / (ms * 1e-3) / 1e12
+            # context only: a dense bf16 GEMM of the same shape (torch.matmul,
+            # the vendor library), the matrix cores' achievable rate on it
+            a_bf = a.view(torch.bfloat16)
+            b_dense = torch.randn((K, N), dtype=torch.bfloat16, device="cuda")
+            c_bf = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            with torch.cuda.stream(stream):
+                for _ in range(2):
+                    torch.matmul(a_bf, b_dense, out=c_bf)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = max(3, args.steps // 5)
+                e0.record(stream)
+                for _ in range(reps):
+                    torch.matmul(a_bf, b_dense, out=c_bf)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            dense_ms = e0.elapsed_time(e1) / reps
             res["M=%d K=%d N=%d" % (M, K, N)] = dict(us=round(ms * 1e3, 1), TFLOPs=round(tf, 1),
-                                                     pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2))
+                                                     pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2),
+                                                     dense_bf16_matmul_us=round(dense_ms * 1e3, 1),
+                                                     dense_bf16_matmul_TFLOPs=round(flop / (dense_ms * 1e-3) / 1e12, 1))
             total_flop += flop
             total_ms += ms
-            del graph
+            del graph, b_dense, c_bf
     agg = total_flop / (total_ms * 1e-3) / 1e12
     return {"metric": "W4 prefill GEMM TFLOP/s (bf16 MFMA, fp32 accumulate)", "value": round(agg, 1),
             "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
             "vs_baseline": None, "config": {"workload": "w4-prefill-gemm", "group_size": G},
             "roofline": {"bound": "mfma", "achieved": round(agg, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
             "per_shape": res}
 
 
