@@ -33,9 +33,11 @@ Other workloads (--workload), one JSON line each:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
+import glob
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -145,6 +147,75 @@ def capture(torch, fn, stream):
     return graph
 
 
+SCLK_SAMPLES = []                   # MHz, sampled during every graph-timed region
+
+
+class ClockSampler:
+    """Polls the driver's current shader-clock level (sysfs pp_dpm_sclk, the
+    line marked '*') every 2 ms on a host thread while the block runs."""
+
+    def __init__(self):
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.stop = threading.Event()
+        self.thread = None
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                for line in open(p).read().splitlines():
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = self._read()
+            if v is not None:
+                SCLK_SAMPLES.append(v)
+            self.stop.wait(0.002)
+
+    def __enter__(self):
+        if self.paths:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.thread is not None:
+            self.stop.set()
+            self.thread.join()
+
+
+class PinnedOneCore:
+    """Runs the block on one host core (the oracle legs are single-threaded)."""
+
+    def __enter__(self):
+        self.saved = None
+        if hasattr(os, "sched_getaffinity"):
+            self.saved = os.sched_getaffinity(0)
+            os.sched_setaffinity(0, {min(self.saved)})
+        return self
+
+    def __exit__(self, *exc):
+        if self.saved is not None:
+            os.sched_setaffinity(0, self.saved)
+
+
+def host_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "cpus_available": n}
+
+
 def time_graph(torch, graph, stream, steps, warmup):
     """Exactly `steps` replays after `warmup`, synchronized on both sides.
     Returns (wall ms per replay, GPU-event ms per replay)."""
@@ -154,14 +225,15 @@ def time_graph(torch, graph, stream, steps, warmup):
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(steps):
-            graph.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler():
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
@@ -219,12 +291,13 @@ def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0
                 pid, K, N = projs[name]
                 w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
                                      layer=layer, part=pid)
-                t0 = time.perf_counter()
-                if a8:
-                    oracle.w4a8_matmul(x, w["qweight"], w["scales"], w["zeros"], G)
-                else:
-                    oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
-                t_total += time.perf_counter() - t0
+                with PinnedOneCore():
+                    t0 = time.perf_counter()
+                    if a8:
+                        oracle.w4a8_matmul(x, w["qweight"], w["scales"], w["zeros"], G)
+                    else:
+                        oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
+                    t_total += time.perf_counter() - t0
                 nbytes += w4_bytes(K, N, M, G, asym)
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample="layers 0..%d of the 32-layer step (%d GEMVs, %.1f MB), one thread, %.1f s"
@@ -482,9 +555,10 @@ def bench_decode_bits(args, torch, lb, synth):
             for name in group:
                 pid, K, N = projs[name]
                 w = synth.wb_weights(N, K, G, ref["bits"], workload_id=wid, layer=0, part=pid)
-                t0 = time.perf_counter()
-                oracle.wb_matmul(x, w["codes"], w["scales"], None, ref["bits"], G)
-                t_total += time.perf_counter() - t0
+                with PinnedOneCore():
+                    t0 = time.perf_counter()
+                    oracle.wb_matmul(x, w["codes"], w["scales"], None, ref["bits"], G)
+                    t_total += time.perf_counter() - t0
                 nbytes += wb_bytes(K, N, M, G, ref["bits"])
         out["cpu_baseline"] = {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
@@ -668,9 +742,10 @@ def bench_moe(args, torch, lb, synth):
     if args.cpu_layers > 0:
         import oracle
         tok = np.arange(0, T, T // 16)
-        t0 = time.perf_counter()
-        oracle.moe_layer(weights["w13"], weights["w2"], x_np[tok], topk_np[tok], w_np[tok])
-        dt = time.perf_counter() - t0
+        with PinnedOneCore():
+            t0 = time.perf_counter()
+            oracle.moe_layer(weights["w13"], weights["w2"], x_np[tok], topk_np[tok], w_np[tok])
+            dt = time.perf_counter() - t0
         full = dt * T / len(tok)
         out["cpu_baseline"] = {"value": round(layer_bytes / full / 1e9, 5), "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
@@ -717,7 +792,14 @@ def main():
         del src, dst
     fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "decode-w4a8": bench_decode_w4a8,
           "decode-bits": bench_decode_bits, "prefill": bench_prefill, "moe": bench_moe}[args.workload]
-    print(json.dumps(fn(args, torch, lb, synth)), flush=True)
+    out = fn(args, torch, lb, synth)
+    if SCLK_SAMPLES:
+        v = sorted(SCLK_SAMPLES)
+        out["gpu_sclk_mhz"] = {"min": v[0], "median": v[len(v) // 2], "max": v[-1], "samples": len(v),
+                               "source": "sysfs pp_dpm_sclk, polled every 2 ms during the timed replays"}
+    if "cpu_baseline" in out:
+        out["cpu_baseline"].update(host_info())
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
