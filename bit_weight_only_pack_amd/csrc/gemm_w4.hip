@@ -7,11 +7,14 @@
 // and a dequantized weight tile are staged in on-chip memory and multiplied.)
 //
 // MI355X design:
-//   * Workgroup tile BM x BN, K in steps of 128 (one packed weight tile).  The
-//     A tile (BM x 128, bf16 or fp16) is staged in LDS and shared by all
-//     waves; each wave owns TN 16-column strips of the weight and reads its B
-//     operands straight from the packed 16 x 128 tiles, already in the lane
-//     order of v_mfma_f32_16x16x32_{bf16,f16}: no LDS traffic for B.
+//   * Workgroup tile 128 x 256, K in steps of 128 (one packed weight tile),
+//     8 waves of 64 x 64.  The A tile (128 x 128, bf16 or fp16), the
+//     workgroup's 16 packed 16 x 128 weight tiles (already in the lane order
+//     of v_mfma_f32_16x16x32_{bf16,f16}) and their scales move to LDS by
+//     LDS-direct loads in a 3-stage ring; each wave reads its operands from
+//     there.  With one quantization group per K tile the two wave groups run
+//     a phase apart (one wave of each SIMD unpacks while the other issues
+//     MFMAs); see the kernel for the schedule.
 //   * Weights stay exact, in offset form.  The B operand holds each code
 //     plus a constant, made by masking it into the mantissa of a power of
 //     two: bf16 activations 128 + q (mask-or with bf16 128.0); fp16
