@@ -629,13 +629,15 @@ def bench_prefill(args, torch, lb, synth):
 def bench_moe(args, torch, lb, synth):
     """One whole MoE layer through lowbit_moe_layer, captured as one graph:
     MXFP8 of the hidden rows and routing alignment (one launch), gate/up
-    grouped GEMM, SiLU(gate) * up re-quantized to MXFP8, down grouped GEMM,
-    router-weighted combine.  Two distinct weight sets (together larger than
-    the MALL) alternate: one graph replay runs the layer on each, and the
-    reported step is one layer.  The per-kernel breakdown times the same
-    stages through their own entry points (quant_x and align separately),
-    alternating the sets as well.  The dominant kernel's roofline entry is
-    the gate/up GEMM's."""
+    grouped GEMM with SiLU(gate) * up -> MXFP8 in its epilogue, down grouped
+    GEMM, router-weighted combine.  Two distinct weight sets (together larger
+    than the MALL) alternate: one graph replay runs the layer on each, and the
+    reported step is one layer; its bytes are those of the layer's own
+    kernels.  The per-kernel breakdown times the same stages through their
+    own entry points (quant_x and align separately), alternating the sets as
+    well, plus the unfused pair (gate/up GEMM to bf16 rows, then SiLU * up ->
+    MXFP8) for comparison.  The dominant kernel's roofline entry is the fused
+    gate/up GEMM's."""
     T, E, top_k, bm, H, I = 256, 128, 8, 16, 2048, 768
     L3 = lb.LOWBIT_LUT3_E4M3
     S = T * top_k
@@ -676,18 +678,23 @@ def bench_moe(args, torch, lb, synth):
     st = stream.cuda_stream
 
     def stages(pk):
+        # (name, call, algorithmic bytes, part of the layer)
         return [
-            ("quant_x", lambda: lb.lowbit_mxfp8_quant(x, T, H, xq, xs, st), T * H * 2 + T * H + T * H // 32),
-            ("align", lambda: lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, st), S * 4),
+            ("quant_x", lambda: lb.lowbit_mxfp8_quant(x, T, H, xq, xs, st), T * H * 2 + T * H + T * H // 32, True),
+            ("align", lambda: lb.lowbit_moe_align(topk, T, top_k, E, bm, None, ids, offs, blk, npp, st), S * 4, True),
             ("gate_up", lambda: lb.lowbit_moe_gemm(L3, E, 2 * I, H, pk["w13"][0], E, xq, xs, T, top_k, ids, offs, blk,
                                                    S, bm, gu, st),
-             pk["w13"][1] + T * H + T * H // 32 + S * 2 * I * 2),
+             pk["w13"][1] + T * H + T * H // 32 + S * 2 * I * 2, False),
             ("silu_mul_quant", lambda: lb.lowbit_moe_silu_mul_quant(gu, S, I, aq, as_, st),
-             S * 2 * I * 2 + S * I + S * I // 32),
+             S * 2 * I * 2 + S * I + S * I // 32, False),
+            ("gate_up_silu", lambda: lb.lowbit_moe_gemm_silu_quant(L3, E, I, H, pk["w13"][0], E, xq, xs, T, top_k, ids,
+                                                                   offs, blk, S, bm, aq, as_, st),
+             pk["w13"][1] + T * H + T * H // 32 + S * I + S * I // 32, True),
             ("down", lambda: lb.lowbit_moe_gemm(L3, E, H, I, pk["w2"][0], E, aq, as_, S, 1, ids, offs, blk, S, bm, down,
                                                 st),
-             pk["w2"][1] + S * I + S * I // 32 + S * H * 2),
-            ("combine", lambda: lb.lowbit_moe_combine(down, wts, T, top_k, H, y, st), S * H * 2 + S * 4 + T * H * 2),
+             pk["w2"][1] + S * I + S * I // 32 + S * H * 2, True),
+            ("combine", lambda: lb.lowbit_moe_combine(down, wts, T, top_k, H, y, st), S * H * 2 + S * 4 + T * H * 2,
+             True),
         ]
     steps_by_set = [stages(packs[0]), stages(packs[1])]
     steps = steps_by_set[0]
@@ -702,12 +709,12 @@ def bench_moe(args, torch, lb, synth):
     graph = capture(torch, layer_pair, stream)
     ms2, gpu_ms2 = time_graph(torch, graph, stream, args.steps, args.warmup)
     ms, gpu_ms = ms2 / 2, gpu_ms2 / 2                           # per layer
-    per = {name: [] for name, _, _ in steps}
+    per = {name: [] for name, _, _, _ in steps}
     with torch.cuda.stream(stream):
         for rep in range(6):
             evs = []
             torch.cuda._sleep(20_000_000)
-            for name, fn, _ in steps_by_set[rep % 2]:
+            for name, fn, _, _ in steps_by_set[rep % 2]:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -718,11 +725,12 @@ def bench_moe(args, torch, lb, synth):
             for name, a, b in evs:
                 per[name].append(a.elapsed_time(b) * 1e3)
     us = {k: float(np.median(v)) for k, v in per.items()}
-    nbytes = {name: b for name, _, b in steps}
-    layer_bytes = sum(nbytes.values())
+    nbytes = {name: b for name, _, b, _ in steps}
+    layer_bytes = sum(b for _, _, b, in_layer in steps if in_layer)
     gbps = layer_bytes / (ms * 1e-3) / 1e9
-    gu_gbps = nbytes["gate_up"] / (us["gate_up"] * 1e-6) / 1e9
-    out = {"metric": "3-bit LUT MoE layer (MXFP8 in, align, gate/up, SiLU*up MXFP8, down, combine) effective HBM GB/s",
+    gu_gbps = nbytes["gate_up_silu"] / (us["gate_up_silu"] * 1e-6) / 1e9
+    out = {"metric": "3-bit LUT MoE layer (MXFP8 in, align, gate/up with SiLU*up MXFP8, down, combine) "
+                     "effective HBM GB/s",
            "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": 2 * args.steps,
            "warmup": 2 * args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8 (MXFP8 x LUT3 E4M3), fp32 accumulate, bf16 in/out",
@@ -735,8 +743,8 @@ def bench_moe(args, torch, lb, synth):
            "gpu_ms_per_step": round(gpu_ms, 4),
            "roofline": {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                        "kernel": "moe_lut3_gemm_lds_kernel (gate/up)", "bytes_per_launch": nbytes["gate_up"],
-                        "avg_launch_us": round(us["gate_up"], 3)},
+                        "kernel": "moe_lut3_gemm_lds_kernel (gate/up, SiLU*up MXFP8 epilogue)",
+                        "bytes_per_launch": nbytes["gate_up_silu"], "avg_launch_us": round(us["gate_up_silu"], 3)},
            "per_kernel_us": {k: round(v, 2) for k, v in us.items()},
            "per_kernel_GBps": {k: round(nbytes[k] / (us[k] * 1e-6) / 1e9, 1) for k in us if k != "align"}}
     if args.cpu_layers > 0:

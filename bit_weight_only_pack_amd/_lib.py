@@ -82,6 +82,8 @@ SIGNATURES = {
     "lowbit_moe_gemm": (_i, [_i, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "lowbit_mxfp8_quant": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "lowbit_moe_silu_mul_quant": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "lowbit_moe_gemm_silu_quant": (_i, [_i, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                                        _vp]),
     "lowbit_moe_combine": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     "lowbit_moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_moe_layer": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp]),
@@ -201,6 +203,13 @@ def lowbit_mxfp8_quant(x, R, K, q, scale, stream=None):
 
 def lowbit_moe_silu_mul_quant(gate_up, R, I, q, scale, stream=None):
     return lib().lowbit_moe_silu_mul_quant(_ptr(gate_up), R, I, _ptr(q), _ptr(scale), _stream(stream))
+
+
+def lowbit_moe_gemm_silu_quant(fmt, E_local, I, K, packed, E, a_e4m3, a_ue8m0, a_rows, a_row_div, sorted_ids,
+                               expert_offsets, block_expert, num_valid, block_m, q, scale, stream=None):
+    return lib().lowbit_moe_gemm_silu_quant(fmt, E_local, I, K, _ptr(packed), E, _ptr(a_e4m3), _ptr(a_ue8m0), a_rows,
+                                            a_row_div, _ptr(sorted_ids), _ptr(expert_offsets), _ptr(block_expert),
+                                            num_valid, block_m, _ptr(q), _ptr(scale), _stream(stream))
 
 
 def lowbit_moe_combine(expert_out, topk_weights, T, top_k, H, y, stream=None):

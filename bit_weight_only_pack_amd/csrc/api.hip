@@ -527,6 +527,30 @@ int lowbit_moe_gemm(int fmt, int E_local, int N, int K, const void *packed, int 
                                       static_cast<uint16_t *>(out), (hipStream_t)stream));
 }
 
+int lowbit_moe_gemm_silu_quant(int fmt, int E_local, int I, int K, const void *packed, int E, const uint8_t *a_e4m3,
+                               const uint8_t *a_ue8m0, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                               const int32_t *expert_offsets, const int32_t *block_expert, int num_valid,
+                               int block_m, uint8_t *q, uint8_t *scale, void *stream)
+{
+    if (!is_lut3(fmt)) return LOWBIT_E_UNSUPPORTED;
+    if (I < 0 || I > (1 << 29)) return LOWBIT_E_INVALID_ARG;
+    int st = check_lut3_shape(E_local, 2 * I, K);
+    if (st != LOWBIT_OK) return st;
+    if (E <= 0 || a_rows < 0 || a_row_div <= 0 || num_valid < 0 || block_m <= 0) return LOWBIT_E_INVALID_ARG;
+    if (block_m % 16 != 0 || I % 128 != 0 || K > 4864) return LOWBIT_E_UNSUPPORTED;
+    if (num_valid > 0 && (int64_t)(num_valid - 1) / a_row_div >= a_rows) return LOWBIT_E_INVALID_ARG;
+    if ((int64_t)a_rows * K >= ((int64_t)1 << 31) || (int64_t)num_valid * I >= ((int64_t)1 << 31))
+        return LOWBIT_E_UNSUPPORTED;
+    if (num_valid == 0 || I == 0) return LOWBIT_OK;
+    if (packed == nullptr || q == nullptr || scale == nullptr || sorted_ids == nullptr ||
+        expert_offsets == nullptr || block_expert == nullptr || (K > 0 && (a_e4m3 == nullptr || a_ue8m0 == nullptr)))
+        return LOWBIT_E_INVALID_ARG;
+    const hipError_t e = launch_moe_gemm_silu(lut3_layout(E_local, 2 * I, K), static_cast<const uint8_t *>(packed),
+                                              E, a_e4m3, a_ue8m0, a_rows, a_row_div, sorted_ids, expert_offsets,
+                                              block_expert, num_valid, block_m, q, scale, (hipStream_t)stream);
+    return e == hipErrorNotSupported ? LOWBIT_E_UNSUPPORTED : hip_status(e);
+}
+
 int lowbit_mxfp8_quant(const void *x, int R, int K, uint8_t *q, uint8_t *scale, void *stream)
 {
     if (R < 0 || K < 0 || K % 32 != 0) return LOWBIT_E_INVALID_ARG;
@@ -610,10 +634,17 @@ int lowbit_moe_layer(const void *w13, const void *w2, int E_local, int E, int H,
     const int slots = T * top_k;
     hipError_t e = launch_moe_prep(static_cast<const uint16_t *>(x), T, H, xq, xs, topk_ids, slots, E, block_m,
                                    expert_map, sorted, offs, blk, npp, (int)w.capacity, s);
-    if (e == hipSuccess)
-        e = launch_moe_gemm(lut3_layout(E_local, 2 * I, H), static_cast<const uint8_t *>(w13), E, xq, xs, T, top_k,
-                            sorted, offs, blk, slots, block_m, gu, s);
-    if (e == hipSuccess) e = launch_mxfp8_rows(gu, slots, I, true, aq, as, s);
+    if (e == hipSuccess) {
+        // gate/up with SiLU(gate) * up -> MXFP8 in its epilogue where the shape
+        // allows it; otherwise bf16 gate/up rows and the stand-alone pass
+        e = launch_moe_gemm_silu(lut3_layout(E_local, 2 * I, H), static_cast<const uint8_t *>(w13), E, xq, xs, T,
+                                 top_k, sorted, offs, blk, slots, block_m, aq, as, s);
+        if (e == hipErrorNotSupported) {
+            e = launch_moe_gemm(lut3_layout(E_local, 2 * I, H), static_cast<const uint8_t *>(w13), E, xq, xs, T,
+                                top_k, sorted, offs, blk, slots, block_m, gu, s);
+            if (e == hipSuccess) e = launch_mxfp8_rows(gu, slots, I, true, aq, as, s);
+        }
+    }
     if (e == hipSuccess)
         e = launch_moe_gemm(lut3_layout(E_local, H, I), static_cast<const uint8_t *>(w2), E, aq, as, slots, 1, sorted,
                             offs, blk, slots, block_m, down, s);

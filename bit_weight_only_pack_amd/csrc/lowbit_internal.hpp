@@ -232,6 +232,13 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
                            const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
                            const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
                            uint16_t *out, hipStream_t s);
+// the gate/up GEMM (N = 2I) with SiLU(gate) * up as MXFP8 for its output
+// (act_q [num_valid][I] E4M3, act_s [num_valid][I/32] UE8M0) instead of the bf16
+// rows; hipErrorNotSupported (nothing launched) when the shape does not allow it
+hipError_t launch_moe_gemm_silu(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
+                                const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                                const int32_t *expert_offsets, const int32_t *block_expert, int num_valid,
+                                int block_m, uint8_t *act_q, uint8_t *act_s, hipStream_t s);
 
 // The MoE layer around the grouped GEMMs (moe_layer.hip)
 hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t R, int K, bool silu, uint8_t *q, uint8_t *scale,

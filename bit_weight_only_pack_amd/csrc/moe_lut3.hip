@@ -26,8 +26,12 @@
 //     32-K halves of a 64-K tile), accumulating in fp32.
 //   * One workgroup per (expert, 128-column tile) loops over all 16-row
 //     blocks of its expert, so each expert's weights stream from HBM once.
+//   * The gate/up GEMM of the layer can leave as SiLU(gate) * up in MXFP8
+//     (FUSE): a tile pairs gate columns with the matching up columns, and the
+//     epilogue encodes them with the stand-alone kernels' definitions.
 #include "lowbit_internal.hpp"
 #include "moe_align.hpp"
+#include "mxfp8.hpp"
 
 #include <algorithm>
 
@@ -163,6 +167,7 @@ struct MoeArgs {
     const uint8_t *aq, *as;            // activations [rows][K] E4M3, scales [rows][K/32] UE8M0
     const int32_t *sorted_ids, *expert_offsets, *block_expert;
     uint16_t *out;                     // bf16 [num_valid][N]
+    uint8_t *fq, *fs;                  // fused gate/up: SiLU(gate) * up as MXFP8 [num_valid][N/2], [..][N/64]
     int E, N, K, strips, ksteps, a_row_div, num_valid, block_m, n_tiles, a_rows;
 };
 
@@ -364,7 +369,12 @@ struct MoeGroupArgs {
     int gtiles, tiles_per_group, n_groups;         // tiles of 256 columns; tiles per workgroup
 };
 
-template <int MB, int D>
+// FUSE (the gate/up GEMM of the layer, N = 2I, I % 128 == 0): a tile is 128
+// gate columns (waves 0-7) and the matching 128 up columns (waves 8-15), and
+// the pass's output leaves as SiLU(gate) * up in MXFP8 (mxfp8.hpp) instead of
+// bf16 gate/up rows; gate and up are rounded to bf16 first, as the layer's
+// stand-alone kernels see them.
+template <int MB, int D, bool FUSE>
 __global__ __launch_bounds__(kGWaves * 64)
 void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
 {
@@ -387,13 +397,29 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
     if ((int)threadIdx.x < min(MB * 16, row1 - row0)) sid_first = p.sorted_ids[row0 + threadIdx.x];
     const int local = p.block_expert[row0 / p.block_m];
     const int col0 = tile0 * kGTileStrips * 16, col1 = min(p.N, (tile0 + ntl) * kGTileStrips * 16);
+    constexpr int kHalf = kGTileStrips / 2;                    // FUSE: gate (and up) strips per tile
+    const int half_strips = p.strips / 2;
 
     if (local < 0) {
-        // expert not on this device: its routed slots get zero rows
-        for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kGWaves * 4) {
-            const int sid = p.sorted_ids[rr];
-            if (sid >= p.num_valid) continue;
-            for (int n = col0 + (threadIdx.x & 15); n < col1; n += 16) p.out[(int64_t)sid * p.N + n] = 0;
+        // expert not on this device: its routed slots get zero rows (FUSE: the
+        // zero activation, codes 0 and scale byte 127, as MXFP8 gives for zeros)
+        if constexpr (FUSE) {
+            const int I = p.N / 2;
+            const int a0 = tile0 * kHalf * 16, a1 = min(I, (tile0 + ntl) * kHalf * 16);
+            for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kGWaves * 4) {
+                const int sid = p.sorted_ids[rr];
+                if (sid >= p.num_valid) continue;
+                for (int a = a0 + (threadIdx.x & 15); a < a1; a += 16) {
+                    p.fq[(int64_t)sid * I + a] = 0;
+                    if ((a & 31) == 0) p.fs[(int64_t)sid * (I / 32) + a / 32] = 127;
+                }
+            }
+        } else {
+            for (int rr = row0 + (threadIdx.x >> 4); rr < row1; rr += kGWaves * 4) {
+                const int sid = p.sorted_ids[rr];
+                if (sid >= p.num_valid) continue;
+                for (int n = col0 + (threadIdx.x & 15); n < col1; n += 16) p.out[(int64_t)sid * p.N + n] = 0;
+            }
         }
         return;
     }
@@ -425,7 +451,8 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
         const bool live = g < total;
 #pragma unroll
         for (int j = 0; j < kGSPW; ++j) {
-            const int s = (tile0 + ti) * kGTileStrips + wave * kGSPW + j;
+            const int s = FUSE ? (wave / kHalf) * half_strips + (tile0 + ti) * kHalf + wave % kHalf
+                               : (tile0 + ti) * kGTileStrips + wave * kGSPW + j;
             const bool ok = live && s < p.strips;
             const uint32_t unit = (uint32_t)(s * ksteps + t);
             const auto iv = __builtin_amdgcn_raw_buffer_load_b96(irs, ok ? unit * 768 + lane * 12 : kBufferOob, 0, 0);
@@ -576,6 +603,31 @@ void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
 
         // 4. the pass's output rows, 16 bytes per thread and step
         __syncthreads();
+        if constexpr (FUSE) {
+            // SiLU(gate) * up of 8 activation columns per thread; the four
+            // threads of a 32-block are one lane quad (rows change every 16
+            // threads), as mx_block_put needs
+            const int I = p.N / 2;
+            constexpr int kActChunks = kTileCols / 2 / 8;      // 16 per row
+            for (int idx = threadIdx.x; idx < ntl * nmb * 16 * kActChunks; idx += kGWaves * 64) {
+                const int cc = idx % kActChunks;
+                const int rr = idx / kActChunks;
+                const int tl = rr / (nmb * 16), row = rr - tl * nmb * 16;
+                const int sid = sid_lds[row];
+                const int a = (tile0 + tl) * (kTileCols / 2) + cc * 8;
+                if (sid >= p.num_valid || a >= I) continue;
+                const uint16_t *src = o_lds + (tl * MB * 16 + row) * kTileCols + cc * 8;
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float act = mx::silu_f32(mx::bf16_to_f32(src[i])) * mx::bf16_to_f32(src[kTileCols / 2 + i]);
+                    v[i] = mx::bf16_to_f32(mx::f32_to_bf16(act));
+                }
+                mx::mx_block_put(v, p.fq + (int64_t)sid * I + a, p.fs + (int64_t)sid * (I / 32) + a / 32,
+                                 (cc & 3) == 0);
+            }
+            continue;
+        }
         constexpr int kChunksPerRow = kTileCols / 8;
         for (int idx = threadIdx.x; idx < ntl * nmb * 16 * kChunksPerRow; idx += kGWaves * 64) {
             const int cc = idx % kChunksPerRow;
@@ -647,11 +699,15 @@ hipError_t launch_moe_align(const int32_t *topk_ids, int num_valid, int E, int b
     return hipGetLastError();
 }
 
-hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
+namespace {
+// fq / fs non-null: the fused gate/up form (FUSE); returns hipErrorNotSupported
+// when the shape does not allow it, before launching anything
+hipError_t moe_gemm_common(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
                            const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
                            const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
-                           uint16_t *out, hipStream_t s)
+                           uint16_t *out, uint8_t *fq, uint8_t *fs, hipStream_t s)
 {
+    const bool fuse = fq != nullptr;
     MoeArgs p;
     p.idx = packed + L.idx_off;
     p.cb = packed + L.cb_off;
@@ -662,6 +718,8 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
     p.expert_offsets = expert_offsets;
     p.block_expert = block_expert;
     p.out = out;
+    p.fq = fq;
+    p.fs = fs;
     p.E = (int)L.E;
     p.N = (int)L.N;
     p.K = (int)L.K;
@@ -679,13 +737,14 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
     constexpr int kMaxLds = 80 * 1024;
     constexpr int kMaxGroupLds = 150 * 1024;
     const int mb = moe_lds_bytes(2, p.K) <= kMaxLds ? 2 : (moe_lds_bytes(1, p.K) <= kMaxLds ? 1 : 0);
+    if (fuse && (mb == 0 || L.N % 256 != 0)) return hipErrorNotSupported;
     if (mb > 0) {
         // workgroups of 8 waves over groups of 256-column tiles: about 256
         // workgroups in all, so each expert's activations are staged once per
         // group instead of once per tile
         MoeGroupArgs ga;
         ga.m = p;
-        ga.gtiles = (int)((L.strips + kGTileStrips - 1) / kGTileStrips);
+        ga.gtiles = (int)((L.strips + kGTileStrips - 1) / kGTileStrips);   // FUSE: 128 activation columns each
         const int64_t want = (E_global * (int64_t)ga.gtiles + 255) / 256;     // tiles per workgroup for ~256
         ga.tiles_per_group = (int)std::max<int64_t>(1, std::min<int64_t>(want, ga.gtiles));
         // the group's output block has to fit the LDS as well
@@ -694,7 +753,8 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
         ga.n_groups = (ga.gtiles + ga.tiles_per_group - 1) / ga.tiles_per_group;
         const unsigned gblocks = (unsigned)((int64_t)E_global * ga.n_groups);
         const int lds = moe_lds_layout(mb, p.K, ga.tiles_per_group).bytes;
-        auto k = mb == 2 ? moe_lut3_gemm_lds_kernel<2, 5> : moe_lut3_gemm_lds_kernel<1, 5>;
+        auto k = fuse ? (mb == 2 ? moe_lut3_gemm_lds_kernel<2, 5, true> : moe_lut3_gemm_lds_kernel<1, 5, true>)
+                      : (mb == 2 ? moe_lut3_gemm_lds_kernel<2, 5, false> : moe_lut3_gemm_lds_kernel<1, 5, false>);
         hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         k<<<gblocks, kGWaves * 64, lds, s>>>(ga);
@@ -703,5 +763,25 @@ hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_glo
     }
     return hipGetLastError();
 }
+}  // namespace
+
+hipError_t launch_moe_gemm(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
+                           const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                           const int32_t *expert_offsets, const int32_t *block_expert, int num_valid, int block_m,
+                           uint16_t *out, hipStream_t s)
+{
+    return moe_gemm_common(L, packed, E_global, aq, as, a_rows, a_row_div, sorted_ids, expert_offsets, block_expert,
+                           num_valid, block_m, out, nullptr, nullptr, s);
+}
+
+hipError_t launch_moe_gemm_silu(const Lut3Layout &L, const uint8_t *packed, int E_global, const uint8_t *aq,
+                                const uint8_t *as, int a_rows, int a_row_div, const int32_t *sorted_ids,
+                                const int32_t *expert_offsets, const int32_t *block_expert, int num_valid,
+                                int block_m, uint8_t *act_q, uint8_t *act_s, hipStream_t s)
+{
+    return moe_gemm_common(L, packed, E_global, aq, as, a_rows, a_row_div, sorted_ids, expert_offsets, block_expert,
+                           num_valid, block_m, nullptr, act_q, act_s, s);
+}
+
 
 }  // namespace lowbit

@@ -400,6 +400,28 @@ int lowbit_mxfp8_quant(const void *x, int R, int K, uint8_t *q, uint8_t *scale, 
 int lowbit_moe_silu_mul_quant(const void *gate_up, int R, int I, uint8_t *q, uint8_t *scale, void *stream);
 
 /*
+ * The gate/up grouped GEMM and the SiLU(gate) * up MXFP8 step in one launch
+ * (the expert MLP of the "vLLM PR #62759 analysis", sections "Format" and
+ * "Emulation path"): the bytes written equal those of lowbit_moe_gemm with
+ * N = 2I into a bf16 [num_valid][2I] buffer followed by
+ * lowbit_moe_silu_mul_quant on it, without that buffer.  Slots of experts
+ * that are not local read as zero gate/up rows (q = 0, scale = 127).
+ *   fmt, E_local, K, packed : as lowbit_moe_gemm with N = 2I (the stacked
+ *                    gate and up projections, gate rows first)
+ *   E, a_e4m3, a_ue8m0, a_rows, a_row_div, sorted_ids, expert_offsets,
+ *   block_expert, num_valid, block_m : as lowbit_moe_gemm
+ *   q, scale       : u8 [num_valid][I] and u8 [num_valid][I/32] (outputs),
+ *                    rows indexed by slot id; rows no slot names are not written
+ * I % 128 == 0 and K <= 4864 (16 activation rows of K bytes fit the 80 KB
+ * staging area), else LOWBIT_E_UNSUPPORTED.
+ */
+int lowbit_moe_gemm_silu_quant(int fmt, int E_local, int I, int K, const void *packed, int E,
+                               const uint8_t *a_e4m3, const uint8_t *a_ue8m0, int a_rows, int a_row_div,
+                               const int32_t *sorted_ids, const int32_t *expert_offsets,
+                               const int32_t *block_expert, int num_valid, int block_m, uint8_t *q,
+                               uint8_t *scale, void *stream);
+
+/*
  * Router-weighted combine of the routed experts' outputs:
  *   y[t][h] = RNE_bf16( sum_{j < top_k} topk_weights[t][j] * expert_out[t*top_k + j][h] )
  * in fp32, j ascending.  Slots of experts that are not local have zero rows

@@ -198,6 +198,17 @@ def test_moe_layer_argument_checks():
     assert lb.lowbit_mxfp8_quant(None, 0, 64, None, None) == lb.LOWBIT_OK
     assert lb.lowbit_moe_silu_mul_quant(FAKE, 4, 40, FAKE, FAKE) == E_ARG         # I % 32
     assert lb.lowbit_moe_silu_mul_quant(FAKE, 4, 64, None, FAKE) == E_ARG
+    L3 = lb.LOWBIT_LUT3_E4M3
+    fused = lambda fmt, I, K, bm, q: lb.lowbit_moe_gemm_silu_quant(fmt, 4, I, K, FAKE, 4, FAKE, FAKE, 8, 2, FAKE,
+                                                                   FAKE, FAKE, 16, bm, q, FAKE)
+    assert fused(lb.LOWBIT_W4_SYM, 128, 256, 16, FAKE) == E_UNS
+    assert fused(L3, 192, 256, 16, FAKE) == E_UNS                                  # I % 128
+    assert fused(L3, 128, 4928, 16, FAKE) == E_UNS                                 # K past the staging area
+    assert fused(L3, 128, 256, 24, FAKE) == E_UNS                                  # block_m % 16
+    assert fused(L3, 128, 250, 16, FAKE) == E_ARG                                  # K % 64
+    assert fused(L3, 128, 256, 16, None) == E_ARG
+    assert lb.lowbit_moe_gemm_silu_quant(L3, 4, 128, 256, None, 4, None, None, 0, 2, None, None, None, 0, 16, None,
+                                         None) == lb.LOWBIT_OK
     assert lb.lowbit_moe_combine(FAKE, FAKE, 4, 2, 60, FAKE) == E_ARG             # H % 8
     assert lb.lowbit_moe_combine(None, None, 0, 2, 64, None) == lb.LOWBIT_OK
     wsb = lb.lowbit_moe_layer_workspace_bytes(256, 8, 128, 2048, 768, 16)
