@@ -174,7 +174,12 @@ void gemv_w4_kernel(const GemvBatch b)
 //   2. Each wave then issues the weight and metadata loads of its K tiles (a
 //      contiguous run of the strip), tile by tile.
 //   3. A wait for the x part only (issued first; vector loads retire in
-//      order) and one barrier.
+//      order) and one barrier.  With eight tiles per wave (16-wave
+//      workgroups, one per compute unit) the wait and barrier come after the
+//      first tile's loads and before the other seven: x reads issued ahead of
+//      a whole compute unit's weight stream still land behind much of it
+//      (measured 3.4-4.8 us into the down projection's launch, against
+//      0.7-1.1 us this way), and every tile product waits for x.
 //   4. Tiles in issue order, each waiting only for its own loads; the
 //      offset-split product (two MFMA chains per group, see gemv_tile.hpp).
 //   5. Fixed-order cross-wave sum through LDS, fp16 RNE store.
@@ -253,28 +258,35 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. weights and metadata of this wave's tiles
+    // 2. weights and metadata of this wave's tiles, in tile order; 3. x in
+    //    LDS everywhere, waited for after the first EARLY tiles' loads
     u4 q[T];
     MetaRaw<G, ASYM> mr[T];
-    {
-        const int64_t tiles0 = (int64_t)strip * kt;
-        const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
-        const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
-        const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+    constexpr int EARLY = T >= 8 ? 1 : T;
+    constexpr int LPT = ASYM ? 3 : 2;                // loads per tile (codes, scales[, zeros])
+    static_assert(NW == T * LPT, "load count");
+    const int64_t tiles0 = (int64_t)strip * kt;
+    const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
+    const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+    const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
 #pragma unroll
-        for (int u = 0; u < T; ++u) {
-            const int t = t0 + u;
-            const bool ok = u < tw && t < kt;
-            q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
-                                                         kStreamLoad);
-            mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
-            __builtin_amdgcn_sched_barrier(0);       // keep the loads in tile order
+    for (int u = 0; u < T; ++u) {
+        if (u == EARLY) {
+            wait_vm<EARLY * LPT>();                  // x has landed; tiles < EARLY may be in flight
+            wg_barrier();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        const int t = t0 + u;
+        const bool ok = u < tw && t < kt;
+        q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
+                                                     kStreamLoad);
+        mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+        __builtin_amdgcn_sched_barrier(0);           // keep the loads in tile order
     }
-
-    // 3. x in LDS everywhere
-    wait_vm<NW>();
-    wg_barrier();
+    if constexpr (EARLY == T) {
+        wait_vm<NW>();
+        wg_barrier();
+    }
 
     // 4. products, tile by tile in load order
     uint32_t mlo = kMagicLo, mhi = kMagicHi;
