@@ -228,28 +228,38 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. weights and metadata of this wave's tiles, tile by tile
+    // 2. weights and metadata of this wave's tiles, tile by tile; 3. the
+    //    activation loads landed (issued first; loads retire in order),
+    //    waited for after the first EARLY tiles' loads (eight tiles per wave:
+    //    after the first, so they do not land behind the compute unit's whole
+    //    weight stream)
     u4 q[T];
     MetaRaw<G, ASYM> mr[T];
-    {
-        const int64_t tiles0 = (int64_t)strip * kt;
-        const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
-        const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
-        const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+    constexpr int EARLY = T >= 8 ? 1 : T;
+    constexpr int LPT = ASYM ? 3 : 2;                // loads per tile (codes, scales[, zeros])
+    static_assert(NW == T * LPT, "load count");
+    const int64_t tiles0 = (int64_t)strip * kt;
+    const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
+    const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+    const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
 #pragma unroll
-        for (int u = 0; u < T; ++u) {
-            const int t = t0 + u;
-            const bool ok = u < tw && t < kt;
-            q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
-                                                         kStreamLoad);
-            mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+    for (int u = 0; u < T; ++u) {
+        if (u == EARLY) {
+            wait_vm<EARLY * LPT>();
+            wg_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
+        const int t = t0 + u;
+        const bool ok = u < tw && t < kt;
+        q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
+                                                     kStreamLoad);
+        mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+        __builtin_amdgcn_sched_barrier(0);
     }
-
-    // 3. activation loads landed (issued first; loads retire in order)
-    wait_vm<NW>();
-    wg_barrier();
+    if constexpr (EARLY == T) {
+        wait_vm<NW>();
+        wg_barrier();
+    }
 
     if constexpr (FUSED) {
         // 4. per-token maximum magnitude: each wave over the 8-K blocks of its

@@ -165,27 +165,36 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. codes and metadata of this wave's tiles
+    // 2. codes and metadata of this wave's tiles; 3. x in LDS everywhere,
+    //    waited for after the first EARLY tiles' loads (eight tiles per wave:
+    //    after the first, so the x reads do not land behind the compute
+    //    unit's whole weight stream)
     TT q[T];
     MetaRaw<G, ASYM> mr[T];
-    {
-        const int64_t tiles0 = (int64_t)strip * kt;
-        const auto crs = buffer_rsrc(codes + tiles0 * 256 * BITS, (uint32_t)kt * 256 * BITS);
-        const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
-        const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+    constexpr int EARLY = T >= 8 ? 1 : T;
+    constexpr int LPT = NLD + (ASYM ? 2 : 1);        // loads per tile (code planes, scales[, zeros])
+    static_assert(NW == T * LPT, "load count");
+    const int64_t tiles0 = (int64_t)strip * kt;
+    const auto crs = buffer_rsrc(codes + tiles0 * 256 * BITS, (uint32_t)kt * 256 * BITS);
+    const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+    const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
 #pragma unroll
-        for (int u = 0; u < T; ++u) {
-            const int t = t0 + u;
-            const bool ok = u < tw && t < kt;
-            q[u] = load_wb<BITS>(crs, ok, (uint32_t)t * 256 * BITS, lane);
-            mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+    for (int u = 0; u < T; ++u) {
+        if (u == EARLY) {
+            wait_vm<EARLY * LPT>();                  // x has landed; tiles < EARLY may be in flight
+            asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
+        const int t = t0 + u;
+        const bool ok = u < tw && t < kt;
+        q[u] = load_wb<BITS>(crs, ok, (uint32_t)t * 256 * BITS, lane);
+        mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+        __builtin_amdgcn_sched_barrier(0);
     }
-
-    // 3. x in LDS everywhere
-    wait_vm<NW>();
-    asm volatile("s_barrier" ::: "memory");
+    if constexpr (EARLY == T) {
+        wait_vm<NW>();
+        asm volatile("s_barrier" ::: "memory");
+    }
 
     // 4. products, tile by tile in load order
     uint32_t magic = 0x64006400u;                    // fp16 1024.0 in both halves
