@@ -179,7 +179,10 @@ void gemv_w4_kernel(const GemvBatch b)
 //      first tile's loads and before the other seven: x reads issued ahead of
 //      a whole compute unit's weight stream still land behind much of it
 //      (measured 3.4-4.8 us into the down projection's launch, against
-//      0.7-1.1 us this way), and every tile product waits for x.
+//      0.7-1.1 us this way), and every tile product waits for x.  A
+//      single-problem launch with four tiles per wave (the o projection)
+//      waits after two tiles; the batched four-tile launches after all four
+//      (an earlier wait measured slower there).
 //   4. Tiles in issue order, each waiting only for its own loads; the
 //      offset-split product (two MFMA chains per group, see gemv_tile.hpp).
 //   5. Fixed-order cross-wave sum through LDS, fp16 RNE store.
@@ -224,7 +227,7 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // workgroups, one per compute unit) 4.
 // The streaming kernel's work for one strip, once its problem's fields are
 // known (in scalar registers).
-template <int G, bool ASYM, int MR, int T>
+template <int G, bool ASYM, int MR, int T, bool SINGLE = false>
 __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_t *scales, const uint8_t *zeros,
                                               const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M,
                                               int W, int strip)
@@ -262,7 +265,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     //    LDS everywhere, waited for after the first EARLY tiles' loads
     u4 q[T];
     MetaRaw<G, ASYM> mr[T];
-    constexpr int EARLY = T >= 8 ? 1 : T;
+    constexpr int EARLY = T >= 8 ? 1 : (SINGLE && T == 4 ? 2 : T);
     constexpr int LPT = ASYM ? 3 : 2;                // loads per tile (codes, scales[, zeros])
     static_assert(NW == T * LPT, "load count");
     const int64_t tiles0 = (int64_t)strip * kt;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 
 void gemv_w4_v2_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
                        int kt, int tw, int M, int W, const uint8_t *zeros)
 {
-    gemv_v2_strip<G, ASYM, MR, T>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
+    gemv_v2_strip<G, ASYM, MR, T, true>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
 }
 
 // raises a kernel's dynamic LDS limit when a launch needs more than the default
