@@ -390,11 +390,22 @@ def bench_decode_asym(args, torch, lb, synth):
                                kernel_sum_ms=round(float(med.sum()) / 1e3, 4))
         del graph, keep, launches
         torch.cuda.empty_cache()
-    best = max(v["GBps"] for v in res.values())
-    return {"metric": "W4 asymmetric G=32 small-batch decode step effective HBM GB/s", "value": best,
-            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
-            "dtype": "f16", "data": "synthetic", "vs_baseline": None,
-            "config": {"workload": "llama3-8b-w4-asym-g32-decode-step", "M": [1, 2, 4, 8], "group_size": G},
+    r1 = res["M=1"]
+    nl = 128                                         # launches per step (32 layers x 4 groups)
+    ach = r1["bytes_per_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
+    return {"metric": "W4 asymmetric G=32 decode step effective HBM GB/s (M=1; M=2, 4, 8 in per_M)",
+            "value": r1["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": r1["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "dtype": "f16", "data": "synthetic (seeded; INT4 codes, fp16 scales, int8 zero points, 1 % outlier "
+                                    "fp16 inputs)", "vs_baseline": None,
+            "config": {"workload": "llama3-8b-w4-asym-g32-decode-step", "M": 1, "M_list": [1, 2, 4, 8],
+                       "group_size": G},
+            "tokens_per_s": r1["tokens_per_s"],
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "gemv_w4_v2 (G=32, asymmetric, M=1)",
+                         "bytes_per_launch": r1["bytes_per_step"] // nl,
+                         "avg_launch_us": round(r1["ms_per_step"] * 1e3 / nl, 3)},
             "per_M": res}
 
 
@@ -619,7 +630,9 @@ def bench_prefill(args, torch, lb, synth):
             del graph, b_dense, c_bf
     agg = total_flop / (total_ms * 1e-3) / 1e12
     return {"metric": "W4 prefill GEMM TFLOP/s (bf16 MFMA, fp32 accumulate)", "value": round(agg, 1),
-            "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": max(3, args.steps // 5), "warmup": 2,
+            "ms_per_step": round(total_ms, 4), "higher_is_better": True, "scaling": "weak", "dtype": "bf16",
+            "data": "synthetic",
             "vs_baseline": None, "config": {"workload": "w4-prefill-gemm", "group_size": G},
             "roofline": {"bound": "mfma", "achieved": round(agg, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
