@@ -128,7 +128,7 @@ __device__ __forceinline__ h8 wb_offset(int z)
     return h8{o, o, o, o, o, o, o, o};
 }
 
-template <int BITS, int G, bool ASYM, int MR, int T>
+template <int BITS, int G, bool ASYM, int MR, int T, bool SINGLE = false>
 __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *scales, const uint8_t *zeros,
                                          const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M, int W,
                                          int strip)
@@ -168,10 +168,11 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     // 2. codes and metadata of this wave's tiles; 3. x in LDS everywhere,
     //    waited for after the first EARLY tiles' loads (eight tiles per wave:
     //    after the first, so the x reads do not land behind the compute
-    //    unit's whole weight stream)
+    //    unit's whole weight stream; a single-problem launch with four tiles
+    //    per wave: after two)
     TT q[T];
     MetaRaw<G, ASYM> mr[T];
-    constexpr int EARLY = T >= 8 ? 1 : T;
+    constexpr int EARLY = T >= 8 ? 1 : (SINGLE && T == 4 ? 2 : T);
     constexpr int LPT = NLD + (ASYM ? 2 : 1);        // loads per tile (code planes, scales[, zeros])
     static_assert(NW == T * LPT, "load count");
     const int64_t tiles0 = (int64_t)strip * kt;
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 
 void gemv_wb_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
                     int kt, int tw, int M, int W, const uint8_t *zeros)
 {
-    wb_strip<BITS, G, ASYM, MR, T>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
+    wb_strip<BITS, G, ASYM, MR, T, true>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
 }
 
 // problems laid end to end over blockIdx.x (b.first[i] = first workgroup of
