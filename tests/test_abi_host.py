@@ -25,7 +25,7 @@ def _declared():
     return names
 
 
-def test_header_declares_the_north_star_entry_points():
+def test_header_declares_the_hot_path_entry_points():
     d = _declared()
     for name in ("lowbit_pack_weights", "lowbit_gemv"):
         assert name in d
