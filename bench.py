@@ -29,6 +29,8 @@ Other workloads (--workload), one JSON line each:
                 256 tokens, hidden 2048, intermediate 768: MXFP8 of the hidden
                 rows, alignment, gate/up GEMM, SiLU*up -> MXFP8, down GEMM,
                 router-weighted combine
+  tiny        : the 1x256x256 G=32 GEMV, latency per call (graph of 100 calls,
+                and one call with a host synchronize), the oracle beside it
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -776,13 +778,90 @@ def bench_moe(args, torch, lb, synth):
     return out
 
 
+def bench_tiny(args, torch, lb, synth):
+    """The tiny GEMV workload (M=1, K=256, N=256, G=32, symmetric, scales
+    U[0.005, 0.02]): latency per call.  On the GPU: a graph of CALLS
+    back-to-back calls (stream order, each a full launch) replayed, and a graph
+    of one call replayed with a host synchronize after each replay (launch +
+    completion as a caller sees it).  Beside it the CPU oracle on the same
+    inputs, one thread on one pinned core."""
+    N = K = 256
+    G, M, CALLS = 32, 1, 100
+    fmt = lb.LOWBIT_W4_SYM
+    w = synth.w4_weights(N, K, G, scale_range=(0.005, 0.02), workload_id=0)
+    x_np = synth.activations_f16(M, K, workload_id=0)
+    nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
+    packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, torch.from_numpy(w["qweight"]).cuda(),
+                                    torch.from_numpy(w["scales"].view(np.uint16)).cuda(), None, packed, nb))
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    st = stream.cuda_stream
+
+    def calls(n):
+        for _ in range(n):
+            r = lb.lowbit_gemv(fmt, M, N, K, G, packed, x, y, None, 0, st)
+            if r != 0:
+                raise lb.LowbitError(r)
+    g100 = capture(torch, lambda: calls(CALLS), stream)
+    ms100, gpu100 = time_graph(torch, g100, stream, args.steps, args.warmup)
+    g1 = capture(torch, lambda: calls(1), stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            g1.replay()
+    torch.cuda.synchronize()
+    lat = []
+    for _ in range(max(args.steps, 20)):
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            g1.replay()
+        stream.synchronize()
+        lat.append((time.perf_counter() - t0) * 1e6)
+    # parity of the timed output against the oracle (smoke-level check)
+    import oracle
+    _, ref = oracle.w4_matmul(x_np, "f16", w["qweight"], w["scales"], None, G, "f16")
+    got = y.cpu().numpy().astype(np.float64)
+    refd = ref.view(np.float16).astype(np.float64)
+    rel = float(np.linalg.norm(got - refd) / np.linalg.norm(refd))
+    reps = 2000
+    with PinnedOneCore():
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.w4_matmul(x_np, "f16", w["qweight"], w["scales"], None, G, "f16")
+        cpu_s = (time.perf_counter() - t0) / reps
+    nbytes = w4_bytes(K, N, M, G, False)
+    us_call = gpu100 * 1e3 / CALLS
+    out = {"metric": "W4A16 GEMV 1x256x256 G=32 latency (us per call)", "value": round(us_call, 3), "unit": "us",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(gpu100 / CALLS, 6),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic (seeded; INT4 codes U{0..15}, fp16 scales U[0.005,0.02], N(0,1) fp16 input)",
+           "config": {"workload": "w4a16-gemv-1x256x256-g32", "M": M, "N": N, "K": K, "group_size": G,
+                      "calls_per_graph": CALLS, "bytes_per_call": nbytes},
+           "us_per_call_graph_of_%d" % CALLS: round(us_call, 3),
+           "us_single_call_with_host_sync": {"median": round(float(np.median(lat)), 2),
+                                             "p10": round(float(np.percentile(lat, 10)), 2),
+                                             "p90": round(float(np.percentile(lat, 90)), 2)},
+           "parity_rel_l2_vs_oracle": rel,
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / (us_call * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(nbytes / (us_call * 1e-6) / 1e9 / HBM_PEAK_GBPS, 6),
+                        "traffic": None, "kernel": "gemv_w4_v2_single<G=32,sym,MR=1,T=2> (one workgroup per "
+                                                   "16-row strip: 16 workgroups)",
+                        "bytes_per_launch": nbytes, "avg_launch_us": round(us_call, 3),
+                        "note": "latency-bound: 37,888 bytes stay in L2, the figure is launch and dependency cost"},
+           "cpu_baseline": {"value": round(cpu_s * 1e6, 2), "unit": "us", "cores": 1, "kind": "oracle",
+                            "sample": "the same GEMV, %d calls on one pinned core, %.2f s" % (reps, cpu_s * reps),
+                            "ms_per_call": round(cpu_s * 1e3, 4)}}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-asym", "decode-w4a8", "decode-bits", "prefill", "moe"])
+                    choices=["decode", "decode-asym", "decode-w4a8", "decode-bits", "prefill", "moe", "tiny"])
     ap.add_argument("--mode", default="batched", choices=["chain", "batched", "unfused"],
                     help="decode: chain = the whole step as one persistent launch with stage dependencies; "
                          "batched = one launch per group of GEMVs sharing an input (4 per layer); "
@@ -812,7 +891,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"decode": bench_decode, "decode-asym": bench_decode_asym, "decode-w4a8": bench_decode_w4a8,
-          "decode-bits": bench_decode_bits, "prefill": bench_prefill, "moe": bench_moe}[args.workload]
+          "decode-bits": bench_decode_bits, "prefill": bench_prefill, "moe": bench_moe,
+          "tiny": bench_tiny}[args.workload]
     out = fn(args, torch, lb, synth)
     if SCLK_SAMPLES:
         v = sorted(SCLK_SAMPLES)

@@ -58,6 +58,14 @@ W4Layout dense_layout(int fmt, int64_t N, int64_t K, int G)
 // canonical code bytes of one matrix: two codes per byte for INT4, one otherwise
 int64_t dense_code_bytes(int fmt, int64_t N, int64_t K) { return is_uint_fmt(fmt) ? N * K : N * (K / 2); }
 
+// The GEMV and GEMM kernels address their operands through buffer
+// descriptors with 32-bit byte offsets, and an offset of 2^31 stands for "past
+// the end" (it reads zeros).  Every region one descriptor spans must therefore
+// stay below 2^31 bytes: the activation rows, one 16-row strip of codes (the
+// GEMV's descriptors are per strip), and for the GEMM the whole packed blob.
+constexpr int64_t kOffsetLimit = (int64_t)1 << 31;
+bool gemv_offsets_ok(int M, int64_t K) { return (int64_t)M * K * 2 < kOffsetLimit && K * 16 < kOffsetLimit; }
+
 bool is_lut3(int fmt) { return fmt == LOWBIT_LUT3_E4M3; }
 
 int check_lut3_shape(int E, int N, int K)
@@ -223,6 +231,7 @@ int lowbit_gemv(int fmt, int M, int N, int K, int group_size, const void *packed
     if (M == 0 || N == 0) return LOWBIT_OK;
     if (packed == nullptr || y == nullptr || (K > 0 && x == nullptr)) return LOWBIT_E_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+    if (!gemv_offsets_ok(M, K)) return LOWBIT_E_UNSUPPORTED;
     if (ws_bytes < gemv_w4_workspace(M, N, K, group_size)) return LOWBIT_E_WORKSPACE;
     const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
     return hip_status(launch_gemv_w4(L, M, static_cast<const uint8_t *>(packed),
@@ -249,6 +258,7 @@ int lowbit_gemv_batched(int fmt, int M, int group_size, int count, const lowbit_
         if (p.N == 0) continue;                        // nothing to compute for this one
         if (p.packed == nullptr || p.y == nullptr || (p.K > 0 && p.x == nullptr)) return LOWBIT_E_INVALID_ARG;
         if (reinterpret_cast<uintptr_t>(p.x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+        if (!gemv_offsets_ok(M, p.K)) return LOWBIT_E_UNSUPPORTED;
         L[n] = dense_layout(fmt, p.N, p.K, group_size);
         kt_max = L[n].ktiles > kt_max ? L[n].ktiles : kt_max;
         packed[n] = static_cast<const uint8_t *>(p.packed);
@@ -289,6 +299,7 @@ int w4a8_prepare(int fmt, int M, int group_size, int count, const lowbit_gemv_pr
         if (p.N == 0) continue;
         if (p.packed == nullptr || p.y == nullptr || (p.K > 0 && p.x == nullptr)) return LOWBIT_E_INVALID_ARG;
         if (reinterpret_cast<uintptr_t>(p.x) % 16 != 0) return LOWBIT_E_INVALID_ARG;
+        if (!gemv_offsets_ok(M, p.K)) return LOWBIT_E_UNSUPPORTED;
         L[n] = w4_layout(p.N, p.K, group_size, fmt == LOWBIT_W4_ASYM);
         packed[n] = static_cast<const uint8_t *>(p.packed);
         x[n] = static_cast<const _Float16 *>(p.x);
@@ -481,9 +492,11 @@ int lowbit_gemm(int fmt, int M, int N, int K, int group_size, const void *packed
     if (M == 0 || N == 0) return LOWBIT_OK;
     if (packed == nullptr || c == nullptr || (K > 0 && a == nullptr)) return LOWBIT_E_INVALID_ARG;
     if ((int64_t)M * K > (int64_t)INT32_MAX || (int64_t)M * N > (int64_t)INT32_MAX) return LOWBIT_E_UNSUPPORTED;
+    const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
+    // A and the packed blob are each one 32-bit-offset descriptor
+    if ((int64_t)M * K * 2 >= kOffsetLimit || L.bytes >= kOffsetLimit) return LOWBIT_E_UNSUPPORTED;
     const size_t need = gemm_w4_workspace(M, N, K, group_size);
     if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LOWBIT_E_WORKSPACE;
-    const W4Layout L = w4_layout(N, K, group_size, fmt == LOWBIT_W4_ASYM);
     return hip_status(launch_gemm_w4(L, M, static_cast<const uint8_t *>(packed), a, a_dtype == LOWBIT_BF16, c,
                                      c_dtype == LOWBIT_BF16, workspace, ws_bytes, (hipStream_t)stream));
 }

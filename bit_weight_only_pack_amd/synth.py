@@ -2,7 +2,11 @@
 
 This module only draws random numbers and converts them to the storage types
 with library conversions (numpy float16, torch bfloat16 / float8).  It holds
-none of the method's arithmetic: no dequantization, no products, no packing.
+none of the arithmetic the library computes: no dequantization, no products,
+no packing.  One generator, ``mxfp8_activations``, builds ready-made MXFP8
+inputs for the grouped GEMM with its own numpy block-scale rule (an input
+recipe only: the library's MXFP8 quantizer is never compared with it, and
+the oracle consumes whatever bytes it returns).
 Both the GPU tests and the CPU oracle consume the arrays it returns.
 
 Every tensor has its own generator, ``default_rng(SeedSequence([20261203,

@@ -241,3 +241,21 @@ def test_uint_formats_host_rules():
     assert lb.lowbit_gemv(f3, 1, 64, 16384 + 128, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS       # > 8 tiles per wave
     assert lb.lowbit_gemm(f3, 64, 64, 512, 32, FAKE, FAKE, lb.LOWBIT_BF16, FAKE, lb.LOWBIT_BF16, None, 0) == E_UNS
     assert lb.lowbit_gemv_w4a8(f3, 1, 64, 512, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS
+
+
+def test_32bit_offset_limits_rejected_on_the_host():
+    """The GEMV and GEMM kernels address operands through 32-bit buffer
+    offsets with 2^31 as the out-of-range marker, so a region one descriptor
+    spans must stay below 2^31 bytes; larger shapes are refused before any
+    launch instead of wrapping."""
+    BF = lb.LOWBIT_BF16
+    # packed blob of 2^31 bytes or more (N = K = 65536: 2 GiB of codes)
+    assert lb.lowbit_gemm(SYM, 16, 65536, 65536, 128, FAKE, FAKE, BF, FAKE, BF, FAKE, 1 << 40) == E_UNS
+    # activation rows of 2^31 bytes (M * K * 2)
+    assert lb.lowbit_gemm(SYM, 1 << 16, 256, 1 << 14, 128, FAKE, FAKE, BF, FAKE, BF, FAKE, 1 << 40) == E_UNS
+    # GEMV: M * K * 2 and one strip of codes (16 rows x K bytes at 8 bits)
+    assert lb.lowbit_gemv(SYM, 16, 256, 1 << 26, 128, FAKE, FAKE, FAKE, None, 0) == E_UNS
+    assert lb.lowbit_gemv(lb.LOWBIT_UINT(8), 1, 256, 1 << 27, 128, FAKE, FAKE, FAKE, None, 0) == E_UNS
+    p = lb.make_gemv_problems([(FAKE, FAKE, FAKE, 256, 1 << 26)])
+    assert lb.lowbit_gemv_batched(SYM, 16, 128, 1, p) == E_UNS
+    assert lb.lowbit_gemv_w4a8(ASYM, 16, 256, 1 << 26, 32, FAKE, FAKE, FAKE, FAKE, 1 << 40) == E_UNS

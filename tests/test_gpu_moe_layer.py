@@ -289,3 +289,45 @@ def test_moe_gemm_silu_quant_equals_two_stages(T, E, top_k, H, I, local):
     _, rgu = oracle.moe_gemm(d13["idx"], d13["cb"], d13["ex"], rxq, rxs, top_k, topk, emap)
     raq, ras = oracle.silu_mul_quant(rgu)
     assert (a == raq).mean() >= 0.995 and (sc == ras).mean() >= 0.995
+
+
+def test_moe_layer_stage_fed_down_and_combine_full_config():
+    """The down GEMM and the combine of the 128-expert top-8 layer (T = 256,
+    H = 2048, I = 768) held to the matmul bound (rel-L2 <= 1e-3, max <= 1e-2 *
+    max |y_ref|).  The oracle's down GEMM and combine are fed the GPU's own
+    SiLU(gate) * up MXFP8 codes and scales, so the bf16/E4M3 re-quantization
+    between the GEMMs (which the whole-layer bound above accounts for) is
+    taken out; the layer's output must equal the stages' bit for bit
+    ("vLLM PR #62759 analysis", emulation path: MXFP8 activations before each
+    expert GEMM; A gather: slot rows of the down GEMM)."""
+    T, E, top_k, H, I, bm = 256, 128, 8, 2048, 768, 16
+    S = T * top_k
+    d13, d2, x, topk, w = _layer_case(T, E, top_k, H, I, seed=4)
+    y_layer = _run_layer(d13, d2, x, topk, w, E, H, I, block_m=bm)
+    xq, xs = _quant(lb.lowbit_mxfp8_quant, x, T, H)
+    cap = S + E * (bm - 1)
+    ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    blk = torch.empty(cap // bm, dtype=torch.int32, device="cuda")
+    npp = torch.empty(1, dtype=torch.int32, device="cuda")
+    lb.check(lb.lowbit_moe_align(dev(topk), T, top_k, E, bm, None, ids, offs, blk, npp))
+    L3 = lb.LOWBIT_LUT3_E4M3
+    aq = torch.full((S, I), 0x55, dtype=torch.uint8, device="cuda")
+    as_ = torch.full((S, I // 32), 0x55, dtype=torch.uint8, device="cuda")
+    lb.check(lb.lowbit_moe_gemm_silu_quant(L3, E, I, H, _pack(d13, E, 2 * I, H), E, dev(xq), dev(xs), T, top_k, ids,
+                                           offs, blk, S, bm, aq, as_))
+    down = torch.zeros((S, H), dtype=torch.int16, device="cuda")
+    lb.check(lb.lowbit_moe_gemm(L3, E, H, I, _pack(d2, E, H, I), E, aq, as_, S, 1, ids, offs, blk, S, bm, down))
+    y = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    lb.check(lb.lowbit_moe_combine(down, dev(w), T, top_k, H, y))
+    torch.cuda.synchronize()
+    assert np.array_equal(y_layer, y.cpu().numpy().view(np.uint16))
+    # the oracle's down GEMM + combine on the GPU's codes, for 32 seeded tokens
+    # (a token's output depends only on its own top_k slot rows)
+    tok = np.sort(np.random.default_rng(11).choice(T, 32, replace=False))
+    slots = (tok[:, None] * top_k + np.arange(top_k)[None, :]).reshape(-1)
+    a_sub = aq.cpu().numpy()[slots]
+    s_sub = as_.cpu().numpy()[slots]
+    _, rdown = oracle.moe_gemm(d2["idx"], d2["cb"], d2["ex"], a_sub, s_sub, 1, topk[tok])
+    _, ry = oracle.moe_combine(rdown, w[tok], top_k)
+    assert_close(bf16_bits_to_f64(y_layer[tok]), bf16_bits_to_f64(ry), "layer fed the GPU's SiLU*up codes")

@@ -156,10 +156,13 @@ def test_gemv_llama3_8b_shapes_sym(proj):
 
 
 @pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
 def test_gemv_llama3_8b_shapes_asym_g32(proj, M):
     """Asymmetric G=32 with 1% outlier channels x20 at full size; outputs of a
-    seeded sample of 128 weight rows are checked against the oracle."""
+    seeded sample of 128 weight rows are checked against the oracle.  The
+    down projection (K = 14336) at M = 2 runs the streaming kernel with two
+    accumulator rows and eight tiles per wave, the one the asymmetric decode
+    step times at M = 2."""
     _, K, N = next(p for p in synth.LLAMA3_8B_PROJS if p[0] == proj)
     pid = [p[0] for p in synth.LLAMA3_8B_PROJS].index(proj)
     w = synth.w4_weights(N, K, 32, asym=True, workload_id=2, layer=0, part=pid)
