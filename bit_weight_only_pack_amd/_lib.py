@@ -73,6 +73,7 @@ SIGNATURES = {
     "lowbit_gemv_w4a8": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lowbit_gemv_w4a8_batched_workspace_bytes": (_sz, [_i, _i, _i, _i, _vp]),
     "lowbit_gemv_w4a8_batched": (_i, [_i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "lowbit_gemv_w4a8_batched_noalloc": (_i, [_i, _i, _i, _i, _vp, _vp]),
     "lowbit_gemv_chain_bytes": (_sz, [_i, _i]),
     "lowbit_gemv_chain_init": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, ctypes.c_uint, _vp, _sz, _vp]),
     "lowbit_gemv_chain_run": (_i, [_vp, _vp]),
@@ -259,6 +260,12 @@ def lowbit_gemv_w4a8_batched(fmt, M, group_size, count, problems, workspace=None
     """problems: a ctypes array from make_gemv_problems (host memory)."""
     return lib().lowbit_gemv_w4a8_batched(fmt, M, group_size, count, ctypes.cast(problems, ctypes.c_void_p),
                                           _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def lowbit_gemv_w4a8_batched_noalloc(fmt, M, group_size, count, problems, stream=None):
+    """problems: a ctypes array from make_gemv_problems (host memory)."""
+    return lib().lowbit_gemv_w4a8_batched_noalloc(fmt, M, group_size, count, ctypes.cast(problems, ctypes.c_void_p),
+                                                  _stream(stream))
 
 
 def lowbit_gemv_chain_bytes(count, stages):

@@ -289,7 +289,8 @@ namespace {
 // Shared by the single and batched W4A8 entry points: validates the
 // problems, keeps the non-empty ones, checks the plan and the workspace.
 int w4a8_prepare(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems, void *workspace,
-                 size_t ws_bytes, W4Layout *L, const uint8_t **packed, const _Float16 **x, _Float16 **y, int *n_out)
+                 size_t ws_bytes, W4Layout *L, const uint8_t **packed, const _Float16 **x, _Float16 **y, int *n_out,
+                 size_t *need_out = nullptr)
 {
     int n = 0;
     for (int i = 0; i < count; ++i) {
@@ -311,6 +312,7 @@ int w4a8_prepare(int fmt, int M, int group_size, int count, const lowbit_gemv_pr
     size_t need = 0;
     const int mode = gemv_w4a8_plan(L, n, M, &need);
     if (mode < 0) return LOWBIT_E_UNSUPPORTED;
+    if (need_out) *need_out = need;
     if (need > 0 && (workspace == nullptr || ws_bytes < need)) return LOWBIT_E_WORKSPACE;
     if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return LOWBIT_E_INVALID_ARG;
     return LOWBIT_OK;
@@ -362,6 +364,32 @@ int lowbit_gemv_w4a8_batched(int fmt, int M, int group_size, int count, const lo
     int st = w4a8_prepare(fmt, M, group_size, count, problems, workspace, ws_bytes, L, packed, x, y, &n);
     if (st != LOWBIT_OK || n == 0) return st;
     return hip_status(launch_gemv_w4a8_batch(L, n, M, packed, x, y, workspace, (hipStream_t)stream));
+}
+
+int lowbit_gemv_w4a8_batched_noalloc(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems,
+                                     void *stream)
+{
+    if (count < 0 || M < 0) return LOWBIT_E_INVALID_ARG;
+    if (count > kMaxGemvBatch || M > 16) return LOWBIT_E_UNSUPPORTED;
+    if (count == 0 || M == 0) return LOWBIT_OK;
+    if (problems == nullptr) return LOWBIT_E_INVALID_ARG;
+    W4Layout L[kMaxGemvBatch];
+    const uint8_t *packed[kMaxGemvBatch];
+    const _Float16 *x[kMaxGemvBatch];
+    _Float16 *y[kMaxGemvBatch];
+    int n = 0;
+    size_t need = 0;
+    // validated against the scratch size before any HIP call; the address is a
+    // placeholder here (never dereferenced: only its alignment is checked)
+    int st = w4a8_prepare(fmt, M, group_size, count, problems, reinterpret_cast<void *>(256), kW4a8ScratchBytes, L,
+                          packed, x, y, &n, &need);
+    if (st != LOWBIT_OK || n == 0) return st;
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = w4a8_scratch(&ws);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(launch_gemv_w4a8_batch(L, n, M, packed, x, y, ws, (hipStream_t)stream));
 }
 
 size_t lowbit_gemv_chain_bytes(int count, int stages)

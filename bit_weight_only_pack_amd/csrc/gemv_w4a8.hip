@@ -30,10 +30,41 @@
 //   * Schedule of the W4A16 streaming GEMV: one workgroup per 16-row strip,
 //     waves split K into runs of at most 8 tiles, every weight load issued up
 //     front with the non-temporal hint, fixed-order cross-wave sum.
+#include <mutex>
+
 #include "lowbit_internal.hpp"
 #include "gemv_tile.hpp"
 
 namespace lowbit {
+
+// Scratch for the entry point that allocates nothing
+// (lowbit_gemv_w4a8_batched_noalloc): the activation blocks of up to eight
+// problems, written by quant_act_kernel and read by the GEMV of the same
+// call.  Each GPU the library runs on holds one copy until the process ends.
+// In host code `scratch` is only a stand-in for the symbol; kernels receive
+// the device address that w4a8_scratch() looked up for the current device.
+static __device__ __align__(256) uint8_t scratch[kW4a8ScratchBytes];
+
+hipError_t w4a8_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // once per device, with that device current: each GPU has its own copy
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 namespace {
 

@@ -160,6 +160,10 @@ int gemv_w4a8_plan(const W4Layout *L, int count, int M, size_t *ws_bytes);
 hipError_t launch_gemv_w4a8_batch(const W4Layout *L, int count, int M, const uint8_t *const *packed,
                                   const _Float16 *const *x, _Float16 *const *y, void *ws, hipStream_t s);
 hipError_t launch_quant_act_i8(int M, int K, const _Float16 *x, int8_t *xq, float *sx, hipStream_t s);
+// The W4A8 GEMV's static scratch (gemv_w4a8.hip): its size, and its device
+// address on the current device (looked up once per device)
+constexpr size_t kW4a8ScratchBytes = (size_t)512 << 10;
+hipError_t w4a8_scratch(void **ptr);
 
 // A chain of dependent GEMV stages run by one persistent launch
 // (gemv_chain.hip).  Device buffer: counters, then the ChainProb table, then

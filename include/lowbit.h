@@ -235,6 +235,26 @@ int lowbit_gemv_w4a8_batched(int fmt, int M, int group_size, int count, const lo
                              void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * lowbit_gemv_w4a8_batched without a workspace argument, for callers that
+ * cannot allocate device memory at all (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The activation blocks go
+ * to a static 512 KiB device array inside the library instead of a caller
+ * workspace; the call allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine).  Results equal lowbit_gemv_w4a8_batched's bit
+ * for bit (same kernels).
+ *   Limit: the plan's workspace (lowbit_gemv_w4a8_batched_workspace_bytes for
+ *   the same problems) must be <= 512 KiB, else LOWBIT_E_WORKSPACE before
+ *   anything is enqueued; every 8B decode launch up to M = 8 fits (at most 130 KB; M = 1 needs
+ *   none).  The scratch address of a device is looked up on the first call
+ *   made with that device current (a failure returns LOWBIT_E_HIP).
+ *   Calls that overlap on one GPU (different streams, or different host
+ *   threads) share that GPU's array and race: serialize them.  Each call
+ *   rewrites every scratch byte it later reads, so nothing needs clearing.
+ */
+int lowbit_gemv_w4a8_batched_noalloc(int fmt, int M, int group_size, int count, const lowbit_gemv_problem *problems,
+                                     void *stream);
+
+/*
  * A chain of dependent GEMV stages executed by ONE persistent launch: a whole
  * decode step (every projection of every layer) as a single submission
  * ("BaseRT" wiki chapter, limitations and approach: at batch 1 the per-command
