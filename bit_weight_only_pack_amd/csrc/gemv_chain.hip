@@ -125,20 +125,52 @@ __device__ __forceinline__ void load_round(Slot<G, ASYM> &s, const Cursor &p, CP
     }
 }
 
+// Constants of the offset-split product (gemv_tile.hpp), kept in registers.
+struct SplitConst {
+    uint32_t mlo, mhi;
+    h8 psym;
+};
+
 // Branch-free: a tile past the strip's end has zero codes and zero scales
 // (its loads read out of range), so its product adds exactly zero; its
 // activation address is clamped to the last real tile so it only reads
-// finite values.
+// finite values.  The product is the offset-split one of the streaming GEMV
+// (gemv_tile.hpp): one MFMA chain over the codes and, for batch-1 symmetric
+// weights, the offset terms of up to four tiles from one shared chain whose
+// A rows carry the K blocks of different (tile, group) pairs; otherwise a
+// second chain per tile over the zero-point operand.
 template <int G, bool ASYM, int MR>
 __device__ __forceinline__ void compute_round(const Slot<G, ASYM> &s, const Cursor &c, CProb *P,
-                                              const _Float16 *xa, int wave, uint32_t magic, f4 &acc)
+                                              const _Float16 *xs, const _Float16 *xa, int wave, int lane,
+                                              const SplitConst &k, f4 &acc)
 {
+    constexpr int GPT = 128 / G;
+    constexpr int MPG = G / 32;
+    constexpr bool PRE = !ASYM && MR == 1;
+    constexpr int TPS = 4 / GPT;                     // tiles per shared offset chain
     const int kt = P[c.pi].ktiles;
+    const int r = lane & 15, kq = lane >> 4;
+    f4 cps = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kTilesPerWave; ++u) {
         const int t = c.rr * kRoundTiles + wave + u * kComputeWaves;
         const int tx = t < kt ? t : kt - 1;
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PRE) {
+            if (u % TPS == 0) {
+                // A row j < 4: tile u + j / GPT, group j % GPT (C row j = its offset term)
+                const int rr = r < 4 ? r : 0;
+                const int tu = c.rr * kRoundTiles + wave + (u + rr / GPT) * kComputeWaves;
+                const int txu = tu < kt ? tu : kt - 1;
+                const _Float16 *xb = xs + txu * 128 + (rr % GPT) * G + kq * 8;
+#pragma unroll
+                for (int b = 0; b < MPG; ++b) {
+                    const h8 ab = *reinterpret_cast<const h8 *>(xb + b * 32);
+                    cps = __builtin_amdgcn_mfma_f32_16x16x32_f16(ab, k.psym, b == 0 ? f4{0.f, 0.f, 0.f, 0.f} : cps, 0,
+                                                                 0, 0);
+                }
+            }
+        }
         u4 qv = s.q[u];
         asm volatile("" : "+v"(qv));
         MetaRaw<G, ASYM> mv = s.m[u];
@@ -146,7 +178,14 @@ __device__ __forceinline__ void compute_round(const Slot<G, ASYM> &s, const Curs
         h8 av[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const h8 *>(xa + tx * 128 + i * 32);
-        tile_product<G, ASYM, MR>(qv, mv, av, magic, acc);
+        if constexpr (PRE) {
+            float off[GPT];
+#pragma unroll
+            for (int g = 0; g < GPT; ++g) off[g] = cps[(u % TPS) * GPT + g];
+            tile_product_pre<G>(qv, mv, av, off, k.mlo, k.mhi, acc);
+        } else {
+            tile_product_split<G, ASYM, MR>(qv, mv, av, k.psym, k.mlo, k.mhi, acc);
+        }
     }
 }
 
@@ -205,8 +244,15 @@ __device__ __forceinline__ void compute_loop(const ChainArgs &a, CProb *P, const
     const int nprob = a.nprob, nwg = gridDim.x;
     const int r = lane & 15, kq = lane >> 4;
     const _Float16 *xa = xs + (r < a.M ? r : a.M - 1) * a.xrow + kq * 8;
-    uint32_t magic = 0x64006400u;
-    asm volatile("" : "+v"(magic));
+    SplitConst kc;
+    kc.mlo = kMagicLo;
+    kc.mhi = kMagicHi;
+    asm volatile("" : "+v"(kc.mlo), "+v"(kc.mhi));   // in registers: each mask-or is one operation
+    {
+        u4 pw = __builtin_bit_cast(u4, offset8(8));
+        asm volatile("" : "+v"(pw));
+        kc.psym = __builtin_bit_cast(h8, pw);
+    }
 
     Slot<G, ASYM> s[D];
     Cursor c = {0, (int)blockIdx.x, 0};
@@ -232,7 +278,7 @@ __device__ __forceinline__ void compute_loop(const ChainArgs &a, CProb *P, const
             x_pi = c.pi;
             __syncthreads();                                   // (A) control wave: dependency met, x staged
         }
-        compute_round<G, ASYM, MR>(cur, cc, P, xa, wave, magic, acc);
+        compute_round<G, ASYM, MR>(cur, cc, P, xs, xa, wave, lane, kc, acc);
         if (alive && c.rr == P[cc.pi].rounds - 1) {
             float *rbuf = red + rb * (kComputeWaves * MR * 64);
 #pragma unroll
