@@ -448,6 +448,246 @@ void gemv_w4_v2_single(const uint8_t *codes, const uint8_t *scales, const _Float
     gemv_v2_strip<G, ASYM, MR, T, true>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel with a per-wave activation ring (M >= 2 when the whole
+// activation block does not fit in LDS, e.g. M = 8 with K = 14336: 229 KB).
+// A wave only ever reads the activations of its own tiles, so instead of the
+// workgroup's whole block each wave keeps a ring of NC tile slots (M rows x
+// 128 K each) in its own part of LDS, filled by LDS-direct loads: the slots of
+// its first NC tiles go out first, then all its weight loads, and after each
+// tile's product the slot just read is refilled with the tile NC ahead.  No
+// barrier is needed until the cross-wave sum; the wave waits only on its own
+// load counter (explicit vmcnt counts: the compiler does not track what
+// LDS-direct loads write).
+// ---------------------------------------------------------------------------
+constexpr int kXrSlots = 4;                         // activation slots per wave
+constexpr int kXrMaxLds = 160 * 1024;
+
+// rows staged per tile: a multiple of 4 (one LDS-direct load moves 4 rows of
+// 128 K), at least M
+__host__ __device__ inline int xr_rows(int M) { return (M + 3) / 4 * 4; }
+__host__ __device__ inline int xr_lds(int M, int W, int MR)
+{
+    return W * kXrSlots * xr_rows(M) * 256 + W * MR * 64 * 4;
+}
+
+// s_waitcnt vmcnt(n) for an n the optimizer folds to a constant (unrolled loops)
+__device__ __forceinline__ void vm_wait_n(int n)
+{
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(3952); break;
+    case 1: __builtin_amdgcn_s_waitcnt(3953); break;
+    case 2: __builtin_amdgcn_s_waitcnt(3954); break;
+    case 3: __builtin_amdgcn_s_waitcnt(3955); break;
+    case 4: __builtin_amdgcn_s_waitcnt(3956); break;
+    case 5: __builtin_amdgcn_s_waitcnt(3957); break;
+    case 6: __builtin_amdgcn_s_waitcnt(3958); break;
+    case 7: __builtin_amdgcn_s_waitcnt(3959); break;
+    case 8: __builtin_amdgcn_s_waitcnt(3960); break;
+    case 9: __builtin_amdgcn_s_waitcnt(3961); break;
+    case 10: __builtin_amdgcn_s_waitcnt(3962); break;
+    case 11: __builtin_amdgcn_s_waitcnt(3963); break;
+    case 12: __builtin_amdgcn_s_waitcnt(3964); break;
+    case 13: __builtin_amdgcn_s_waitcnt(3965); break;
+    case 14: __builtin_amdgcn_s_waitcnt(3966); break;
+    case 15: __builtin_amdgcn_s_waitcnt(3967); break;
+    case 16: __builtin_amdgcn_s_waitcnt(20336); break;
+    case 17: __builtin_amdgcn_s_waitcnt(20337); break;
+    case 18: __builtin_amdgcn_s_waitcnt(20338); break;
+    case 19: __builtin_amdgcn_s_waitcnt(20339); break;
+    case 20: __builtin_amdgcn_s_waitcnt(20340); break;
+    case 21: __builtin_amdgcn_s_waitcnt(20341); break;
+    case 22: __builtin_amdgcn_s_waitcnt(20342); break;
+    case 23: __builtin_amdgcn_s_waitcnt(20343); break;
+    case 24: __builtin_amdgcn_s_waitcnt(20344); break;
+    case 25: __builtin_amdgcn_s_waitcnt(20345); break;
+    case 26: __builtin_amdgcn_s_waitcnt(20346); break;
+    case 27: __builtin_amdgcn_s_waitcnt(20347); break;
+    case 28: __builtin_amdgcn_s_waitcnt(20348); break;
+    case 29: __builtin_amdgcn_s_waitcnt(20349); break;
+    case 30: __builtin_amdgcn_s_waitcnt(20350); break;
+    case 31: __builtin_amdgcn_s_waitcnt(20351); break;
+    case 32: __builtin_amdgcn_s_waitcnt(36720); break;
+    case 33: __builtin_amdgcn_s_waitcnt(36721); break;
+    case 34: __builtin_amdgcn_s_waitcnt(36722); break;
+    case 35: __builtin_amdgcn_s_waitcnt(36723); break;
+    case 36: __builtin_amdgcn_s_waitcnt(36724); break;
+    case 37: __builtin_amdgcn_s_waitcnt(36725); break;
+    case 38: __builtin_amdgcn_s_waitcnt(36726); break;
+    case 39: __builtin_amdgcn_s_waitcnt(36727); break;
+    case 40: __builtin_amdgcn_s_waitcnt(36728); break;
+    case 41: __builtin_amdgcn_s_waitcnt(36729); break;
+    case 42: __builtin_amdgcn_s_waitcnt(36730); break;
+    case 43: __builtin_amdgcn_s_waitcnt(36731); break;
+    case 44: __builtin_amdgcn_s_waitcnt(36732); break;
+    case 45: __builtin_amdgcn_s_waitcnt(36733); break;
+    case 46: __builtin_amdgcn_s_waitcnt(36734); break;
+    case 47: __builtin_amdgcn_s_waitcnt(36735); break;
+    case 48: __builtin_amdgcn_s_waitcnt(53104); break;
+    case 49: __builtin_amdgcn_s_waitcnt(53105); break;
+    case 50: __builtin_amdgcn_s_waitcnt(53106); break;
+    case 51: __builtin_amdgcn_s_waitcnt(53107); break;
+    case 52: __builtin_amdgcn_s_waitcnt(53108); break;
+    case 53: __builtin_amdgcn_s_waitcnt(53109); break;
+    case 54: __builtin_amdgcn_s_waitcnt(53110); break;
+    case 55: __builtin_amdgcn_s_waitcnt(53111); break;
+    case 56: __builtin_amdgcn_s_waitcnt(53112); break;
+    case 57: __builtin_amdgcn_s_waitcnt(53113); break;
+    case 58: __builtin_amdgcn_s_waitcnt(53114); break;
+    case 59: __builtin_amdgcn_s_waitcnt(53115); break;
+    case 60: __builtin_amdgcn_s_waitcnt(53116); break;
+    case 61: __builtin_amdgcn_s_waitcnt(53117); break;
+    case 62: __builtin_amdgcn_s_waitcnt(53118); break;
+    case 63: __builtin_amdgcn_s_waitcnt(53119); break;
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+    }
+}
+
+template <int G, bool ASYM, int MR, int T, int XI>
+__device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_t *scales, const uint8_t *zeros,
+                                              const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M,
+                                              int W, int strip)
+{
+    constexpr int GPT = 128 / G;
+    constexpr int NC = kXrSlots;
+    constexpr int LPT = ASYM ? 3 : 2;                // weight loads per tile (codes, scales[, zeros])
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, kq = lane >> 4;
+    const int t0 = wave * tw;
+    const int XS = XI * 1024;                        // bytes of one slot: 4 XI rows x 256 bytes
+    uint8_t *ring = smem + wave * NC * XS;
+    float *red = reinterpret_cast<float *>(smem + W * NC * XS);
+    const auto xrs = buffer_rsrc(xg, (uint32_t)(M * K * 2));
+
+    // slot of tile u: row m (0 .. 4 XI - 1) at m * 256 bytes; 16-byte block b
+    // of row m holds K offsets 8 (b ^ (m & 15)) .. + 7 of the tile
+    auto stage = [&](int u) __attribute__((always_inline)) {
+        const int t = t0 + u;
+        const bool live = u < tw && t < kt;
+        uint8_t *slot = ring + (u % NC) * XS;
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {
+            const int m = 4 * i + (lane >> 4), b = lane & 15;
+            const int k = t * 128 + 8 * (b ^ (m & 15));
+            const bool ok = live && m < M && k < K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void *)(slot + i * 1024),
+                                                     16, ok ? (uint32_t)((m * K + k) * 2) : kBufferOob, 0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < NC && u < T; ++u) stage(u);
+
+    u4 q[T];
+    MetaRaw<G, ASYM> mr[T];
+    const int64_t tiles0 = (int64_t)strip * kt;
+    const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
+    const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
+    const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        const int t = t0 + u;
+        const bool ok = u < tw && t < kt;
+        q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
+                                                     kStreamLoad);
+        mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+        __builtin_amdgcn_sched_barrier(0);           // keep the loads in tile order
+    }
+
+    uint32_t mlo = kMagicLo, mhi = kMagicHi;
+    asm volatile("" : "+v"(mlo), "+v"(mhi));
+    h8 psym = offset8(8);
+    {
+        u4 pw = __builtin_bit_cast(u4, psym);
+        asm volatile("" : "+v"(pw));
+        psym = __builtin_bit_cast(h8, pw);
+    }
+    const int xr = r < M ? r : M - 1;                // A row r reads token min(r, M-1)
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int tvalid = min(tw, kt - t0);
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        if (u < tvalid) {
+            __builtin_amdgcn_sched_barrier(0);
+            // wait until slot u has landed: count the loads issued after it.
+            // A first slot (u < NC) is followed by the later first slots, all
+            // T tiles' weight loads and the slots refilled at steps before u;
+            // a refilled slot (issued after tile u - NC) by the slots refilled
+            // at the steps since.
+            const int after = u < NC ? (NC - 1 - u) * XI + T * LPT + min(u, T - NC > 0 ? T - NC : 0) * XI
+                                     : min(NC - 1, T - 1 - u) * XI;
+            vm_wait_n(after);
+            asm volatile("" ::: "memory");
+            const uint8_t *slot = ring + (u % NC) * XS + xr * 256;
+            h8 a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const h8 *>(slot + (((i * 4 + kq) ^ (xr & 15)) * 16));
+            u4 qv = q[u];
+            asm volatile("" : "+v"(qv));
+            MetaRaw<G, ASYM> mv = mr[u];
+            pin_meta<G, ASYM>(mv);
+            tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
+        }
+        if (u + NC < T) {
+            // the slot's reads have returned; refill it with tile u + NC
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            stage(u + NC);
+        }
+    }
+
+    // fixed-order cross-wave sum (all partials read at once, added in wave
+    // order), fp16 RNE store
+    if (W > 1) {
+#pragma unroll
+        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                float part[16];
+#pragma unroll
+                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
+                float v = red[j * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < 16; ++w)
+                    if (w < W) v += part[w];
+                acc[j] = v;
+            }
+        }
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    if (wave == 0) {
+        const int n = strip * 16 + r;
+#pragma unroll
+        for (int j = 0; j < MR; ++j) {
+            const int m = kq * 4 + j;
+            if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[j];
+        }
+    }
+}
+
+template <int G, bool ASYM, int MR, int T, int XI>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_xr_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
+                    int kt, int tw, int M, int W, const uint8_t *zeros)
+{
+    gemv_xr_strip<G, ASYM, MR, T, XI>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
+}
+
+// batched form: blockIdx.y = problem, strips past its end exit
+template <int G, bool ASYM, int MR, int T, int XI>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_xr_batch(const GemvBatch b)
+{
+    const GemvProblem &p = b.p[blockIdx.y];
+    if ((int)blockIdx.x >= p.strips) return;
+    gemv_xr_strip<G, ASYM, MR, T, XI>(p.codes, p.scales, p.zeros, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W,
+                                      (int)blockIdx.x);
+}
+
 // raises a kernel's dynamic LDS limit when a launch needs more than the default
 // (`raised` belongs to the caller's instantiation, i.e. to one kernel)
 inline hipError_t v2_lds_limit(const void *k, size_t lds, bool &raised)
@@ -499,6 +739,47 @@ hipError_t launch_v2(int MR, int T, dim3 grid, dim3 block, size_t lds, hipStream
     if (MR == 1) return launch_v2_t<G, ASYM, 1>(T, grid, block, lds, st, b);
     if (MR == 2) return launch_v2_t<G, ASYM, 2>(T, grid, block, lds, st, b);
     return launch_v2_t<G, ASYM, 4>(T, grid, block, lds, st, b);
+}
+
+template <int G, bool ASYM, int T, int XI>
+hipError_t launch_xr_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    if (b.count == 1) {
+        static bool raised = false;
+        auto k = gemv_xr_single<G, ASYM, 4, T, XI>;
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kXrMaxLds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+        const GemvProblem &p = b.p[0];
+        k<<<grid, block, lds, st>>>(p.codes, p.scales, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W, p.zeros);
+    } else {
+        static bool raised = false;
+        auto k = gemv_xr_batch<G, ASYM, 4, T, XI>;
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kXrMaxLds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+        k<<<grid, block, lds, st>>>(b);
+    }
+    return hipGetLastError();
+}
+
+template <int G, bool ASYM>
+hipError_t launch_xr(int T, int XI, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    if (T <= 4) {
+        if (XI == 1) return launch_xr_k<G, ASYM, 4, 1>(grid, block, lds, st, b);
+        if (XI == 2) return launch_xr_k<G, ASYM, 4, 2>(grid, block, lds, st, b);
+        return launch_xr_k<G, ASYM, 4, 4>(grid, block, lds, st, b);
+    }
+    if (XI == 1) return launch_xr_k<G, ASYM, 8, 1>(grid, block, lds, st, b);
+    if (XI == 2) return launch_xr_k<G, ASYM, 8, 2>(grid, block, lds, st, b);
+    return launch_xr_k<G, ASYM, 8, 4>(grid, block, lds, st, b);
 }
 
 template <int G, bool ASYM, int MR>
@@ -585,6 +866,24 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
                                  : launch_v2<64, false>(MR, (int)T, g2, block, lds, s, b);
             default: return asym ? launch_v2<128, true>(MR, (int)T, g2, block, lds, s, b)
                                  : launch_v2<128, false>(MR, (int)T, g2, block, lds, s, b);
+            }
+        }
+    }
+
+    // M >= 3 when the whole activation block does not fit: per-wave activation
+    // rings (up to 8 rows with 8 tiles per wave, 16 rows with 4)
+    if (T <= 8 && MR == 4) {
+        const int XI = xr_rows(M) / 4;
+        const int64_t lds = xr_lds(M, W, MR);
+        if (lds <= kXrMaxLds) {
+            b.ct = 0;
+            switch (G) {
+            case 32: return asym ? launch_xr<32, true>((int)T, XI, grid, block, (size_t)lds, s, b)
+                                 : launch_xr<32, false>((int)T, XI, grid, block, (size_t)lds, s, b);
+            case 64: return asym ? launch_xr<64, true>((int)T, XI, grid, block, (size_t)lds, s, b)
+                                 : launch_xr<64, false>((int)T, XI, grid, block, (size_t)lds, s, b);
+            default: return asym ? launch_xr<128, true>((int)T, XI, grid, block, (size_t)lds, s, b)
+                                 : launch_xr<128, false>((int)T, XI, grid, block, (size_t)lds, s, b);
             }
         }
     }
