@@ -239,42 +239,65 @@ def time_graph(torch, graph, stream, steps, warmup):
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
-def time_launches(torch, lb, fmt, M, G, launches, stream, reps, call=None):
-    """Each launch bracketed by its own HIP event pair on the launch stream,
-    queued behind a bounded spin kernel so no host gap falls inside a pair.
-    Returns the median duration (us) of every launch over `reps` passes.
-    call(L, stream_handle) -> status issues one launch (default: the W4A16
-    batched GEMV)."""
-    if call is None:
-        def call(L, st):
-            return lb.lowbit_gemv_batched(fmt, M, G, L["count"], L["probs"], st)
-    per = []
-    with torch.cuda.stream(stream):
-        for _ in range(reps):
-            pairs = []
-            torch.cuda._sleep(50_000_000)                       # bounded spin while the launches are queued
-            for L in launches:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                st = call(L, stream.cuda_stream)
-                b.record(stream)
-                if st != 0:
-                    raise lb.LowbitError(st)
-                pairs.append((a, b))
-            torch.cuda.synchronize()
-            per.append([a.elapsed_time(b) * 1e3 for a, b in pairs])
-    return np.median(np.array(per), axis=0)
+KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/gemv_w4.hip", "bit_weight_only_pack_amd/csrc/gemv_tile.hpp",
+                  "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
+
+
+def kernel_source_hash(paths=KERNEL_SOURCES):
+    """sha256 over the sources of the decode GEMV kernels (recorded with the
+    counter profiles, so a profile of an older kernel is not reported)."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic(name):
-    """HBM bytes per launch measured with rocprofv3 counters, if recorded."""
+    """HBM bytes per launch from a committed rocprofv3 counter profile
+    (FETCH_SIZE and WRITE_SIZE runs, calibrated), and the profile's name;
+    (None, reason) when there is none or it was taken on other kernel
+    sources than the ones this tree builds."""
     path = os.path.join(ROOT, "profiles", name)
-    if name and os.path.exists(path):
-        for line in open(path):
-            if line.startswith("traffic_bytes_per_launch:"):
-                return float(line.split(":")[1])
-    return None
+    if not name or not os.path.exists(path):
+        return None, "no counter profile"
+    value, src = None, None
+    for line in open(path):
+        if line.startswith("traffic_bytes_per_launch:"):
+            value = float(line.split(":")[1])
+        if line.startswith("kernel_source_sha256:"):
+            src = line.split(":")[1].strip()
+    if value is None:
+        return None, "no counter profile"
+    if src != kernel_source_hash():
+        return None, "profiles/%s was taken on other kernel sources" % name
+    return value, "profiles/%s (rocprofv3 FETCH_SIZE and WRITE_SIZE runs, calibrated)" % name
+
+
+def time_launch_groups(torch, lb, fmt, M, G, launches, stream, steps, warmup, run=None):
+    """Mean duration of each launch group's launches: the group's launches of
+    all layers, in layer order, captured as one graph and replayed (HIP events
+    on the launch stream around the timed replays) -- the kernel's own
+    average launch duration, back to back as in the step.  run(Ls) issues a
+    list of launches (default: the W4A16 batched GEMV)."""
+    if run is None:
+        def run(Ls):
+            run_step(lb, fmt, M, G, Ls, stream.cuda_stream)
+    groups = {}
+    for L in launches:
+        groups.setdefault("+".join(L["names"]), []).append(L)
+    out = {}
+    reps = 4                   # copies of the group per graph: a replay's GPU time well above its launch cost
+    for name, Ls in groups.items():
+        g = capture(torch, lambda: [run(Ls) for _ in range(reps)], stream)
+        _, gpu_ms = time_graph(torch, g, stream, steps, warmup)
+        us = gpu_ms * 1e3 / (reps * len(Ls))
+        nbytes = sum(L["bytes"] for L in Ls) / len(Ls)
+        out[name] = dict(us=round(us, 3), bytes_per_launch=round(nbytes), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                         launches=len(Ls))
+        del g
+    return out
 
 
 def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0, a8=False):
@@ -320,28 +343,32 @@ def bench_decode(args, torch, lb, synth):
         graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
     ms_per_step, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
     st_err = 0
+    per_group = None
     if mode == "chain":
         # one launch per step: its duration is the event-timed replay region per step
-        n_launch, kernel = 1, "gemv_chain_kernel<G=128,sym,M=1> (whole step, one launch)"
         st, st_err = lb.lowbit_gemv_chain_error(chain, stream.cuda_stream)
         lb.check(st)
         if st_err:
             raise RuntimeError("chain dependency wait timed out (error word %d)" % st_err)
-        per_group = None
+        roof = dict(kernel="gemv_chain_kernel<G=128,sym,MR=1> (the whole step, one launch)",
+                    bytes_per_launch=step_bytes, avg_launch_us=gpu_ms * 1e3, traffic_name="")
     else:
-        med = time_launches(torch, lb, fmt, M, G, launches, stream, args.kernel_reps)
-        n_launch, kernel = len(launches), "gemv_w4_v2_kernel<G=128,sym,M=1>"
-        groups = {}
-        for L, t in zip(launches, med):
-            groups.setdefault("+".join(L["names"]), []).append((t, L["bytes"]))
-        per_group = {k: dict(us=round(float(np.mean([a for a, _ in v])), 3),
-                             GBps=round(float(np.mean([b / (a * 1e-6) / 1e9 for a, b in v])), 1))
-                     for k, v in groups.items()}
-    # the graph's nodes run back to back on `stream`: the event-timed replay
-    # region divided by the launches of a step is their mean duration
-    avg_launch_us = gpu_ms * 1e3 / n_launch
-    bytes_per_launch = step_bytes / n_launch
-    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+        per_group = time_launch_groups(torch, lb, fmt, M, G, launches, stream, args.steps, args.warmup)
+        if mode == "batched":
+            # the dominant kernel: gemv_w4_v2_kernel<128,sym,MR=1,T=4,NP=4> runs
+            # the q+k+v and gate+up launches (4 of every 7 GEMVs, ~2/3 of the
+            # step's time); its figure is the bytes of those launches over their
+            # measured durations
+            dom = [per_group["q+k+v"], per_group["gate+up"]]
+            us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+            nb = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+            roof = dict(kernel="gemv_w4_v2_kernel<G=128,sym,MR=1,T=4,NP=4> (the q+k+v and gate+up launches)",
+                        bytes_per_launch=nb, avg_launch_us=us, traffic_name="w4_gemv_decode_step_traffic.txt")
+        else:
+            roof = dict(kernel="gemv_w4_v2 (one launch per GEMV, M=1)", bytes_per_launch=step_bytes / len(launches),
+                        avg_launch_us=gpu_ms * 1e3 / len(launches), traffic_name="")
+    achieved = roof["bytes_per_launch"] / (roof["avg_launch_us"] * 1e-6) / 1e9
+    traffic, traffic_source = read_traffic(roof["traffic_name"]) if roof["traffic_name"] else (None, "not taken")
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -357,17 +384,20 @@ def bench_decode(args, torch, lb, synth):
         "dtype": "f16",
         "data": "synthetic (seeded; random INT4 codes, U[0.002,0.01] fp16 scales, N(0,1) fp16 inputs)",
         "config": {"workload": "llama3-8b-w4-decode-step", "layers": LAYERS, "gemvs_per_step": 7 * LAYERS,
-                   "launches_per_step": n_launch, "M": M, "group_size": G, "mode": mode,
+                   "launches_per_step": len(launches) if mode != "chain" else 1, "M": M, "group_size": G, "mode": mode,
                    "format": "int4 symmetric, fp16 scales", "bytes_per_step": step_bytes},
         "tokens_per_s": round(1e3 / ms_per_step, 2),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "gpu_ms_per_step": round(gpu_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic({"batched": "w4_gemv_decode_step_traffic.txt",
-                                              "chain": "w4_gemv_chain_decode_step_traffic.txt"}.get(mode, "")),
-                     "kernel": kernel, "bytes_per_launch": round(bytes_per_launch),
-                     "avg_launch_us": round(avg_launch_us, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_source, "kernel": roof["kernel"],
+                     "bytes_per_launch": round(roof["bytes_per_launch"]),
+                     "avg_launch_us": round(roof["avg_launch_us"], 3),
+                     "timing": "HIP events on the launch stream around graph replays of this kernel's launches"},
+        "step_mean_per_launch": {"launches_per_step": len(launches) if mode != "chain" else 1,
+                                 "us": round(gpu_ms * 1e3 / (len(launches) if mode != "chain" else 1), 3),
+                                 "GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1)},
     }
     if per_group is not None:
         out["per_launch_group"] = per_group
@@ -386,15 +416,18 @@ def bench_decode_asym(args, torch, lb, synth):
         stream = torch.cuda.Stream()
         graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
         ms, _ = time_graph(torch, graph, stream, args.steps, args.warmup)
-        med = time_launches(torch, lb, fmt, M, G, launches, stream, 2)
+        pg = time_launch_groups(torch, lb, fmt, M, G, launches, stream, max(5, args.steps // 5), 2)
         res["M=%d" % M] = dict(ms_per_step=round(ms, 4), GBps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                                tokens_per_s=round(M * 1e3 / ms, 1), bytes_per_step=step_bytes,
-                               kernel_sum_ms=round(float(med.sum()) / 1e3, 4))
+                               kernel_sum_ms=round(sum(v["us"] * v["launches"] for v in pg.values()) / 1e3, 4),
+                               per_launch_group=pg)
         del graph, keep, launches
         torch.cuda.empty_cache()
     r1 = res["M=1"]
-    nl = 128                                         # launches per step (32 layers x 4 groups)
-    ach = r1["bytes_per_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
+    dom = [r1["per_launch_group"]["q+k+v"], r1["per_launch_group"]["gate+up"]]
+    us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    nb = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    ach = nb / (us * 1e-6) / 1e9
     return {"metric": "W4 asymmetric G=32 decode step effective HBM GB/s (M=1; M=2, 4, 8 in per_M)",
             "value": r1["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": r1["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -404,10 +437,12 @@ def bench_decode_asym(args, torch, lb, synth):
                        "group_size": G},
             "tokens_per_s": r1["tokens_per_s"],
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "kernel": "gemv_w4_v2 (G=32, asymmetric, M=1)",
-                         "bytes_per_launch": r1["bytes_per_step"] // nl,
-                         "avg_launch_us": round(r1["ms_per_step"] * 1e3 / nl, 3)},
+                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
+                         "kernel": "gemv_w4_v2_kernel<G=32,asym,MR=1,T=4,NP=4> (the q+k+v and gate+up launches, "
+                                   "M=1)",
+                         "bytes_per_launch": round(nb), "avg_launch_us": round(us, 3),
+                         "timing": "HIP events on the launch stream around graph replays of this kernel's "
+                                   "launches"},
             "per_M": res}
 
 
@@ -436,26 +471,24 @@ def bench_decode_w4a8(args, torch, lb, synth):
         graph = capture(torch, lambda: run_step_a8(lb, fmt, M, G, launches, ws, wsb, stream.cuda_stream), stream)
         ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
 
-        def call(L, st):
-            return lb.lowbit_gemv_w4a8_batched(fmt, M, G, L["count"], L["probs"], ws, wsb, st)
-        med = time_launches(torch, lb, fmt, M, G, launches, stream, 2, call)
-        groups = {}
-        for L, t in zip(launches, med):
-            groups.setdefault("+".join(L["names"]), []).append(t)
+        pg = time_launch_groups(torch, lb, fmt, M, G, launches, stream, max(5, args.steps // 5), 2,
+                                run=lambda Ls: run_step_a8(lb, fmt, M, G, Ls, ws, wsb, stream.cuda_stream))
         res["M=%d" % M] = dict(ms_per_step=round(ms, 4), GBps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                                tokens_per_s=round(M * 1e3 / ms, 1), bytes_per_step=step_bytes,
-                               workspace_bytes=wsb, kernel_sum_ms=round(float(med.sum()) / 1e3, 4),
-                               per_launch_us={k: round(float(np.mean(v)), 2) for k, v in groups.items()})
+                               workspace_bytes=wsb,
+                               kernel_sum_ms=round(sum(v["us"] * v["launches"] for v in pg.values()) / 1e3, 4),
+                               per_launch_group=pg)
         if M == 1:
             g16 = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
             ms16, _ = time_graph(torch, g16, stream, args.steps, args.warmup)
             res["M=1"]["w4a16_same_step_ms"] = round(ms16, 4)
             del g16
-            m1 = dict(ms=ms, gpu_ms=gpu_ms, bytes=step_bytes, n=len(launches))
+            m1 = dict(ms=ms, gpu_ms=gpu_ms, bytes=step_bytes, n=len(launches), pg=pg)
         del graph, keep, launches, ws
         torch.cuda.empty_cache()
-    avg_us = m1["gpu_ms"] * 1e3 / m1["n"]
-    bpl = m1["bytes"] / m1["n"]
+    dom = [m1["pg"]["q+k+v"], m1["pg"]["gate+up"]]
+    avg_us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    bpl = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
     ach = bpl / (avg_us * 1e-6) / 1e9
     out = {"metric": "W4A8 (dynamic INT8 activations) decode step effective HBM GB/s",
            "value": res["M=1"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -469,9 +502,11 @@ def bench_decode_w4a8(args, torch, lb, synth):
            "tokens_per_s": res["M=1"]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res["M=1"]["GBps"] / HBM_PEAK_GBPS, 2),
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                        "kernel": "gemv_w4a8 (fused quantization, G=32, asym, M=1)", "bytes_per_launch": round(bpl),
-                        "avg_launch_us": round(avg_us, 3)},
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
+                        "kernel": "gemv_w4a8_batch<G=32,asym,MR=1,T=4,FUSED> (the q+k+v and gate+up launches, M=1)",
+                        "bytes_per_launch": round(bpl), "avg_launch_us": round(avg_us, 3),
+                        "timing": "HIP events on the launch stream around graph replays of this kernel's "
+                                  "launches"},
            "per_M": res}
     if args.cpu_layers > 0:
         out["cpu_baseline"] = cpu_baseline_decode(synth, 3 * args.cpu_layers, 1, G, asym, wid, outlier_frac=0.01,
@@ -527,21 +562,17 @@ def bench_decode_bits(args, torch, lb, synth):
         stream = torch.cuda.Stream()
         graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
         ms, gpu_ms = time_graph(torch, graph, stream, args.steps, args.warmup)
-        med = time_launches(torch, lb, fmt, M, G, launches, stream, 2)
-        groups = {}
-        for L, t in zip(launches, med):
-            groups.setdefault("+".join(L["names"]), []).append(t)
+        pg = time_launch_groups(torch, lb, fmt, M, G, launches, stream, max(5, args.steps // 5), 2)
         res["b=%d" % bits] = dict(ms_per_step=round(ms, 4), GBps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                                   tokens_per_s=round(1e3 / ms, 1), bytes_per_step=step_bytes,
-                                  bytes_per_weight=bits / 8 + 2 / G,
-                                  per_launch_us={k: round(float(np.mean(v)), 2) for k, v in groups.items()})
+                                  bytes_per_weight=bits / 8 + 2 / G, per_launch_group=pg)
         if ref is None or bits == 3:
-            n = len(launches)
-            ref = dict(bits=bits, gpu_ms=gpu_ms, bytes=step_bytes, n=n)
+            ref = dict(bits=bits, pg=pg)
         del graph, keep, launches
         torch.cuda.empty_cache()
-    avg_us = ref["gpu_ms"] * 1e3 / ref["n"]
-    bpl = ref["bytes"] / ref["n"]
+    dom = [ref["pg"]["q+k+v"], ref["pg"]["gate+up"]]
+    avg_us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    bpl = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
     ach = bpl / (avg_us * 1e-6) / 1e9
     key = "b=%d" % ref["bits"]
     out = {"metric": "b-bit decode step effective HBM GB/s and tokens/s at 8B shapes", "value": res[key]["GBps"],
@@ -550,13 +581,16 @@ def bench_decode_bits(args, torch, lb, synth):
            "vs_baseline": None, "dtype": "f16",
            "data": "synthetic (seeded; uniform b-bit codes, U[0.002,0.01] fp16 scales, N(0,1) fp16 inputs)",
            "config": {"workload": "llama3-8b-uint-decode-step", "bits": [int(v) for v in args.bits.split(",")],
-                      "value_bits": ref["bits"], "M": M, "group_size": G, "launches_per_step": ref["n"]},
+                      "value_bits": ref["bits"], "M": M, "group_size": G, "launches_per_step": 4 * LAYERS},
            "tokens_per_s": res[key]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res[key]["GBps"] / HBM_PEAK_GBPS, 2),
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                        "kernel": "gemv_wb (b=%d, G=128, sym, M=1)" % ref["bits"], "bytes_per_launch": round(bpl),
-                        "avg_launch_us": round(avg_us, 3)},
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
+                        "kernel": "gemv_wb_batch<b=%d,G=128,sym,MR=1,T=4> (the q+k+v and gate+up launches)"
+                                  % ref["bits"],
+                        "bytes_per_launch": round(bpl), "avg_launch_us": round(avg_us, 3),
+                        "timing": "HIP events on the launch stream around graph replays of this kernel's "
+                                  "launches"},
            "per_bits": res}
     if args.cpu_layers > 0:
         import oracle
@@ -867,7 +901,6 @@ def main():
                          "batched = one launch per group of GEMVs sharing an input (4 per layer); "
                          "unfused = one launch per GEMV (7 per layer)")
     ap.add_argument("--cpu-layers", type=int, default=4, help="decode: layers the CPU oracle runs (0 = skip)")
-    ap.add_argument("--kernel-reps", type=int, default=5, help="decode: event-timed passes over the launches")
     ap.add_argument("--m-list", default="1,2,4,8", help="decode-w4a8: token counts to run (must include 1)")
     ap.add_argument("--bits", default="2,3,8", help="decode-bits: code widths to run (1..8)")
     ap.add_argument("--calibrate-copy", action="store_true",
