@@ -659,7 +659,7 @@ int lowbit_moe_layer(const void *w13, const void *w2, int E_local, int E, int H,
     if (st != LOWBIT_OK) return st;
     if (T == 0) return LOWBIT_OK;
     if (x == nullptr || topk_ids == nullptr || topk_weights == nullptr || y == nullptr || workspace == nullptr ||
-        (E_local > 0 && (w13 == nullptr || w2 == nullptr)))
+        (E_local > 0 && (w13 == nullptr || w2 == nullptr)) || (expert_map == nullptr && E > E_local))
         return LOWBIT_E_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(y) % 16 != 0 ||
         reinterpret_cast<uintptr_t>(workspace) % 256 != 0)

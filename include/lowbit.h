@@ -465,7 +465,9 @@ size_t lowbit_moe_layer_workspace_bytes(int T, int top_k, int E, int H, int I, i
  *              each expert's gate (rows 0..I-1) and up (rows I..2I-1) stacked
  *   w2       : lowbit_pack_weights(LOWBIT_LUT3_E4M3, E_local, H, I, ...)
  *   E        : global experts (routing ids are in [0, E)); expert_map as in
- *              lowbit_moe_align (NULL = all local)
+ *              lowbit_moe_align (NULL = all local, which needs E <= E_local:
+ *              else LOWBIT_E_INVALID_ARG, as slots would name experts that
+ *              w13 and w2 do not hold)
  *   x        : bf16 [T][H] hidden states, 16-byte aligned; H % 64 == 0, I % 64 == 0
  *   topk_ids : i32 [T][top_k]; topk_weights: f32 [T][top_k]
  *   y        : bf16 [T][H] (output), 16-byte aligned

@@ -221,6 +221,8 @@ def test_moe_layer_argument_checks():
     assert lb.lowbit_moe_layer(*args, FAKE + 128, wsb) == E_ARG                   # workspace alignment
     assert lb.lowbit_moe_layer(FAKE, FAKE, 128, 128, 2048, 736, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE,
                                FAKE, wsb) == E_ARG                                  # I % 64
+    assert lb.lowbit_moe_layer(FAKE, FAKE, 64, 128, 2048, 768, FAKE, FAKE, FAKE, 256, 8, None, 16, FAKE,
+                               FAKE, wsb) == E_ARG                                  # no map, E > E_local
 
 
 def test_uint_formats_host_rules():
