@@ -188,6 +188,8 @@ void gemv_w4_kernel(const GemvBatch b)
 //   5. Fixed-order cross-wave sum through LDS, fp16 RNE store.
 // ---------------------------------------------------------------------------
 constexpr int kV2MaxLds = 80 * 1024;               // two workgroups still fit a compute unit's 160 KiB
+constexpr int64_t kNs2MinStrips = 1024;             // launches of at least this many strips take two per workgroup
+constexpr int kNs2MinM = 5;                         // ... with at least this many tokens
 
 struct V2Lds {
     int rowp;                                        // 16-byte blocks per LDS row of x
@@ -197,12 +199,12 @@ struct V2Lds {
 // whose shared offset chain reads the same block of four consecutive tiles at
 // once (the 64-byte pad puts those reads in different banks)
 __host__ __device__ constexpr int v2_tile_blocks(bool asym, int MR) { return !asym && MR == 1 ? 20 : 16; }
-__host__ __device__ inline V2Lds v2_lds(int M, int kt, int W, int MR, bool asym)
+__host__ __device__ inline V2Lds v2_lds(int M, int kt, int W, int MR, bool asym, int NS = 1)
 {
     V2Lds l;
     l.rowp = (int)round_up((int64_t)kt * v2_tile_blocks(asym, MR), 64);
     l.red = M * l.rowp * 16;
-    l.total = l.red + W * MR * 64 * 4;
+    l.total = l.red + NS * W * MR * 64 * 4;
     return l;
 }
 
@@ -224,14 +226,19 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // Occupancy targets: batch-1 symmetric with up to 4 tiles per wave keeps 8
 // waves per SIMD (64 VGPRs), so four 8-wave workgroups share a compute unit;
 // other forms with up to 4 tiles per wave 6; 8 tiles per wave (16-wave
-// workgroups, one per compute unit) 4.
-// The streaming kernel's work for one strip, once its problem's fields are
-// known (in scalar registers).
-template <int G, bool ASYM, int MR, int T, bool SINGLE = false>
+// workgroups, one per compute unit), or two strips of 4 tiles, 4.
+// The streaming kernel's work for NS consecutive strips strip0 .. strip0 +
+// NS - 1 (those below nst), once their problem's fields are known (in scalar
+// registers).  NS = 2 (several tokens, launches of many strips): the two
+// strips share one staged activation block, whose LDS-direct copy is the
+// larger part of a workgroup's vector-memory traffic at M = 8, and each tile's
+// A fragments are read from LDS once for both.
+template <int G, bool ASYM, int MR, int T, bool SINGLE = false, int NS = 1>
 __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_t *scales, const uint8_t *zeros,
                                               const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M,
-                                              int W, int strip)
+                                              int W, int strip0, int nst = 0x7FFFFFFF)
 {
+    static_assert(NS == 1 || (NS == 2 && !(!ASYM && MR == 1) && !SINGLE), "two strips: the general product only");
     constexpr int GPT = 128 / G;
     constexpr int NW = T * (ASYM ? 3 : 2);          // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -240,8 +247,8 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     const int r = lane & 15, kq = lane >> 4;
     const int t0 = wave * tw;
     constexpr int TB = v2_tile_blocks(ASYM, MR);
-    const V2Lds L = v2_lds(M, kt, W, MR, ASYM);
-    float *red = reinterpret_cast<float *>(smem + L.red);
+    const V2Lds L = v2_lds(M, kt, W, MR, ASYM, NS);
+    float *red = reinterpret_cast<float *>(smem + L.red);     // [NS][W][MR][64]
 
     // 1. activations -> LDS: chunk cc of row m holds blocks 64 cc .. 64 cc + 63
     //    of the row; block b < 16 of tile t of row m holds
@@ -263,31 +270,40 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
 
     // 2. weights and metadata of this wave's tiles, in tile order; 3. x in
     //    LDS everywhere, waited for after the first EARLY tiles' loads
-    u4 q[T];
-    MetaRaw<G, ASYM> mr[T];
+    u4 q[NS][T];
+    MetaRaw<G, ASYM> mr[NS][T];
     constexpr int EARLY = T >= 8 ? 1 : (SINGLE && T == 4 ? 2 : T);
     constexpr int LPT = ASYM ? 3 : 2;                // loads per tile (codes, scales[, zeros])
     static_assert(NW == T * LPT, "load count");
-    const int64_t tiles0 = (int64_t)strip * kt;
-    const auto crs = buffer_rsrc(codes + tiles0 * 1024, (uint32_t)kt * 1024);
-    const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)kt * 16 * GPT * 2);
-    const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)kt * 16 * GPT : 0u);
+    __amdgpu_buffer_rsrc_t crs[NS], srs[NS], zrs[NS];
+#pragma unroll
+    for (int sj = 0; sj < NS; ++sj) {
+        // (a strip past the problem's end reads zeros and stores nothing)
+        const bool live = strip0 + sj < nst;
+        const int64_t tiles0 = (int64_t)(live ? strip0 + sj : 0) * kt;
+        crs[sj] = buffer_rsrc(codes + tiles0 * 1024, live ? (uint32_t)kt * 1024 : 0u);
+        srs[sj] = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, live ? (uint32_t)kt * 16 * GPT * 2 : 0u);
+        zrs[sj] = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM && live ? (uint32_t)kt * 16 * GPT : 0u);
+    }
 #pragma unroll
     for (int u = 0; u < T; ++u) {
         if (u == EARLY) {
-            wait_vm<EARLY * LPT>();                  // x has landed; tiles < EARLY may be in flight
+            wait_vm<EARLY * LPT * NS>();             // x has landed; tiles < EARLY may be in flight
             wg_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
         const int t = t0 + u;
         const bool ok = u < tw && t < kt;
-        q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob, 0,
-                                                     kStreamLoad);
-        mr[u] = load_meta<G, ASYM>(srs, zrs, ok ? t * 16 + r : -1);
+#pragma unroll
+        for (int sj = 0; sj < NS; ++sj) {
+            q[sj][u] = __builtin_amdgcn_raw_buffer_load_b128(crs[sj], ok ? (uint32_t)t * 1024 + lane * 16 : kBufferOob,
+                                                             0, kStreamLoad);
+            mr[sj][u] = load_meta<G, ASYM>(srs[sj], zrs[sj], ok ? t * 16 + r : -1);
+        }
         __builtin_amdgcn_sched_barrier(0);           // keep the loads in tile order
     }
     if constexpr (EARLY == T) {
-        wait_vm<NW>();
+        wait_vm<NW * NS>();
         wg_barrier();
     }
 
@@ -305,7 +321,9 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         xa[i] = reinterpret_cast<const _Float16 *>(smem) + (xr * L.rowp + t0 * TB + ((i * 4 + kq) ^ (xr & 15))) * 8;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    f4 acc[NS];
+#pragma unroll
+    for (int sj = 0; sj < NS; ++sj) acc[sj] = f4{0.f, 0.f, 0.f, 0.f};
     // Batch-1 symmetric weights: the offset chain x . p does not depend on
     // the codes or the weight row, so one MFMA chain serves several tiles.
     // Its A rows 0..3 carry K blocks of different (tile, group) pairs
@@ -338,53 +356,67 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
             h8 a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const h8 *>(xa[i] + u * TB * 8);
-            u4 qv = q[u];
-            asm volatile("" : "+v"(qv));
-            MetaRaw<G, ASYM> mv = mr[u];
-            pin_meta<G, ASYM>(mv);
-            if constexpr (PRE) {
-                float off[GPT];
 #pragma unroll
-                for (int g = 0; g < GPT; ++g) off[g] = cps[(u % TPS) * GPT + g];
-                tile_product_pre<G>(qv, mv, a, off, mlo, mhi, acc);
-            } else {
-                tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
+            for (int sj = 0; sj < NS; ++sj) {
+                u4 qv = q[sj][u];
+                asm volatile("" : "+v"(qv));
+                MetaRaw<G, ASYM> mv = mr[sj][u];
+                pin_meta<G, ASYM>(mv);
+                if constexpr (PRE) {
+                    float off[GPT];
+#pragma unroll
+                    for (int g = 0; g < GPT; ++g) off[g] = cps[(u % TPS) * GPT + g];
+                    tile_product_pre<G>(qv, mv, a, off, mlo, mhi, acc[sj]);
+                } else {
+                    tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc[sj]);
+                }
             }
         }
     }
 
     // 5. fixed-order cross-wave sum (all partials read at once, added in wave
-    //    order), fp16 RNE store
+    //    order), fp16 RNE store; wave sj sums and stores strip sj (wave 0
+    //    both when the workgroup has one wave)
     if (W > 1) {
 #pragma unroll
-        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        for (int sj = 0; sj < NS; ++sj)
+#pragma unroll
+            for (int j = 0; j < MR; ++j) red[((sj * W + wave) * MR + j) * 64 + lane] = acc[sj][j];
         __syncthreads();
-        if (wave == 0) {
 #pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                float part[16];
+        for (int sj = 0; sj < NS; ++sj) {
+            if (wave == sj) {
+                const float *rs = red + sj * W * MR * 64;
 #pragma unroll
-                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
-                float v = red[j * 64 + lane];
+                for (int j = 0; j < MR; ++j) {
+                    float part[16];
 #pragma unroll
-                for (int w = 1; w < 16; ++w)
-                    if (w < W) v += part[w];
-                acc[j] = v;
+                    for (int w = 1; w < 16; ++w) part[w] = w < W ? rs[(w * MR + j) * 64 + lane] : 0.f;
+                    float v = rs[j * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < 16; ++w)
+                        if (w < W) v += part[w];
+                    acc[sj][j] = v;
+                }
             }
         }
     }
-    if (wave == 0) {
-        const int n = strip * 16 + r;
 #pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            const int m = kq * 4 + j;
-            if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[j];
+    for (int sj = 0; sj < NS; ++sj) {
+        if (wave == (W > 1 ? sj : 0) && strip0 + sj < nst) {
+            const int n = (strip0 + sj) * 16 + r;
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                const int m = kq * 4 + j;
+                if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[sj][j];
+            }
         }
     }
 }
 
-template <int G, bool ASYM, int MR, int T, int NP>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
+template <int G, bool ASYM, int MR, int T, int NP, int NS = 1>
+__global__ __launch_bounds__(1024)
+__attribute__((amdgpu_waves_per_eu(T > 4 || NS > 1 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
 void gemv_w4_v2_kernel(const GemvBatch b)
 {
     // One round of kernel-argument reads.  NP = 4:
@@ -433,8 +465,9 @@ void gemv_w4_v2_kernel(const GemvBatch b)
     asm volatile("" : "+s"(codes), "+s"(scales), "+s"(xg), "+s"(yp), "+s"(N), "+s"(K), "+s"(kt), "+s"(nst),
                  "+s"(tw), "+s"(M), "+s"(W));
     if constexpr (ASYM) asm volatile("" : "+s"(zeros));
-    if (strip >= nst) return;
-    gemv_v2_strip<G, ASYM, MR, T>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, strip);
+    // (strip counts workgroups: NS row strips each)
+    if (strip * NS >= nst) return;
+    gemv_v2_strip<G, ASYM, MR, T, false, NS>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, strip * NS, nst);
 }
 
 // One problem: every field is a kernel argument of its own (16 dwords), so
@@ -733,6 +766,18 @@ hipError_t launch_v2_t(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st,
     return launch_v2_k<G, ASYM, MR, 8>(grid, block, lds, st, b);
 }
 
+// two strips per workgroup: 2-4 problems laid end to end, several tokens
+template <int G, bool ASYM>
+hipError_t launch_v2_ns2(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    static bool raised2 = false, raised4 = false;
+    auto k = T <= 2 ? gemv_w4_v2_kernel<G, ASYM, 4, 2, 4, 2> : gemv_w4_v2_kernel<G, ASYM, 4, 4, 4, 2>;
+    const hipError_t e = v2_lds_limit((const void *)k, lds, T <= 2 ? raised2 : raised4);
+    if (e != hipSuccess) return e;
+    k<<<grid, block, lds, st>>>(b);
+    return hipGetLastError();
+}
+
 template <int G, bool ASYM>
 hipError_t launch_v2(int MR, int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
@@ -852,7 +897,31 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
     const dim3 grid((unsigned)max_strips, (unsigned)count), block((unsigned)(W * 64));
     const dim3 grid_flat((unsigned)strips);
 
-    // streaming kernel whenever the x block fits
+    // streaming kernel whenever the x block fits.  Two strips per workgroup
+    // for 5 or more tokens and up to four tiles per wave when the launch has at
+    // least 1024 strips (512 workgroups: two per compute unit) and the two
+    // strips' partial sums fit beside x.  (Measured on the 8B gate+up launch,
+    // asymmetric G=32: 25.4 -> 23.4 us at M = 8, but 20.1 -> 21.6 us at M = 4,
+    // where one-strip workgroups still fit three to a compute unit.)
+    if (T <= 4 && MR == 4 && M >= kNs2MinM && count >= 2 && count <= 4 && strips >= kNs2MinStrips &&
+        v2_lds(M, (int)kt, W, MR, asym, 2).total <= kV2MaxLds) {
+        b.ct = 0;
+        int64_t wgs = 0;
+        for (int i = 0; i < count; ++i) {
+            b.first[i] = (int)wgs;
+            wgs += (L[i].strips + 1) / 2;
+        }
+        const dim3 g2((unsigned)wgs);
+        const size_t lds = (size_t)v2_lds(M, (int)kt, W, MR, asym, 2).total;
+        switch (G) {
+        case 32: return asym ? launch_v2_ns2<32, true>((int)T, g2, block, lds, s, b)
+                             : launch_v2_ns2<32, false>((int)T, g2, block, lds, s, b);
+        case 64: return asym ? launch_v2_ns2<64, true>((int)T, g2, block, lds, s, b)
+                             : launch_v2_ns2<64, false>((int)T, g2, block, lds, s, b);
+        default: return asym ? launch_v2_ns2<128, true>((int)T, g2, block, lds, s, b)
+                             : launch_v2_ns2<128, false>((int)T, g2, block, lds, s, b);
+        }
+    }
     if (T <= 8) {
         const V2Lds lay = v2_lds(M, (int)kt, W, MR, asym);
         if (lay.total <= kV2MaxLds) {

@@ -79,6 +79,44 @@ def test_w4_gemv_batched_grid(G, asym, K, M, count):
         assert_close(f16_to_f64(it[2].cpu().numpy()), ref[i], "batched %d/%d" % (i, count))
 
 
+@pytest.mark.parametrize("M", [4, 5, 8, 16])
+@pytest.mark.parametrize("G,asym", [(32, True), (128, False)])
+def test_w4_gemv_two_strip_batches(G, asym, M):
+    """Batches of 2-4 problems with at least 1024 strips and 5 or more tokens
+    run two 16-row strips per workgroup (M = 4: one, the other side of the
+    boundary).  Each problem here has an odd strip
+    count with a ragged last strip (N = 8200: 513 strips, the last of 8 rows),
+    so the last workgroup of each problem has a strip past the end.  The
+    outputs equal the one-problem launches' (one strip per workgroup) bit for
+    bit, and the oracle within the bar."""
+    n, K = 8200, 2048
+    ws, xs, packs, singles = [], [], [], []
+    for i in range(2):
+        w = synth.w4_weights(n, K, G, asym=asym, workload_id=WL, layer=90 + M, part=i)
+        x = synth.activations_f16(M, K, outlier_frac=0.01, workload_id=WL, layer=90 + M, part=i)
+        fmt, packed, _ = pack_w4(w, G)
+        y1 = _y(M, n)
+        lb.check(lb.lowbit_gemv(fmt, M, n, K, G, packed, dev(x), y1, None, 0))
+        ws.append(w)
+        xs.append(dev(x))
+        packs.append(packed)
+        singles.append(y1)
+    yb = [_y(M, n) for _ in range(2)]
+    probs = lb.make_gemv_problems([(packs[i], xs[i], yb[i], n, K) for i in range(2)])
+    lb.check(lb.lowbit_gemv_batched(fmt, M, G, 2, probs))
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 64), np.arange(n - 72, n)])
+    for i in range(2):
+        got = yb[i].cpu().numpy()
+        assert np.array_equal(got.view(np.uint16), singles[i].cpu().numpy().view(np.uint16)), "problem %d" % i
+        w = ws[i]
+        sub = dict(qweight=w["qweight"][rows], scales=w["scales"][rows],
+                   zeros=None if w["zeros"] is None else w["zeros"][rows])
+        x = xs[i].cpu().numpy()
+        _, ref = oracle.w4_matmul(x, "f16", sub["qweight"], sub["scales"], sub["zeros"], G, "f16")
+        assert_close(f16_to_f64(got[:, rows]), f16_to_f64(ref), "two-strip G=%d M=%d problem %d" % (G, M, i))
+
+
 # ---------------------------------------------------------------- uniform b-bit
 @pytest.mark.parametrize("K", [256, 2048, 9216])
 @pytest.mark.parametrize("M", [1, 4])
