@@ -14,7 +14,9 @@
 // which feeds the offset-split product of gemv_tile.hpp: x.(1024 + q) -
 // x.(1024 + z) by two MFMA chains over the same activations (at batch 1 with
 // symmetric weights one chain of offsets serves four tiles), so codes equal
-// to the zero point give exactly zero.
+// to the zero point give exactly zero.  b = 3 has its own nibble-aligned
+// layout (lowbit_internal.hpp): its codes unpack in the INT4 offset-split form,
+// 1024 + q and 64 + q, with a 3-bit mask.
 #include "lowbit_internal.hpp"
 #include "gemv_tile.hpp"
 
@@ -64,6 +66,12 @@ __device__ __forceinline__ WbTile<BITS> load_wb(__amdgpu_buffer_rsrc_t rs, bool 
 {
     using TT = WbTile<BITS>;
     TT w;
+    if constexpr (BITS == 3) {                         // the lane's three dwords, one load
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(rs, ok ? base + lane * 12 : kBufferOob, 0, kStreamLoad);
+        w.b = make_uint2(v[0], v[1]);
+        w.c = v[2];
+        return w;
+    }
 #pragma unroll
     for (int p = 0; p < TT::N4; ++p)
         w.a[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + 1024 * p + lane * 16 : kBufferOob, 0,
@@ -121,6 +129,31 @@ __device__ __forceinline__ h8 wb_operand(const WbTile<BITS> &w, uint32_t magic)
     return __builtin_bit_cast(h8, v);
 }
 
+// b = 3: the dword of block I (block 3's gathered from the spare nibble bits)
+// -> 1024 + q at K offsets 0, 1, 4, 5 and 64 + q at 2, 3, 6, 7, the INT4
+// offset-split form with a 3-bit mask (one shift and four mask-or operations)
+template <int I>
+__device__ __forceinline__ h8 wb3_operand(const WbTile<3> &w, uint32_t mlo, uint32_t mhi)
+{
+    uint32_t d;
+    if constexpr (I == 0) d = w.b.x;
+    else if constexpr (I == 1) d = w.b.y;
+    else if constexpr (I == 2) d = w.c;
+    else d = ((w.b.x >> 3) & 0x11111111u) | ((w.b.y >> 2) & 0x22222222u) | ((w.c >> 1) & 0x44444444u);
+    const uint32_t d8 = d >> 8;
+    const u4 v = {(d & 0x00070007u) | mlo, (d & 0x00700070u) | mhi, (d8 & 0x00070007u) | mlo,
+                  (d8 & 0x00700070u) | mhi};
+    return __builtin_bit_cast(h8, v);
+}
+
+// the offset operand of zero point z in the slots of the operand above
+__device__ __forceinline__ h8 wb3_offset(int z)
+{
+    const _Float16 lo = (_Float16)(1024.0f + (float)z);   // exact: integers below 2048
+    const _Float16 hi = (_Float16)(64.0f + (float)z);
+    return h8{lo, lo, hi, hi, lo, lo, hi, hi};
+}
+
 // offset operand of zero point z: 1024 + z in every half
 __device__ __forceinline__ h8 wb_offset(int z)
 {
@@ -139,7 +172,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     constexpr bool PRE = !ASYM && MR == 1;                  // shared offset chain (batch 1, symmetric)
     constexpr int TB = wb_tile_blocks(PRE);
     constexpr int TPS = 4 / GPT;                            // tiles per offset set
-    constexpr int NLD = TT::N4 + TT::N2 + TT::N1;           // code loads per tile
+    constexpr int NLD = BITS == 3 ? 1 : TT::N4 + TT::N2 + TT::N1;   // code loads per tile
     constexpr int NW = T * (NLD + (ASYM ? 2 : 1));           // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
@@ -199,8 +232,10 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
 
     // 4. products, tile by tile in load order
     uint32_t magic = 0x64006400u;                    // fp16 1024.0 in both halves
+    uint32_t magic_hi = 0x54005400u;                 // fp16 64.0 (b = 3)
     asm volatile("" : "+v"(magic));
-    h8 psym = wb_offset(1 << (BITS - 1));
+    if constexpr (BITS == 3) asm volatile("" : "+v"(magic_hi));
+    h8 psym = BITS == 3 ? wb3_offset(1 << (BITS - 1)) : wb_offset(1 << (BITS - 1));
     {
         u4 pw = __builtin_bit_cast(u4, psym);
         asm volatile("" : "+v"(pw));
@@ -240,10 +275,17 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
             h8 vs[4];
-            vs[0] = wb_operand<BITS, 0>(w, magic);
-            vs[1] = wb_operand<BITS, 1>(w, magic);
-            vs[2] = wb_operand<BITS, 2>(w, magic);
-            vs[3] = wb_operand<BITS, 3>(w, magic);
+            if constexpr (BITS == 3) {
+                vs[0] = wb3_operand<0>(w, magic, magic_hi);
+                vs[1] = wb3_operand<1>(w, magic, magic_hi);
+                vs[2] = wb3_operand<2>(w, magic, magic_hi);
+                vs[3] = wb3_operand<3>(w, magic, magic_hi);
+            } else {
+                vs[0] = wb_operand<BITS, 0>(w, magic);
+                vs[1] = wb_operand<BITS, 1>(w, magic);
+                vs[2] = wb_operand<BITS, 2>(w, magic);
+                vs[3] = wb_operand<BITS, 3>(w, magic);
+            }
             f4 cv = zero4, cp = zero4;
             h8 p = psym;
 #pragma unroll
@@ -255,7 +297,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
                         if constexpr (G == 128) zb = mv.z >> (8 * (r & 3));
                         else if constexpr (G == 64) zb = mv.z >> (16 * (r & 1) + 8 * g);
                         else zb = mv.z >> (8 * g);
-                        p = wb_offset((int)(int8_t)(uint8_t)zb);
+                        p = BITS == 3 ? wb3_offset((int)(int8_t)(uint8_t)zb) : wb_offset((int)(int8_t)(uint8_t)zb);
                     }
                 }
                 const h8 a = *reinterpret_cast<const h8 *>(xa[i] + u * TB * 8);

@@ -69,9 +69,17 @@ constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
 //     pair q of block i at bits 4 i + q and 16 + 4 i + q.
 // A shift and a mask therefore give two codes in the two 16-bit halves, ready
 // to be or-ed into fp16 1024.0.  At b = 4 the layout is the INT4 one.
+//
+// b = 3 instead keeps a lane's three dwords together (12 bytes, one load)
+// and nibble-aligns them: dword d (0..2) holds the codes of MFMA block d in
+// bits 0..2 of the INT4 nibble slots, so they unpack exactly as INT4 codes
+// with a 3-bit mask; block 3's codes sit in the spare bit 3 of every nibble,
+// code bit c in dword c, and three shift-and-merge steps gather them into a
+// fourth dword of the same form.
 // dword index inside a tile of plane dword k (0..b-1) of lane l
 __host__ __device__ inline int wb_word(int bits, int lane, int k)
 {
+    if (bits == 3) return lane * 3 + k;
     const int n4 = bits / 4, n2 = (bits % 4) >= 2 ? 1 : 0;
     if (k < 4 * n4) return (k / 4) * 256 + lane * 4 + (k % 4);
     k -= 4 * n4;

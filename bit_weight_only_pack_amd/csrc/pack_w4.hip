@@ -146,6 +146,11 @@ __host__ __device__ inline WbPlanes wb_planes(int bits) { return WbPlanes{bits /
 __device__ inline void wb_bit(const WbPlanes &P, int i, int j, int cb, int &dw, int &pos)
 {
     const int q = j >> 1, h = (j & 1) * 16;
+    if (P.n4 == 0 && P.n2 == 1 && P.n1 == 1) {             // b = 3: nibble-aligned dwords
+        dw = i < 3 ? i : cb;
+        pos = 4 * w4_slot(j) + (i < 3 ? cb : 3);
+        return;
+    }
     if (cb < 4 * P.n4) {                                   // a 4-bit plane
         dw = (cb / 4) * 4 + i;
         pos = 4 * w4_slot(j) + (cb & 3);
