@@ -8,8 +8,9 @@ accumulator rows (1 for M = 1, 2 for M = 2, 4 above), the K tiles per wave
 or a batch.  These small cases (N = 48, three 16-row strips, the last K tile
 complete) reach every combination, so no instantiation that a decode workload
 may select goes unchecked.  At M = 4 and K = 9216 the W4A16 activation block
-no longer fits the streaming kernel's LDS and the round-based kernel runs
-(eight tiles per wave per round).
+no longer fits the streaming kernel's LDS and the per-wave activation-ring
+kernel runs; K = 20480 (more than 8 tiles per wave) reaches the round-based
+kernel.
 
 Bar: rel-L2 <= 1e-3 and max |error| <= 1e-2 * max |y_ref| against the
 oracle's fp16-rounded output ("Low Bit ARM kernels", group-wise quantization;
@@ -58,6 +59,23 @@ def test_w4_gemv_grid(G, asym, M, K):
     torch.cuda.synchronize()
     _, ref = oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
     assert_close(f16_to_f64(y.cpu().numpy()), f16_to_f64(ref), "W4 G=%d asym=%s M=%d K=%d" % (G, asym, M, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("G,asym", [(128, False), (32, True)])
+def test_w4_gemv_round_based_long_k(G, asym, M):
+    """K = 20480 (160 K tiles): more than 8 tiles per wave even with 16
+    waves, so neither streaming form applies and the round-based kernel
+    (activations staged a round of K tiles at a time) runs."""
+    K = 20480
+    w = _w4(K, G, asym, 30)
+    x = _x(M, K, 30)
+    fmt, packed, _ = pack_w4(w, G)
+    y = _y(M)
+    lb.check(lb.lowbit_gemv(fmt, M, N, K, G, packed, dev(x), y, None, 0))
+    torch.cuda.synchronize()
+    _, ref = oracle.w4_matmul(x, "f16", w["qweight"], w["scales"], w["zeros"], G, "f16")
+    assert_close(f16_to_f64(y.cpu().numpy()), f16_to_f64(ref), "round-based G=%d asym=%s M=%d" % (G, asym, M))
 
 
 @pytest.mark.parametrize("count", [3, 6])          # 4-problem and 8-problem batch kernels
@@ -160,7 +178,8 @@ def test_w4a8_gemv_grid(G, asym, M, K):
 def test_w4_gemv_down_shape_sym_g128_small_batch(M):
     """K = 14336, N = 4096, symmetric G = 128 at M = 2 (the streaming kernel
     with two accumulator rows and eight tiles per wave) and M = 3, 4, 8 (the
-    round-based kernel); 128 seeded weight rows against the oracle."""
+    per-wave activation-ring kernel); 128 seeded weight rows against the
+    oracle."""
     K, Nd, G = 14336, 4096, 128
     w = synth.w4_weights(Nd, K, G, scale_range=(0.002, 0.01), workload_id=1, layer=M, part=6)
     x = synth.activations_f16(M, K, workload_id=1, layer=M, part=6)
