@@ -457,9 +457,14 @@ struct GemmPlan {
     int m_tiles, n_tiles;
 };
 
-// 128 x 256 output tiles (8 waves of 64 x 64); split K over workgroups while
-// the tiles alone give fewer than 256 work units and each split keeps >= 8
-// K tiles.
+// 128 x 256 output tiles (8 waves of 64 x 64), one workgroup per compute
+// unit at a time.  Split K over workgroups by the estimated makespan: rounds
+// of 256 workgroups x K tiles per workgroup, plus, when split, the reduce
+// pass's bytes (S fp32 partials read, the output written) in units of one
+// workgroup's K tile (about 12 MB of HBM traffic in the time one K tile
+// takes); each split keeps >= 8 K tiles.  (224 tiles of 32 K tiles: two
+// splits give 448 workgroups, two rounds of 16, the same makespan as one
+// round of 32, so the reduce pass would be pure cost.)
 GemmPlan plan_gemm(int M, int N, int K)
 {
     const int ktiles = (K + 127) / 128;
@@ -468,7 +473,17 @@ GemmPlan plan_gemm(int M, int N, int K)
     pl.n_tiles = (N + kV2BN - 1) / kV2BN;
     const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
     pl.splits = 1;
-    while (tiles * pl.splits < 256 && ktiles / (pl.splits * 2) >= 8) pl.splits *= 2;
+    double best = -1.0;
+    for (int s = 1;; s *= 2) {
+        const int64_t rounds = (tiles * s + 255) / 256;
+        const double reduce = s == 1 ? 0.0 : ((double)s * M * N * 4 + (double)M * N * 2) / 12e6;
+        const double cost = (double)rounds * ((ktiles + s - 1) / s) + reduce;
+        if (best < 0.0 || cost < best - 1e-9) {
+            best = cost;
+            pl.splits = s;
+        }
+        if (ktiles / (s * 2) < 8) break;
+    }
     return pl;
 }
 

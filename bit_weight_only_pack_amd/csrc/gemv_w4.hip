@@ -278,8 +278,9 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     __amdgpu_buffer_rsrc_t crs[NS], srs[NS], zrs[NS];
 #pragma unroll
     for (int sj = 0; sj < NS; ++sj) {
-        // (a strip past the problem's end reads zeros and stores nothing)
-        const bool live = strip0 + sj < nst;
+        // (a strip past the problem's end reads zeros and stores nothing; with
+        // one strip the caller has already checked it)
+        const bool live = NS == 1 || strip0 + sj < nst;
         const int64_t tiles0 = (int64_t)(live ? strip0 + sj : 0) * kt;
         crs[sj] = buffer_rsrc(codes + tiles0 * 1024, live ? (uint32_t)kt * 1024 : 0u);
         srs[sj] = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, live ? (uint32_t)kt * 16 * GPT * 2 : 0u);
@@ -403,7 +404,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     }
 #pragma unroll
     for (int sj = 0; sj < NS; ++sj) {
-        if (wave == (W > 1 ? sj : 0) && strip0 + sj < nst) {
+        if (wave == (W > 1 ? sj : 0) && (NS == 1 || strip0 + sj < nst)) {
             const int n = (strip0 + sj) * 16 + r;
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
