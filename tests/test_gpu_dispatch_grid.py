@@ -97,17 +97,22 @@ def test_w4_gemv_batched_grid(G, asym, K, M, count):
         assert_close(f16_to_f64(it[2].cpu().numpy()), ref[i], "batched %d/%d" % (i, count))
 
 
-@pytest.mark.parametrize("M", [4, 5, 8, 16])
-@pytest.mark.parametrize("G,asym", [(32, True), (128, False)])
-def test_w4_gemv_two_strip_batches(G, asym, M):
+TWO_STRIP_CASES = ([(32, True, 2048, M) for M in (4, 5, 8, 16)] + [(128, False, 2048, M) for M in (4, 5, 8, 16)] +
+                   [(G, asym, K, 8) for G in (32, 64, 128) for asym in (False, True) for K in (256, 2048)
+                    if (G, asym, K) not in ((32, True, 2048), (128, False, 2048))])
+
+
+@pytest.mark.parametrize("G,asym,K,M", TWO_STRIP_CASES)
+def test_w4_gemv_two_strip_batches(G, asym, K, M):
     """Batches of 2-4 problems with at least 1024 strips and 5 or more tokens
     run two 16-row strips per workgroup (M = 4: one, the other side of the
-    boundary).  Each problem here has an odd strip
-    count with a ragged last strip (N = 8200: 513 strips, the last of 8 rows),
-    so the last workgroup of each problem has a strip past the end.  The
-    outputs equal the one-problem launches' (one strip per workgroup) bit for
-    bit, and the oracle within the bar."""
-    n, K = 8200, 2048
+    boundary), for every group size, both weight forms and both tile counts
+    per wave it takes (K = 256: 2, K = 2048: 4).  Each problem here has an odd
+    strip count with a ragged last strip (N = 8200: 513 strips, the last of 8
+    rows), so the last workgroup of each problem has a strip past the end.
+    The outputs equal the one-problem launches' (one strip per workgroup) bit
+    for bit, and the oracle within the bar."""
+    n = 8200
     ws, xs, packs, singles = [], [], [], []
     for i in range(2):
         w = synth.w4_weights(n, K, G, asym=asym, workload_id=WL, layer=90 + M, part=i)
