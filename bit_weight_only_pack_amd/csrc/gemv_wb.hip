@@ -146,6 +146,16 @@ __device__ __forceinline__ h8 wb3_operand(const WbTile<3> &w, uint32_t mlo, uint
     return __builtin_bit_cast(h8, v);
 }
 
+// b = 8: block I's two dwords (a code per byte) -> 1024 + q at K offsets 0..7
+template <int I>
+__device__ __forceinline__ h8 wb8_operand(const WbTile<8> &w, uint32_t magic)
+{
+    const uint32_t d0 = w.a[I >> 1][2 * (I & 1)], d1 = w.a[I >> 1][2 * (I & 1) + 1];
+    const u4 v = {(d0 & 0x00FF00FFu) | magic, ((d0 >> 8) & 0x00FF00FFu) | magic, (d1 & 0x00FF00FFu) | magic,
+                  ((d1 >> 8) & 0x00FF00FFu) | magic};
+    return __builtin_bit_cast(h8, v);
+}
+
 // the offset operand of zero point z in the slots of the operand above
 __device__ __forceinline__ h8 wb3_offset(int z)
 {
@@ -172,7 +182,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
     constexpr bool PRE = !ASYM && MR == 1;                  // shared offset chain (batch 1, symmetric)
     constexpr int TB = wb_tile_blocks(PRE);
     constexpr int TPS = 4 / GPT;                            // tiles per offset set
-    constexpr int NLD = BITS == 3 ? 1 : TT::N4 + TT::N2 + TT::N1;   // code loads per tile
+    constexpr int NLD = BITS == 3 ? 1 : TT::N4 + TT::N2 + TT::N1;   // code loads per tile (b = 8: 2)
     constexpr int NW = T * (NLD + (ASYM ? 2 : 1));           // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
@@ -275,7 +285,12 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
             h8 vs[4];
-            if constexpr (BITS == 3) {
+            if constexpr (BITS == 8) {
+                vs[0] = wb8_operand<0>(w, magic);
+                vs[1] = wb8_operand<1>(w, magic);
+                vs[2] = wb8_operand<2>(w, magic);
+                vs[3] = wb8_operand<3>(w, magic);
+            } else if constexpr (BITS == 3) {
                 vs[0] = wb3_operand<0>(w, magic, magic_hi);
                 vs[1] = wb3_operand<1>(w, magic, magic_hi);
                 vs[2] = wb3_operand<2>(w, magic, magic_hi);

@@ -76,6 +76,12 @@ constexpr int64_t align256(int64_t v) { return round_up(v, 256); }
 // with a 3-bit mask; block 3's codes sit in the spare bit 3 of every nibble,
 // code bit c in dword c, and three shift-and-merge steps gather them into a
 // fourth dword of the same form.
+//
+// b = 8 keeps the two 1 KiB regions of the 4-bit planes (so each load of a
+// wave is one dense KiB) but stores a code per byte: the lane's dword 2i + h
+// (region (2i + h) / 4) holds block i's K offsets 4h, 4h + 2, 4h + 1, 4h + 3
+// in bytes 0..3, so masking it (and its 8-bit shift) with 0x00FF00FF gives two
+// codes in the two 16-bit halves, ready for fp16 1024.0.
 // dword index inside a tile of plane dword k (0..b-1) of lane l
 __host__ __device__ inline int wb_word(int bits, int lane, int k)
 {

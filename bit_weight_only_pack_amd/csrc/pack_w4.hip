@@ -151,6 +151,11 @@ __device__ inline void wb_bit(const WbPlanes &P, int i, int j, int cb, int &dw, 
         pos = 4 * w4_slot(j) + (i < 3 ? cb : 3);
         return;
     }
+    if (P.n4 == 2 && P.n2 == 0 && P.n1 == 0) {             // b = 8: a byte per code
+        dw = 2 * i + (j >> 2);
+        pos = 8 * (((j & 1) << 1) | ((j >> 1) & 1)) + cb;  // K offsets 4h, 4h+2, 4h+1, 4h+3 in bytes 0..3
+        return;
+    }
     if (cb < 4 * P.n4) {                                   // a 4-bit plane
         dw = (cb / 4) * 4 + i;
         pos = 4 * w4_slot(j) + (cb & 3);
