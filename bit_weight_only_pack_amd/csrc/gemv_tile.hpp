@@ -11,6 +11,22 @@ namespace tile {
 template <typename T>
 __device__ __forceinline__ T bitcast(uint32_t v) { return __builtin_bit_cast(T, v); }
 
+// Token placement in the 16 x 16 MFMA with MR accumulators per lane.  A lane
+// holds C rows 4 kq + j (kq = lane / 16, j < 4); only j < MR are kept, and C
+// row 4 kq + j carries token kq MR + j, so MR accumulators cover 4 MR tokens
+// (M = 1: MR = 1, M <= 8: 2, M <= 16: 4).  A row r therefore reads token
+// (r / 4) MR + r % 4; rows with r % 4 >= MR feed C rows that are never kept
+// and read a valid token instead.
+template <int MR>
+__device__ __forceinline__ int a_token(int r, int M)
+{
+    const int j = r & 3;
+    const int t = (r >> 2) * MR + (j < MR ? j : 0);
+    return t < M ? t : M - 1;
+}
+template <int MR>
+__device__ __forceinline__ int c_token(int kq, int j) { return kq * MR + j; }
+
 // 8 codes of one dword -> 8 exact fp16 values q - z, element j = K offset j.
 // blo = -(1024 + z), bhi = -(64 + z) in both halves.
 __device__ __forceinline__ h8 unpack8(uint32_t w, uint32_t magic, h2 blo, h2 bhi)
@@ -200,6 +216,49 @@ __device__ __forceinline__ void tile_product_split(const u4 &q, const MetaRaw<G,
 #pragma unroll
             for (int j = 0; j < MR; ++j) acc[j] = __builtin_fmaf(sc, cv[j] - cp[j], acc[j]);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Asymmetric weights with G = 32 (one dword of codes per group and lane): the
+// MFMA operand is q - z itself, so one chain per group and no offset chain.
+// Codes at K offsets 0, 1, 4, 5 are masked into fp16 1152.0 (0x6480, low
+// seven mantissa bits clear), giving 1152 + q; codes at 2, 3, 6, 7 into 64.0
+// as in the offset-split form, giving 64 + q.  The zero point becomes
+// 1152 + z = 0x6400 | (z + 128) by flipping the top bit of its byte (one
+// byte permute per group places it in both halves under 0x64), and
+// 64 + z = (1152 + z) - 1088.  All of these are integers (or 64 + q with
+// one unit 1/16) that fp16 holds exactly, and so are the differences
+// (1152 + q) - (1152 + z) = q - z and (64 + q) - (64 + z) = q - z, which
+// IEEE subtraction therefore returns exactly.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMagic1152 = 0x64806480u;  // fp16 1152.0 in both halves
+
+template <int MR>
+__device__ __forceinline__ void tile_product_zp32(const u4 &q, const MetaRaw<32, true> &mr, const h8 *a,
+                                                  uint32_t m1152, uint32_t mhi, f4 &acc)
+{
+    const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t zx = mr.z ^ 0x80808080u;          // byte g: z_g + 128
+    const h2 k1088 = {(_Float16)1088.0f, (_Float16)1088.0f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        // bytes {z_g + 128, 0x64, z_g + 128, 0x64}: 1152 + z_g in both halves
+        const uint32_t tl = __builtin_amdgcn_perm(0x64646464u, zx, (uint32_t)g | (4u << 8) | ((uint32_t)g << 16) | (4u << 24));
+        const h2 tlo = bitcast<h2>(tl);
+        const h2 thi = tlo - k1088;
+        const uint32_t w = wd[g], w8 = w >> 8;
+        const h2 b0 = bitcast<h2>((w & 0x000F000Fu) | m1152) - tlo;    // k+0, k+1
+        const h2 b1 = bitcast<h2>((w & 0x00F000F0u) | mhi) - thi;      // k+2, k+3
+        const h2 b2 = bitcast<h2>((w8 & 0x000F000Fu) | m1152) - tlo;   // k+4, k+5
+        const h2 b3 = bitcast<h2>((w8 & 0x00F000F0u) | mhi) - thi;     // k+6, k+7
+        const h8 b = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+        const f4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], b, zero4, 0, 0, 0);
+        const uint16_t hb = (uint16_t)(mr.s[g / 2] >> (16 * (g & 1)));
+        const float sc = (float)__builtin_bit_cast(_Float16, hb);
+#pragma unroll
+        for (int j = 0; j < MR; ++j) acc[j] = __builtin_fmaf(sc, c[j], acc[j]);
     }
 }
 

@@ -82,8 +82,7 @@ void gemv_w4_kernel(const GemvBatch b)
     const auto srs = buffer_rsrc(scales + tiles0 * 16 * GPT * 2, (uint32_t)ktiles * 16 * GPT * 2);
     const auto zrs = buffer_rsrc(ASYM ? zeros + tiles0 * 16 * GPT : scales, ASYM ? (uint32_t)ktiles * 16 * GPT : 0u);
     const auto xrs = buffer_rsrc(x, (uint32_t)((int64_t)M * K * 2));
-    // A row r reads token min(r, M-1): rows past M only feed C rows that are never stored
-    const _Float16 *xa = xs + (r < M ? r : M - 1) * xrow + kq * 8;
+    const _Float16 *xa = xs + a_token<MR>(r, M) * xrow + kq * 8;
 
     uint32_t magic = 0x64006400u;                    // fp16 1024.0 in both halves
     asm volatile("" : "+v"(magic));                  // keep it in a register: mask+or becomes one op
@@ -158,7 +157,7 @@ void gemv_w4_kernel(const GemvBatch b)
         const int n = strip * 16 + r;
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const int m = kq * 4 + j;
+            const int m = c_token<MR>(kq, j);
             if (m < M && n < N) y[(int64_t)m * N + n] = (_Float16)acc[j];
         }
     }
@@ -309,15 +308,15 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     }
 
     // 4. products, tile by tile in load order
-    uint32_t mlo = kMagicLo, mhi = kMagicHi;
-    asm volatile("" : "+v"(mlo), "+v"(mhi));         // in registers: each mask-or is one operation
+    uint32_t mlo = kMagicLo, mhi = kMagicHi, m1152 = kMagic1152;
+    asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(m1152));   // in registers: each mask-or is one operation
     h8 psym = offset8(8);
     {
         u4 pw = __builtin_bit_cast(u4, psym);
         asm volatile("" : "+v"(pw));                 // materialised once, outside the tile loop
         psym = __builtin_bit_cast(h8, pw);
     }
-    const int xr = r < M ? r : M - 1;                // A row r reads token min(r, M-1)
+    const int xr = a_token<MR>(r, M);
     const _Float16 *xa[4];                           // A fragment i of this wave's first tile
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -368,6 +367,8 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
 #pragma unroll
                     for (int g = 0; g < GPT; ++g) off[g] = cps[(u % TPS) * GPT + g];
                     tile_product_pre<G>(qv, mv, a, off, mlo, mhi, acc[sj]);
+                } else if constexpr (ASYM && G == 32) {
+                    tile_product_zp32<MR>(qv, mv, a, m1152, mhi, acc[sj]);
                 } else {
                     tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc[sj]);
                 }
@@ -408,7 +409,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
             const int n = (strip0 + sj) * 16 + r;
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                const int m = kq * 4 + j;
+                const int m = c_token<MR>(kq, j);
                 if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[sj][j];
             }
         }
@@ -497,9 +498,9 @@ void gemv_w4_v2_single(const uint8_t *codes, const uint8_t *scales, const _Float
 constexpr int kXrSlots = 4;                         // activation slots per wave
 constexpr int kXrMaxLds = 160 * 1024;
 
-// rows staged per tile: a multiple of 4 (one LDS-direct load moves 4 rows of
-// 128 K), at least M
-__host__ __device__ inline int xr_rows(int M) { return (M + 3) / 4 * 4; }
+// rows staged per tile: 4, 8 or 16 (one LDS-direct load moves 4 rows of
+// 128 K), at least M; the kernels are instantiated for these three
+__host__ __device__ inline int xr_rows(int M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 16); }
 __host__ __device__ inline int xr_lds(int M, int W, int MR)
 {
     return W * kXrSlots * xr_rows(M) * 256 + W * MR * 64 * 4;
@@ -629,15 +630,15 @@ __device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_
         __builtin_amdgcn_sched_barrier(0);           // keep the loads in tile order
     }
 
-    uint32_t mlo = kMagicLo, mhi = kMagicHi;
-    asm volatile("" : "+v"(mlo), "+v"(mhi));
+    uint32_t mlo = kMagicLo, mhi = kMagicHi, m1152 = kMagic1152;
+    asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(m1152));
     h8 psym = offset8(8);
     {
         u4 pw = __builtin_bit_cast(u4, psym);
         asm volatile("" : "+v"(pw));
         psym = __builtin_bit_cast(h8, pw);
     }
-    const int xr = r < M ? r : M - 1;                // A row r reads token min(r, M-1)
+    const int xr = a_token<MR>(r, M);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     const int tvalid = min(tw, kt - t0);
 #pragma unroll
@@ -662,7 +663,10 @@ __device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_
             asm volatile("" : "+v"(qv));
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
-            tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
+            if constexpr (ASYM && G == 32)
+                tile_product_zp32<MR>(qv, mv, a, m1152, mhi, acc);
+            else
+                tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
         }
         if (u + NC < T) {
             // the slot's reads have returned; refill it with tile u + NC
@@ -697,7 +701,7 @@ __device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_
         const int n = strip * 16 + r;
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const int m = kq * 4 + j;
+            const int m = c_token<MR>(kq, j);
             if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[j];
         }
     }
@@ -768,15 +772,21 @@ hipError_t launch_v2_t(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st,
 }
 
 // two strips per workgroup: 2-4 problems laid end to end, several tokens
-template <int G, bool ASYM>
-hipError_t launch_v2_ns2(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+template <int G, bool ASYM, int MR>
+hipError_t launch_v2_ns2_m(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
     static bool raised2 = false, raised4 = false;
-    auto k = T <= 2 ? gemv_w4_v2_kernel<G, ASYM, 4, 2, 4, 2> : gemv_w4_v2_kernel<G, ASYM, 4, 4, 4, 2>;
+    auto k = T <= 2 ? gemv_w4_v2_kernel<G, ASYM, MR, 2, 4, 2> : gemv_w4_v2_kernel<G, ASYM, MR, 4, 4, 2>;
     const hipError_t e = v2_lds_limit((const void *)k, lds, T <= 2 ? raised2 : raised4);
     if (e != hipSuccess) return e;
     k<<<grid, block, lds, st>>>(b);
     return hipGetLastError();
+}
+template <int G, bool ASYM>
+hipError_t launch_v2_ns2(int MR, int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
+{
+    return MR == 2 ? launch_v2_ns2_m<G, ASYM, 2>(T, grid, block, lds, st, b)
+                   : launch_v2_ns2_m<G, ASYM, 4>(T, grid, block, lds, st, b);
 }
 
 template <int G, bool ASYM>
@@ -787,12 +797,15 @@ hipError_t launch_v2(int MR, int T, dim3 grid, dim3 block, size_t lds, hipStream
     return launch_v2_t<G, ASYM, 4>(T, grid, block, lds, st, b);
 }
 
+// XI = staged rows / 4: up to 8 tokens (XI <= 2) take two accumulators per
+// lane, up to 16 four
 template <int G, bool ASYM, int T, int XI>
 hipError_t launch_xr_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
+    constexpr int MR = XI <= 2 ? 2 : 4;
     if (b.count == 1) {
         static bool raised = false;
-        auto k = gemv_xr_single<G, ASYM, 4, T, XI>;
+        auto k = gemv_xr_single<G, ASYM, MR, T, XI>;
         if (!raised) {
             const hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      kXrMaxLds);
@@ -803,7 +816,7 @@ hipError_t launch_xr_k(dim3 grid, dim3 block, size_t lds, hipStream_t st, const 
         k<<<grid, block, lds, st>>>(p.codes, p.scales, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W, p.zeros);
     } else {
         static bool raised = false;
-        auto k = gemv_xr_batch<G, ASYM, 4, T, XI>;
+        auto k = gemv_xr_batch<G, ASYM, MR, T, XI>;
         if (!raised) {
             const hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      kXrMaxLds);
@@ -874,7 +887,7 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
     b.M = M;
     b.W = 0;
     if (strips == 0) return hipSuccess;
-    const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const int MR = M == 1 ? 1 : (M <= 8 ? 2 : 4);     // accumulators per lane (see a_token)
     const int G = L[0].G;
     const bool asym = L[0].asym;
     // waves per workgroup: enough that each wave holds at most 4 tiles (8 for
@@ -904,7 +917,7 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
     // strips' partial sums fit beside x.  (Measured on the 8B gate+up launch,
     // asymmetric G=32: 25.4 -> 23.4 us at M = 8, but 20.1 -> 21.6 us at M = 4,
     // where one-strip workgroups still fit three to a compute unit.)
-    if (T <= 4 && MR == 4 && M >= kNs2MinM && count >= 2 && count <= 4 && strips >= kNs2MinStrips &&
+    if (T <= 4 && MR >= 2 && M >= kNs2MinM && count >= 2 && count <= 4 && strips >= kNs2MinStrips &&
         v2_lds(M, (int)kt, W, MR, asym, 2).total <= kV2MaxLds) {
         b.ct = 0;
         int64_t wgs = 0;
@@ -915,12 +928,12 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
         const dim3 g2((unsigned)wgs);
         const size_t lds = (size_t)v2_lds(M, (int)kt, W, MR, asym, 2).total;
         switch (G) {
-        case 32: return asym ? launch_v2_ns2<32, true>((int)T, g2, block, lds, s, b)
-                             : launch_v2_ns2<32, false>((int)T, g2, block, lds, s, b);
-        case 64: return asym ? launch_v2_ns2<64, true>((int)T, g2, block, lds, s, b)
-                             : launch_v2_ns2<64, false>((int)T, g2, block, lds, s, b);
-        default: return asym ? launch_v2_ns2<128, true>((int)T, g2, block, lds, s, b)
-                             : launch_v2_ns2<128, false>((int)T, g2, block, lds, s, b);
+        case 32: return asym ? launch_v2_ns2<32, true>(MR, (int)T, g2, block, lds, s, b)
+                             : launch_v2_ns2<32, false>(MR, (int)T, g2, block, lds, s, b);
+        case 64: return asym ? launch_v2_ns2<64, true>(MR, (int)T, g2, block, lds, s, b)
+                             : launch_v2_ns2<64, false>(MR, (int)T, g2, block, lds, s, b);
+        default: return asym ? launch_v2_ns2<128, true>(MR, (int)T, g2, block, lds, s, b)
+                             : launch_v2_ns2<128, false>(MR, (int)T, g2, block, lds, s, b);
         }
     }
     if (T <= 8) {
@@ -942,7 +955,7 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
 
     // M >= 3 when the whole activation block does not fit: per-wave activation
     // rings (up to 8 rows with 8 tiles per wave, 16 rows with 4)
-    if (T <= 8 && MR == 4) {
+    if (T <= 8 && MR >= 2) {
         const int XI = xr_rows(M) / 4;
         const int64_t lds = xr_lds(M, W, MR);
         if (lds <= kXrMaxLds) {

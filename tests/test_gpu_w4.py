@@ -81,7 +81,7 @@ def test_gemv_tiny_workload():
     assert_close(f16_to_f64(gemv(w, x, 32)), _ref(w, x, 32), "tiny")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 12, 16])
 @pytest.mark.parametrize("N,K,G,asym", [
     (256, 256, 32, False),
     (300, 1056, 32, True),      # ragged N, ragged last K tile (1056 = 8*128 + 32)
