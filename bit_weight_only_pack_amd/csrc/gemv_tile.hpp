@@ -234,9 +234,17 @@ __device__ __forceinline__ void tile_product_split(const u4 &q, const MetaRaw<G,
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMagic1152 = 0x64806480u;  // fp16 1152.0 in both halves
 
+// sel[g]: byte-permute selectors {z_g + 128, 0x64, z_g + 128, 0x64}, kept in
+// registers by the caller.
+__device__ __forceinline__ void zp32_selectors(uint32_t *sel)
+{
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sel[g] = (uint32_t)g | (4u << 8) | ((uint32_t)g << 16) | (4u << 24);
+}
+
 template <int MR>
 __device__ __forceinline__ void tile_product_zp32(const u4 &q, const MetaRaw<32, true> &mr, const h8 *a,
-                                                  uint32_t m1152, uint32_t mhi, f4 &acc)
+                                                  uint32_t m1152, uint32_t mhi, const uint32_t *sel, f4 &acc)
 {
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
@@ -244,10 +252,8 @@ __device__ __forceinline__ void tile_product_zp32(const u4 &q, const MetaRaw<32,
     const h2 k1088 = {(_Float16)1088.0f, (_Float16)1088.0f};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        // bytes {z_g + 128, 0x64, z_g + 128, 0x64}: 1152 + z_g in both halves
-        const uint32_t tl = __builtin_amdgcn_perm(0x64646464u, zx, (uint32_t)g | (4u << 8) | ((uint32_t)g << 16) | (4u << 24));
-        const h2 tlo = bitcast<h2>(tl);
-        const h2 thi = tlo - k1088;
+        const h2 tlo = bitcast<h2>(__builtin_amdgcn_perm(0x64646464u, zx, sel[g]));   // 1152 + z_g
+        const h2 thi = tlo - k1088;                                                   // 64 + z_g
         const uint32_t w = wd[g], w8 = w >> 8;
         const h2 b0 = bitcast<h2>((w & 0x000F000Fu) | m1152) - tlo;    // k+0, k+1
         const h2 b1 = bitcast<h2>((w & 0x00F000F0u) | mhi) - thi;      // k+2, k+3

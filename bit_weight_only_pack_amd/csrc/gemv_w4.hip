@@ -310,6 +310,9 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     // 4. products, tile by tile in load order
     uint32_t mlo = kMagicLo, mhi = kMagicHi, m1152 = kMagic1152;
     asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(m1152));   // in registers: each mask-or is one operation
+    uint32_t zsel[4];
+    zp32_selectors(zsel);
+    if constexpr (ASYM && G == 32) asm volatile("" : "+v"(zsel[0]), "+v"(zsel[1]), "+v"(zsel[2]), "+v"(zsel[3]));
     h8 psym = offset8(8);
     {
         u4 pw = __builtin_bit_cast(u4, psym);
@@ -368,7 +371,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
                     for (int g = 0; g < GPT; ++g) off[g] = cps[(u % TPS) * GPT + g];
                     tile_product_pre<G>(qv, mv, a, off, mlo, mhi, acc[sj]);
                 } else if constexpr (ASYM && G == 32) {
-                    tile_product_zp32<MR>(qv, mv, a, m1152, mhi, acc[sj]);
+                    tile_product_zp32<MR>(qv, mv, a, m1152, mhi, zsel, acc[sj]);
                 } else {
                     tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc[sj]);
                 }
@@ -632,6 +635,9 @@ __device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_
 
     uint32_t mlo = kMagicLo, mhi = kMagicHi, m1152 = kMagic1152;
     asm volatile("" : "+v"(mlo), "+v"(mhi), "+v"(m1152));
+    uint32_t zsel[4];
+    zp32_selectors(zsel);
+    if constexpr (ASYM && G == 32) asm volatile("" : "+v"(zsel[0]), "+v"(zsel[1]), "+v"(zsel[2]), "+v"(zsel[3]));
     h8 psym = offset8(8);
     {
         u4 pw = __builtin_bit_cast(u4, psym);
@@ -664,7 +670,7 @@ __device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_
             MetaRaw<G, ASYM> mv = mr[u];
             pin_meta<G, ASYM>(mv);
             if constexpr (ASYM && G == 32)
-                tile_product_zp32<MR>(qv, mv, a, m1152, mhi, acc);
+                tile_product_zp32<MR>(qv, mv, a, m1152, mhi, zsel, acc);
             else
                 tile_product_split<G, ASYM, MR>(qv, mv, a, psym, mlo, mhi, acc);
         }

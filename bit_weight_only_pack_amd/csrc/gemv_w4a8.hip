@@ -325,9 +325,9 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
     }
 
     // 6. products, tile by tile in load order
-    const int xr = r < M ? r : M - 1;                // A row r reads token min(r, M-1)
+    const int xr = a_token<MR>(r, M);
     const int MS = a8_ms(M);
-    const int row0 = min(4 * kq, MS - MR);           // first token row of this lane's C elements
+    const int row0 = min(c_token<MR>(kq, 0), MS - MR);   // first token of this lane's C elements
     const uint8_t *img = smem + B.img + xr * 8;
     const int *xsum = reinterpret_cast<const int *>(smem + B.xs) + row0;
     const i4v zero4 = {0, 0, 0, 0};
@@ -424,7 +424,7 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
         const int n = strip * 16 + r;
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const int m = kq * 4 + j;
+            const int m = c_token<MR>(kq, j);
             if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)(sxv[m] * acc[j]);
         }
     }
@@ -549,7 +549,7 @@ A8Plan a8_plan(const W4Layout *L, int count, int M)
     p.mode = -1;
     p.ws = 0;
     p.lds = 0;
-    p.MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    p.MR = M == 1 ? 1 : (M <= 8 ? 2 : 4);          // accumulators per lane (see a_token)
     int64_t kt = 0;
     for (int i = 0; i < count; ++i) kt = L[i].ktiles > kt ? L[i].ktiles : kt;
     p.kt = kt;
