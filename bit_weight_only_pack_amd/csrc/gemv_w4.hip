@@ -37,10 +37,37 @@ constexpr size_t kMaxLds = 64 * 1024;
 // Dynamic LDS of one workgroup: a chunk of `ct` K tiles of every activation
 // row, each row padded by 16 bytes (so the 16 A rows of an MFMA operand fall
 // in different banks), followed by the cross-wave reduction buffer.
+// Cross-wave sum of a workgroup's per-wave partials (W <= 16 waves along K).
+// Every partial has one of kRedSlots slots per value; wave w writes slot w,
+// and slots W .. 15 hold +0 (written by the waves too), so the summing wave
+// reads all sixteen with fixed offsets and adds them as a balanced tree:
+// ((s0 + s1) + (s2 + s3)) + ...  The order is fixed, so the result is
+// deterministic, and it does not branch on W.
+constexpr int kRedSlots = 16;
+
+// writes this wave's partial v into slot `wave` of the value at `base`
+// (stride: floats between slots) and +0 into its share of slots W .. 15
+__device__ __forceinline__ void red_put(float *base, int stride, int wave, int W, float v)
+{
+    base[wave * stride] = v;
+    for (int w = wave + W; w < kRedSlots; w += W) base[w * stride] = 0.f;
+}
+__device__ __forceinline__ float red_sum(const float *base, int stride)
+{
+    float v[kRedSlots];
+#pragma unroll
+    for (int w = 0; w < kRedSlots; ++w) v[w] = base[w * stride];
+#pragma unroll
+    for (int s = 1; s < kRedSlots; s *= 2)
+#pragma unroll
+        for (int i = 0; i < kRedSlots; i += 2 * s) v[i] += v[i + s];
+    return v[0];
+}
+
 __host__ __device__ inline int x_row_halfs(int ct) { return ct * 128 + 8; }
 __host__ __device__ inline int64_t gemv_lds_bytes(int M, int ct, int W, int MR)
 {
-    return (int64_t)M * x_row_halfs(ct) * 2 + (int64_t)W * MR * 64 * 4;
+    return (int64_t)M * x_row_halfs(ct) * 2 + (int64_t)kRedSlots * MR * 64 * 4;
 }
 
 // One workgroup = one 16-row strip (all of K) of one problem of the batch
@@ -141,15 +168,11 @@ void gemv_w4_kernel(const GemvBatch b)
     // 4. fixed-order cross-wave sum, fp16 RNE store
     if (W > 1) {
 #pragma unroll
-        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        for (int j = 0; j < MR; ++j) red_put(red + j * 64 + lane, MR * 64, wave, W, acc[j]);
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                float s = red[j * 64 + lane];
-                for (int w = 1; w < W; ++w) s += red[(w * MR + j) * 64 + lane];
-                acc[j] = s;
-            }
+            for (int j = 0; j < MR; ++j) acc[j] = red_sum(red + j * 64 + lane, MR * 64);
         }
     }
     if (wave == 0) {
@@ -203,7 +226,7 @@ __host__ __device__ inline V2Lds v2_lds(int M, int kt, int W, int MR, bool asym,
     V2Lds l;
     l.rowp = (int)round_up((int64_t)kt * v2_tile_blocks(asym, MR), 64);
     l.red = M * l.rowp * 16;
-    l.total = l.red + NS * W * MR * 64 * 4;
+    l.total = l.red + (W > 1 ? NS * kRedSlots * MR * 64 * 4 : 0);
     return l;
 }
 
@@ -247,7 +270,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     const int t0 = wave * tw;
     constexpr int TB = v2_tile_blocks(ASYM, MR);
     const V2Lds L = v2_lds(M, kt, W, MR, ASYM, NS);
-    float *red = reinterpret_cast<float *>(smem + L.red);     // [NS][W][MR][64]
+    float *red = reinterpret_cast<float *>(smem + L.red);     // [NS][kRedSlots][MR][64]
 
     // 1. activations -> LDS: chunk cc of row m holds blocks 64 cc .. 64 cc + 63
     //    of the row; block b < 16 of tile t of row m holds
@@ -379,30 +402,21 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
         }
     }
 
-    // 5. fixed-order cross-wave sum (all partials read at once, added in wave
-    //    order), fp16 RNE store; wave sj sums and stores strip sj (wave 0
-    //    both when the workgroup has one wave)
+    // 5. fixed-order cross-wave sum (a balanced tree over the sixteen
+    //    partial slots), fp16 RNE store; wave sj sums and stores strip sj
+    //    (wave 0 both when the workgroup has one wave)
     if (W > 1) {
 #pragma unroll
         for (int sj = 0; sj < NS; ++sj)
 #pragma unroll
-            for (int j = 0; j < MR; ++j) red[((sj * W + wave) * MR + j) * 64 + lane] = acc[sj][j];
+            for (int j = 0; j < MR; ++j)
+                red_put(red + (sj * kRedSlots * MR + j) * 64 + lane, MR * 64, wave, W, acc[sj][j]);
         __syncthreads();
 #pragma unroll
         for (int sj = 0; sj < NS; ++sj) {
             if (wave == sj) {
-                const float *rs = red + sj * W * MR * 64;
 #pragma unroll
-                for (int j = 0; j < MR; ++j) {
-                    float part[16];
-#pragma unroll
-                    for (int w = 1; w < 16; ++w) part[w] = w < W ? rs[(w * MR + j) * 64 + lane] : 0.f;
-                    float v = rs[j * 64 + lane];
-#pragma unroll
-                    for (int w = 1; w < 16; ++w)
-                        if (w < W) v += part[w];
-                    acc[sj][j] = v;
-                }
+                for (int j = 0; j < MR; ++j) acc[sj][j] = red_sum(red + (sj * kRedSlots * MR + j) * 64 + lane, MR * 64);
             }
         }
     }
@@ -506,7 +520,7 @@ constexpr int kXrMaxLds = 160 * 1024;
 __host__ __device__ inline int xr_rows(int M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 16); }
 __host__ __device__ inline int xr_lds(int M, int W, int MR)
 {
-    return W * kXrSlots * xr_rows(M) * 256 + W * MR * 64 * 4;
+    return W * kXrSlots * xr_rows(M) * 256 + kRedSlots * MR * 64 * 4;
 }
 
 // s_waitcnt vmcnt(n) for an n the optimizer folds to a constant (unrolled loops)
@@ -681,24 +695,15 @@ __device__ __forceinline__ void gemv_xr_strip(const uint8_t *codes, const uint8_
         }
     }
 
-    // fixed-order cross-wave sum (all partials read at once, added in wave
-    // order), fp16 RNE store
+    // fixed-order cross-wave sum (a balanced tree over the sixteen partial
+    // slots), fp16 RNE store
     if (W > 1) {
 #pragma unroll
-        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        for (int j = 0; j < MR; ++j) red_put(red + j * 64 + lane, MR * 64, wave, W, acc[j]);
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                float part[16];
-#pragma unroll
-                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
-                float v = red[j * 64 + lane];
-#pragma unroll
-                for (int w = 1; w < 16; ++w)
-                    if (w < W) v += part[w];
-                acc[j] = v;
-            }
+            for (int j = 0; j < MR; ++j) acc[j] = red_sum(red + j * 64 + lane, MR * 64);
         }
     } else {
         __builtin_amdgcn_s_waitcnt(0);
