@@ -11,6 +11,33 @@ namespace tile {
 template <typename T>
 __device__ __forceinline__ T bitcast(uint32_t v) { return __builtin_bit_cast(T, v); }
 
+// Cross-wave sum of a workgroup's per-wave partials (W <= 16 waves along K).
+// Every partial has one of kRedSlots slots per value; wave w writes slot w,
+// and slots W .. 15 hold +0 (written by the waves too), so the summing wave
+// reads all sixteen with fixed offsets and adds them as a balanced tree:
+// ((s0 + s1) + (s2 + s3)) + ...  The order is fixed, so the result is
+// deterministic, and it does not branch on W.
+constexpr int kRedSlots = 16;
+
+// writes this wave's partial v into slot `wave` of the value at `base`
+// (stride: floats between slots) and +0 into its share of slots W .. 15
+__device__ __forceinline__ void red_put(float *base, int stride, int wave, int W, float v)
+{
+    base[wave * stride] = v;
+    for (int w = wave + W; w < kRedSlots; w += W) base[w * stride] = 0.f;
+}
+__device__ __forceinline__ float red_sum(const float *base, int stride)
+{
+    float v[kRedSlots];
+#pragma unroll
+    for (int w = 0; w < kRedSlots; ++w) v[w] = base[w * stride];
+#pragma unroll
+    for (int s = 1; s < kRedSlots; s *= 2)
+#pragma unroll
+        for (int i = 0; i < kRedSlots; i += 2 * s) v[i] += v[i + s];
+    return v[0];
+}
+
 // Token placement in the 16 x 16 MFMA with MR accumulators per lane.  A lane
 // holds C rows 4 kq + j (kq = lane / 16, j < 4); only j < MR are kept, and C
 // row 4 kq + j carries token kq MR + j, so MR accumulators cover 4 MR tokens

@@ -37,33 +37,6 @@ constexpr size_t kMaxLds = 64 * 1024;
 // Dynamic LDS of one workgroup: a chunk of `ct` K tiles of every activation
 // row, each row padded by 16 bytes (so the 16 A rows of an MFMA operand fall
 // in different banks), followed by the cross-wave reduction buffer.
-// Cross-wave sum of a workgroup's per-wave partials (W <= 16 waves along K).
-// Every partial has one of kRedSlots slots per value; wave w writes slot w,
-// and slots W .. 15 hold +0 (written by the waves too), so the summing wave
-// reads all sixteen with fixed offsets and adds them as a balanced tree:
-// ((s0 + s1) + (s2 + s3)) + ...  The order is fixed, so the result is
-// deterministic, and it does not branch on W.
-constexpr int kRedSlots = 16;
-
-// writes this wave's partial v into slot `wave` of the value at `base`
-// (stride: floats between slots) and +0 into its share of slots W .. 15
-__device__ __forceinline__ void red_put(float *base, int stride, int wave, int W, float v)
-{
-    base[wave * stride] = v;
-    for (int w = wave + W; w < kRedSlots; w += W) base[w * stride] = 0.f;
-}
-__device__ __forceinline__ float red_sum(const float *base, int stride)
-{
-    float v[kRedSlots];
-#pragma unroll
-    for (int w = 0; w < kRedSlots; ++w) v[w] = base[w * stride];
-#pragma unroll
-    for (int s = 1; s < kRedSlots; s *= 2)
-#pragma unroll
-        for (int i = 0; i < kRedSlots; i += 2 * s) v[i] += v[i + s];
-    return v[0];
-}
-
 __host__ __device__ inline int x_row_halfs(int ct) { return ct * 128 + 8; }
 __host__ __device__ inline int64_t gemv_lds_bytes(int M, int ct, int W, int MR)
 {

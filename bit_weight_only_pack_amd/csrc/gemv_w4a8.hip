@@ -105,7 +105,7 @@ __host__ __device__ inline A8Lds a8_lds(int M, int K, int kt, int G, int W, int 
     const A8Block b = a8_block(M, kt, G);
     A8Lds l;
     l.red = b.bytes;
-    l.amx = l.red + W * MR * 64 * 4;
+    l.amx = l.red + (W > 1 ? kRedSlots * MR * 64 * 4 : 0);
     l.xf = fused ? l.amx + 1024 : l.amx;
     l.total = l.xf + (fused ? M * (int)round_up(K, 512) * 2 : 0);
     return l;
@@ -398,25 +398,16 @@ __device__ __forceinline__ void a8_strip(const uint8_t *codes, const uint8_t *sc
         }
     }
 
-    // 7. fixed-order cross-wave sum (all partials read at once, added in wave
-    //    order), y = fp16(s[m] * sum)
+    // 7. fixed-order cross-wave sum (a balanced tree over the sixteen
+    //    partial slots), y = fp16(s[m] * sum)
     float *red = reinterpret_cast<float *>(smem + L.red);
     if (W > 1) {
 #pragma unroll
-        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        for (int j = 0; j < MR; ++j) red_put(red + j * 64 + lane, MR * 64, wave, W, acc[j]);
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                float part[16];
-#pragma unroll
-                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
-                float v = red[j * 64 + lane];
-#pragma unroll
-                for (int w = 1; w < 16; ++w)
-                    if (w < W) v += part[w];
-                acc[j] = v;
-            }
+            for (int j = 0; j < MR; ++j) acc[j] = red_sum(red + j * 64 + lane, MR * 64);
         }
     }
     if (wave == 0) {

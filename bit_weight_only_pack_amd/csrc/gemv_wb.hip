@@ -36,7 +36,7 @@ __host__ __device__ constexpr int wb_tile_blocks(bool pre) { return pre ? 20 : 1
 __host__ __device__ inline int wb_rowp(int kt, bool pre) { return (int)round_up((int64_t)kt * wb_tile_blocks(pre), 64); }
 __host__ __device__ inline int wb_lds(int M, int kt, int W, int MR, bool pre)
 {
-    return M * wb_rowp(kt, pre) * 16 + W * MR * 64 * 4;
+    return M * wb_rowp(kt, pre) * 16 + (W > 1 ? kRedSlots * MR * 64 * 4 : 0);
 }
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t *lds, uint32_t off)
@@ -334,23 +334,15 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
         }
     }
 
-    // 5. fixed-order cross-wave sum, fp16 RNE store
+    // 5. fixed-order cross-wave sum (a balanced tree over the sixteen
+    //    partial slots), fp16 RNE store
     if (W > 1) {
 #pragma unroll
-        for (int j = 0; j < MR; ++j) red[(wave * MR + j) * 64 + lane] = acc[j];
+        for (int j = 0; j < MR; ++j) red_put(red + j * 64 + lane, MR * 64, wave, W, acc[j]);
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                float part[16];
-#pragma unroll
-                for (int w = 1; w < 16; ++w) part[w] = w < W ? red[(w * MR + j) * 64 + lane] : 0.f;
-                float v = red[j * 64 + lane];
-#pragma unroll
-                for (int w = 1; w < 16; ++w)
-                    if (w < W) v += part[w];
-                acc[j] = v;
-            }
+            for (int j = 0; j < MR; ++j) acc[j] = red_sum(red + j * 64 + lane, MR * 64);
         }
     }
     if (wave == 0) {
