@@ -8,10 +8,13 @@ gate, up, down; K x N = 4096x4096, 4096x1024, 4096x1024, 4096x4096,
 layer, q/k/v read one input vector and gate/up another; o and down have their
 own), fp16 outputs.  Every weight is distinct (3.49 GB of packed
 codes, 0.11 GB of scales): the step streams 3,603,955,712 algorithmic bytes
-and no cache can hold it.  The projections that read the same layer input run
-as one batched launch (q/k/v, gate/up), so a layer is 4 launches in
-dependency order (--mode unfused runs 7; --mode chain runs the whole step as
-one persistent launch whose stages wait for each other on the GPU).  The step
+and no cache can hold it.  The projections that read the same layer input
+(q/k/v, gate/up) are stacked into one weight matrix each, as serving stacks
+store them, and run as one launch, so a layer is 4 launches in dependency
+order (--mode batched packs each projection on its own and runs a group as
+one lowbit_gemv_batched launch; --mode unfused runs 7; --mode chain runs the
+whole step as one persistent launch whose stages wait for each other on the
+GPU).  The step
 is captured once as a HIP graph and replayed.  Printed: one JSON line with the step's effective HBM GB/s (the
 metric), tokens/s (= steps/s at M = 1), the dominant kernel's roofline entry
 and the CPU oracle's rate on a bounded sample of the same step.
@@ -67,37 +70,63 @@ def w4_bytes(K, N, M, G, asym):
 GROUPS_FUSED = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
-def build_step(lb, synth, torch, M, G, asym, workload_id, fused, outlier_frac=0.0):
+def stack_weights(ws):
+    """The projections of one group as one weight matrix, rows in group order
+    (q, k, v -> 6144 rows; gate, up -> 28672): the layout serving stacks keep
+    for projections that read the same input.  Row n of the stacked product
+    is row n of its projection's product."""
+    out = {}
+    for key in ws[0]:
+        out[key] = None if ws[0][key] is None else np.concatenate([w[key] for w in ws], axis=0)
+    return out
+
+
+def build_step(lb, synth, torch, M, G, asym, workload_id, layout="stacked", outlier_frac=0.0):
     """Pack every weight of the 32-layer step on the GPU; return the launch list.
-    Each launch = one lowbit_gemv_batched call over a group of projections.
     As in a decoder layer, the projections of one group read the same input
     row(s): q/k/v share one activation vector, gate/up share one (drawn with
-    the seed of the group's first projection); o and down have their own."""
+    the seed of the group's first projection); o and down have their own.
+    layout: "stacked" (a group's weights stacked into one matrix, one
+    single-problem launch per group), "batched" (each projection packed on
+    its own, one lowbit_gemv_batched call per group) or "unfused" (one
+    launch per projection)."""
     fmt = lb.LOWBIT_W4_ASYM if asym else lb.LOWBIT_W4_SYM
     projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
     launches = []
     keep = []
+
+    def pack(w, N, K):
+        nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
+        packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        codes = torch.from_numpy(w["qweight"]).cuda()
+        scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
+        zeros = torch.from_numpy(w["zeros"]).cuda() if asym else None
+        lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, zeros, packed, nb))
+        return packed
+
     for layer in range(LAYERS):
         for group in GROUPS_FUSED:
             pid0, K0, _ = projs[group[0]]
             x = torch.from_numpy(synth.activations_f16(M, K0, outlier_frac=outlier_frac, workload_id=workload_id,
                                                        layer=layer, part=pid0)).cuda()
-            items = []
+            ws = []
             for name in group:
                 pid, K, N = projs[name]
-                w = synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
-                                     layer=layer, part=pid)
-                nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
-                packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
-                codes = torch.from_numpy(w["qweight"]).cuda()
-                scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
-                zeros = torch.from_numpy(w["zeros"]).cuda() if asym else None
-                lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, zeros, packed, nb))
+                ws.append(synth.w4_weights(N, K, G, asym=asym, scale_range=(0.002, 0.01), workload_id=workload_id,
+                                           layer=layer, part=pid))
+            items = []
+            if layout == "stacked":
+                N = sum(projs[name][2] for name in group)
                 y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-                items.append((packed, x, y, N, K))
-                del codes, scales, zeros
+                items.append((pack(stack_weights(ws), N, K0), x, y, N, K0))
+            else:
+                for name, w in zip(group, ws):
+                    _, K, N = projs[name]
+                    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                    items.append((pack(w, N, K), x, y, N, K))
+            del ws
             keep.append(items)
-            if fused:
+            if layout != "unfused":
                 launches.append(dict(names=group, probs=lb.make_gemv_problems(items), count=len(items),
                                      bytes=sum(w4_bytes(K, N, M, G, asym) for (_, _, _, N, K) in items)))
             else:
@@ -300,6 +329,18 @@ def time_launch_groups(torch, lb, fmt, M, G, launches, stream, steps, warmup, ru
     return out
 
 
+def dominant_groups(per_group, layout):
+    """(group names, mean us per launch, mean algorithmic bytes per launch) of
+    the launches the step's dominant kernel runs: with stacked weights the
+    single-problem streaming kernel runs q+k+v, o and gate+up; with batched
+    ones the batch kernel runs q+k+v and gate+up."""
+    names = ("q+k+v", "o", "gate+up") if layout == "stacked" else ("q+k+v", "gate+up")
+    dom = [per_group[n] for n in names]
+    us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    nb = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    return names, us, nb
+
+
 def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0, a8=False):
     """The CPU oracle on the first `layers` layers of the same step (single
     thread); a8: the W4A8 product (dynamic INT8 activations)."""
@@ -333,7 +374,8 @@ def cpu_baseline_decode(synth, layers, M, G, asym, workload_id, outlier_frac=0.0
 def bench_decode(args, torch, lb, synth):
     M, G, asym, wid = 1, 128, False, 1
     mode = args.mode
-    fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=(mode != "unfused"))
+    fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid,
+                                     layout="stacked" if mode == "chain" else mode)
     step_bytes = sum(L["bytes"] for L in launches)
     stream = torch.cuda.Stream()
     if mode == "chain":
@@ -354,16 +396,24 @@ def bench_decode(args, torch, lb, synth):
                     bytes_per_launch=step_bytes, avg_launch_us=gpu_ms * 1e3, traffic_name="")
     else:
         per_group = time_launch_groups(torch, lb, fmt, M, G, launches, stream, args.steps, args.warmup)
-        if mode == "batched":
-            # the dominant kernel: gemv_w4_v2_kernel<128,sym,MR=1,T=4,NP=4> runs
-            # the q+k+v and gate+up launches (4 of every 7 GEMVs, ~2/3 of the
-            # step's time); its figure is the bytes of those launches over their
-            # measured durations
-            dom = [per_group["q+k+v"], per_group["gate+up"]]
+        if mode in ("stacked", "batched"):
+            # the dominant kernel.  Stacked: gemv_w4_v2_single<128,sym,MR=1,T=4>
+            # runs the q+k+v, o and gate+up launches (3 of every 4, about 3/4 of
+            # the step's time).  Batched: gemv_w4_v2_kernel<128,sym,MR=1,T=4,NP=4>
+            # runs q+k+v and gate+up.  Its figure is the bytes of those launches
+            # over their measured durations.
+            if mode == "stacked":
+                names = ("q+k+v", "o", "gate+up")
+                kname = "gemv_w4_v2_single<G=128,sym,MR=1,T=4> (the q+k+v, o and gate+up launches)"
+                tname = "w4_gemv_decode_step_traffic.txt"
+            else:
+                names = ("q+k+v", "gate+up")
+                kname = "gemv_w4_v2_kernel<G=128,sym,MR=1,T=4,NP=4> (the q+k+v and gate+up launches)"
+                tname = ""
+            dom = [per_group[n] for n in names]
             us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
             nb = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
-            roof = dict(kernel="gemv_w4_v2_kernel<G=128,sym,MR=1,T=4,NP=4> (the q+k+v and gate+up launches)",
-                        bytes_per_launch=nb, avg_launch_us=us, traffic_name="w4_gemv_decode_step_traffic.txt")
+            roof = dict(kernel=kname, bytes_per_launch=nb, avg_launch_us=us, traffic_name=tname)
         else:
             roof = dict(kernel="gemv_w4_v2 (one launch per GEMV, M=1)", bytes_per_launch=step_bytes / len(launches),
                         avg_launch_us=gpu_ms * 1e3 / len(launches), traffic_name="")
@@ -411,7 +461,7 @@ def bench_decode_asym(args, torch, lb, synth):
     G, asym, wid = 32, True, 2
     res = {}
     for M in (1, 2, 4, 8):
-        fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=True, outlier_frac=0.01)
+        fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, layout=args.layout, outlier_frac=0.01)
         step_bytes = sum(L["bytes"] for L in launches)
         stream = torch.cuda.Stream()
         graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
@@ -424,22 +474,21 @@ def bench_decode_asym(args, torch, lb, synth):
         del graph, keep, launches
         torch.cuda.empty_cache()
     r1 = res["M=1"]
-    dom = [r1["per_launch_group"]["q+k+v"], r1["per_launch_group"]["gate+up"]]
-    us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
-    nb = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    names, us, nb = dominant_groups(r1["per_launch_group"], args.layout)
     ach = nb / (us * 1e-6) / 1e9
+    kname = ("gemv_w4_v2_single<G=32,asym,MR=1,T=4>" if args.layout == "stacked"
+             else "gemv_w4_v2_kernel<G=32,asym,MR=1,T=4,NP=4>")
     return {"metric": "W4 asymmetric G=32 decode step effective HBM GB/s (M=1; M=2, 4, 8 in per_M)",
             "value": r1["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": r1["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "dtype": "f16", "data": "synthetic (seeded; INT4 codes, fp16 scales, int8 zero points, 1 % outlier "
                                     "fp16 inputs)", "vs_baseline": None,
             "config": {"workload": "llama3-8b-w4-asym-g32-decode-step", "M": 1, "M_list": [1, 2, 4, 8],
-                       "group_size": G},
+                       "group_size": G, "layout": args.layout},
             "tokens_per_s": r1["tokens_per_s"],
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
-                         "kernel": "gemv_w4_v2_kernel<G=32,asym,MR=1,T=4,NP=4> (the q+k+v and gate+up launches, "
-                                   "M=1)",
+                         "kernel": "%s (the %s launches, M=1)" % (kname, ", ".join(names)),
                          "bytes_per_launch": round(nb), "avg_launch_us": round(us, 3),
                          "timing": "HIP events on the launch stream around graph replays of this kernel's "
                                    "launches"},
@@ -463,7 +512,7 @@ def bench_decode_w4a8(args, torch, lb, synth):
     res = {}
     m1 = None
     for M in [int(v) for v in args.m_list.split(",")]:
-        fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, fused=True, outlier_frac=0.01)
+        fmt, launches, keep = build_step(lb, synth, torch, M, G, asym, wid, layout=args.layout, outlier_frac=0.01)
         step_bytes = sum(L["bytes"] for L in launches)
         wsb = max(lb.lowbit_gemv_w4a8_batched_workspace_bytes(fmt, M, G, L["count"], L["probs"]) for L in launches)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
@@ -486,10 +535,10 @@ def bench_decode_w4a8(args, torch, lb, synth):
             m1 = dict(ms=ms, gpu_ms=gpu_ms, bytes=step_bytes, n=len(launches), pg=pg)
         del graph, keep, launches, ws
         torch.cuda.empty_cache()
-    dom = [m1["pg"]["q+k+v"], m1["pg"]["gate+up"]]
-    avg_us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
-    bpl = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    names, avg_us, bpl = dominant_groups(m1["pg"], args.layout)
     ach = bpl / (avg_us * 1e-6) / 1e9
+    kname = ("gemv_w4a8_single<G=32,asym,MR=1,T=4,FUSED>" if args.layout == "stacked"
+             else "gemv_w4a8_batch<G=32,asym,MR=1,T=4,FUSED>")
     out = {"metric": "W4A8 (dynamic INT8 activations) decode step effective HBM GB/s",
            "value": res["M=1"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": res["M=1"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -497,13 +546,13 @@ def bench_decode_w4a8(args, torch, lb, synth):
            "data": "synthetic (seeded; asymmetric INT4 G=32, zero points U{0..15}, N(0,1) fp16 inputs with 1% "
                    "outlier channels x20)",
            "config": {"workload": "llama3-8b-w4a8-asym-g32-decode-step", "M": [int(v) for v in args.m_list.split(",")],
-                      "group_size": G,
+                      "group_size": G, "layout": args.layout,
                       "launches_per_step": m1["n"]},
            "tokens_per_s": res["M=1"]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res["M=1"]["GBps"] / HBM_PEAK_GBPS, 2),
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
-                        "kernel": "gemv_w4a8_batch<G=32,asym,MR=1,T=4,FUSED> (the q+k+v and gate+up launches, M=1)",
+                        "kernel": "%s (the %s launches, M=1)" % (kname, ", ".join(names)),
                         "bytes_per_launch": round(bpl), "avg_launch_us": round(avg_us, 3),
                         "timing": "HIP events on the launch stream around graph replays of this kernel's "
                                   "launches"},
@@ -520,29 +569,39 @@ def wb_bytes(K, N, M, G, bits):
     return N * K * bits // 8 + N * (K // G) * 2 + M * K * 2 + M * N * 2
 
 
-def build_step_wb(lb, synth, torch, bits, G, workload_id):
+def build_step_wb(lb, synth, torch, bits, G, workload_id, layout="stacked"):
     """The 224-GEMV step with uniform b-bit weights (symmetric), packed on the
-    GPU layer by layer; batched launches as in build_step."""
+    GPU layer by layer; the launch groups and layouts of build_step."""
     M = 1
     fmt = lb.LOWBIT_UINT(bits)
     projs = {name: (pid, K, N) for pid, (name, K, N) in enumerate(synth.LLAMA3_8B_PROJS)}
     launches, keep = [], []
+
+    def pack(w, N, K):
+        nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
+        packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        codes = torch.from_numpy(w["codes"]).cuda()
+        scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
+        lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, None, packed, nb))
+        return packed
+
     for layer in range(LAYERS):
         for group in GROUPS_FUSED:
             pid0, K0, _ = projs[group[0]]
             x = torch.from_numpy(synth.activations_f16(M, K0, workload_id=workload_id, layer=layer, part=pid0)).cuda()
+            ws = [synth.wb_weights(projs[name][2], projs[name][1], G, bits, workload_id=workload_id, layer=layer,
+                                   part=projs[name][0]) for name in group]
             items = []
-            for name in group:
-                pid, K, N = projs[name]
-                w = synth.wb_weights(N, K, G, bits, workload_id=workload_id, layer=layer, part=pid)
-                nb = lb.lowbit_packed_bytes(fmt, 1, N, K, G)
-                packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
-                codes = torch.from_numpy(w["codes"]).cuda()
-                scales = torch.from_numpy(w["scales"].view(np.uint16)).cuda()
-                lb.check(lb.lowbit_pack_weights(fmt, 1, N, K, G, codes, scales, None, packed, nb))
+            if layout == "stacked":
+                N = sum(projs[name][2] for name in group)
                 y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-                items.append((packed, x, y, N, K))
-                del codes, scales, w
+                items.append((pack(stack_weights(ws), N, K0), x, y, N, K0))
+            else:
+                for name, w in zip(group, ws):
+                    _, K, N = projs[name]
+                    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                    items.append((pack(w, N, K), x, y, N, K))
+            del ws
             keep.append(items)
             launches.append(dict(names=group, probs=lb.make_gemv_problems(items), count=len(items),
                                  bytes=sum(wb_bytes(K, N, M, G, bits) for (_, _, _, N, K) in items)))
@@ -557,7 +616,7 @@ def bench_decode_bits(args, torch, lb, synth):
     res = {}
     ref = None
     for bits in [int(v) for v in args.bits.split(",")]:
-        fmt, launches, keep = build_step_wb(lb, synth, torch, bits, G, wid)
+        fmt, launches, keep = build_step_wb(lb, synth, torch, bits, G, wid, args.layout)
         step_bytes = sum(L["bytes"] for L in launches)
         stream = torch.cuda.Stream()
         graph = capture(torch, lambda: run_step(lb, fmt, M, G, launches, stream.cuda_stream), stream)
@@ -570,10 +629,10 @@ def bench_decode_bits(args, torch, lb, synth):
             ref = dict(bits=bits, pg=pg)
         del graph, keep, launches
         torch.cuda.empty_cache()
-    dom = [ref["pg"]["q+k+v"], ref["pg"]["gate+up"]]
-    avg_us = sum(d["us"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
-    bpl = sum(d["bytes_per_launch"] * d["launches"] for d in dom) / sum(d["launches"] for d in dom)
+    names, avg_us, bpl = dominant_groups(ref["pg"], args.layout)
     ach = bpl / (avg_us * 1e-6) / 1e9
+    kname = ("gemv_wb_single<b=%d,G=128,sym,MR=1,T=4>" if args.layout == "stacked"
+             else "gemv_wb_batch<b=%d,G=128,sym,MR=1,T=4>") % ref["bits"]
     key = "b=%d" % ref["bits"]
     out = {"metric": "b-bit decode step effective HBM GB/s and tokens/s at 8B shapes", "value": res[key]["GBps"],
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -581,13 +640,13 @@ def bench_decode_bits(args, torch, lb, synth):
            "vs_baseline": None, "dtype": "f16",
            "data": "synthetic (seeded; uniform b-bit codes, U[0.002,0.01] fp16 scales, N(0,1) fp16 inputs)",
            "config": {"workload": "llama3-8b-uint-decode-step", "bits": [int(v) for v in args.bits.split(",")],
-                      "value_bits": ref["bits"], "M": M, "group_size": G, "launches_per_step": 4 * LAYERS},
+                      "value_bits": ref["bits"], "M": M, "group_size": G, "launches_per_step": 4 * LAYERS,
+                      "layout": args.layout},
            "tokens_per_s": res[key]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res[key]["GBps"] / HBM_PEAK_GBPS, 2),
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
-                        "kernel": "gemv_wb_batch<b=%d,G=128,sym,MR=1,T=4> (the q+k+v and gate+up launches)"
-                                  % ref["bits"],
+                        "kernel": "%s (the %s launches)" % (kname, ", ".join(names)),
                         "bytes_per_launch": round(bpl), "avg_launch_us": round(avg_us, 3),
                         "timing": "HIP events on the launch stream around graph replays of this kernel's "
                                   "launches"},
@@ -896,10 +955,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "decode-asym", "decode-w4a8", "decode-bits", "prefill", "moe", "tiny"])
-    ap.add_argument("--mode", default="batched", choices=["chain", "batched", "unfused"],
-                    help="decode: chain = the whole step as one persistent launch with stage dependencies; "
-                         "batched = one launch per group of GEMVs sharing an input (4 per layer); "
-                         "unfused = one launch per GEMV (7 per layer)")
+    ap.add_argument("--mode", default="stacked", choices=["stacked", "chain", "batched", "unfused"],
+                    help="decode: stacked = the GEMVs sharing an input as one stacked weight matrix, one "
+                         "launch each (4 per layer); batched = the same groups with each projection packed on "
+                         "its own, one lowbit_gemv_batched launch per group; unfused = one launch per GEMV "
+                         "(7 per layer); chain = the whole step as one persistent launch with stage "
+                         "dependencies (stacked weights)")
+    ap.add_argument("--layout", default="stacked", choices=["stacked", "batched"],
+                    help="decode-asym, decode-w4a8, decode-bits: weights of the GEMVs sharing an input stacked "
+                         "into one matrix, or packed one by one and batched")
     ap.add_argument("--cpu-layers", type=int, default=4, help="decode: layers the CPU oracle runs (0 = skip)")
     ap.add_argument("--m-list", default="1,2,4,8", help="decode-w4a8: token counts to run (must include 1)")
     ap.add_argument("--bits", default="2,3,8", help="decode-bits: code widths to run (1..8)")

@@ -233,7 +233,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
                                               const _Float16 *xg, _Float16 *yp, int N, int K, int kt, int tw, int M,
                                               int W, int strip0, int nst = 0x7FFFFFFF)
 {
-    static_assert(NS == 1 || (NS == 2 && !(!ASYM && MR == 1) && !SINGLE), "two strips: the general product only");
+    static_assert(NS == 1 || (NS == 2 && !(!ASYM && MR == 1)), "two strips: the general product only");
     constexpr int GPT = 128 / G;
     constexpr int NW = T * (ASYM ? 3 : 2);          // weight + metadata loads per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -267,7 +267,7 @@ __device__ __forceinline__ void gemv_v2_strip(const uint8_t *codes, const uint8_
     //    LDS everywhere, waited for after the first EARLY tiles' loads
     u4 q[NS][T];
     MetaRaw<G, ASYM> mr[NS][T];
-    constexpr int EARLY = T >= 8 ? 1 : (SINGLE && T == 4 ? 2 : T);
+    constexpr int EARLY = T >= 8 ? 1 : (SINGLE && NS == 1 && T == 4 ? 2 : T);
     constexpr int LPT = ASYM ? 3 : 2;                // loads per tile (codes, scales[, zeros])
     static_assert(NW == T * LPT, "load count");
     __amdgpu_buffer_rsrc_t crs[NS], srs[NS], zrs[NS];
@@ -465,12 +465,15 @@ void gemv_w4_v2_kernel(const GemvBatch b)
 // One problem: every field is a kernel argument of its own (16 dwords), so
 // the hardware preloads them into scalar registers before the first
 // instruction and the first load needs no kernel-argument read.
-template <int G, bool ASYM, int MR, int T>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(T > 4 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
+// NS = 2: two strips per workgroup (the problem's strip count follows from N).
+template <int G, bool ASYM, int MR, int T, int NS = 1>
+__global__ __launch_bounds__(1024)
+__attribute__((amdgpu_waves_per_eu(T > 4 || NS > 1 ? 4 : (!ASYM && MR == 1) ? 8 : 6)))
 void gemv_w4_v2_single(const uint8_t *codes, const uint8_t *scales, const _Float16 *xg, _Float16 *yp, int N, int K,
                        int kt, int tw, int M, int W, const uint8_t *zeros)
 {
-    gemv_v2_strip<G, ASYM, MR, T, true>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x);
+    gemv_v2_strip<G, ASYM, MR, T, true, NS>(codes, scales, zeros, xg, yp, N, K, kt, tw, M, W, (int)blockIdx.x * NS,
+                                           (N + 15) / 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -755,10 +758,20 @@ hipError_t launch_v2_t(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st,
     return launch_v2_k<G, ASYM, MR, 8>(grid, block, lds, st, b);
 }
 
-// two strips per workgroup: 2-4 problems laid end to end, several tokens
+// two strips per workgroup, several tokens: one problem (its fields as kernel
+// arguments) or 2-4 laid end to end
 template <int G, bool ASYM, int MR>
 hipError_t launch_v2_ns2_m(int T, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvBatch &b)
 {
+    if (b.count == 1) {
+        static bool raised2s = false, raised4s = false;
+        auto k = T <= 2 ? gemv_w4_v2_single<G, ASYM, MR, 2, 2> : gemv_w4_v2_single<G, ASYM, MR, 4, 2>;
+        const hipError_t e = v2_lds_limit((const void *)k, lds, T <= 2 ? raised2s : raised4s);
+        if (e != hipSuccess) return e;
+        const GemvProblem &p = b.p[0];
+        k<<<grid, block, lds, st>>>(p.codes, p.scales, p.x, p.y, p.N, p.K, p.ktiles, p.tw, b.M, b.W, p.zeros);
+        return hipGetLastError();
+    }
     static bool raised2 = false, raised4 = false;
     auto k = T <= 2 ? gemv_w4_v2_kernel<G, ASYM, MR, 2, 4, 2> : gemv_w4_v2_kernel<G, ASYM, MR, 4, 4, 2>;
     const hipError_t e = v2_lds_limit((const void *)k, lds, T <= 2 ? raised2 : raised4);
@@ -901,7 +914,7 @@ hipError_t launch_gemv_w4_batch(const W4Layout *L, int count, int M, const uint8
     // strips' partial sums fit beside x.  (Measured on the 8B gate+up launch,
     // asymmetric G=32: 25.4 -> 23.4 us at M = 8, but 20.1 -> 21.6 us at M = 4,
     // where one-strip workgroups still fit three to a compute unit.)
-    if (T <= 4 && MR >= 2 && M >= kNs2MinM && count >= 2 && count <= 4 && strips >= kNs2MinStrips &&
+    if (T <= 4 && MR >= 2 && M >= kNs2MinM && count <= 4 && strips >= kNs2MinStrips &&
         v2_lds(M, (int)kt, W, MR, asym, 2).total <= kV2MaxLds) {
         b.ct = 0;
         int64_t wgs = 0;

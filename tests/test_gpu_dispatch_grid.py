@@ -3,7 +3,8 @@ oracle, through the C ABI.
 
 Each GEMV family (W4A16, uniform b-bit, W4A8) picks a kernel instantiation
 from the problem: the group size G, symmetric or asymmetric weights, the
-accumulator rows (1 for M = 1, 2 for M = 2, 4 above), the K tiles per wave
+accumulators per lane (W4A16 and W4A8: 1 for M = 1, 2 for M <= 8, 4 above;
+b-bit: 1 for M = 1, 4 above), the K tiles per wave
 (K = 256 -> 2, K = 2048 -> 4, K = 9216 -> 5 of an 8-tile wave) and one problem
 or a batch.  These small cases (N = 48, three 16-row strips, the last K tile
 complete) reach every combination, so no instantiation that a decode workload
@@ -23,7 +24,7 @@ import torch
 import bit_weight_only_pack_amd as lb
 import oracle
 from bit_weight_only_pack_amd import synth
-from gpu_util import assert_close, dev, f16_to_f64, pack_w4
+from gpu_util import assert_close, dev, f16_to_f64, gemv, pack_w4
 
 pytestmark = pytest.mark.gpu
 
@@ -176,6 +177,27 @@ def test_w4a8_gemv_grid(G, asym, M, K):
     torch.cuda.synchronize()
     _, ref = oracle.w4a8_matmul(x, w["qweight"], w["scales"], w["zeros"], G)
     assert_close(f16_to_f64(y.cpu().numpy()), f16_to_f64(ref), "W4A8 G=%d asym=%s M=%d K=%d" % (G, asym, M, K))
+
+
+@pytest.mark.parametrize("G,asym,K,M", TWO_STRIP_CASES)
+def test_w4_gemv_two_strip_single_problem(G, asym, K, M):
+    """One problem of at least 1024 strips with 5 or more tokens (a stacked
+    weight matrix) runs two strips per workgroup with its fields as kernel
+    arguments (M = 4: one).  N = 16392 gives 1025 strips, the last of 8 rows,
+    so the last workgroup has a strip past the end.  The output equals two
+    launches over the matrix's halves (512 and 513 strips, one strip per
+    workgroup) bit for bit, and the oracle within the bar."""
+    n, h = 16392, 8192
+    w = synth.w4_weights(n, K, G, asym=asym, workload_id=WL, layer=95 + M, part=K)
+    x = synth.activations_f16(M, K, outlier_frac=0.01, workload_id=WL, layer=95 + M, part=K)
+    y = gemv(w, x, G)
+    halves = [{k: None if v is None else v[a:b] for k, v in w.items()} for a, b in ((0, h), (h, n))]
+    sep = np.concatenate([gemv(wh, x, G) for wh in halves], axis=1)
+    assert np.array_equal(y.view(np.uint16), sep.view(np.uint16))
+    rows = np.concatenate([np.arange(0, 64), np.arange(h - 8, h + 8), np.arange(n - 40, n)])
+    _, ref = oracle.w4_matmul(x, "f16", w["qweight"][rows], w["scales"][rows],
+                              None if w["zeros"] is None else w["zeros"][rows], G, "f16")
+    assert_close(f16_to_f64(y[:, rows]), f16_to_f64(ref), "two-strip single G=%d M=%d" % (G, M))
 
 
 # ---------------------------------------------------------------- the down projection at small batch

@@ -173,6 +173,26 @@ def test_gemv_llama3_8b_shapes_asym_g32(proj, M):
     assert_close(y[:, rows], _ref(sub, x, 32), "%s M=%d" % (proj, M))
 
 
+# ---------------------------------------------------------------- stacked projections
+@pytest.mark.parametrize("group,M,G,asym", [(("q", "k", "v"), 1, 128, False), (("gate", "up"), 8, 32, True)])
+def test_gemv_stacked_equals_separate(group, M, G, asym):
+    """Projections that read the same input, stacked into one weight matrix
+    (q, k, v: 6144 rows; gate, up: 28672 rows, which at M = 8 runs two strips
+    per workgroup), give each projection's own single-GEMV output bit for
+    bit: every 16-row strip is computed the same way whatever the matrix it
+    sits in."""
+    projs = {name: (K, N) for name, K, N in synth.LLAMA3_8B_PROJS}
+    K = projs[group[0]][0]
+    ws = [synth.w4_weights(projs[n][1], K, G, asym=asym, workload_id=WL, layer=85, part=i)
+          for i, n in enumerate(group)]
+    x = synth.activations_f16(M, K, outlier_frac=0.01 if asym else 0.0, workload_id=WL, layer=85)
+    sep = np.concatenate([gemv(w, x, G) for w in ws], axis=1)
+    st = {k: None if ws[0][k] is None else np.concatenate([w[k] for w in ws], axis=0) for k in ws[0]}
+    y = gemv(st, x, G)
+    assert y.shape == sep.shape
+    assert np.array_equal(y.view(np.uint16), sep.view(np.uint16))
+
+
 # ---------------------------------------------------------------- batched GEMV
 def test_gemv_batched_matches_single_bitexact():
     """q/k/v-shaped problems (same K) in one launch give exactly the single-GEMV results."""
