@@ -62,12 +62,13 @@ def test_w4_gemv_grid(G, asym, M, K):
     assert_close(f16_to_f64(y.cpu().numpy()), f16_to_f64(ref), "W4 G=%d asym=%s M=%d K=%d" % (G, asym, M, K))
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("G,asym", [(128, False), (32, True)])
 def test_w4_gemv_round_based_long_k(G, asym, M):
     """K = 20480 (160 K tiles): more than 8 tiles per wave even with 16
     waves, so neither streaming form applies and the round-based kernel
-    (activations staged a round of K tiles at a time) runs."""
+    (activations staged a round of K tiles at a time) runs, with one, two
+    (M = 2..8) and four (M = 16) accumulators per lane."""
     K = 20480
     w = _w4(K, G, asym, 30)
     x = _x(M, K, 30)
