@@ -374,11 +374,27 @@ struct MoeGroupArgs {
 // the pass's output leaves as SiLU(gate) * up in MXFP8 (mxfp8.hpp) instead of
 // bf16 gate/up rows; gate and up are rounded to bf16 first, as the layer's
 // stand-alone kernels see them.
+// The fields the prologue's dependent reads need come first as scalar kernel
+// arguments (13 dwords), which the hardware preloads into scalar registers:
+// the first routing read goes out without a kernel-argument round trip.  The
+// rest arrive with the argument block, read in parallel.
 template <int MB, int D, bool FUSE>
 __global__ __launch_bounds__(kGWaves * 64)
-void moe_lut3_gemm_lds_kernel(MoeGroupArgs ga)
+void moe_lut3_gemm_lds_kernel(const int32_t *expert_offsets, const int32_t *block_expert, const int32_t *sorted_ids,
+                              int n_groups_a, int tiles_per_group_a, int gtiles_a, int block_m_a, int num_valid_a,
+                              int strips_a, int ksteps_a, MoeGroupArgs ga)
 {
-    const MoeArgs &p = ga.m;
+    MoeArgs p = ga.m;
+    p.expert_offsets = expert_offsets;
+    p.block_expert = block_expert;
+    p.sorted_ids = sorted_ids;
+    p.block_m = block_m_a;
+    p.num_valid = num_valid_a;
+    p.strips = strips_a;
+    p.ksteps = ksteps_a;
+    ga.n_groups = n_groups_a;
+    ga.tiles_per_group = tiles_per_group_a;
+    ga.gtiles = gtiles_a;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -757,7 +773,9 @@ hipError_t moe_gemm_common(const Lut3Layout &L, const uint8_t *packed, int E_glo
                       : (mb == 2 ? moe_lut3_gemm_lds_kernel<2, 5, false> : moe_lut3_gemm_lds_kernel<1, 5, false>);
         hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        k<<<gblocks, kGWaves * 64, lds, s>>>(ga);
+        k<<<gblocks, kGWaves * 64, lds, s>>>(p.expert_offsets, p.block_expert, p.sorted_ids, ga.n_groups,
+                                             ga.tiles_per_group, ga.gtiles, p.block_m, p.num_valid, p.strips,
+                                             p.ksteps, ga);
     } else {
         moe_lut3_gemm_kernel<<<blocks, kMoeWaves * 64, 0, s>>>(p);
     }
