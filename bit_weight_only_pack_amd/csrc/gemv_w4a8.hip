@@ -484,13 +484,14 @@ struct A8QuantBatch {
     int M;
 };
 
+// One 256-thread workgroup per token row m of one problem: the row's
+// maximum magnitude, then its codes (IMAGE: into the GEMV's prepared block;
+// else int8 [M][K] and the canonical scale).
 template <int G, bool IMAGE>
-__global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
+__device__ __forceinline__ void quant_act_row(const _Float16 *x, uint8_t *out, float *sx, int K, int kt, int M, int m)
 {
     __shared__ float wmax[4];
-    const int m = (int)blockIdx.x, pi = (int)blockIdx.y;
-    const int M = qb.M, K = qb.K[pi], kt = qb.kt[pi];
-    const _Float16 *xr = qb.x[pi] + (int64_t)m * K;
+    const _Float16 *xr = x + (int64_t)m * K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     us2 mm = {0, 0};
     for (int c = threadIdx.x; c < K / 8; c += 256) mm = a8_absmax8(*reinterpret_cast<const h8 *>(xr + c * 8), mm);
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
     const float s = __fdiv_rn(a, 127.f);
     if constexpr (IMAGE) {
         const A8Block B = a8_block(M, kt, G);
-        uint8_t *blk = qb.out[pi];
+        uint8_t *blk = out;
         for (int kb = threadIdx.x; kb < kt * 16; kb += 256) {
             h8 v = {};
             if (kb * 8 < K) v = *reinterpret_cast<const h8 *>(xr + kb * 8);
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
         }
         if (threadIdx.x == 0) reinterpret_cast<float *>(blk + B.sx)[m] = s;
     } else {
-        uint8_t *o = qb.out[pi] + (int64_t)m * K;
+        uint8_t *o = out + (int64_t)m * K;
         for (int c = threadIdx.x; c < K / 8; c += 256) {
             const h8 v = *reinterpret_cast<const h8 *>(xr + c * 8);
             uint32_t b[8];
@@ -521,8 +522,25 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
             const uint32_t d1 = __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[6], 0x04000C0Cu);
             *reinterpret_cast<uint2 *>(o + c * 8) = make_uint2(d0, d1);
         }
-        if (threadIdx.x == 0) qb.sx[pi][m] = s;
+        if (threadIdx.x == 0) sx[m] = s;
     }
+}
+
+// batch: blockIdx.y = problem
+template <int G, bool IMAGE>
+__global__ __launch_bounds__(256) void quant_act_kernel(const A8QuantBatch qb)
+{
+    const int pi = (int)blockIdx.y;
+    quant_act_row<G, IMAGE>(qb.x[pi], qb.out[pi], qb.sx[pi], qb.K[pi], qb.kt[pi], qb.M, (int)blockIdx.x);
+}
+
+// one problem: its fields as scalar kernel arguments, preloaded into scalar
+// registers (no kernel-argument round trip before the first load)
+template <int G, bool IMAGE>
+__global__ __launch_bounds__(256) void quant_act_single(const _Float16 *x, uint8_t *out, float *sx, int K, int kt,
+                                                        int M)
+{
+    quant_act_row<G, IMAGE>(x, out, sx, K, kt, M, (int)blockIdx.x);
 }
 
 // Launch plan shared by the workspace query and the launcher.
@@ -637,10 +655,16 @@ template <int G>
 hipError_t quant_launch(bool image, const A8QuantBatch &qb, int count, hipStream_t st)
 {
     const dim3 grid((unsigned)qb.M, (unsigned)count);
-    if (image)
+    if (count == 1) {
+        if (image)
+            quant_act_single<G, true><<<grid, 256, 0, st>>>(qb.x[0], qb.out[0], qb.sx[0], qb.K[0], qb.kt[0], qb.M);
+        else
+            quant_act_single<G, false><<<grid, 256, 0, st>>>(qb.x[0], qb.out[0], qb.sx[0], qb.K[0], qb.kt[0], qb.M);
+    } else if (image) {
         quant_act_kernel<G, true><<<grid, 256, 0, st>>>(qb);
-    else
+    } else {
         quant_act_kernel<G, false><<<grid, 256, 0, st>>>(qb);
+    }
     return hipGetLastError();
 }
 
