@@ -143,6 +143,26 @@ def test_gemv_codes_at_zero_point_give_zero():
     assert np.all(gemv(w, x, G) == 0)
 
 
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M", [1, 8])
+def test_gemv_full_int8_zero_points(G, M):
+    """Zero points over the whole int8 range, both ends included (the layout
+    accepts any int8 z; q - z then spans -128 .. 143): asymmetric G = 32 forms
+    the exact operand q - z from 1152 + q and 1152 + z (z + 128 in the low
+    byte), G = 64 / 128 run the offset chains.  Against the oracle."""
+    N, K = 256, 1024
+    rng = np.random.default_rng(77 + G + M)
+    w = _weights(N, K, G, True, part=7)
+    z = rng.integers(-128, 128, size=(N, K // G)).astype(np.int8)
+    z[0, :] = -128
+    z[1, :] = 127
+    z[2, 0::2] = -128
+    z[2, 1::2] = 127
+    w["zeros"] = z
+    x = synth.activations_f16(M, K, workload_id=WL, layer=M, part=G)
+    assert_close(f16_to_f64(gemv(w, x, G)), _ref(w, x, G), "full int8 z G=%d M=%d" % (G, M))
+
+
 # ---------------------------------------------------------------- full 8B shapes
 @pytest.mark.parametrize("proj", [p[0] for p in synth.LLAMA3_8B_PROJS])
 def test_gemv_llama3_8b_shapes_sym(proj):
