@@ -251,7 +251,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
         asm volatile("" : "+v"(pw));
         psym = __builtin_bit_cast(h8, pw);
     }
-    const int xr = r < M ? r : M - 1;
+    const int xr = a_token<MR>(r, M);
     const _Float16 *xa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -349,7 +349,7 @@ __device__ __forceinline__ void wb_strip(const uint8_t *codes, const uint8_t *sc
         const int n = strip * 16 + r;
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const int m = kq * 4 + j;
+            const int m = c_token<MR>(kq, j);
             if (m < M && n < N) yp[(int64_t)m * N + n] = (_Float16)acc[j];
         }
     }
@@ -411,6 +411,8 @@ hipError_t wb_launch_mt(int MR, int T, const GemvBatch &b, dim3 grid, dim3 block
 {
     if (MR == 1) return T <= 4 ? wb_launch_k<BITS, G, ASYM, 1, 4>(b, grid, block, lds, st)
                                : wb_launch_k<BITS, G, ASYM, 1, 8>(b, grid, block, lds, st);
+    if (MR == 2) return T <= 4 ? wb_launch_k<BITS, G, ASYM, 2, 4>(b, grid, block, lds, st)
+                               : wb_launch_k<BITS, G, ASYM, 2, 8>(b, grid, block, lds, st);
     return T <= 4 ? wb_launch_k<BITS, G, ASYM, 4, 4>(b, grid, block, lds, st)
                   : wb_launch_k<BITS, G, ASYM, 4, 8>(b, grid, block, lds, st);
 }
@@ -438,7 +440,7 @@ size_t gemv_wb_lds(int M, int64_t kt_max, bool asym)
     int W = (int)((kt_max + 3) / 4);
     W = W < 1 ? 1 : (W > 16 ? 16 : W);
     const int64_t T = (kt_max + W - 1) / W;
-    const int MR = M == 1 ? 1 : 4;
+    const int MR = M == 1 ? 1 : (M <= 8 ? 2 : 4);     // accumulators per lane (see a_token)
     const int64_t lds = wb_lds(M, (int)kt_max, W, MR, !asym && MR == 1);
     return (T > 8 || lds > kWbMaxLds) ? 0 : (size_t)lds;
 }
@@ -453,7 +455,7 @@ hipError_t launch_gemv_wb_batch(const W4Layout *L, int count, int M, const uint8
     int W = (int)((kt + 3) / 4);
     W = W < 1 ? 1 : (W > 16 ? 16 : W);
     const int T = (int)((kt + W - 1) / W);
-    const int MR = M == 1 ? 1 : 4;
+    const int MR = M == 1 ? 1 : (M <= 8 ? 2 : 4);     // accumulators per lane (see a_token)
     const size_t lds = (size_t)wb_lds(M, (int)kt, W, MR, !L[0].asym && MR == 1);
     if (T > 8 || lds > (size_t)kWbMaxLds) return hipErrorInvalidValue;   // rejected by the caller first
     for (int i = 0; i < kMaxGemvBatch; ++i) b.first[i] = 0x7FFFFFFF;

@@ -3,8 +3,7 @@ oracle, through the C ABI.
 
 Each GEMV family (W4A16, uniform b-bit, W4A8) picks a kernel instantiation
 from the problem: the group size G, symmetric or asymmetric weights, the
-accumulators per lane (W4A16 and W4A8: 1 for M = 1, 2 for M <= 8, 4 above;
-b-bit: 1 for M = 1, 4 above), the K tiles per wave
+accumulators per lane (1 for M = 1, 2 for M <= 8, 4 above), the K tiles per wave
 (K = 256 -> 2, K = 2048 -> 4, K = 9216 -> 5 of an 8-tile wave) and one problem
 or a batch.  These small cases (N = 48, three 16-row strips, the last K tile
 complete) reach every combination, so no instantiation that a decode workload

@@ -99,6 +99,7 @@ def test_uint4_packs_to_the_int4_blob():
     (1, 300, 1056, 32, True),          # ragged N, K not a multiple of 128
     (3, 96, 2048, 128, True),
     (8, 64, 4096, 64, False),
+    (12, 48, 1024, 32, True),          # four accumulators per lane (M > 8)
 ])
 def test_wb_gemv_parity(bits, M, N, K, G, asym):
     w = _w(N, K, G, bits, asym, part=M)
