@@ -7,7 +7,7 @@ gate, up, down; K x N = 4096x4096, 4096x1024, 4096x1024, 4096x4096,
 128, fp16 scales U[0.002, 0.01], fp16 activations N(0,1) (as in a decoder
 layer, q/k/v read one input vector and gate/up another; o and down have their
 own), fp16 outputs.  Every weight is distinct (3.49 GB of packed
-codes, 0.11 GB of scales): the step streams 3,603,955,712 algorithmic bytes
+codes, 0.11 GB of scales): the step streams 3,603,169,280 algorithmic bytes
 and no cache can hold it.  The projections that read the same layer input
 (q/k/v, gate/up) are stacked into one weight matrix each, as serving stacks
 store them, and run as one launch, so a layer is 4 launches in dependency
