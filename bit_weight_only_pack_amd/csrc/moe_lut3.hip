@@ -335,6 +335,15 @@ constexpr int kGWaves = 16;                         // waves per workgroup
 constexpr int kGSPW = 1;                            // strips per wave
 constexpr int kGTileStrips = kGWaves * kGSPW;       // 16 strips = 256 columns per tile
 constexpr int kLdsRowPad = 16;                      // bytes added to each staged row (rows fall in different banks)
+constexpr int kMoeScaleBytesMax = 4 * kGWaves * 64; // block-scale bytes of one pass: four per thread
+
+// LDS-direct load: lane i's 16 bytes land at lds + 16 i (no registers involved)
+template <int BYTES>
+__device__ __forceinline__ void lds_load(__amdgpu_buffer_rsrc_t rs, uint8_t *lds, uint32_t off)
+{
+    static_assert(BYTES == 16, "LDS-direct load size");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
 
 struct WSlot {
     uint32_t w[kGSPW][3];
@@ -355,7 +364,9 @@ struct MoeLds {
 __host__ __device__ inline MoeLds moe_lds_layout(int MB, int K, int tiles)
 {
     MoeLds l;
-    l.s_off = MB * 16 * (moe_kpad(K) + kLdsRowPad);
+    // the rows are filled by LDS-direct loads of 1 KiB per instruction, which
+    // write whole chunks: the region is rounded up to the chunk size
+    l.s_off = (MB * 16 * (moe_kpad(K) + kLdsRowPad) + 1023) & ~1023;
     l.sid_off = l.s_off + MB * 16 * (K / 32);
     l.out_off = (l.sid_off + MB * 16 * 4 + 15) & ~15;
     l.bytes = l.out_off + tiles * MB * 16 * kGTileStrips * 16 * 2;
@@ -406,11 +417,10 @@ void moe_lut3_gemm_lds_kernel(const int32_t *expert_offsets, const int32_t *bloc
     if (ntl <= 0) return;
     const int row0 = p.expert_offsets[e], row1 = p.expert_offsets[e + 1];
     if (row0 >= row1) return;                                  // no slot routed here
-    // the first pass's slot ids go out together with the local-expert read
-    // (both need only row0), so the weight stream can start one round trip
-    // earlier
-    int sid_first = p.num_valid;
-    if ((int)threadIdx.x < min(MB * 16, row1 - row0)) sid_first = p.sorted_ids[row0 + threadIdx.x];
+    // the first pass's slot ids (lane i: row i of the pass, in every wave) go
+    // out together with the local-expert read: both need only row0
+    static_assert(MB * 16 <= 64, "one pass row per lane");
+    int sidv = lane < min(MB * 16, row1 - row0) ? p.sorted_ids[row0 + lane] : p.num_valid;
     const int local = p.block_expert[row0 / p.block_m];
     const int col0 = tile0 * kGTileStrips * 16, col1 = min(p.N, (tile0 + ntl) * kGTileStrips * 16);
     constexpr int kHalf = kGTileStrips / 2;                    // FUSE: gate (and up) strips per tile
@@ -484,71 +494,64 @@ void moe_lut3_gemm_lds_kernel(const int32_t *expert_offsets, const int32_t *bloc
 
     for (int pass = row0; pass < row1; pass += MB * 16) {
         const int nmb = min(MB, (row1 - pass) / 16);
-        // 1. stage the pass's slot ids, then its activation rows and block
-        //    scales (invalid rows: zeros); the first weight loads of the pass
-        //    are issued just before the staging loads so their latencies
-        //    overlap, and the staging loads go out 8 per thread before any
-        //    LDS store
-        __syncthreads();                                       // previous pass done with the LDS rows
+        const int prow = nmb * 16;
+        if (pass != row0) {
+            __syncthreads();                                   // previous pass done with the LDS blocks
+            sidv = lane < prow ? p.sorted_ids[pass + lane] : p.num_valid;
+        }
+        // activation row of each pass row (lane i: row i), -1 for padding slots
+        const int arowv = sidv < p.num_valid ? sidv / p.a_row_div : -1;
+        if (wave == 0 && lane < MB * 16) sid_lds[lane] = lane < prow ? sidv : p.num_valid;
+        // 1. stage the pass's activation rows and block scales.  The rows (each
+        //    with its zero tail to whole 128-K steps and its padding) go
+        //    straight into LDS by LDS-direct loads that cover the region byte
+        //    for byte (bytes past K or past the pass's rows read zeros); the
+        //    scales go to registers.  Both are issued before the pass's first
+        //    weight loads: loads of a wave complete in issue order, so they
+        //    land ahead of the weight ring.
+        {
+            const int abytes = prow * astride;
+            for (int ci = wave; ci * 1024 < abytes; ci += kGWaves) {
+                const int d = ci * 1024 + lane * 16;
+                const int row = d / astride, k = d - row * astride;
+                const int ar = __shfl(arowv, row < 64 ? row : 0);
+                const bool ok = row < prow && ar >= 0 && k < K;
+                lds_load<16>(ars, a_lds + ci * 1024, ok ? (uint32_t)ar * (uint32_t)K + (uint32_t)k : kBufferOob);
+            }
+        }
+        // the block scales (one byte per row and 32-K block) into registers,
+        // issued before the ring as well, written to LDS once they land
+        constexpr int kScalePerThread = kMoeScaleBytesMax / (kGWaves * 64);
+        const int sbytes = prow * k_chunks;
+        uint32_t sv[kScalePerThread];
+        int sidx[kScalePerThread];
+#pragma unroll
+        for (int u = 0; u < kScalePerThread; ++u) {
+            const int b = (int)threadIdx.x + u * kGWaves * 64;
+            const int row = b / k_chunks, c = b - row * k_chunks;
+            const int ar = __shfl(arowv, row < 64 ? row : 0);
+            const bool ok = b < sbytes && ar >= 0;
+            sidx[u] = b;
+            sv[u] = __builtin_amdgcn_raw_buffer_load_b8(srs, ok ? (uint32_t)ar * (uint32_t)k_chunks + (uint32_t)c
+                                                            : kBufferOob, 0, 0);
+        }
+        //    Then the pass's first D - 1 weight steps.
         WSlot wsl[D];
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) load_w(wsl[d], d);
-        static_assert(MB * 16 <= kGWaves * 64, "one slot id per thread");
-        if ((int)threadIdx.x < MB * 16) {
-            const int i = (int)threadIdx.x;
-            sid_lds[i] = pass == row0 ? (i < nmb * 16 ? sid_first : p.num_valid)
-                                      : (i < nmb * 16 ? p.sorted_ids[pass + i] : p.num_valid);
-        }
-        __syncthreads();
-        // thread -> (row, lane in row): every thread stages 16-byte chunks of one row
-        constexpr int kRows = MB * 16;
-        constexpr int kTpr = kGWaves * 64 / kRows;            // threads per staged row
-        constexpr int kBatch = 8;
-        const int srow = threadIdx.x / kTpr, sl = threadIdx.x % kTpr;
-        const int ssid = sid_lds[srow];
-        const bool srow_ok = ssid < p.num_valid;
-        const uint32_t arow_off = srow_ok ? (uint32_t)(ssid / p.a_row_div) : 0u;
-        const int chunks = moe_kpad(K) / 16;                  // 16-byte chunks per staged row
-        const int kchunks = K / 16;                            // of which these hold data
-        for (int c0 = 0; c0 < chunks; c0 += kBatch * kTpr) {
-            u4 v[kBatch];
+        //    Every load issued before them has landed (the ring's may be in
+        //    flight): scales to LDS, and publish rows, scales and slot ids.
+        constexpr int kRing = (D - 1) * 3 * kGSPW;             // loads per ring step: codes, codebooks, exponents
+        static_assert(kRing < 64, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt((kRing & 15) | ((kRing >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(kRing)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 + sl + u * kTpr;
-                v[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    ars, srow_ok && c < kchunks ? arow_off * (uint32_t)K + c * 16 : kBufferOob, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 + sl + u * kTpr;
-                if (c < chunks)
-                    *reinterpret_cast<u4 *>(a_lds + srow * astride + c * 16) = v[u];
-                else
-                    asm volatile("" ::"v"(v[u]));      // consumed on every path: nothing stays pending
-            }
-        }
-        for (int c0 = 0; c0 < k_chunks; c0 += kBatch * kTpr) {
-            uint32_t v[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 + sl + u * kTpr;
-                v[u] = __builtin_amdgcn_raw_buffer_load_b8(
-                    srs, srow_ok && c < k_chunks ? arow_off * (uint32_t)k_chunks + c : kBufferOob, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 + sl + u * kTpr;
-                if (c < k_chunks)
-                    s_lds[srow * k_chunks + c] = (uint8_t)v[u];
-                else
-                    asm volatile("" ::"v"(v[u]));
-            }
-        }
-        // every staging load has landed (they were issued after the ring's
-        // first loads, so this waits for those too): the streaming loop below
-        // starts with nothing in flight but its own ring
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
-        __syncthreads();
+        for (int u = 0; u < kScalePerThread; ++u)
+            if (sidx[u] < sbytes) s_lds[sidx[u]] = (uint8_t)sv[u];
+        __builtin_amdgcn_s_waitcnt((7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
 
         f4 acc[MB][kGSPW];
 #pragma unroll
@@ -752,7 +755,8 @@ hipError_t moe_gemm_common(const Lut3Layout &L, const uint8_t *packed, int E_glo
     // otherwise the kernel that reads activations straight from memory.
     constexpr int kMaxLds = 80 * 1024;
     constexpr int kMaxGroupLds = 150 * 1024;
-    const int mb = moe_lds_bytes(2, p.K) <= kMaxLds ? 2 : (moe_lds_bytes(1, p.K) <= kMaxLds ? 1 : 0);
+    auto fits = [&](int m) { return moe_lds_bytes(m, p.K) <= kMaxLds && m * 16 * (p.K / 32) <= kMoeScaleBytesMax; };
+    const int mb = fits(2) ? 2 : (fits(1) ? 1 : 0);
     if (fuse && (mb == 0 || L.N % 256 != 0)) return hipErrorNotSupported;
     if (mb > 0) {
         // workgroups of 8 waves over groups of 256-column tiles: about 256
