@@ -17,7 +17,10 @@ namespace lowbit {
 //      expert's bitmask of the chunk; a slot's rank among its expert's slots
 //      is the number of set bits below its own plus that expert's count from
 //      earlier chunks -- a stable order with no sequential pass;
-//   3. block_expert (sentinels and empty blocks are written first, in step 0).
+//   3. block_expert.
+// Every output position is written exactly once (slot ids by the placement,
+// the sentinel in each expert's padding and past the padded length, -1 for
+// the blocks past it), so no store has to complete before another one.
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
@@ -41,13 +44,6 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 
-    // 0. every sorted position starts as the sentinel and every block as "no
-    //    expert"; placement and step 3 overwrite what they own.  The stores
-    //    complete (vmcnt 0) before the barrier that ends step 1, so no later
-    //    store to the same address can be overtaken by them.
-    for (int i = tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;
-    for (int b = tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
-
     // 1. counts and padded offsets (thread e owns expert e, E <= 1024)
     counts[tid] = 0;
     running[tid] = 0;
@@ -58,7 +54,6 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
         if (i < kAlignIdCache) ids[i] = (int16_t)e;
         if (e >= 0) atomicAdd(&counts[e], 1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): the step-0 stores are done
     __syncthreads();
     const int padded = tid < E ? (counts[tid] + block_m - 1) / block_m * block_m : 0;
     int incl = padded;                                // inclusive prefix inside the wave
@@ -86,6 +81,12 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
         expert_offsets[E] = total;                    // (E may equal the thread count)
         num_post_padded[0] = total;
     }
+    // the sentinel in each expert's padding and past the padded length; -1
+    // for the blocks past it
+    if (tid < E)
+        for (int i = offs[tid] + counts[tid]; i < offs[tid + 1]; ++i) sorted_ids[i] = num_valid;
+    for (int i = total + tid; i < capacity; i += kAlignThreads) sorted_ids[i] = num_valid;
+    for (int b = total / block_m + tid; b < capacity / block_m; b += kAlignThreads) block_expert[b] = -1;
 
     // 2. stable placement, chunk by chunk: a chunk's bitmask holds
     //    chunk / 32 words per expert, rows one word longer than that so the
@@ -123,7 +124,7 @@ __device__ __forceinline__ void moe_align_block(const int32_t *__restrict__ topk
         __syncthreads();
     }
 
-    // 3. expert of every block (the sentinels were written in step 0)
+    // 3. expert of every block below the padded length
     if (tid < E) {
         const int local = expert_map ? expert_map[tid] : tid;
         for (int b = offs[tid] / block_m; b < offs[tid + 1] / block_m; ++b) block_expert[b] = local;
