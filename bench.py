@@ -268,6 +268,35 @@ def time_graph(torch, graph, stream, steps, warmup):
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
+READ_CEILING_BYTES = 2 << 30        # 8x the 256 MB MALL
+
+
+def read_ceiling(torch, lb, stream, reps=20):
+    """The practical ceiling of HBM reads on this machine: lowbit_hbm_read (every
+    16-byte block of a 2 GiB buffer read once, non-temporal loads) captured
+    four times in a graph and replayed; bytes read per launch / time per
+    launch, the best of three timed blocks.  Its shader-clock samples are kept
+    out of the workload's."""
+    buf = torch.zeros(READ_CEILING_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(lb.LOWBIT_HBM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    st = stream.cuda_stream
+
+    def run():
+        for _ in range(4):
+            lb.check(lb.lowbit_hbm_read(buf, READ_CEILING_BYTES, sink, st))
+    n0 = len(SCLK_SAMPLES)
+    graph = capture(torch, run, stream)
+    gpu_ms = min(time_graph(torch, graph, stream, reps, 2)[1] for _ in range(3))   # best of three timed blocks
+    del SCLK_SAMPLES[n0:]
+    del graph, buf
+    us = gpu_ms * 1e3 / 4
+    return {"GBps": round(READ_CEILING_BYTES / (us * 1e-6) / 1e9, 1), "bytes_per_launch": READ_CEILING_BYTES,
+            "us_per_launch": round(us, 2),
+            "kernel": "hbm_read_kernel (lowbit_hbm_read: 1024 workgroups of 4 waves, a contiguous chunk per "
+                      "wave, 16 KiB of 16-byte non-temporal loads in flight per wave)",
+            "timing": "HIP events on the launch stream around graph replays of 4 launches, best of 3 blocks"}
+
+
 KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/gemv_w4.hip", "bit_weight_only_pack_amd/csrc/gemv_tile.hpp",
                   "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
 
@@ -451,9 +480,12 @@ def bench_decode(args, torch, lb, synth):
     }
     if per_group is not None:
         out["per_launch_group"] = per_group
+    del keep
+    ceil = read_ceiling(torch, lb, stream)
+    out["hbm_read_ceiling"] = ceil
+    out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceil["GBps"], 4)
     if args.cpu_layers > 0:
         out["cpu_baseline"] = cpu_baseline_decode(synth, args.cpu_layers, M, G, asym, wid)
-    del keep
     return out
 
 
@@ -855,6 +887,9 @@ def bench_moe(args, torch, lb, synth):
                         "bytes_per_launch": nbytes["gate_up_silu"], "avg_launch_us": round(us["gate_up_silu"], 3)},
            "per_kernel_us": {k: round(v, 2) for k, v in us.items()},
            "per_kernel_GBps": {k: round(nbytes[k] / (us[k] * 1e-6) / 1e9, 1) for k in us if k != "align"}}
+    ceil = read_ceiling(torch, lb, stream)
+    out["hbm_read_ceiling"] = ceil
+    out["roofline"]["frac_of_read_ceiling"] = round(gu_gbps / ceil["GBps"], 4)
     if args.cpu_layers > 0:
         import oracle
         tok = np.arange(0, T, T // 16)

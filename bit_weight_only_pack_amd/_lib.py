@@ -37,6 +37,7 @@ LOWBIT_OP_GEMV = 0
 LOWBIT_OP_GEMM = 1
 LOWBIT_OP_GEMV_W4A8 = 2
 
+LOWBIT_HBM_READ_SINK_WORDS = 1024   # sink words of lowbit_hbm_read (include/lowbit.h)
 _lib = None
 
 _vp = ctypes.c_void_p
@@ -66,6 +67,7 @@ SIGNATURES = {
     "lowbit_pack_weights": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lowbit_unpack_weights": (_i, [_i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp]),
     "lowbit_dequant": (_i, [_i, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "lowbit_hbm_read": (_i, [_vp, ctypes.c_int64, _vp, _vp]),
     "lowbit_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "lowbit_gemv": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lowbit_gemv_batched": (_i, [_i, _i, _i, _i, _vp, _vp]),
@@ -165,6 +167,10 @@ def lowbit_pack_weights(fmt, E, N, K, group_size, codes, scales, zeros, packed, 
 def lowbit_unpack_weights(fmt, E, N, K, group_size, packed, packed_bytes, codes, scales, zeros, stream=None):
     return lib().lowbit_unpack_weights(fmt, E, N, K, group_size, _ptr(packed), packed_bytes, _ptr(codes),
                                        _ptr(scales), _ptr(zeros), _stream(stream))
+
+
+def lowbit_hbm_read(buf, nbytes, sink, stream=None):
+    return lib().lowbit_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
 
 
 def lowbit_dequant(fmt, N, K, group_size, packed, packed_bytes, w_out, stream=None):

@@ -5,6 +5,11 @@
 
 #include <vector>
 
+namespace lowbit {
+// hbm_read.hip: read-only streaming of `bytes` (a multiple of 16), *sink ^= XOR of all 32-bit words
+hipError_t launch_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
+}  // namespace lowbit
+
 using namespace lowbit;
 
 namespace {
@@ -199,6 +204,16 @@ int lowbit_dequant(int fmt, int N, int K, int group_size, const void *packed, si
     const uint8_t *src = static_cast<const uint8_t *>(packed);
     return hip_status(is_w4(fmt) ? launch_w4_dequant(L, src, w_out, (hipStream_t)stream)
                                  : launch_wb_dequant(L, src, w_out, (hipStream_t)stream));
+}
+
+int lowbit_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes < 0 || bytes % 16 != 0) return LOWBIT_E_INVALID_ARG;
+    if (bytes == 0) return LOWBIT_OK;
+    if (buf == nullptr || sink == nullptr || (reinterpret_cast<uintptr_t>(buf) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
+        return LOWBIT_E_INVALID_ARG;
+    return hip_status(launch_hbm_read(buf, bytes, sink, (hipStream_t)stream));
 }
 
 size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_size)

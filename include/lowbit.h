@@ -138,6 +138,25 @@ int lowbit_dequant(int fmt, int N, int K, int group_size,
                    const void *packed, size_t packed_bytes, float *w_out, void *stream);
 
 /*
+ * Read-only streaming of a device buffer: the practical ceiling of HBM reads,
+ * measured beside the kernels' rooflines ("Low Bit Metal Kernels", practice
+ * sequence: measure the memory-bandwidth utilisation of a bandwidth-bound
+ * kernel).  Every 16-byte block is read once with non-temporal loads by
+ * LOWBIT_HBM_READ_SINK_WORDS workgroups, each of which stores the XOR of the
+ * 32-bit words it read to its own sink word, so that
+ *   XOR of sink[0 .. LOWBIT_HBM_READ_SINK_WORDS)  ==  XOR of all 32-bit words of buf
+ * (no load is dead and the result can be checked; with bytes > 0 every sink
+ * word is written).
+ *   buf   : device pointer, 16-byte aligned, `bytes` readable bytes
+ *   bytes : a multiple of 16 (0: nothing is enqueued)
+ *   sink  : device uint32 [LOWBIT_HBM_READ_SINK_WORDS] (output), 4-byte aligned
+ * Errors: LOWBIT_E_INVALID_ARG for a negative or ragged size, a null or
+ * misaligned pointer; nothing is enqueued then.
+ */
+#define LOWBIT_HBM_READ_SINK_WORDS 1024
+int lowbit_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
+/*
  * Workspace bytes an operation needs for this shape (0 if none).  Pass a
  * workspace of at least this size to that operation.
  */

@@ -261,3 +261,16 @@ def test_32bit_offset_limits_rejected_on_the_host():
     p = lb.make_gemv_problems([(FAKE, FAKE, FAKE, 256, 1 << 26)])
     assert lb.lowbit_gemv_batched(SYM, 16, 128, 1, p) == E_UNS
     assert lb.lowbit_gemv_w4a8(ASYM, 16, 256, 1 << 26, 32, FAKE, FAKE, FAKE, FAKE, 1 << 40) == E_UNS
+
+
+def test_hbm_read_argument_checks():
+    """The read-ceiling helper rejects ragged sizes and null or misaligned
+    pointers before enqueueing anything; an empty read enqueues nothing."""
+    assert lb.lowbit_hbm_read(FAKE, 0, FAKE) == lb.LOWBIT_OK
+    assert lb.lowbit_hbm_read(None, 0, None) == lb.LOWBIT_OK
+    assert lb.lowbit_hbm_read(FAKE, 24, FAKE) == E_ARG          # not a multiple of 16
+    assert lb.lowbit_hbm_read(FAKE, -16, FAKE) == E_ARG
+    assert lb.lowbit_hbm_read(None, 16, FAKE) == E_ARG
+    assert lb.lowbit_hbm_read(FAKE, 16, None) == E_ARG
+    assert lb.lowbit_hbm_read(FAKE + 8, 16, FAKE) == E_ARG       # buffer not 16-byte aligned
+    assert lb.lowbit_hbm_read(FAKE, 16, FAKE + 2) == E_ARG       # sink not 4-byte aligned
