@@ -15,7 +15,8 @@
 // arithmetic, same fixed-order reduction).
 //
 // MI355X design:
-//   * Grid = one workgroup per compute unit, all resident at once.  Each
+//   * Grid = one workgroup per compute unit, all resident at once (a
+//     cooperative launch: the runtime guarantees it or refuses).  Each
 //     workgroup has 9 waves: waves 0..7 ("compute waves") stream weights and
 //     run the MFMAs; wave 8 (the "control wave") never loads weights.  It
 //     waits for the previous stage, stages activations into LDS with
@@ -388,8 +389,13 @@ hipError_t launch_chain_t(const ChainArgs &a, int grid, size_t lds, hipStream_t 
     auto k = gemv_chain_kernel<G, ASYM, MR>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    k<<<dim3(grid), dim3(kChainThreads), lds, s>>>(a);
-    return hipGetLastError();
+    // a cooperative launch: the runtime starts every workgroup at once or
+    // refuses the launch (hipErrorCooperativeLaunchTooLarge), so the waits
+    // never depend on a workgroup that is not running; it can be captured
+    // in a graph
+    ChainArgs args = a;
+    void *kargs[] = {&args};
+    return hipLaunchCooperativeKernel((const void *)k, dim3(grid), dim3(kChainThreads), kargs, (unsigned)lds, s);
 }
 
 template <int G, bool ASYM, int MR>

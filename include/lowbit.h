@@ -329,7 +329,10 @@ int lowbit_gemv_chain_init(lowbit_gemv_chain *chain, int fmt, int M, int group_s
                            const lowbit_gemv_problem *problems, const int *stage_of,
                            unsigned spin_limit, void *buf, size_t buf_bytes, void *stream);
 
-/* Enqueue one run of the chain on `stream`. */
+/* Enqueue one run of the chain on `stream`, as a cooperative launch: every
+ * workgroup is resident at once, or the launch is refused (LOWBIT_E_HIP with
+ * hipErrorCooperativeLaunchTooLarge, e.g. when other work holds the compute
+ * units' resources) and nothing runs.  Capturable in a graph. */
 int lowbit_gemv_chain_run(const lowbit_gemv_chain *chain, void *stream);
 
 /* Read the chain's error word (0 = every wait so far was met) into *error;
