@@ -535,13 +535,16 @@ void moe_lut3_gemm_lds_kernel(const int32_t *expert_offsets, const int32_t *bloc
             sv[u] = __builtin_amdgcn_raw_buffer_load_b8(srs, ok ? (uint32_t)ar * (uint32_t)k_chunks + (uint32_t)c
                                                             : kBufferOob, 0, 0);
         }
-        //    Then the pass's first D - 1 weight steps.
+        //    Then the pass's first D - 1 weight steps (kept after the staging
+        //    loads: the wait below counts on that order).
+        __builtin_amdgcn_sched_barrier(0);
         WSlot wsl[D];
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) load_w(wsl[d], d);
+        __builtin_amdgcn_sched_barrier(0);
         //    Every load issued before them has landed (the ring's may be in
         //    flight): scales to LDS, and publish rows, scales and slot ids.
-        constexpr int kRing = (D - 1) * 3 * kGSPW;             // loads per ring step: codes, codebooks, exponents
+        constexpr int kRing = (D - 1) * 3 * kGSPW;             // the ring's loads: D - 1 steps x (codes, codebooks, exponents)
         static_assert(kRing < 64, "vmcnt range");
         __builtin_amdgcn_s_waitcnt((kRing & 15) | ((kRing >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(kRing)
         __builtin_amdgcn_sched_barrier(0);
