@@ -168,8 +168,10 @@ size_t lowbit_workspace_bytes(int op, int fmt, int M, int N, int K, int group_si
  *   y[m][n] = sum_k x[m][k] * (q[n][k] - z) * s[n][k / group_size]
  * accumulated in fp32, rounded to nearest even into fp16.
  *   fmt     : LOWBIT_W4_SYM, LOWBIT_W4_ASYM or LOWBIT_UINT(bits, asym)
- *             (b-bit codes: M * round_up(K, 512) halfs of x must fit 160 KiB
- *             of LDS and K <= 16384, else LOWBIT_E_UNSUPPORTED)
+ *             (b-bit codes: K <= 16384, and M * round_up(2K, 1024) bytes of x
+ *             -- 2.5K per row for M = 1 symmetric -- plus 4, 8 or 16 KiB of
+ *             partial sums for M = 1, <= 8, <= 16 must fit 160 KiB of LDS;
+ *             else LOWBIT_E_UNSUPPORTED.  At K = 16384: M <= 4)
  *   M       : 0..16 rows (tokens); larger M -> LOWBIT_E_UNSUPPORTED (use lowbit_gemm)
  *   packed  : blob from lowbit_pack_weights(fmt, 1, N, K, group_size, ...)
  *   x       : f16 [M][K], 16-byte aligned

@@ -240,6 +240,7 @@ def test_uint_formats_host_rules():
     assert lb.lowbit_pack_weights(f3, 1, 64, 512, 32, FAKE, FAKE, None, FAKE, nb) == E_ARG    # asym needs zeros
     assert lb.lowbit_gemv(f3, 17, 64, 512, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS
     assert lb.lowbit_gemv(f3, 16, 64, 16384, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS            # x over the LDS budget
+    assert lb.lowbit_gemv(f3, 5, 64, 16384, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS             # 160 KiB of x + partial sums
     assert lb.lowbit_gemv(f3, 1, 64, 16384 + 128, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS       # > 8 tiles per wave
     assert lb.lowbit_gemm(f3, 64, 64, 512, 32, FAKE, FAKE, lb.LOWBIT_BF16, FAKE, lb.LOWBIT_BF16, None, 0) == E_UNS
     assert lb.lowbit_gemv_w4a8(f3, 1, 64, 512, 32, FAKE, FAKE, FAKE, None, 0) == E_UNS

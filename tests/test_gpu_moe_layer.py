@@ -246,14 +246,16 @@ def test_moe_layer_intermediate_codes():
     assert np.all((np.abs(ordinal(a) - ordinal(ref["aq"])) <= 1) | sub)
 
 
-@pytest.mark.parametrize("T,E,top_k,H,I,local", [(64, 16, 4, 512, 256, False), (40, 8, 2, 3072, 128, True)])
+@pytest.mark.parametrize("T,E,top_k,H,I,local", [(64, 16, 4, 512, 256, False), (40, 8, 2, 3072, 128, True),
+                                                   (24, 4, 2, 4864, 128, False)])
 def test_moe_gemm_silu_quant_equals_two_stages(T, E, top_k, H, I, local):
     """lowbit_moe_gemm_silu_quant (the gate/up GEMM with SiLU(gate) * up ->
     MXFP8 in its epilogue) writes the bytes of lowbit_moe_gemm followed by
     lowbit_moe_silu_mul_quant, every slot row included (outputs start as a
     0x55 pattern), and its codes meet the oracle chain as the two stages do.
     The second case stages 16 rows per pass (K = 3072) and has non-local
-    experts (codes 0, scale byte 127)."""
+    experts (codes 0, scale byte 127); the third is the longest K the fused
+    form accepts (4864: 16 staged rows fill the 80 KB LDS window)."""
     bm = 16
     S = T * top_k
     d13, _, x, topk, _ = _layer_case(T, E, top_k, H, I, seed=E + H)

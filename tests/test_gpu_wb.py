@@ -100,6 +100,8 @@ def test_uint4_packs_to_the_int4_blob():
     (3, 96, 2048, 128, True),
     (8, 64, 4096, 64, False),
     (12, 48, 1024, 32, True),          # four accumulators per lane (M > 8)
+    (1, 64, 16384, 128, False),        # the longest K the b-bit GEMV accepts
+    (4, 48, 16384, 32, True),          # longest K with the most tokens whose x and partial sums fit the LDS
 ])
 def test_wb_gemv_parity(bits, M, N, K, G, asym):
     w = _w(N, K, G, bits, asym, part=M)
