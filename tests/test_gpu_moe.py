@@ -52,6 +52,7 @@ def test_lut3_pack_roundtrip(E, N, K):
 @pytest.mark.parametrize("T,E,top_k,bm,use_map", [
     (1, 8, 2, 16, False), (3, 4, 2, 16, True), (256, 128, 8, 16, False), (256, 128, 8, 32, True),
     (2048, 64, 8, 16, False), (7, 1024, 6, 16, False), (50, 1, 1, 48, False), (0, 16, 8, 16, False),
+    (20, 4, 2, 4096, False), (5, 1024, 4, 4096, True),    # the largest block the align accepts
 ])
 def test_moe_align_bitexact(T, E, top_k, bm, use_map):
     r = np.random.default_rng(T * 7 + E)
@@ -68,6 +69,7 @@ def test_moe_align_bitexact(T, E, top_k, bm, use_map):
     assert np.array_equal(ids.cpu().numpy()[:P], ref_ids)
     assert np.all(ids.cpu().numpy()[P:] == T * top_k)
     assert np.array_equal(blk.cpu().numpy()[:P // bm], ref_blk)
+    assert np.all(blk.cpu().numpy()[P // bm:] == -1)        # blocks past the padded length: no expert
     o = offs.cpu().numpy()
     counts = np.bincount(topk.ravel(), minlength=E) if T else np.zeros(E, np.int64)
     assert o[0] == 0 and o[E] == P
