@@ -86,8 +86,12 @@ def test_silu_mul_quant_bitexact(R, I):
     assert np.array_equal(q, rq)
 
 
-@pytest.mark.parametrize("T,top_k,H", [(3, 2, 64), (256, 8, 2048)])
+@pytest.mark.parametrize("T,top_k,H", [(3, 2, 64), (256, 8, 2048), (5, 10, 4160), (7, 1, 2112)])
 def test_moe_combine(T, top_k, H):
+    """Router-weighted sum over the top-k slots (top_k = 1, 2, 8 and 10), for
+    row widths whose 8-column lanes fill whole workgroups (H = 2048) or end
+    inside one (H = 64, 2112, 4160), against the oracle within the bar.  A
+    one-hot weight returns its row exactly."""
     r = np.random.default_rng(T + H)
     out = _bf16(r.standard_normal((T * top_k, H)))
     w = r.dirichlet(np.ones(top_k), T).astype(np.float32)
