@@ -299,11 +299,14 @@ def read_ceiling(torch, lb, stream, reps=20):
 
 KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/gemv_w4.hip", "bit_weight_only_pack_amd/csrc/gemv_tile.hpp",
                   "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
+MOE_KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/moe_lut3.hip", "bit_weight_only_pack_amd/csrc/moe_align.hpp",
+                      "bit_weight_only_pack_amd/csrc/mxfp8.hpp", "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
 
 
 def kernel_source_hash(paths=KERNEL_SOURCES):
-    """sha256 over the sources of the decode GEMV kernels (recorded with the
-    counter profiles, so a profile of an older kernel is not reported)."""
+    """sha256 over the sources of a kernel (default: the decode GEMV's),
+    recorded with its counter profile, so a profile of an older kernel is not
+    reported."""
     import hashlib
     h = hashlib.sha256()
     for p in paths:
@@ -312,7 +315,7 @@ def kernel_source_hash(paths=KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def read_traffic(name):
+def read_traffic(name, paths=KERNEL_SOURCES):
     """HBM bytes per launch from a committed rocprofv3 counter profile
     (FETCH_SIZE and WRITE_SIZE runs, calibrated), and the profile's name;
     (None, reason) when there is none or it was taken on other kernel
@@ -328,7 +331,7 @@ def read_traffic(name):
             src = line.split(":")[1].strip()
     if value is None:
         return None, "no counter profile"
-    if src != kernel_source_hash():
+    if src != kernel_source_hash(paths):
         return None, "profiles/%s was taken on other kernel sources" % name
     return value, "profiles/%s (rocprofv3 FETCH_SIZE and WRITE_SIZE runs, calibrated)" % name
 
@@ -866,6 +869,7 @@ def bench_moe(args, torch, lb, synth):
     layer_bytes = sum(b for _, _, b, in_layer in steps if in_layer)
     gbps = layer_bytes / (ms * 1e-3) / 1e9
     gu_gbps = nbytes["gate_up_silu"] / (us["gate_up_silu"] * 1e-6) / 1e9
+    moe_traffic, moe_traffic_source = read_traffic("moe_lut3_layer_traffic.txt", MOE_KERNEL_SOURCES)
     out = {"metric": "3-bit LUT MoE layer (MXFP8 in, align, gate/up with SiLU*up MXFP8, down, combine) "
                      "effective HBM GB/s",
            "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": 2 * args.steps,
@@ -879,7 +883,8 @@ def bench_moe(args, torch, lb, synth):
            "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
            "gpu_ms_per_step": round(gpu_ms, 4),
            "roofline": {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": moe_traffic,
+                        "traffic_source": moe_traffic_source,
                         "kernel": "moe_lut3_gemm_lds_kernel (gate/up, SiLU*up MXFP8 epilogue)",
                         "bytes_per_launch": nbytes["gate_up_silu"], "avg_launch_us": round(us["gate_up_silu"], 3)},
            "per_kernel_us": {k: round(v, 2) for k, v in us.items()},
