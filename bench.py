@@ -510,6 +510,8 @@ def bench_decode_asym(args, torch, lb, synth):
     ach = nb / (us * 1e-6) / 1e9
     kname = ("gemv_w4_v2_single<G=32,asym,MR=1,T=4>" if args.layout == "stacked"
              else "gemv_w4_v2_kernel<G=32,asym,MR=1,T=4,NP=4>")
+    traffic, traffic_source = (read_traffic("w4_gemv_asym_step_traffic.txt") if args.layout == "stacked"
+                               else (None, "not taken for the batched layout"))
     return {"metric": "W4 asymmetric G=32 decode step effective HBM GB/s (M=1; M=2, 4, 8 in per_M)",
             "value": r1["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": r1["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -519,7 +521,7 @@ def bench_decode_asym(args, torch, lb, synth):
                        "group_size": G, "layout": args.layout},
             "tokens_per_s": r1["tokens_per_s"],
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
+                         "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_source": traffic_source,
                          "kernel": "%s (the %s launches, M=1)" % (kname, ", ".join(names)),
                          "bytes_per_launch": round(nb), "avg_launch_us": round(us, 3),
                          "timing": "HIP events on the launch stream around graph replays of this kernel's "
