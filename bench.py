@@ -299,6 +299,10 @@ def read_ceiling(torch, lb, stream, reps=20):
 
 KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/gemv_w4.hip", "bit_weight_only_pack_amd/csrc/gemv_tile.hpp",
                   "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
+W4A8_KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/gemv_w4a8.hip", "bit_weight_only_pack_amd/csrc/gemv_tile.hpp",
+                       "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
+WB_KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/gemv_wb.hip", "bit_weight_only_pack_amd/csrc/gemv_tile.hpp",
+                     "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
 MOE_KERNEL_SOURCES = ("bit_weight_only_pack_amd/csrc/moe_lut3.hip", "bit_weight_only_pack_amd/csrc/moe_align.hpp",
                       "bit_weight_only_pack_amd/csrc/mxfp8.hpp", "bit_weight_only_pack_amd/csrc/lowbit_internal.hpp")
 
@@ -573,6 +577,8 @@ def bench_decode_w4a8(args, torch, lb, synth):
     ach = bpl / (avg_us * 1e-6) / 1e9
     kname = ("gemv_w4a8_single<G=32,asym,MR=1,T=4,FUSED>" if args.layout == "stacked"
              else "gemv_w4a8_batch<G=32,asym,MR=1,T=4,FUSED>")
+    traffic, traffic_source = (read_traffic("w4a8_gemv_decode_step_traffic.txt", W4A8_KERNEL_SOURCES)
+                               if args.layout == "stacked" else (None, "not taken for the batched layout"))
     out = {"metric": "W4A8 (dynamic INT8 activations) decode step effective HBM GB/s",
            "value": res["M=1"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": res["M=1"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -585,7 +591,7 @@ def bench_decode_w4a8(args, torch, lb, synth):
            "tokens_per_s": res["M=1"]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res["M=1"]["GBps"] / HBM_PEAK_GBPS, 2),
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_source": traffic_source,
                         "kernel": "%s (the %s launches, M=1)" % (kname, ", ".join(names)),
                         "bytes_per_launch": round(bpl), "avg_launch_us": round(avg_us, 3),
                         "timing": "HIP events on the launch stream around graph replays of this kernel's "
@@ -668,6 +674,9 @@ def bench_decode_bits(args, torch, lb, synth):
     kname = ("gemv_wb_single<b=%d,G=128,sym,MR=1,T=4>" if args.layout == "stacked"
              else "gemv_wb_batch<b=%d,G=128,sym,MR=1,T=4>") % ref["bits"]
     key = "b=%d" % ref["bits"]
+    traffic, traffic_source = (read_traffic("wb_gemv_decode_step_traffic.txt", WB_KERNEL_SOURCES)
+                               if args.layout == "stacked" and ref["bits"] == 3
+                               else (None, "taken for b = 3 with the stacked layout only"))
     out = {"metric": "b-bit decode step effective HBM GB/s and tokens/s at 8B shapes", "value": res[key]["GBps"],
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": res[key]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -679,7 +688,7 @@ def bench_decode_bits(args, torch, lb, synth):
            "tokens_per_s": res[key]["tokens_per_s"],
            "pct_of_hbm_peak": round(100 * res[key]["GBps"] / HBM_PEAK_GBPS, 2),
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "traffic_source": "not taken",
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_source": traffic_source,
                         "kernel": "%s (the %s launches)" % (kname, ", ".join(names)),
                         "bytes_per_launch": round(bpl), "avg_launch_us": round(avg_us, 3),
                         "timing": "HIP events on the launch stream around graph replays of this kernel's "
